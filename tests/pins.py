@@ -1,0 +1,344 @@
+"""Pins for the fp64 oracle: facts fixed by the pages or by mathematics.
+
+Each pin takes a module ``o`` that exposes the oracle's functions, so the same
+pins run on the real oracle (tests/test_oracle_pins.py) and on copies with a
+planted mistake (tests/test_oracle_mutants.py).  Citations name sections of
+"RidgeFill: Training-Free Late-Layer Cache Fill for Faster Prefill".
+"""
+import json
+import math
+import os
+
+import numpy as np
+
+import workloads
+from tests import brute
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _rng(seed):
+    return np.random.default_rng(seed)
+
+
+def _bits(a):
+    return workloads.f32_to_bf16_bits(np.asarray(a, dtype=np.float32))
+
+
+# ---------------------------------------------------------------- fill: rows
+
+def pin_fill_rows_partition(o):
+    """Section 2.1: each prefix row is exact or filled and the tail is exact,
+    so filled and exact rows partition the prompt."""
+    for name in ("tiny", "27b_120k", "8b_ragged_host"):
+        s = workloads.spec(name)
+        e = workloads.exact_row_list(s)
+        f = o.fill_row_set(s.n_rows, e)
+        assert np.all(np.diff(f) > 0), "fill rows must ascend"
+        assert len(set(f.tolist()) & set(e.tolist())) == 0
+        assert len(f) + len(set(e.tolist())) == s.n_rows
+        start = 0
+        for n in s.prompt_lens:
+            tail = set(range(start + n - s.tail, start + n))
+            assert not (tail & set(f.tolist())), "a tail row was filled"
+            start += n
+    # small case against Python sets, exact rows given unsorted and repeated
+    e = [9, 3, 3, 17, 0]
+    f = o.fill_row_set(20, np.array(e))
+    assert f.tolist() == sorted(set(range(20)) - set(e))
+
+
+# ---------------------------------------------------------------- fill: map
+
+def pin_identity_map_is_exact_kv(o):
+    """Sections 6-7: the identity fill (A = I, b = 0, POP's fill) makes each
+    skipped layer project the unchanged state, so the fill equals the exact
+    layer's cache write from the same input, bit for bit in fp64."""
+    g = _rng(1)
+    n, d, hd, nkv = 7, 64, 16, 2
+    x = o.bf16_bits_to_f64(_bits(g.standard_normal((n, d))))
+    gamma = 1 + 0.1 * g.standard_normal(d)
+    wk = g.standard_normal((nkv * hd, d)) / 8
+    wv = g.standard_normal((nkv * hd, d)) / 8
+    pos = g.integers(0, 5000, n)
+    y = o.predicted_input(x, np.eye(d), np.zeros(d))
+    assert np.array_equal(y, x)
+    k1, v1 = o.fill_layer(x, np.eye(d), np.zeros(d), gamma, wk, wv, pos, 1e4, hd, 1e-5)
+    k2, v2 = o.layer_kv(x, gamma, wk, wv, pos, 1e4, hd, 1e-5)
+    assert np.array_equal(k1, k2) and np.array_equal(v1, v2)
+
+
+def pin_map_orientation(o):
+    """Section 2.2: A_l has d_out rows and d_in columns and x_hat = A_l x_S + b_l.
+    A cyclic-shift matrix must move feature k to output (k+1) mod d, and a wide
+    map [I | 0] (d_in > d_out, as on Flash-Next) must keep the leading d_out
+    features; both are checked against numpy indexing."""
+    g = _rng(2)
+    d = 12
+    x = g.standard_normal((5, d))
+    perm = (np.arange(d) - 1) % d         # output n reads feature n-1
+    a = np.zeros((d, d))
+    a[np.arange(d), perm] = 1.0
+    b = g.standard_normal(d)
+    y = o.predicted_input(x, a, b)
+    assert np.allclose(y, np.take(x, perm, axis=1) + b, rtol=0, atol=1e-15)
+    d_in, d_out = 20, 8
+    wide = np.zeros((d_out, d_in))
+    wide[np.arange(d_out), np.arange(d_out)] = 1.0
+    xw = g.standard_normal((3, d_in))
+    yw = o.predicted_input(xw, wide, np.zeros(d_out))
+    assert yw.shape == (3, d_out)
+    assert np.array_equal(yw, xw[:, :d_out])
+
+
+def pin_bias_only_map(o):
+    """Section 2.2: with A = 0 every prediction is b; then every filled row's V is
+    the same vector and each K is that one key rotated to the row's position
+    (the rotation written as complex multiplication)."""
+    g = _rng(3)
+    d, hd, nkv, n = 32, 8, 2, 6
+    bvec = g.standard_normal(d)
+    gamma = 1 + 0.1 * g.standard_normal(d)
+    wk = g.standard_normal((nkv * hd, d))
+    wv = g.standard_normal((nkv * hd, d))
+    pos = np.array([0, 1, 7, 100, 4095, 65535])
+    x = g.standard_normal((n, d))
+    k, v = o.fill_layer(x, np.zeros((d, d)), bvec, gamma, wk, wv, pos, 1e4, hd, 1e-5)
+    assert np.allclose(v, v[0][None, :], rtol=0, atol=1e-13)
+    k0 = k[0]  # position 0: unrotated
+    half = hd // 2
+    for r in range(n):
+        for h in range(nkv):
+            z0 = k0[h * hd:h * hd + half] + 1j * k0[h * hd + half:(h + 1) * hd]
+            z = z0 * np.exp(1j * pos[r] * 1e4 ** (-2.0 * np.arange(half) / hd))
+            got = k[r, h * hd:h * hd + half] + 1j * k[r, h * hd + half:(h + 1) * hd]
+            assert np.allclose(got, z, rtol=1e-12, atol=1e-12)
+
+
+# ---------------------------------------------------------------- fill: norm
+
+def pin_rmsnorm_closed_forms(o):
+    """The layer's RMSNorm (section 2.2 "At inference"): for a constant row c the
+    output is gamma * c / sqrt(c^2 + eps); for any row, mean((h/gamma)^2) equals
+    m / (m + eps) with m = mean(y^2); with eps = 0 it is scale free."""
+    g = _rng(4)
+    d = 40
+    gamma = 1 + 0.1 * g.standard_normal(d)
+    for c in (0.3, -2.0, 17.0):
+        h = o.rms_norm(np.full((1, d), c), gamma, 1e-5)
+        assert np.allclose(h[0], gamma * c / math.sqrt(c * c + 1e-5), rtol=1e-14, atol=0)
+    y = g.standard_normal((9, d)) * g.uniform(0.1, 10, (9, 1))
+    eps = 0.37
+    h = o.rms_norm(y, gamma, eps)
+    m = np.mean(y * y, axis=1)
+    assert np.allclose(np.mean((h / gamma) ** 2, axis=1), m / (m + eps), rtol=1e-13)
+    h1 = o.rms_norm(y, gamma, 0.0)
+    h2 = o.rms_norm(5.5 * y, gamma, 0.0)
+    assert np.allclose(h1, h2, rtol=1e-13, atol=1e-14)
+
+
+def pin_one_hot_layer_kv(o):
+    """Layer cache write for a scaled one-hot input c e_j (sections 2.1-2.2): the
+    norm gives gamma_j c / sqrt(c^2/d + eps) on feature j only, so V is that
+    number times column j of W_v, and at position 0 K is it times column j of
+    W_k; V does not depend on the position."""
+    g = _rng(5)
+    d, hd, nkv = 24, 8, 3
+    gamma = 1 + 0.1 * g.standard_normal(d)
+    wk = g.standard_normal((nkv * hd, d))
+    wv = g.standard_normal((nkv * hd, d))
+    for j, c in ((0, 1.5), (5, -0.25), (23, 40.0)):
+        hin = np.zeros((2, d))
+        hin[:, j] = c
+        k, v = o.layer_kv(hin, gamma, wk, wv, np.array([0, 12345]), 5e5, hd, 1e-5)
+        s = gamma[j] * c / math.sqrt(c * c / d + 1e-5)
+        assert np.allclose(v[0], s * wv[:, j], rtol=1e-13, atol=1e-13)
+        assert np.allclose(v[1], v[0], rtol=0, atol=0)
+        assert np.allclose(k[0], s * wk[:, j], rtol=1e-13, atol=1e-13)
+        assert not np.allclose(k[1], k[0])
+
+
+# ---------------------------------------------------------------- fill: rope
+
+def pin_rope_is_complex_rotation(o):
+    """Rotary embedding (section 2.2; section 6.6 "rotated at their own
+    positions"): in each head, (k_j, k_{j+hd/2}) as the complex number
+    k_j + i k_{j+hd/2} is multiplied by exp(i pos theta^(-2j/hd))."""
+    g = _rng(6)
+    for hd, theta in ((64, 1e4), (128, 5e5)):
+        n, nkv = 5, 3
+        k = g.standard_normal((n, nkv * hd))
+        pos = np.array([0, 1, 511, 65535, 122879])
+        out = o.rope(k, pos, theta, hd)
+        half = hd // 2
+        freq = theta ** (-2.0 * np.arange(half) / hd)
+        for r in range(n):
+            for h in range(nkv):
+                z = (k[r, h * hd:h * hd + half] + 1j * k[r, h * hd + half:(h + 1) * hd]) \
+                    * np.exp(1j * pos[r] * freq)
+                assert np.allclose(out[r, h * hd:h * hd + half], z.real, rtol=1e-12, atol=1e-12)
+                assert np.allclose(out[r, h * hd + half:(h + 1) * hd], z.imag, rtol=1e-12, atol=1e-12)
+
+
+def pin_rope_invariants(o):
+    """Rotations keep each pair's norm, position 0 is the identity, the dot
+    product of two rotated keys depends only on the position difference, and
+    pair 0 turns by exactly pos radians."""
+    g = _rng(7)
+    hd, theta = 128, 5e5
+    half = hd // 2
+    a = g.standard_normal((1, 2 * hd))
+    c = g.standard_normal((1, 2 * hd))
+    assert np.array_equal(o.rope(a, np.array([0]), theta, hd), a)
+    ra = o.rope(a, np.array([9999]), theta, hd)
+    for h in range(2):
+        s = slice(h * hd, (h + 1) * hd)
+        n0 = a[0, s][:half] ** 2 + a[0, s][half:] ** 2
+        n1 = ra[0, s][:half] ** 2 + ra[0, s][half:] ** 2
+        assert np.allclose(n0, n1, rtol=1e-12)
+    for m, n, sh in ((3, 10, 1000), (0, 70000, 52879)):
+        d1 = np.sum(o.rope(a, np.array([m]), theta, hd)[0, :hd] * o.rope(c, np.array([n]), theta, hd)[0, :hd])
+        d2 = np.sum(o.rope(a, np.array([m + sh]), theta, hd)[0, :hd]
+                    * o.rope(c, np.array([n + sh]), theta, hd)[0, :hd])
+        assert abs(d1 - d2) < 1e-9 * (1 + abs(d1))
+    e = np.zeros((1, hd))
+    e[0, 0] = 1.0
+    r = o.rope(e, np.array([2]), theta, hd)
+    assert abs(r[0, 0] - math.cos(2.0)) < 1e-15 and abs(r[0, half] - math.sin(2.0)) < 1e-15
+
+
+# ---------------------------------------------------------------- fill: whole
+
+def pin_brute_force_tiny(o):
+    """A separately written pure-Python loop version of the whole fill agrees
+    with the vectorised oracle on a few rows of the tiny workload, every layer,
+    including a large position."""
+    w = workloads.make(workloads.spec("tiny"))
+    s = w.spec
+    rows = np.array([0, 1, 255, 447])
+    ref = o.fill_workload(w, rows=rows)
+    for l in range(s.n_late):
+        for i, r in enumerate(rows):
+            kb, vb = brute.filled_row(w.x[r].tolist(), w.map_a[l].tolist(), w.map_b[l].tolist(),
+                                      w.gamma[l].tolist(), w.w_k[l].tolist(), w.w_v[l].tolist(),
+                                      int(w.positions[r]), s.rope_theta, s.head_dim, s.rms_eps)
+            kr, vr = ref[l][0][i], ref[l][1][i]
+            assert np.max(np.abs(np.array(kb) - kr)) <= 1e-12 * np.max(np.abs(kr))
+            assert np.max(np.abs(np.array(vb) - vr)) <= 1e-12 * np.max(np.abs(vr))
+
+
+def pin_fill_row_independence(o):
+    """Section 2.1: a filled row's input comes straight from its own split state,
+    so its K/V do not depend on which other rows are filled with it."""
+    w = workloads.make(workloads.spec("tiny", n_late=2))
+    rows = np.array([3, 40, 41, 300])
+    full = o.fill_workload(w, rows=rows)
+    for i, r in enumerate(rows):
+        one = o.fill_workload(w, rows=np.array([r]))
+        for l in full:
+            assert np.allclose(one[l][0][0], full[l][0][i], rtol=1e-13, atol=1e-13)
+            assert np.allclose(one[l][1][0], full[l][1][i], rtol=1e-13, atol=1e-13)
+
+
+# ---------------------------------------------------------------- ridge
+
+def _linear_data(seed, n, d_in, d_out, noise=0.0):
+    g = _rng(seed)
+    x = g.standard_normal((n, d_in)) * g.uniform(0.2, 3.0, d_in) + g.standard_normal(d_in)
+    m = g.standard_normal((d_out, d_in))
+    c = g.standard_normal(d_out)
+    y = x @ m.T + c + noise * g.standard_normal((n, d_out))
+    return x, y, m, c
+
+
+def pin_ridge_recovers_linear_map(o):
+    """Section 2.2: on noise-free data from a known affine map, the ridge map's
+    error falls monotonically to zero as lambda goes to zero."""
+    x, y, m, c = _linear_data(8, 200, 16, 12)
+    errs = []
+    for lam in (1e-1, 1e-3, 1e-6, 1e-12):
+        a, b = o.ridge_fit(x, y, lam)
+        errs.append(np.linalg.norm(a - m) / np.linalg.norm(m))
+        if lam == 1e-12:
+            assert np.allclose(b, c, rtol=0, atol=1e-8)
+    assert all(e1 > e2 for e1, e2 in zip(errs, errs[1:]))
+    assert errs[-1] < 1e-8
+
+
+def pin_ridge_svd_form(o):
+    """Section 2.2 at an intermediate lambda: with Xc = U S V^T and Y = X M^T + c
+    the solution is A^T = V diag(s^2/(s^2+alpha)) V^T M^T, alpha = lambda sum(s^2)/d_in
+    (the trace of the centred Gram matrix), and b = mu_Y - A mu_X."""
+    x, y, m, c = _linear_data(9, 90, 10, 7)
+    lam = 0.03
+    xc = x - x.mean(axis=0)
+    _, sv, vt = np.linalg.svd(xc, full_matrices=False)
+    alpha = lam * np.sum(sv ** 2) / x.shape[1]
+    at = vt.T @ np.diag(sv ** 2 / (sv ** 2 + alpha)) @ vt @ m.T
+    a, b = o.ridge_fit(x, y, lam)
+    assert np.allclose(a, at.T, rtol=1e-10, atol=1e-11)
+    assert np.allclose(b, y.mean(axis=0) - at.T @ x.mean(axis=0), rtol=1e-10, atol=1e-10)
+
+
+def pin_ridge_running_sums(o):
+    """Section 2.2 "Fitting": sums accumulated one document at a time give the same
+    map as one solve on all rows, and a new lambda needs only a new solve."""
+    x, y, _, _ = _linear_data(10, 300, 14, 9, noise=0.5)
+    acc = o.RidgeSums(14, 9)
+    for a0, a1 in ((0, 17), (17, 150), (150, 151), (151, 300)):
+        acc.add(x[a0:a1], y[a0:a1])
+    for lam in (0.03, 0.001):
+        a1, b1 = acc.solve(lam)
+        a2, b2 = o.ridge_fit(x, y, lam)
+        assert np.allclose(a1, a2, rtol=1e-9, atol=1e-11)
+        assert np.allclose(b1, b2, rtol=1e-9, atol=1e-11)
+
+
+def pin_ridge_penalty_scale(o):
+    """Section 2.2 "The penalty": alpha = lambda tr(X^T X)/d_in scales with the
+    inputs, so scaling X by c scales A by 1/c and leaves b and every prediction
+    unchanged (a fixed alpha would not)."""
+    x, y, _, _ = _linear_data(11, 120, 8, 5, noise=1.0)
+    a1, b1 = o.ridge_fit(x, y, 0.2)
+    a2, b2 = o.ridge_fit(7.0 * x, y, 0.2)
+    assert np.allclose(a2, a1 / 7.0, rtol=1e-10, atol=1e-13)
+    assert np.allclose(b1, b2, rtol=1e-10, atol=1e-12)
+    assert np.allclose(x @ a1.T + b1, (7.0 * x) @ a2.T + b2, rtol=1e-10, atol=1e-10)
+
+
+def pin_ridge_raw_form(o):
+    """The uncentred form W = (X^T X + lambda I)^(-1) X^T Y tends to the least
+    squares solution (numpy lstsq) as lambda -> 0 and has no offset."""
+    g = _rng(12)
+    x = g.standard_normal((80, 6))
+    y = g.standard_normal((80, 4))
+    a, b = o.ridge_fit_raw(x, y, 1e-13)
+    w_ls = np.linalg.lstsq(x, y, rcond=None)[0]
+    assert np.allclose(a, w_ls.T, rtol=1e-9, atol=1e-11)
+    assert np.array_equal(b, np.zeros(4))
+    a2, _ = o.ridge_fit_raw(x, y, 5.0)
+    assert np.allclose(a2.T, np.linalg.solve(x.T @ x + 5.0 * np.eye(6), x.T @ y), rtol=1e-12)
+
+
+# ---------------------------------------------------------------- ceilings
+
+def pin_printed_ceilings(o):
+    """Values the pages print (tests/golden/ceilings.json)."""
+    with open(os.path.join(GOLDEN, "ceilings.json")) as f:
+        gold = json.load(f)
+    for c in gold["layer_ceiling"]["cases"]:
+        v = o.layer_ceiling(c["L"], c["S"], c["T"], c["N"])
+        assert abs(v - c["printed"]) <= 0.005 + 1e-12, (c, v)
+    for c in gold["mac_ceiling"]["cases"]:
+        v = o.mac_ceiling(c["skipped"])
+        assert abs(v - c["printed"]) <= 0.005 + 1e-12, (c, v)
+
+
+FILL_PINS = [pin_fill_rows_partition, pin_identity_map_is_exact_kv, pin_map_orientation,
+             pin_bias_only_map, pin_rmsnorm_closed_forms, pin_one_hot_layer_kv,
+             pin_rope_is_complex_rotation, pin_rope_invariants, pin_brute_force_tiny,
+             pin_fill_row_independence]
+RIDGE_PINS = [pin_ridge_recovers_linear_map, pin_ridge_svd_form, pin_ridge_running_sums,
+              pin_ridge_penalty_scale, pin_ridge_raw_form]
+CEILING_PINS = [pin_printed_ceilings]
+ALL_PINS = FILL_PINS + RIDGE_PINS + CEILING_PINS

@@ -1,0 +1,95 @@
+"""Planted mistakes in copies of the oracle must each fail some pin (CPU only).
+
+Every mutant is the oracle's own source with one plausible mistake edited in
+(a transposed operand, a dropped term, a wrong sign or index, a wrong axis),
+executed as a fresh module.  The real oracle is never modified.
+"""
+import os
+import types
+
+import pytest
+
+from tests import pins
+
+ORACLE_DIR = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "oracle")
+FILES = ("fill.py", "ridge.py", "ceiling.py")
+
+MUTANTS = {
+    # the map
+    "map_transposed": ("fill.py", [("return x_s @ a.T + b", "return x_s @ a + b")]),
+    "map_bias_dropped": ("fill.py", [("return x_s @ a.T + b", "return x_s @ a.T")]),
+    "map_bias_sign": ("fill.py", [("return x_s @ a.T + b", "return x_s @ a.T - b")]),
+    # the norm
+    "norm_eps_outside_root": ("fill.py", [(
+        "gamma * y / np.sqrt(np.mean(y * y, axis=-1, keepdims=True) + eps)",
+        "gamma * y / (np.sqrt(np.mean(y * y, axis=-1, keepdims=True)) + eps)")]),
+    "norm_one_plus_gamma": ("fill.py", [("return gamma * y / np.sqrt", "return (1 + gamma) * y / np.sqrt")]),
+    "norm_sum_not_mean": ("fill.py", [("np.mean(y * y, axis=-1", "np.sum(y * y, axis=-1")]),
+    "norm_wrong_axis": ("fill.py", [("np.mean(y * y, axis=-1", "np.mean(y * y, axis=0")]),
+    "norm_skipped": ("fill.py", [("h = rms_norm(h_in, gamma, eps)", "h = h_in")]),
+    # the projections
+    "proj_transposed": ("fill.py", [("return h @ w.T", "return h @ w")]),
+    "proj_k_v_swapped": ("fill.py", [("k = rope(project(h, w_k)", "k = rope(project(h, w_v)"),
+                                     ("v = project(h, w_v)", "v = project(h, w_k)")]),
+    # the rotation
+    "rope_freq_exponent": ("fill.py", [("-2.0 * j / head_dim", "-1.0 * j / head_dim")]),
+    "rope_direction": ("fill.py", [("[lo * c - hi * s, hi * c + lo * s]", "[lo * c + hi * s, hi * c - lo * s]")]),
+    "rope_interleaved_pairs": ("fill.py", [("lo = kh[..., :half]", "lo = kh[..., 0::2]"),
+                                           ("hi = kh[..., half:]", "hi = kh[..., 1::2]")]),
+    "rope_position_off_by_one": ("fill.py", [("np.asarray(positions, dtype=np.float64)[:, None]",
+                                              "(np.asarray(positions, dtype=np.float64)[:, None] + 1)")]),
+    "rope_on_values_too": ("fill.py", [("v = project(h, w_v)", "v = rope(project(h, w_v), positions, theta, head_dim)")]),
+    # rows and decoding
+    "rows_union_not_difference": ("fill.py", [("np.setdiff1d(", "np.union1d(")]),
+    "rows_wrong_positions": ("fill.py", [("pos = w.positions[r]\n    out = {}\n    for l in (range(s.n_late) if layers is None else layers):\n        out[l] = fill_layer",
+                                          "pos = w.positions[:len(r)]\n    out = {}\n    for l in (range(s.n_late) if layers is None else layers):\n        out[l] = fill_layer")]),
+    "bf16_decode_shift": ("fill.py", [("astype(np.uint32) << 16", "astype(np.uint32) << 15")]),
+    # the ridge fit
+    "ridge_not_centred": ("ridge.py", [("xc = x - mu_s", "xc = x")]),
+    "ridge_alpha_not_trace_scaled": ("ridge.py", [("alpha = lam * np.trace(gram) / x.shape[1]", "alpha = lam")]),
+    "ridge_offset_sign": ("ridge.py", [("b = mu_l - a @ mu_s\n    return a, b", "b = mu_l + a @ mu_s\n    return a, b")]),
+    "ridge_sums_not_centred": ("ridge.py", [("cxx = self.sxx - self.n * np.outer(mu_s, mu_s)", "cxx = self.sxx")]),
+    "ridge_raw_penalty": ("ridge.py", [("x.T @ x + lam * np.eye", "x.T @ x + lam * lam * np.eye")]),
+    # the ceilings
+    "ceiling_prefix_denominator": ("ceiling.py", [("* tail / n_rows", "* tail / (n_rows - tail)")]),
+    "ceiling_mac_sign": ("ceiling.py", [("1.0 / (1.0 - skipped_share)", "1.0 / (1.0 + skipped_share)")]),
+}
+
+PINS_FOR = {"fill.py": pins.FILL_PINS, "ridge.py": pins.RIDGE_PINS, "ceiling.py": pins.CEILING_PINS}
+
+
+def _load(target, edits):
+    ns = types.SimpleNamespace()
+    for fn in FILES:
+        with open(os.path.join(ORACLE_DIR, fn)) as f:
+            src = f.read()
+        if fn == target:
+            for old, new in edits:
+                assert src.count(old) >= 1, f"mutation anchor not found in {fn}: {old!r}"
+                src = src.replace(old, new, 1)
+        mod = types.ModuleType("oracle_mutant_" + fn[:-3])
+        exec(compile(src, os.path.join(ORACLE_DIR, fn), "exec"), mod.__dict__)
+        for k, v in vars(mod).items():
+            if not k.startswith("_"):
+                setattr(ns, k, v)
+    return ns
+
+
+def test_unmutated_copy_passes():
+    o = _load(None, [])
+    for p in pins.ALL_PINS:
+        p(o)
+
+
+@pytest.mark.parametrize("name", sorted(MUTANTS))
+def test_mutant_is_caught(name):
+    target, edits = MUTANTS[name]
+    o = _load(target, edits)
+    caught = []
+    for p in PINS_FOR[target]:
+        try:
+            p(o)
+        except Exception as e:  # an assertion or a shape error both count
+            caught.append((p.__name__, type(e).__name__))
+            break
+    assert caught, f"no pin fails for the planted mistake {name}"
