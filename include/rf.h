@@ -1,0 +1,202 @@
+/*
+ * rf.h - late-layer KV cache fill for AMD MI355X (gfx950).
+ *
+ * The operation is the cache fill of "RidgeFill: Training-Free Late-Layer
+ * Cache Fill for Faster Prefill" (arXiv 2611.09709).  Layers below a split run
+ * exactly.  For every prompt row outside the exact set (section 2.1: the tail
+ * plus chosen prefix rows) and every late layer l, the fill
+ *
+ *   1. predicts the layer's input from the split state:  y = A_l x_S + b_l
+ *      (section 2.2, the map equation);
+ *   2. applies the layer's own RMSNorm:  h = gamma_l * y / sqrt(mean(y^2) + eps)
+ *      (section 2.2, "At inference the predicted input goes through the layer's
+ *      own normalization and projections");
+ *   3. applies its key and value projections:  k = W_k h,  v = W_v h
+ *      (sections 2.1-2.2: a late layer computes only what later tokens read);
+ *   4. rotates k with RoPE at the row's own position (section 2.2; section 6.6);
+ *   5. stores bf16 k and v in that layer's cache slot for the row.  Exact rows
+ *      are not touched (section 2.1; Figure 5, first sweep).
+ *
+ * Conventions for every call
+ *  - bf16 values are passed as uint16_t bit patterns.  Matrices are row-major.
+ *  - Pointers are device memory unless the comment says HOST.  The caller owns
+ *    all memory; the library never frees a caller pointer.
+ *  - Device work is enqueued on the caller's HIP stream (`hip_stream`, a
+ *    hipStream_t; NULL = the default stream).  A call returns RF_OK once its
+ *    work is enqueued; device faults surface at the caller's next sync.
+ *  - Argument, shape and workspace errors are detected on the host before
+ *    anything is enqueued; then nothing is written.  rf_last_error() returns a
+ *    thread-local message for the last non-OK status.
+ *  - rf_fill, rf_kv_project and rf_fill_rows allocate no device memory: all
+ *    scratch comes from the caller's workspace.
+ *  - Calls that share a plan must be issued from one host thread at a time.
+ *
+ * Layouts (per late layer l, all bf16):
+ *    x       [n_rows][ld_x]               split state x_S, first d_in columns used
+ *    map_a   [d_out][d_in]                A_l, row n = output feature n (the
+ *                                         paper's orientation, section 2.2)
+ *    map_b   [d_out]                      b_l
+ *    gamma   [d_out]                      RMSNorm gain
+ *    w_k,w_v [n_kv*head_dim][d_out]       projection weights, [out][in]
+ *    k_cache, v_cache [n_slots][n_kv][head_dim]
+ *  RoPE: rotate-half.  Within each head, dimension j < head_dim/2 is paired
+ *  with j + head_dim/2 and the pair is turned by pos * theta^(-2j/head_dim).
+ */
+#ifndef RF_H
+#define RF_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum rf_status {
+  RF_OK = 0,
+  RF_E_ARG = -1,        /* null pointer, bad flag, bad count                     */
+  RF_E_SHAPE = -2,      /* a dimension the kernels do not support               */
+  RF_E_ROWS = -3,       /* RF_VALIDATE found bad fill rows, positions or slots   */
+  RF_E_WORKSPACE = -4,  /* workspace too small or misaligned                     */
+  RF_E_HIP = -5,        /* a HIP runtime call failed (message in rf_last_error)  */
+  RF_E_LINALG = -6      /* ridge system not positive definite                    */
+} rf_status;
+
+/* rf_plan_create flags */
+enum {
+  RF_MAPS_HOST = 1, /* map_a/map_b given to rf_fill are pinned HOST pointers; they are
+                       streamed to the GPU one layer at a time on a side stream,
+                       overlapped with the previous layer's fill (section 4.2:
+                       maps resident or streamed, identical outputs)          */
+  RF_VALIDATE = 2   /* rf_fill / rf_kv_project check their row indices on the
+                       device and synchronise the stream before launching     */
+};
+
+/* rf_ridge_solve / rf_ridge_fit flags */
+enum {
+  RF_RIDGE_RAW = 1 /* W = (X^T X + lambda I)^(-1) X^T Y, no centring, no offset */
+};
+
+typedef struct rf_shape {
+  int32_t d_in;        /* width of the split state x_S; multiple of 64            */
+  int32_t d_out;       /* width of a late layer's input; multiple of 256          */
+  int32_t n_late;      /* late layers (layers from the split up); >= 1            */
+  int32_t n_kv;        /* key/value heads per layer                              */
+  int32_t head_dim;    /* 64 or 128; n_kv*head_dim must be a multiple of 128     */
+  float rms_eps;       /* RMSNorm epsilon (inside the square root); >= 0         */
+  double rope_theta;   /* RoPE base theta; > 1                                   */
+  int32_t n_rows;      /* rows of x (all prompts of a batch concatenated)        */
+  int32_t n_slots;     /* slots per layer cache                                  */
+  int32_t max_pos;     /* every position lies in [0, max_pos)                    */
+} rf_shape;
+
+typedef struct rf_plan rf_plan;
+
+/* Create a plan for one shape.  Validates the shape (RF_E_SHAPE / RF_E_ARG).
+ * With RF_MAPS_HOST the plan owns two device map buffers, one side stream and
+ * four events; these are allocated here, on the current device, and released
+ * by rf_plan_destroy.  Without it the plan allocates nothing on the device. */
+rf_status rf_plan_create(const rf_shape* shape, int32_t flags, rf_plan** out);
+void rf_plan_destroy(rf_plan* plan);
+
+/* Workspace bytes rf_fill needs for n_fill rows when `layers_per_launch` late
+ * layers are processed per launch (1 .. n_late; larger means fewer, wider
+ * launches).  rf_fill uses the widest grouping the given workspace allows, so
+ * any size >= rf_fill_workspace_bytes(plan, n_fill, 1) works.  The figure
+ * includes the RoPE table that rf_fill builds when none is passed.
+ * Returns 0 for a bad argument. */
+size_t rf_fill_workspace_bytes(const rf_plan* plan, int32_t n_fill, int32_t layers_per_launch);
+
+/* Workspace bytes rf_kv_project needs (one prepared [W_k|W_v] copy per layer
+ * group plus the RoPE table if none is passed); same grouping rule. */
+size_t rf_kv_project_workspace_bytes(const rf_plan* plan, int32_t layers_per_launch);
+
+/* Fill `table` (device, fp32 [max_pos][head_dim/2][2] = (cos, sin)) with the
+ * rotation of every position and pair, angles formed in double precision.
+ * rf_fill and rf_kv_project accept this table or build it themselves. */
+rf_status rf_rope_table(const rf_plan* plan, float* table, void* hip_stream);
+
+/* Section 2.1: the rows the fill writes are all rows minus the exact set.
+ *   exact_rows  [n_exact] int32, any order, duplicates allowed, each in [0, n_rows)
+ *   fill_rows   [n_rows]  int32 out: the fill rows, ascending, in the first
+ *               *n_fill entries (the rest is left untouched)
+ *   n_fill      [1] int32 out (device)
+ *   workspace   >= rf_fill_rows_workspace_bytes(n_rows) bytes, 256-byte aligned
+ * Out-of-range exact rows are ignored by the kernels (RF_VALIDATE reports them). */
+size_t rf_fill_rows_workspace_bytes(int32_t n_rows);
+rf_status rf_fill_rows(const rf_plan* plan, const int32_t* exact_rows, int32_t n_exact,
+                       int32_t* fill_rows, int32_t* n_fill,
+                       void* workspace, size_t ws_bytes, void* hip_stream);
+
+/* The fill (steps 1-5 above) for n_fill rows and every late layer.
+ *   x              [n_rows][ld_x] bf16, ld_x >= d_in, ld_x % 8 == 0, 16-byte aligned;
+ *                  n_rows*ld_x*2 must be below 2^32 bytes
+ *   fill_rows      [n_fill] int32, ascending, unique, in [0, n_rows)
+ *   positions      [n_rows] int32, RoPE position of each row, in [0, max_pos)
+ *   slot_of_row    [n_rows] int32 cache slot of each row in [0, n_slots), or
+ *                  NULL for slot = row
+ *   map_a, map_b   HOST arrays of n_late pointers to A_l, b_l (device pointers,
+ *                  or pinned host pointers with RF_MAPS_HOST; the caller keeps
+ *                  pinned maps alive until the stream has completed)
+ *   gamma, w_k, w_v, k_cache, v_cache   HOST arrays of n_late device pointers
+ *   rope_cos_sin   table from rf_rope_table, or NULL (built in the workspace)
+ *   workspace      >= rf_fill_workspace_bytes(plan, n_fill, 1), 256-byte aligned
+ * Rows whose position or slot is out of range are skipped by the kernels
+ * (RF_VALIDATE turns them into RF_E_ROWS).  n_fill == 0 enqueues nothing and
+ * leaves every cache byte untouched.  Results do not depend on the grouping
+ * of layers per launch or on RF_MAPS_HOST: the outputs are bitwise identical. */
+rf_status rf_fill(rf_plan* plan,
+                  const uint16_t* x, int64_t ld_x,
+                  const int32_t* fill_rows, int32_t n_fill,
+                  const int32_t* positions, const int32_t* slot_of_row,
+                  const uint16_t* const* map_a, const uint16_t* const* map_b,
+                  const uint16_t* const* gamma,
+                  const uint16_t* const* w_k, const uint16_t* const* w_v,
+                  const float* rope_cos_sin,
+                  uint16_t* const* k_cache, uint16_t* const* v_cache,
+                  void* workspace, size_t ws_bytes, void* hip_stream);
+
+/* The exact cache write of each late layer from given true inputs: steps 2-5
+ * only (no map).  Section 2.1: exact rows and the tail run the layer from its
+ * exact input; with every layer_in[l] = x and A_l = I, b_l = 0, rf_fill gives
+ * the same bytes (the identity fill of section 7, POP's fill).
+ *   layer_in   HOST array of n_late device pointers, each bf16 [n_rows][ld_in]
+ *              (entries may alias), ld_in >= d_out, ld_in % 8 == 0
+ *   rows       [n] int32 rows to write, in [0, n_rows), unique
+ *   other arguments as for rf_fill. */
+rf_status rf_kv_project(rf_plan* plan,
+                        const uint16_t* const* layer_in, int64_t ld_in,
+                        const int32_t* rows, int32_t n,
+                        const int32_t* positions, const int32_t* slot_of_row,
+                        const uint16_t* const* gamma,
+                        const uint16_t* const* w_k, const uint16_t* const* w_v,
+                        const float* rope_cos_sin,
+                        uint16_t* const* k_cache, uint16_t* const* v_cache,
+                        void* workspace, size_t ws_bytes, void* hip_stream);
+
+/* ---- Closed-form ridge map, HOST memory, float64 inside (validation only) ----
+ * Section 2.2: with X and Y centred, A = Y^T X (X^T X + alpha I)^(-1) and
+ * b = mu_Y - A mu_X, alpha = lambda * tr(Xc^T Xc) / d_in; only A is penalised.
+ * "Fitting": running sums of X^T X, X^T Y and the means over documents give
+ * the same result as one solve, and a new lambda needs only a new solve.
+ * X is [n][d_in] fp32, Y is [n][d_out] fp32 (row-major, HOST).  Products are
+ * formed and summed in float64.  A is returned [d_out][d_in] (the layout
+ * rf_fill's map_a takes) and b [d_out], both fp32 HOST. */
+typedef struct rf_ridge_acc rf_ridge_acc;
+rf_status rf_ridge_acc_create(int32_t d_in, int32_t d_out, rf_ridge_acc** out);
+rf_status rf_ridge_acc_add(rf_ridge_acc* acc, const float* x, const float* y, int64_t n);
+rf_status rf_ridge_solve(const rf_ridge_acc* acc, double lambda, int32_t flags,
+                         float* a, float* b);
+void rf_ridge_acc_destroy(rf_ridge_acc* acc);
+/* create + add + solve + destroy in one call */
+rf_status rf_ridge_fit(const float* x, const float* y, int64_t n, int32_t d_in, int32_t d_out,
+                       double lambda, int32_t flags, float* a, float* b);
+
+/* Thread-local message for the last non-OK status of this thread ("" if none). */
+const char* rf_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* RF_H */

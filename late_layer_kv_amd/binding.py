@@ -1,0 +1,239 @@
+"""ctypes binding of librf.so (include/rf.h).
+
+Argument marshalling only: every step of the fill runs in the HIP kernels of
+the library.  Tensors are torch tensors (device memory, or pinned host memory
+for streamed maps); bf16 data may be given as torch.bfloat16 or as int16 /
+uint16 bit patterns.  Work goes on torch's current HIP stream unless a stream
+is passed.  If the library is not built this module raises on first use; there
+is no fallback.
+"""
+from __future__ import annotations
+
+import ctypes as C
+import os
+from typing import List, Optional, Sequence
+
+import numpy as np
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "librf.so")
+
+RF_MAPS_HOST = 1
+RF_VALIDATE = 2
+RF_RIDGE_RAW = 1
+
+STATUS = {0: "RF_OK", -1: "RF_E_ARG", -2: "RF_E_SHAPE", -3: "RF_E_ROWS", -4: "RF_E_WORKSPACE",
+          -5: "RF_E_HIP", -6: "RF_E_LINALG"}
+
+# Every symbol include/rf.h declares.
+EXPORTS = [
+    "rf_plan_create", "rf_plan_destroy", "rf_fill_workspace_bytes", "rf_kv_project_workspace_bytes",
+    "rf_rope_table", "rf_fill_rows_workspace_bytes", "rf_fill_rows", "rf_fill", "rf_kv_project",
+    "rf_ridge_acc_create", "rf_ridge_acc_add", "rf_ridge_solve", "rf_ridge_acc_destroy", "rf_ridge_fit",
+    "rf_last_error",
+]
+
+
+class RfError(RuntimeError):
+    def __init__(self, fn: str, status: int, msg: str):
+        super().__init__(f"{fn}: {STATUS.get(status, status)}: {msg}")
+        self.status = status
+
+
+class Shape(C.Structure):
+    _fields_ = [("d_in", C.c_int32), ("d_out", C.c_int32), ("n_late", C.c_int32), ("n_kv", C.c_int32),
+                ("head_dim", C.c_int32), ("rms_eps", C.c_float), ("rope_theta", C.c_double),
+                ("n_rows", C.c_int32), ("n_slots", C.c_int32), ("max_pos", C.c_int32)]
+
+
+_lib = None
+P = C.c_void_p
+PP = C.POINTER(C.c_void_p)
+
+
+def lib():
+    """Load librf.so (built in-tree by late_layer_kv_amd.build)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(f"{LIB_PATH} is not built: run `python -m late_layer_kv_amd.build`")
+    L = C.CDLL(LIB_PATH)
+    i32, i64, sz, dbl = C.c_int32, C.c_int64, C.c_size_t, C.c_double
+    sig = {
+        "rf_plan_create": (i32, [C.POINTER(Shape), i32, C.POINTER(P)]),
+        "rf_plan_destroy": (None, [P]),
+        "rf_fill_workspace_bytes": (sz, [P, i32, i32]),
+        "rf_kv_project_workspace_bytes": (sz, [P, i32]),
+        "rf_rope_table": (i32, [P, P, P]),
+        "rf_fill_rows_workspace_bytes": (sz, [i32]),
+        "rf_fill_rows": (i32, [P, P, i32, P, P, P, sz, P]),
+        "rf_fill": (i32, [P, P, i64, P, i32, P, P, PP, PP, PP, PP, PP, P, PP, PP, P, sz, P]),
+        "rf_kv_project": (i32, [P, PP, i64, P, i32, P, P, PP, PP, PP, P, PP, PP, P, sz, P]),
+        "rf_ridge_acc_create": (i32, [i32, i32, C.POINTER(P)]),
+        "rf_ridge_acc_add": (i32, [P, P, P, i64]),
+        "rf_ridge_solve": (i32, [P, dbl, i32, P, P]),
+        "rf_ridge_acc_destroy": (None, [P]),
+        "rf_ridge_fit": (i32, [P, P, i64, i32, i32, dbl, i32, P, P]),
+        "rf_last_error": (C.c_char_p, []),
+    }
+    for name, (res, args) in sig.items():
+        f = getattr(L, name)
+        f.restype = res
+        f.argtypes = args
+    _lib = L
+    return L
+
+
+def last_error() -> str:
+    return lib().rf_last_error().decode()
+
+
+def _check(fn: str, st: int) -> None:
+    if st != 0:
+        raise RfError(fn, st, last_error())
+
+
+def _ptr(t) -> Optional[int]:
+    """Data pointer of a tensor (None passes NULL)."""
+    if t is None:
+        return None
+    return t.data_ptr()
+
+
+def _ptr_array(ts: Sequence) -> C.Array:
+    arr = (C.c_void_p * len(ts))()
+    for i, t in enumerate(ts):
+        arr[i] = t if isinstance(t, int) else t.data_ptr()
+    return arr
+
+
+def _stream(stream) -> Optional[int]:
+    if stream is not None:
+        return stream if isinstance(stream, int) else stream.cuda_stream
+    import torch
+    return torch.cuda.current_stream().cuda_stream
+
+
+class Plan:
+    """An rf_plan for one shape (see rf_plan_create)."""
+
+    def __init__(self, d_in: int, d_out: int, n_late: int, n_kv: int, head_dim: int, rms_eps: float,
+                 rope_theta: float, n_rows: int, n_slots: int, max_pos: int,
+                 maps_on_host: bool = False, validate: bool = False):
+        self.shape = Shape(d_in, d_out, n_late, n_kv, head_dim, rms_eps, rope_theta, n_rows, n_slots, max_pos)
+        self.flags = (RF_MAPS_HOST if maps_on_host else 0) | (RF_VALIDATE if validate else 0)
+        h = C.c_void_p()
+        _check("rf_plan_create", lib().rf_plan_create(C.byref(self.shape), self.flags, C.byref(h)))
+        self.handle = h
+
+    @classmethod
+    def for_spec(cls, s, **kw) -> "Plan":
+        """Plan for a workloads.Spec."""
+        kw.setdefault("maps_on_host", s.maps_on_host)
+        return cls(s.d_in, s.d_out, s.n_late, s.n_kv, s.head_dim, s.rms_eps, s.rope_theta,
+                   s.n_rows, s.n_rows, s.max_pos, **kw)
+
+    def close(self) -> None:
+        if self.handle:
+            lib().rf_plan_destroy(self.handle)
+            self.handle = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+    def fill_workspace_bytes(self, n_fill: int, layers_per_launch: int = 1) -> int:
+        return int(lib().rf_fill_workspace_bytes(self.handle, n_fill, layers_per_launch))
+
+    def kv_project_workspace_bytes(self, layers_per_launch: int = 1) -> int:
+        return int(lib().rf_kv_project_workspace_bytes(self.handle, layers_per_launch))
+
+
+def fill_rows_workspace_bytes(n_rows: int) -> int:
+    return int(lib().rf_fill_rows_workspace_bytes(n_rows))
+
+
+def rope_table(plan: Plan, table, stream=None) -> None:
+    _check("rf_rope_table", lib().rf_rope_table(plan.handle, _ptr(table), _stream(stream)))
+
+
+def fill_rows(plan: Plan, exact_rows, fill_rows_out, n_fill_out, workspace, stream=None) -> None:
+    n_exact = 0 if exact_rows is None else exact_rows.numel()
+    _check("rf_fill_rows", lib().rf_fill_rows(plan.handle, _ptr(exact_rows), n_exact, _ptr(fill_rows_out),
+                                              _ptr(n_fill_out), _ptr(workspace), workspace.numel() *
+                                              workspace.element_size(), _stream(stream)))
+
+
+def fill(plan: Plan, x, fill_rows_t, n_fill: int, positions, slot_of_row, map_a: Sequence, map_b: Sequence,
+         gamma: Sequence, w_k: Sequence, w_v: Sequence, rope, k_cache: Sequence, v_cache: Sequence,
+         workspace, stream=None, ld_x: Optional[int] = None) -> None:
+    """rf_fill.  map_a/map_b are device tensors, or pinned host tensors for a
+    plan made with maps_on_host."""
+    ld = x.stride(0) if ld_x is None else ld_x
+    _check("rf_fill", lib().rf_fill(
+        plan.handle, _ptr(x), ld, _ptr(fill_rows_t), n_fill, _ptr(positions), _ptr(slot_of_row),
+        _ptr_array(map_a), _ptr_array(map_b), _ptr_array(gamma), _ptr_array(w_k), _ptr_array(w_v),
+        _ptr(rope), _ptr_array(k_cache), _ptr_array(v_cache), _ptr(workspace),
+        workspace.numel() * workspace.element_size(), _stream(stream)))
+
+
+def kv_project(plan: Plan, layer_in: Sequence, rows, n: int, positions, slot_of_row, gamma: Sequence,
+               w_k: Sequence, w_v: Sequence, rope, k_cache: Sequence, v_cache: Sequence, workspace,
+               stream=None, ld_in: Optional[int] = None) -> None:
+    """rf_kv_project: the exact cache write of every late layer from given inputs."""
+    ld = layer_in[0].stride(0) if ld_in is None else ld_in
+    _check("rf_kv_project", lib().rf_kv_project(
+        plan.handle, _ptr_array(layer_in), ld, _ptr(rows), n, _ptr(positions), _ptr(slot_of_row),
+        _ptr_array(gamma), _ptr_array(w_k), _ptr_array(w_v), _ptr(rope), _ptr_array(k_cache),
+        _ptr_array(v_cache), _ptr(workspace), workspace.numel() * workspace.element_size(), _stream(stream)))
+
+
+def _f32(a: np.ndarray) -> np.ndarray:
+    return np.ascontiguousarray(a, dtype=np.float32)
+
+
+class RidgeAccumulator:
+    """rf_ridge_acc: running sums of a ridge fit on the host (float64 inside)."""
+
+    def __init__(self, d_in: int, d_out: int):
+        h = C.c_void_p()
+        _check("rf_ridge_acc_create", lib().rf_ridge_acc_create(d_in, d_out, C.byref(h)))
+        self.handle, self.d_in, self.d_out = h, d_in, d_out
+
+    def add(self, x: np.ndarray, y: np.ndarray) -> None:
+        x, y = _f32(x), _f32(y)
+        if x.shape[1] != self.d_in or y.shape[1] != self.d_out or x.shape[0] != y.shape[0]:
+            raise ValueError("shape mismatch")
+        _check("rf_ridge_acc_add", lib().rf_ridge_acc_add(self.handle, x.ctypes.data, y.ctypes.data, x.shape[0]))
+
+    def solve(self, lam: float, raw: bool = False):
+        a = np.empty((self.d_out, self.d_in), dtype=np.float32)
+        b = np.empty(self.d_out, dtype=np.float32)
+        _check("rf_ridge_solve", lib().rf_ridge_solve(self.handle, lam, RF_RIDGE_RAW if raw else 0,
+                                                      a.ctypes.data, b.ctypes.data))
+        return a, b
+
+    def close(self):
+        if self.handle:
+            lib().rf_ridge_acc_destroy(self.handle)
+            self.handle = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+
+def ridge_fit(x: np.ndarray, y: np.ndarray, lam: float, raw: bool = False):
+    """rf_ridge_fit: A [d_out][d_in] and b [d_out] (float32) of the ridge map."""
+    x, y = _f32(x), _f32(y)
+    n, d_in = x.shape
+    d_out = y.shape[1]
+    a = np.empty((d_out, d_in), dtype=np.float32)
+    b = np.empty(d_out, dtype=np.float32)
+    _check("rf_ridge_fit", lib().rf_ridge_fit(x.ctypes.data, y.ctypes.data, n, d_in, d_out, lam,
+                                              RF_RIDGE_RAW if raw else 0, a.ctypes.data, b.ctypes.data))
+    return a, b

@@ -1,0 +1,426 @@
+// Host side of the C ABI in include/rf.h: argument checks, workspace layout,
+// layer grouping, and the pipeline that streams host-resident maps.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <string>
+
+#include "../../include/rf.h"
+#include "rf_error.h"
+#include "rf_internal.h"
+
+namespace {
+
+thread_local std::string g_err;
+
+rf_status fail(rf_status st, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_err = buf;
+  return st;
+}
+
+rf_status hip_fail(hipError_t e, const char* what) {
+  return fail(RF_E_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+constexpr size_t kAlign = 256;
+size_t up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 0; }
+
+}  // namespace
+
+void rf::set_last_error(const char* msg) { g_err = msg; }
+
+struct rf_plan {
+  rf_shape s{};
+  int32_t flags = 0;
+  // RF_MAPS_HOST only
+  hipStream_t side = nullptr;
+  hipEvent_t ev_start = nullptr;
+  hipEvent_t ev_copied[2] = {nullptr, nullptr};
+  hipEvent_t ev_consumed[2] = {nullptr, nullptr};
+  uint16_t* mapbuf[2] = {nullptr, nullptr};  // [d_out][d_in] then [d_out], per buffer
+  size_t map_elems = 0;
+  size_t bias_off = 0;  // element offset of b inside a buffer
+};
+
+namespace {
+
+int kv_width(const rf_shape& s) { return s.n_kv * s.head_dim; }
+size_t rope_bytes(const rf_shape& s) { return up(static_cast<size_t>(s.max_pos) * (s.head_dim / 2) * 8); }
+size_t prep_bytes(const rf_shape& s, int g) {
+  return up(static_cast<size_t>(g) * 2 * kv_width(s) * s.d_out * 2);
+}
+size_t y_bytes(const rf_shape& s, int n_fill, int g) {
+  return up(static_cast<size_t>(g) * n_fill * s.d_out * 2);
+}
+constexpr size_t kFlagBytes = kAlign;
+
+rf_status check_shape(const rf_shape* s, int32_t flags) {
+  if (!s) return fail(RF_E_ARG, "shape is null");
+  if (flags & ~(RF_MAPS_HOST | RF_VALIDATE)) return fail(RF_E_ARG, "unknown flag bits 0x%x", flags);
+  if (s->d_in <= 0 || s->d_in % rf::kTileK)
+    return fail(RF_E_SHAPE, "d_in=%d must be a positive multiple of %d", s->d_in, rf::kTileK);
+  if (s->d_out <= 0 || s->d_out % rf::kTileN)
+    return fail(RF_E_SHAPE, "d_out=%d must be a positive multiple of %d", s->d_out, rf::kTileN);
+  if (s->n_late < 1) return fail(RF_E_SHAPE, "n_late=%d must be >= 1", s->n_late);
+  if (s->head_dim != 64 && s->head_dim != 128)
+    return fail(RF_E_SHAPE, "head_dim=%d must be 64 or 128", s->head_dim);
+  if (s->n_kv < 1 || (s->n_kv * s->head_dim) % 128)
+    return fail(RF_E_SHAPE, "n_kv*head_dim=%d must be a positive multiple of 128", s->n_kv * s->head_dim);
+  if (!(s->rms_eps >= 0.0f)) return fail(RF_E_SHAPE, "rms_eps must be >= 0");
+  if (!(s->rope_theta > 1.0)) return fail(RF_E_SHAPE, "rope_theta must be > 1");
+  if (s->n_rows < 0 || s->n_slots < 0 || s->max_pos < 1)
+    return fail(RF_E_SHAPE, "n_rows, n_slots must be >= 0 and max_pos >= 1");
+  return RF_OK;
+}
+
+int max_group(const rf_plan* p) { return std::min(p->s.n_late, rf::kMaxGroup); }
+
+rf_status check_layer_ptrs(const void* const* arr, int n, const char* name, bool need16 = true) {
+  if (!arr) return fail(RF_E_ARG, "%s array is null", name);
+  for (int i = 0; i < n; ++i) {
+    if (!arr[i]) return fail(RF_E_ARG, "%s[%d] is null", name, i);
+    if (need16 && !aligned16(arr[i])) return fail(RF_E_ARG, "%s[%d] is not 16-byte aligned", name, i);
+  }
+  return RF_OK;
+}
+
+rf_status run_validate(rf_plan* p, const int32_t* rows, int n, int ascending, const int32_t* positions,
+                       const int32_t* slots, int32_t* flag_dev, hipStream_t st) {
+  hipError_t e = rf::launch_validate(rows, n, p->s.n_rows, ascending, positions, p->s.max_pos, slots,
+                                     p->s.n_slots, flag_dev, st);
+  if (e != hipSuccess) return hip_fail(e, "validate launch");
+  int32_t flag = 0;
+  e = hipMemcpyAsync(&flag, flag_dev, sizeof flag, hipMemcpyDeviceToHost, st);
+  if (e == hipSuccess) e = hipStreamSynchronize(st);
+  if (e != hipSuccess) return hip_fail(e, "validate readback");
+  if (flag)
+    return fail(RF_E_ROWS, "row check failed (bits 0x%x: 1 row range, 2 position range, 4 slot range, 8 order)",
+                flag);
+  return RF_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* rf_last_error(void) { return g_err.c_str(); }
+
+rf_status rf_plan_create(const rf_shape* shape, int32_t flags, rf_plan** out) {
+  if (!out) return fail(RF_E_ARG, "out is null");
+  *out = nullptr;
+  rf_status st = check_shape(shape, flags);
+  if (st != RF_OK) return st;
+  rf_plan* p = new rf_plan();
+  p->s = *shape;
+  p->flags = flags;
+  hipError_t e = hipSuccess;
+  if (flags & RF_MAPS_HOST) {
+    p->map_elems = static_cast<size_t>(shape->d_out) * shape->d_in;
+    p->bias_off = (p->map_elems + 127) / 128 * 128;
+    const size_t bytes = (p->bias_off + shape->d_out) * 2;
+    for (int i = 0; i < 2 && e == hipSuccess; ++i) e = hipMalloc(reinterpret_cast<void**>(&p->mapbuf[i]), bytes);
+    if (e == hipSuccess) e = hipStreamCreateWithFlags(&p->side, hipStreamNonBlocking);
+    if (e == hipSuccess) e = hipEventCreateWithFlags(&p->ev_start, hipEventDisableTiming);
+    for (int i = 0; i < 2 && e == hipSuccess; ++i) e = hipEventCreateWithFlags(&p->ev_copied[i], hipEventDisableTiming);
+    for (int i = 0; i < 2 && e == hipSuccess; ++i)
+      e = hipEventCreateWithFlags(&p->ev_consumed[i], hipEventDisableTiming);
+    if (e != hipSuccess) {
+      rf_plan_destroy(p);
+      return hip_fail(e, "plan resources for streamed maps");
+    }
+  }
+  *out = p;
+  return RF_OK;
+}
+
+void rf_plan_destroy(rf_plan* p) {
+  if (!p) return;
+  if (p->side) (void)hipStreamSynchronize(p->side);
+  for (int i = 0; i < 2; ++i) {
+    if (p->mapbuf[i]) (void)hipFree(p->mapbuf[i]);
+    if (p->ev_copied[i]) (void)hipEventDestroy(p->ev_copied[i]);
+    if (p->ev_consumed[i]) (void)hipEventDestroy(p->ev_consumed[i]);
+  }
+  if (p->ev_start) (void)hipEventDestroy(p->ev_start);
+  if (p->side) (void)hipStreamDestroy(p->side);
+  delete p;
+}
+
+size_t rf_fill_workspace_bytes(const rf_plan* p, int32_t n_fill, int32_t g) {
+  if (!p || n_fill < 0 || g < 1 || g > p->s.n_late) return 0;
+  g = std::min(g, rf::kMaxGroup);
+  if (p->flags & RF_MAPS_HOST) g = 1;
+  return rope_bytes(p->s) + kFlagBytes + prep_bytes(p->s, g) + y_bytes(p->s, n_fill, g);
+}
+
+size_t rf_kv_project_workspace_bytes(const rf_plan* p, int32_t g) {
+  if (!p || g < 1 || g > p->s.n_late) return 0;
+  g = std::min(g, rf::kMaxGroup);
+  return rope_bytes(p->s) + kFlagBytes + prep_bytes(p->s, g);
+}
+
+size_t rf_fill_rows_workspace_bytes(int32_t n_rows) {
+  if (n_rows < 0) return 0;
+  return up(static_cast<size_t>(std::max(n_rows, 1)) * 4);
+}
+
+rf_status rf_rope_table(const rf_plan* p, float* table, void* stream) {
+  if (!p || !table) return fail(RF_E_ARG, "null plan or table");
+  if (!aligned16(table)) return fail(RF_E_ARG, "table must be 16-byte aligned");
+  hipError_t e = rf::launch_rope_table(table, p->s.max_pos, p->s.head_dim, p->s.rope_theta,
+                                       static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? RF_OK : hip_fail(e, "rope table launch");
+}
+
+rf_status rf_fill_rows(const rf_plan* p, const int32_t* exact_rows, int32_t n_exact, int32_t* fill_rows,
+                       int32_t* n_fill, void* ws, size_t ws_bytes, void* stream) {
+  if (!p) return fail(RF_E_ARG, "plan is null");
+  if (n_exact < 0 || (n_exact > 0 && !exact_rows)) return fail(RF_E_ARG, "bad exact rows");
+  if (!fill_rows || !n_fill) return fail(RF_E_ARG, "null output");
+  if (!ws || (reinterpret_cast<uintptr_t>(ws) % kAlign) || ws_bytes < rf_fill_rows_workspace_bytes(p->s.n_rows))
+    return fail(RF_E_WORKSPACE, "workspace needs %zu bytes, 256-byte aligned",
+                rf_fill_rows_workspace_bytes(p->s.n_rows));
+  hipError_t e = rf::launch_fill_rows(exact_rows, n_exact, p->s.n_rows, static_cast<int32_t*>(ws), fill_rows,
+                                      n_fill, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? RF_OK : hip_fail(e, "fill-row launch");
+}
+
+rf_status rf_fill(rf_plan* p, const uint16_t* x, int64_t ld_x, const int32_t* fill_rows, int32_t n_fill,
+                  const int32_t* positions, const int32_t* slot_of_row, const uint16_t* const* map_a,
+                  const uint16_t* const* map_b, const uint16_t* const* gamma, const uint16_t* const* w_k,
+                  const uint16_t* const* w_v, const float* rope, uint16_t* const* k_cache,
+                  uint16_t* const* v_cache, void* ws, size_t ws_bytes, void* stream) {
+  if (!p) return fail(RF_E_ARG, "plan is null");
+  const rf_shape& s = p->s;
+  const int L = s.n_late;
+  if (n_fill < 0 || n_fill > s.n_rows) return fail(RF_E_ARG, "n_fill=%d outside [0, n_rows=%d]", n_fill, s.n_rows);
+  if (!x || !aligned16(x)) return fail(RF_E_ARG, "x is null or not 16-byte aligned");
+  if (ld_x < s.d_in || ld_x % 8) return fail(RF_E_ARG, "ld_x=%lld must be >= d_in and a multiple of 8", (long long)ld_x);
+  if (n_fill > 0 && !fill_rows) return fail(RF_E_ARG, "fill_rows is null");
+  if (!positions) return fail(RF_E_ARG, "positions is null");
+  rf_status st;
+  const bool host_maps = p->flags & RF_MAPS_HOST;
+  if ((st = check_layer_ptrs(reinterpret_cast<const void* const*>(map_a), L, "map_a", !host_maps)) != RF_OK) return st;
+  if ((st = check_layer_ptrs(reinterpret_cast<const void* const*>(map_b), L, "map_b", !host_maps)) != RF_OK) return st;
+  if ((st = check_layer_ptrs(reinterpret_cast<const void* const*>(gamma), L, "gamma")) != RF_OK) return st;
+  if ((st = check_layer_ptrs(reinterpret_cast<const void* const*>(w_k), L, "w_k")) != RF_OK) return st;
+  if ((st = check_layer_ptrs(reinterpret_cast<const void* const*>(w_v), L, "w_v")) != RF_OK) return st;
+  if ((st = check_layer_ptrs(reinterpret_cast<const void* const*>(k_cache), L, "k_cache")) != RF_OK) return st;
+  if ((st = check_layer_ptrs(reinterpret_cast<const void* const*>(v_cache), L, "v_cache")) != RF_OK) return st;
+  if (rope && !aligned16(rope)) return fail(RF_E_ARG, "rope table is not 16-byte aligned");
+  const size_t need1 = rf_fill_workspace_bytes(p, n_fill, 1);
+  if (!ws || (reinterpret_cast<uintptr_t>(ws) % kAlign) || ws_bytes < need1)
+    return fail(RF_E_WORKSPACE, "workspace of %zu bytes given, %zu needed (256-byte aligned)", ws_bytes, need1);
+  if (n_fill == 0) return RF_OK;
+
+  hipStream_t hs = static_cast<hipStream_t>(stream);
+  int G = 1;
+  if (!host_maps)
+    for (int g = max_group(p); g > 1; --g)
+      if (rf_fill_workspace_bytes(p, n_fill, g) <= ws_bytes) {
+        G = g;
+        break;
+      }
+
+  char* w0 = static_cast<char*>(ws);
+  float* rope_ws = reinterpret_cast<float*>(w0);
+  int32_t* flag = reinterpret_cast<int32_t*>(w0 + rope_bytes(s));
+  uint16_t* prep = reinterpret_cast<uint16_t*>(w0 + rope_bytes(s) + kFlagBytes);
+  uint16_t* ybuf = reinterpret_cast<uint16_t*>(w0 + rope_bytes(s) + kFlagBytes + prep_bytes(s, G));
+
+  hipError_t e;
+  if (p->flags & RF_VALIDATE)
+    if ((st = run_validate(p, fill_rows, n_fill, 1, positions, slot_of_row, flag, hs)) != RF_OK) return st;
+  if (!rope) {
+    if ((e = rf::launch_rope_table(rope_ws, s.max_pos, s.head_dim, s.rope_theta, hs)) != hipSuccess)
+      return hip_fail(e, "rope table launch");
+    rope = rope_ws;
+  }
+
+  const int w = kv_width(s);
+  rf::MapParams mp{};
+  mp.x = x;
+  mp.ld_x = ld_x;
+  mp.rows = fill_rows;
+  mp.n_rows = s.n_rows;
+  mp.M = n_fill;
+  mp.K = s.d_in;
+  mp.N = s.d_out;
+  mp.tiles_m = (n_fill + rf::kTileM - 1) / rf::kTileM;
+  mp.tiles_n = s.d_out / rf::kTileN;
+  mp.y = ybuf;
+
+  rf::KvParams kp{};
+  kp.ld_in = s.d_out;
+  kp.in_rows = nullptr;
+  kp.n_in_rows = n_fill;
+  kp.out_rows = fill_rows;
+  kp.M = n_fill;
+  kp.K = s.d_out;
+  kp.w = w;
+  kp.head_dim = s.head_dim;
+  kp.tiles_m = mp.tiles_m;
+  kp.tiles_n = 2 * w / rf::kTileN;
+  kp.wkv = prep;
+  kp.positions = positions;
+  kp.slots = slot_of_row;
+  kp.n_rows = s.n_rows;
+  kp.n_slots = s.n_slots;
+  kp.max_pos = s.max_pos;
+  kp.rope = rope;
+  kp.eps = s.rms_eps;
+
+  rf::PrepParams pp{};
+  pp.d = s.d_out;
+  pp.w = w;
+  pp.out = prep;
+
+  const size_t y_layer = static_cast<size_t>(n_fill) * s.d_out;
+  if (host_maps) {
+    // Double-buffered stream of (A_l, b_l) over the side stream.  Copy l waits
+    // until the map kernel of layer l-2 (same buffer) has run; the map kernel
+    // of layer l waits for copy l.  The first copies also wait for the work
+    // already on the caller's stream, which may still read the buffers.
+    const size_t a_bytes = p->map_elems * 2, b_bytes = static_cast<size_t>(s.d_out) * 2;
+    if ((e = hipEventRecord(p->ev_start, hs)) != hipSuccess) return hip_fail(e, "event record");
+    if ((e = hipStreamWaitEvent(p->side, p->ev_start, 0)) != hipSuccess) return hip_fail(e, "stream wait");
+    for (int l = 0; l < L; ++l) {
+      const int buf = l & 1;
+      if (l >= 2 && (e = hipStreamWaitEvent(p->side, p->ev_consumed[buf], 0)) != hipSuccess)
+        return hip_fail(e, "stream wait");
+      if ((e = hipMemcpyAsync(p->mapbuf[buf], map_a[l], a_bytes, hipMemcpyHostToDevice, p->side)) != hipSuccess ||
+          (e = hipMemcpyAsync(p->mapbuf[buf] + p->bias_off, map_b[l], b_bytes, hipMemcpyHostToDevice, p->side)) !=
+              hipSuccess)
+        return hip_fail(e, "map copy");
+      if ((e = hipEventRecord(p->ev_copied[buf], p->side)) != hipSuccess) return hip_fail(e, "event record");
+
+      pp.gamma[0] = gamma[l];
+      pp.wk[0] = w_k[l];
+      pp.wv[0] = w_v[l];
+      if ((e = rf::launch_prep(pp, 1, hs)) != hipSuccess) return hip_fail(e, "prep launch");
+      if ((e = hipStreamWaitEvent(hs, p->ev_copied[buf], 0)) != hipSuccess) return hip_fail(e, "stream wait");
+      mp.a[0] = p->mapbuf[buf];
+      mp.b[0] = p->mapbuf[buf] + p->bias_off;
+      if ((e = rf::launch_map(mp, 1, hs)) != hipSuccess) return hip_fail(e, "map launch");
+      if ((e = hipEventRecord(p->ev_consumed[buf], hs)) != hipSuccess) return hip_fail(e, "event record");
+      kp.in[0] = ybuf;
+      kp.kc[0] = k_cache[l];
+      kp.vc[0] = v_cache[l];
+      if ((e = rf::launch_kv(kp, 1, hs)) != hipSuccess) return hip_fail(e, "kv launch");
+    }
+    return RF_OK;
+  }
+
+  for (int l0 = 0; l0 < L; l0 += G) {
+    const int g = std::min(G, L - l0);
+    for (int i = 0; i < g; ++i) {
+      pp.gamma[i] = gamma[l0 + i];
+      pp.wk[i] = w_k[l0 + i];
+      pp.wv[i] = w_v[l0 + i];
+      mp.a[i] = map_a[l0 + i];
+      mp.b[i] = map_b[l0 + i];
+      kp.in[i] = ybuf + i * y_layer;
+      kp.kc[i] = k_cache[l0 + i];
+      kp.vc[i] = v_cache[l0 + i];
+    }
+    if ((e = rf::launch_prep(pp, g, hs)) != hipSuccess) return hip_fail(e, "prep launch");
+    if ((e = rf::launch_map(mp, g, hs)) != hipSuccess) return hip_fail(e, "map launch");
+    if ((e = rf::launch_kv(kp, g, hs)) != hipSuccess) return hip_fail(e, "kv launch");
+  }
+  return RF_OK;
+}
+
+rf_status rf_kv_project(rf_plan* p, const uint16_t* const* layer_in, int64_t ld_in, const int32_t* rows, int32_t n,
+                        const int32_t* positions, const int32_t* slot_of_row, const uint16_t* const* gamma,
+                        const uint16_t* const* w_k, const uint16_t* const* w_v, const float* rope,
+                        uint16_t* const* k_cache, uint16_t* const* v_cache, void* ws, size_t ws_bytes,
+                        void* stream) {
+  if (!p) return fail(RF_E_ARG, "plan is null");
+  const rf_shape& s = p->s;
+  const int L = s.n_late;
+  if (n < 0 || n > s.n_rows) return fail(RF_E_ARG, "n=%d outside [0, n_rows=%d]", n, s.n_rows);
+  if (ld_in < s.d_out || ld_in % 8) return fail(RF_E_ARG, "ld_in=%lld must be >= d_out and a multiple of 8", (long long)ld_in);
+  if (n > 0 && !rows) return fail(RF_E_ARG, "rows is null");
+  if (!positions) return fail(RF_E_ARG, "positions is null");
+  rf_status st;
+  if ((st = check_layer_ptrs(reinterpret_cast<const void* const*>(layer_in), L, "layer_in")) != RF_OK) return st;
+  if ((st = check_layer_ptrs(reinterpret_cast<const void* const*>(gamma), L, "gamma")) != RF_OK) return st;
+  if ((st = check_layer_ptrs(reinterpret_cast<const void* const*>(w_k), L, "w_k")) != RF_OK) return st;
+  if ((st = check_layer_ptrs(reinterpret_cast<const void* const*>(w_v), L, "w_v")) != RF_OK) return st;
+  if ((st = check_layer_ptrs(reinterpret_cast<const void* const*>(k_cache), L, "k_cache")) != RF_OK) return st;
+  if ((st = check_layer_ptrs(reinterpret_cast<const void* const*>(v_cache), L, "v_cache")) != RF_OK) return st;
+  if (rope && !aligned16(rope)) return fail(RF_E_ARG, "rope table is not 16-byte aligned");
+  const size_t need1 = rf_kv_project_workspace_bytes(p, 1);
+  if (!ws || (reinterpret_cast<uintptr_t>(ws) % kAlign) || ws_bytes < need1)
+    return fail(RF_E_WORKSPACE, "workspace of %zu bytes given, %zu needed (256-byte aligned)", ws_bytes, need1);
+  if (n == 0) return RF_OK;
+
+  hipStream_t hs = static_cast<hipStream_t>(stream);
+  int G = 1;
+  for (int g = max_group(p); g > 1; --g)
+    if (rf_kv_project_workspace_bytes(p, g) <= ws_bytes) {
+      G = g;
+      break;
+    }
+  char* w0 = static_cast<char*>(ws);
+  float* rope_ws = reinterpret_cast<float*>(w0);
+  int32_t* flag = reinterpret_cast<int32_t*>(w0 + rope_bytes(s));
+  uint16_t* prep = reinterpret_cast<uint16_t*>(w0 + rope_bytes(s) + kFlagBytes);
+  hipError_t e;
+  if (p->flags & RF_VALIDATE)
+    if ((st = run_validate(p, rows, n, 0, positions, slot_of_row, flag, hs)) != RF_OK) return st;
+  if (!rope) {
+    if ((e = rf::launch_rope_table(rope_ws, s.max_pos, s.head_dim, s.rope_theta, hs)) != hipSuccess)
+      return hip_fail(e, "rope table launch");
+    rope = rope_ws;
+  }
+  const int w = kv_width(s);
+  rf::KvParams kp{};
+  kp.ld_in = ld_in;
+  kp.in_rows = rows;
+  kp.n_in_rows = s.n_rows;
+  kp.out_rows = rows;
+  kp.M = n;
+  kp.K = s.d_out;
+  kp.w = w;
+  kp.head_dim = s.head_dim;
+  kp.tiles_m = (n + rf::kTileM - 1) / rf::kTileM;
+  kp.tiles_n = 2 * w / rf::kTileN;
+  kp.wkv = prep;
+  kp.positions = positions;
+  kp.slots = slot_of_row;
+  kp.n_rows = s.n_rows;
+  kp.n_slots = s.n_slots;
+  kp.max_pos = s.max_pos;
+  kp.rope = rope;
+  kp.eps = s.rms_eps;
+  rf::PrepParams pp{};
+  pp.d = s.d_out;
+  pp.w = w;
+  pp.out = prep;
+  for (int l0 = 0; l0 < L; l0 += G) {
+    const int g = std::min(G, L - l0);
+    for (int i = 0; i < g; ++i) {
+      pp.gamma[i] = gamma[l0 + i];
+      pp.wk[i] = w_k[l0 + i];
+      pp.wv[i] = w_v[l0 + i];
+      kp.in[i] = layer_in[l0 + i];
+      kp.kc[i] = k_cache[l0 + i];
+      kp.vc[i] = v_cache[l0 + i];
+    }
+    if ((e = rf::launch_prep(pp, g, hs)) != hipSuccess) return hip_fail(e, "prep launch");
+    if ((e = rf::launch_kv(kp, g, hs)) != hipSuccess) return hip_fail(e, "kv launch");
+  }
+  return RF_OK;
+}
+
+}  // extern "C"

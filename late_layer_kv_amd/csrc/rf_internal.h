@@ -1,0 +1,81 @@
+// Internal interface between the host API (rf_api.cpp) and the kernels
+// (rf_kernels.hip).  Not part of the public ABI.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace rf {
+
+// Layers handled by one launch (kernel arguments carry per-layer pointers).
+constexpr int kMaxGroup = 32;
+// Macro tile of both contractions: 256 output features x 256 rows, 64-deep
+// contraction steps.
+constexpr int kTileN = 256;
+constexpr int kTileM = 256;
+constexpr int kTileK = 64;
+
+// Map contraction, section 2.2 of the paper: Y_g[m][n] = bf16(sum_k A_g[n][k] x[row(m)][k] + b_g[n]).
+struct MapParams {
+  const uint16_t* x;      // [n_rows][ld_x]
+  int64_t ld_x;
+  const int32_t* rows;    // [M] gather index into x
+  int32_t n_rows;
+  int32_t M;              // rows of this call (n_fill)
+  int32_t K;              // d_in
+  int32_t N;              // d_out
+  int32_t tiles_m, tiles_n;
+  uint16_t* y;            // [n_layers][M][N]
+  const uint16_t* a[kMaxGroup];  // [N][K]
+  const uint16_t* b[kMaxGroup];  // [N]
+};
+
+// Norm + key/value contraction with the RoPE and cache-scatter epilogue:
+//   acc[m][f] = sum_k in_g[src(m)][k] * Wp_g[f][k],  Wp_g = bf16(W_kv * gamma)
+//   out = acc / sqrt(mean_k in^2 + eps), RoPE on key features, bf16 to the cache.
+struct KvParams {
+  int64_t ld_in;
+  const int32_t* in_rows;   // [M] gather index into in_g, or null (row m)
+  int32_t n_in_rows;        // rows addressable in in_g
+  const int32_t* out_rows;  // [M] global row id of m (positions/slots), or null
+  int32_t M;
+  int32_t K;                // d_out (normalised width)
+  int32_t w;                // n_kv * head_dim
+  int32_t head_dim;
+  int32_t tiles_m, tiles_n;
+  const uint16_t* wkv;      // [n_layers][2w][K] prepared weights
+  const int32_t* positions; // [n_rows]
+  const int32_t* slots;     // [n_rows] or null (slot = row)
+  int32_t n_rows, n_slots, max_pos;
+  const float* rope;        // [max_pos][head_dim/2][2]
+  float eps;
+  const uint16_t* in[kMaxGroup];
+  uint16_t* kc[kMaxGroup];  // [n_slots][w]
+  uint16_t* vc[kMaxGroup];
+};
+
+// Prepared projection weights: out_g[f][k] = bf16(W[f][k] * gamma_g[k]),
+// W = W_k for f < w, W_v (row f - w) otherwise.
+struct PrepParams {
+  int32_t d;       // d_out
+  int32_t w;
+  uint16_t* out;   // [n_layers][2w][d]
+  const uint16_t* gamma[kMaxGroup];
+  const uint16_t* wk[kMaxGroup];
+  const uint16_t* wv[kMaxGroup];
+};
+
+hipError_t launch_map(const MapParams& p, int n_layers, hipStream_t s);
+hipError_t launch_kv(const KvParams& p, int n_layers, hipStream_t s);
+hipError_t launch_prep(const PrepParams& p, int n_layers, hipStream_t s);
+hipError_t launch_rope_table(float* table, int max_pos, int head_dim, double theta, hipStream_t s);
+hipError_t launch_fill_rows(const int32_t* exact, int n_exact, int n_rows, int32_t* mask,
+                            int32_t* fill_rows, int32_t* n_fill, hipStream_t s);
+// Sets bits in *flag: 1 row out of range, 2 position out of range,
+// 4 slot out of range, 8 rows not strictly ascending.
+hipError_t launch_validate(const int32_t* rows, int n, int n_rows, int ascending,
+                           const int32_t* positions, int max_pos, const int32_t* slots,
+                           int n_slots, int32_t* flag, hipStream_t s);
+
+}  // namespace rf

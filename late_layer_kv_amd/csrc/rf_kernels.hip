@@ -1,0 +1,537 @@
+// HIP kernels of the late-layer cache fill for gfx950 (MI355X).
+//
+// Two bf16 MFMA contractions carry the work ("RidgeFill: Training-Free
+// Late-Layer Cache Fill for Faster Prefill", sections 2.1-2.2):
+//   map_gemm : Y_l = X_F A_l^T + b_l for a group of late layers, the rows of
+//              X gathered through the fill-row index on the way into LDS;
+//   kv_gemm  : K|V = (Y_l W'^T) / rms(Y_l) with W' = [W_k|W_v] * gamma, then
+//              RoPE on the key columns and a bf16 scatter into each layer's
+//              cache slot for the row.
+//
+// Both use one main loop.  A workgroup of 4 waves owns a 256x256 output tile
+// (256 output features x 256 rows); each wave owns 128 features x 128 rows as
+// 4x4 blocks of v_mfma_f32_32x32x16_bf16.  The weight matrix is the MFMA "A"
+// operand and the data rows the "B" operand, so in the accumulator every lane
+// holds whole data rows: lane l owns row (l & 31) of each 32-row block and 16
+// features of each 32-feature block (4 runs of 4 consecutive features).  The
+// RoPE partner of a key feature, the row's norm scale and 4-feature packing for
+// the stores therefore all stay inside one lane.
+//
+// Operand tiles stream global -> LDS with global_load_lds_dwordx4 (no VGPR
+// staging), two 64 KB stages (128 KB of the 160 KB LDS).  Rows are 128 bytes
+// (64 bf16) in LDS; the 16-byte chunk at column c of row r sits at chunk
+// position c ^ (r & 7) so that the MFMA fragment reads of 8 consecutive rows hit
+// distinct banks.  The epilogue reuses the LDS as a 256x256 bf16 staging tile so
+// that every global store is a 16-byte, row-contiguous write.
+//
+// Reduction order is fixed by the tile shape alone (no split-K, no atomics on
+// values), so results are bitwise reproducible and independent of which other
+// rows share a tile and of how many layers share a launch.
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "rf_internal.h"
+
+namespace rf {
+namespace {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef __attribute__((address_space(3))) void lds_ptr_t;
+typedef const __attribute__((address_space(1))) void gbl_ptr_t;
+
+constexpr int kThreads = 256;
+constexpr int kRowBytes = kTileK * 2;                 // 128 B per LDS row
+constexpr int kOperandBytes = 256 * kRowBytes;        // 32 KB per operand tile
+constexpr int kStageBytes = 2 * kOperandBytes;        // 64 KB
+constexpr int kLdsBytes = 2 * kStageBytes;            // 128 KB
+constexpr int kStageRowBytes = kTileN * 2;            // 512 B per staged output row
+static_assert(kTileM * kStageRowBytes <= kLdsBytes, "staging tile must fit in LDS");
+
+__device__ __forceinline__ float bf16_to_f32(uint16_t b) {
+  return __uint_as_float(static_cast<uint32_t>(b) << 16);
+}
+
+// Round-to-nearest-even float -> bf16 pair, packed (lo in bits 0..15).
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  bf16x2 v = {static_cast<__bf16>(lo), static_cast<__bf16>(hi)};
+  return __builtin_bit_cast(uint32_t, v);
+}
+
+// Workgroups are dealt round-robin to the 8 XCDs.  Renumber them so that each
+// XCD works on one contiguous range of logical tiles, which the tile order
+// below makes share operand strips in that XCD's L2.
+__device__ __forceinline__ int xcd_remap(int bid, int n) {
+  const int q = n >> 3, r = n & 7, x = bid & 7, local = bid >> 3;
+  return (x < r) ? x * (q + 1) + local : r * (q + 1) + (x - r) * q + local;
+}
+
+struct TileCoord {
+  int g, tm, tn;
+};
+
+// Logical tile -> (layer, row tile, feature tile).  Inside a layer tiles go
+// down groups of 8 row tiles for one feature tile before moving on, so the 32
+// workgroups an XCD runs at once cover about 8 row strips x 4 weight strips.
+__device__ __forceinline__ TileCoord tile_coord(int t, int tiles_m, int tiles_n) {
+  constexpr int GM = 8;
+  const int per_layer = tiles_m * tiles_n;
+  TileCoord c;
+  c.g = t / per_layer;
+  const int u = t - c.g * per_layer;
+  const int per_group = GM * tiles_n;
+  const int grp = u / per_group;
+  const int first_m = grp * GM;
+  const int gsz = min(tiles_m - first_m, GM);
+  const int v = u - grp * per_group;
+  c.tm = first_m + v % gsz;
+  c.tn = v / gsz;
+  return c;
+}
+
+__device__ __forceinline__ void wait_vm_and_barrier() {
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  __syncthreads();
+}
+
+// One k-step (64 columns) of both operand tiles for this wave: 8 rows per
+// instruction, 8 instructions per operand.  src[j] already points at this
+// lane's 16-byte chunk of column block 0; the LDS destination of instruction j
+// is wave_base + j * 1 KB and lane i lands at + 16 i (row i / 8, chunk
+// position i % 8).
+__device__ __forceinline__ void issue_stage(const char* const (&wsrc)[8], const char* const (&xsrc)[8],
+                                            size_t kbyte, char* wdst, char* xdst) {
+#pragma unroll
+  for (int j = 0; j < 8; ++j)
+    __builtin_amdgcn_global_load_lds((gbl_ptr_t*)(wsrc[j] + kbyte), (lds_ptr_t*)(wdst + j * 1024), 16, 0, 0);
+#pragma unroll
+  for (int j = 0; j < 8; ++j)
+    __builtin_amdgcn_global_load_lds((gbl_ptr_t*)(xsrc[j] + kbyte), (lds_ptr_t*)(xdst + j * 1024), 16, 0, 0);
+}
+
+// Main loop shared by both contractions.  On return acc[nb][mb] holds the
+// 32x32 block (features nb, rows mb) of this wave and, with SUMSQ, ss[mb] the
+// sum of squares of this lane's half of the contraction for row mb.
+template <bool SUMSQ>
+__device__ __forceinline__ void mainloop(const char* const (&wsrc)[8], const char* const (&xsrc)[8], int nk,
+                                         char* smem, f32x16 (&acc)[4][4], float (&ss)[4]) {
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int wn = wave & 1, wm = wave >> 1;
+  const int r31 = lane & 31, hsel = lane >> 5;
+
+  char* const wdst = smem + wave * 8 * 1024;
+  char* const xdst = smem + kOperandBytes + wave * 8 * 1024;
+
+  // Fragment offsets inside a stage.  Row r of a 32-row block is lane & 31;
+  // its 16-byte chunk for contraction slice kk is 2 kk + (lane >> 5).
+  int aoff[4], boff[4];
+#pragma unroll
+  for (int kk = 0; kk < 4; ++kk) {
+    const int pos = ((2 * kk + hsel) ^ (r31 & 7)) << 4;
+    aoff[kk] = (wn * 128 + r31) * kRowBytes + pos;
+    boff[kk] = kOperandBytes + (wm * 128 + r31) * kRowBytes + pos;
+  }
+
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    ss[i] = 0.0f;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) acc[i][j] = f32x16{};
+  }
+
+  issue_stage(wsrc, xsrc, 0, wdst, xdst);
+  wait_vm_and_barrier();
+
+  for (int t = 0; t < nk; ++t) {
+    const int cur = t & 1;
+    if (t + 1 < nk) {
+      const int nxt = cur ^ 1;
+      issue_stage(wsrc, xsrc, static_cast<size_t>(t + 1) * kRowBytes, wdst + nxt * kStageBytes,
+                  xdst + nxt * kStageBytes);
+    }
+    const char* st = smem + cur * kStageBytes;
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) {
+      bf16x8 a[4], b[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) a[i] = *reinterpret_cast<const bf16x8*>(st + aoff[kk] + i * 32 * kRowBytes);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) b[i] = *reinterpret_cast<const bf16x8*>(st + boff[kk] + i * 32 * kRowBytes);
+      if constexpr (SUMSQ) {
+#pragma unroll
+        for (int mb = 0; mb < 4; ++mb) {
+          ss[mb] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(b[mb], b[mb], 0, 1),
+                                                   __builtin_shufflevector(b[mb], b[mb], 0, 1), ss[mb], false);
+          ss[mb] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(b[mb], b[mb], 2, 3),
+                                                   __builtin_shufflevector(b[mb], b[mb], 2, 3), ss[mb], false);
+          ss[mb] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(b[mb], b[mb], 4, 5),
+                                                   __builtin_shufflevector(b[mb], b[mb], 4, 5), ss[mb], false);
+          ss[mb] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(b[mb], b[mb], 6, 7),
+                                                   __builtin_shufflevector(b[mb], b[mb], 6, 7), ss[mb], false);
+        }
+      }
+#pragma unroll
+      for (int nb = 0; nb < 4; ++nb)
+#pragma unroll
+        for (int mb = 0; mb < 4; ++mb)
+          acc[nb][mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[nb], b[mb], acc[nb][mb], 0, 0, 0);
+    }
+    wait_vm_and_barrier();
+  }
+}
+
+// Per-lane source pointers for the 8 load instructions of one operand.  Local
+// row of instruction j is wave * 64 + j * 8 + lane / 8; its LDS chunk position
+// is lane % 8, which holds column chunk (lane % 8) ^ (local row & 7).
+__device__ __forceinline__ int load_chunk(int lane) { return (lane & 7) ^ ((lane >> 3) & 7); }
+
+// The staging tile: row r (0..255) of 512 bytes, 16-byte chunk c stored at
+// chunk position c ^ (r & 31).
+__device__ __forceinline__ int stage_off(int row, int chunk) {
+  return row * kStageRowBytes + ((chunk ^ (row & 31)) << 4);
+}
+
+__global__ void __launch_bounds__(kThreads) map_gemm_kernel(const MapParams p) {
+  __shared__ __attribute__((aligned(1024))) char smem[kLdsBytes];
+  const int t = xcd_remap(blockIdx.x, gridDim.x);
+  const TileCoord c = tile_coord(t, p.tiles_m, p.tiles_n);
+  const int m0 = c.tm * kTileM, n0 = c.tn * kTileN;
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+
+  const char* wsrc[8];
+  const char* xsrc[8];
+  {
+    const int chunk = load_chunk(lane);
+    const char* abase = reinterpret_cast<const char*>(p.a[c.g]);
+    const char* xbase = reinterpret_cast<const char*>(p.x);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const int lr = wave * 64 + j * 8 + (lane >> 3);
+      wsrc[j] = abase + (static_cast<size_t>(n0 + lr) * p.K + chunk * 8) * 2;
+      int m = min(m0 + lr, p.M - 1);
+      int row = p.rows[m];
+      row = (row >= 0 && row < p.n_rows) ? row : 0;  // out-of-range rows read row 0, never stored
+      xsrc[j] = xbase + (static_cast<size_t>(row) * p.ld_x + chunk * 8) * 2;
+    }
+  }
+
+  f32x16 acc[4][4];
+  float ss[4];
+  mainloop<false>(wsrc, xsrc, p.K / kTileK, smem, acc, ss);
+
+  // Epilogue: + b, round to bf16, stage, 16-byte row stores into Y_g.
+  const int wn = wave & 1, wm = wave >> 1, r31 = lane & 31, hsel = lane >> 5;
+  const uint16_t* bias = p.b[c.g] + n0 + wn * 128 + hsel * 4;
+  __syncthreads();  // every wave is done reading the operand stages
+#pragma unroll
+  for (int nb = 0; nb < 4; ++nb) {
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const uint2 braw = *reinterpret_cast<const uint2*>(bias + nb * 32 + q * 8);
+      const float b0 = bf16_to_f32(braw.x & 0xffff), b1 = bf16_to_f32(braw.x >> 16);
+      const float b2 = bf16_to_f32(braw.y & 0xffff), b3 = bf16_to_f32(braw.y >> 16);
+      const int chunk = wn * 16 + nb * 4 + q;
+#pragma unroll
+      for (int mb = 0; mb < 4; ++mb) {
+        const int row = wm * 128 + mb * 32 + r31;
+        const f32x16& v = acc[nb][mb];
+        uint2 o;
+        o.x = pack_bf16x2(v[q * 4 + 0] + b0, v[q * 4 + 1] + b1);
+        o.y = pack_bf16x2(v[q * 4 + 2] + b2, v[q * 4 + 3] + b3);
+        *reinterpret_cast<uint2*>(smem + stage_off(row, chunk) + hsel * 8) = o;
+      }
+    }
+  }
+  __syncthreads();
+  uint16_t* y = p.y + static_cast<size_t>(c.g) * p.M * p.N;
+  const int chunk = threadIdx.x & 31;
+#pragma unroll 4
+  for (int it = 0; it < 32; ++it) {
+    const int row = it * 8 + (threadIdx.x >> 5);
+    const int m = m0 + row;
+    if (m < p.M) {
+      const uint4 v = *reinterpret_cast<const uint4*>(smem + stage_off(row, chunk));
+      *reinterpret_cast<uint4*>(y + static_cast<size_t>(m) * p.N + n0 + chunk * 8) = v;
+    }
+  }
+}
+
+template <int HD>
+__global__ void __launch_bounds__(kThreads) kv_gemm_kernel(const KvParams p) {
+  __shared__ __attribute__((aligned(1024))) char smem[kLdsBytes];
+  __shared__ int slot_of[kTileM];
+  const int t = xcd_remap(blockIdx.x, gridDim.x);
+  const TileCoord c = tile_coord(t, p.tiles_m, p.tiles_n);
+  const int m0 = c.tm * kTileM, n0 = c.tn * kTileN;
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+
+  const char* wsrc[8];
+  const char* xsrc[8];
+  {
+    const int chunk = load_chunk(lane);
+    const char* wbase = reinterpret_cast<const char*>(p.wkv + static_cast<size_t>(c.g) * 2 * p.w * p.K);
+    const char* xbase = reinterpret_cast<const char*>(p.in[c.g]);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const int lr = wave * 64 + j * 8 + (lane >> 3);
+      wsrc[j] = wbase + (static_cast<size_t>(n0 + lr) * p.K + chunk * 8) * 2;
+      const int m = min(m0 + lr, p.M - 1);
+      int row = p.in_rows ? p.in_rows[m] : m;
+      row = (row >= 0 && row < p.n_in_rows) ? row : 0;
+      xsrc[j] = xbase + (static_cast<size_t>(row) * p.ld_in + chunk * 8) * 2;
+    }
+  }
+
+  f32x16 acc[4][4];
+  float ss[4];
+  mainloop<true>(wsrc, xsrc, p.K / kTileK, smem, acc, ss);
+
+  const int wn = wave & 1, wm = wave >> 1, r31 = lane & 31, hsel = lane >> 5;
+  const float inv_k = 1.0f / static_cast<float>(p.K);
+  float rs[4];
+  int pos[4];
+#pragma unroll
+  for (int mb = 0; mb < 4; ++mb) {
+    const float tot = ss[mb] + __shfl_xor(ss[mb], 32);
+    rs[mb] = rsqrtf(tot * inv_k + p.eps);
+    const int lr = wm * 128 + mb * 32 + r31;
+    const int m = m0 + lr;
+    int ps = 0, slot = -1;
+    if (m < p.M) {
+      const int r = p.out_rows ? p.out_rows[m] : m;
+      if (r >= 0 && r < p.n_rows) {
+        ps = p.positions[r];
+        slot = p.slots ? p.slots[r] : r;
+        if (ps < 0 || ps >= p.max_pos || slot < 0 || slot >= p.n_slots) {
+          slot = -1;
+          ps = 0;
+        }
+      }
+    }
+    pos[mb] = ps;
+    if (wn == 0 && hsel == 0) slot_of[lr] = slot;
+  }
+
+  const int fw = n0 + wn * 128;  // first feature of this wave; a whole wave is key or value
+  const bool is_key = fw < p.w;
+  if (is_key) {
+    // RoPE, rotate-half: feature j < hd/2 of a head pairs with j + hd/2.  A
+    // wave spans 128 features = one head of 128 or two heads of 64, so the
+    // partner is block nb + hd/64 at the same register index.
+    constexpr int half = HD / 2;
+    constexpr int pstep = half / 32;  // 2 for hd 128, 1 for hd 64
+    const float2* tab = reinterpret_cast<const float2*>(p.rope);
+#pragma unroll
+    for (int nb = 0; nb < 4; ++nb) {
+      const int jb = (nb * 32) & (HD - 1);
+      if (jb >= half) continue;
+      const int nb2 = nb + pstep;
+#pragma unroll
+      for (int mb = 0; mb < 4; ++mb) {
+        const float2* trow = tab + static_cast<size_t>(pos[mb]) * half + jb + hsel * 4;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const float4 cs01 = *reinterpret_cast<const float4*>(trow + q * 8);
+          const float4 cs23 = *reinterpret_cast<const float4*>(trow + q * 8 + 2);
+          const float cs[8] = {cs01.x, cs01.y, cs01.z, cs01.w, cs23.x, cs23.y, cs23.z, cs23.w};
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const float x1 = acc[nb][mb][q * 4 + i] * rs[mb];
+            const float x2 = acc[nb2][mb][q * 4 + i] * rs[mb];
+            const float co = cs[2 * i], si = cs[2 * i + 1];
+            acc[nb][mb][q * 4 + i] = x1 * co - x2 * si;
+            acc[nb2][mb][q * 4 + i] = x2 * co + x1 * si;
+          }
+        }
+      }
+    }
+  } else {
+#pragma unroll
+    for (int nb = 0; nb < 4; ++nb)
+#pragma unroll
+      for (int mb = 0; mb < 4; ++mb)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) acc[nb][mb][v] *= rs[mb];
+  }
+
+  __syncthreads();  // operand stages free; slot_of visible
+#pragma unroll
+  for (int nb = 0; nb < 4; ++nb) {
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int chunk = wn * 16 + nb * 4 + q;
+#pragma unroll
+      for (int mb = 0; mb < 4; ++mb) {
+        const int row = wm * 128 + mb * 32 + r31;
+        const f32x16& v = acc[nb][mb];
+        uint2 o;
+        o.x = pack_bf16x2(v[q * 4 + 0], v[q * 4 + 1]);
+        o.y = pack_bf16x2(v[q * 4 + 2], v[q * 4 + 3]);
+        *reinterpret_cast<uint2*>(smem + stage_off(row, chunk) + hsel * 8) = o;
+      }
+    }
+  }
+  __syncthreads();
+  const int chunk = threadIdx.x & 31;
+  const int f = n0 + chunk * 8;
+  uint16_t* dst_base = (f < p.w) ? p.kc[c.g] + f : p.vc[c.g] + (f - p.w);
+#pragma unroll 4
+  for (int it = 0; it < 32; ++it) {
+    const int row = it * 8 + (threadIdx.x >> 5);
+    const int slot = slot_of[row];
+    if (slot >= 0) {
+      const uint4 v = *reinterpret_cast<const uint4*>(smem + stage_off(row, chunk));
+      *reinterpret_cast<uint4*>(dst_base + static_cast<size_t>(slot) * p.w) = v;
+    }
+  }
+}
+
+// Prepared weights: one thread per 8 consecutive inputs of one output feature.
+__global__ void __launch_bounds__(256) prep_kv_kernel(const PrepParams p) {
+  const int g = blockIdx.y;
+  const int per_row = p.d >> 3;
+  const int64_t idx = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
+  if (idx >= static_cast<int64_t>(2 * p.w) * per_row) return;
+  const int f = static_cast<int>(idx / per_row);
+  const int k8 = static_cast<int>(idx - static_cast<int64_t>(f) * per_row) * 8;
+  const uint16_t* src = (f < p.w) ? p.wk[g] + static_cast<size_t>(f) * p.d : p.wv[g] + static_cast<size_t>(f - p.w) * p.d;
+  const uint4 wr = *reinterpret_cast<const uint4*>(src + k8);
+  const uint4 gr = *reinterpret_cast<const uint4*>(p.gamma[g] + k8);
+  const uint32_t wv[4] = {wr.x, wr.y, wr.z, wr.w};
+  const uint32_t gv[4] = {gr.x, gr.y, gr.z, gr.w};
+  uint32_t o[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const float lo = bf16_to_f32(wv[i] & 0xffff) * bf16_to_f32(gv[i] & 0xffff);
+    const float hi = bf16_to_f32(wv[i] >> 16) * bf16_to_f32(gv[i] >> 16);
+    o[i] = pack_bf16x2(lo, hi);
+  }
+  *reinterpret_cast<uint4*>(p.out + (static_cast<size_t>(g) * 2 * p.w + f) * p.d + k8) =
+      make_uint4(o[0], o[1], o[2], o[3]);
+}
+
+// (cos, sin) of pos * theta^(-2j/hd), formed and evaluated in double precision.
+__global__ void __launch_bounds__(256) rope_table_kernel(float2* tab, int max_pos, int hd, double theta) {
+  const int half = hd >> 1;
+  const int64_t idx = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
+  if (idx >= static_cast<int64_t>(max_pos) * half) return;
+  const int p = static_cast<int>(idx / half);
+  const int j = static_cast<int>(idx - static_cast<int64_t>(p) * half);
+  const double freq = pow(theta, -2.0 * j / hd);
+  const double ang = static_cast<double>(p) * freq;
+  tab[idx] = make_float2(static_cast<float>(cos(ang)), static_cast<float>(sin(ang)));
+}
+
+__global__ void __launch_bounds__(256) clear_kernel(int32_t* p, int n) {
+  const int i = blockIdx.x * 256 + threadIdx.x;
+  if (i < n) p[i] = 0;
+}
+
+__global__ void __launch_bounds__(256) mark_kernel(const int32_t* exact, int n_exact, int32_t* mask, int n_rows) {
+  const int i = blockIdx.x * 256 + threadIdx.x;
+  if (i >= n_exact) return;
+  const int r = exact[i];
+  if (r >= 0 && r < n_rows) mask[r] = 1;
+}
+
+// One workgroup of 1024 threads: thread t owns a contiguous run of rows,
+// counts the unmarked ones, takes an exclusive scan of the counts and writes
+// its rows in order, so the output ascends.
+__global__ void __launch_bounds__(1024) compact_kernel(const int32_t* mask, int n_rows, int32_t* fill_rows,
+                                                       int32_t* n_fill) {
+  __shared__ int part[1024];
+  const int tid = threadIdx.x;
+  const int per = (n_rows + 1023) / 1024;
+  const int r0 = min(n_rows, tid * per), r1 = min(n_rows, r0 + per);
+  int cnt = 0;
+  for (int r = r0; r < r1; ++r) cnt += (mask[r] == 0);
+  part[tid] = cnt;
+  __syncthreads();
+  for (int off = 1; off < 1024; off <<= 1) {
+    const int v = (tid >= off) ? part[tid - off] : 0;
+    __syncthreads();
+    part[tid] += v;
+    __syncthreads();
+  }
+  int o = part[tid] - cnt;
+  for (int r = r0; r < r1; ++r)
+    if (mask[r] == 0) fill_rows[o++] = r;
+  if (tid == 1023) *n_fill = part[1023];
+}
+
+__global__ void __launch_bounds__(256) validate_kernel(const int32_t* rows, int n, int n_rows, int ascending,
+                                                       const int32_t* positions, int max_pos,
+                                                       const int32_t* slots, int n_slots, int32_t* flag) {
+  const int i = blockIdx.x * 256 + threadIdx.x;
+  if (i >= n) return;
+  const int r = rows[i];
+  int bits = 0;
+  if (r < 0 || r >= n_rows) {
+    bits |= 1;
+  } else {
+    const int ps = positions[r];
+    if (ps < 0 || ps >= max_pos) bits |= 2;
+    const int s = slots ? slots[r] : r;
+    if (s < 0 || s >= n_slots) bits |= 4;
+  }
+  if (ascending && i > 0 && rows[i - 1] >= r) bits |= 8;
+  if (bits) atomicOr(flag, bits);
+}
+
+}  // namespace
+
+hipError_t launch_map(const MapParams& p, int n_layers, hipStream_t s) {
+  const int grid = n_layers * p.tiles_m * p.tiles_n;
+  hipLaunchKernelGGL(map_gemm_kernel, dim3(grid), dim3(kThreads), 0, s, p);
+  return hipGetLastError();
+}
+
+hipError_t launch_kv(const KvParams& p, int n_layers, hipStream_t s) {
+  const int grid = n_layers * p.tiles_m * p.tiles_n;
+  if (p.head_dim == 128)
+    hipLaunchKernelGGL(kv_gemm_kernel<128>, dim3(grid), dim3(kThreads), 0, s, p);
+  else
+    hipLaunchKernelGGL(kv_gemm_kernel<64>, dim3(grid), dim3(kThreads), 0, s, p);
+  return hipGetLastError();
+}
+
+hipError_t launch_prep(const PrepParams& p, int n_layers, hipStream_t s) {
+  const int64_t per_layer = static_cast<int64_t>(2 * p.w) * (p.d >> 3);
+  const int blocks = static_cast<int>((per_layer + 255) / 256);
+  hipLaunchKernelGGL(prep_kv_kernel, dim3(blocks, n_layers), dim3(256), 0, s, p);
+  return hipGetLastError();
+}
+
+hipError_t launch_rope_table(float* table, int max_pos, int head_dim, double theta, hipStream_t s) {
+  const int64_t n = static_cast<int64_t>(max_pos) * (head_dim / 2);
+  const int blocks = static_cast<int>((n + 255) / 256);
+  hipLaunchKernelGGL(rope_table_kernel, dim3(blocks), dim3(256), 0, s, reinterpret_cast<float2*>(table),
+                     max_pos, head_dim, theta);
+  return hipGetLastError();
+}
+
+hipError_t launch_fill_rows(const int32_t* exact, int n_exact, int n_rows, int32_t* mask, int32_t* fill_rows,
+                            int32_t* n_fill, hipStream_t s) {
+  hipLaunchKernelGGL(clear_kernel, dim3((n_rows + 255) / 256 > 0 ? (n_rows + 255) / 256 : 1), dim3(256), 0, s,
+                     mask, n_rows);
+  if (n_exact > 0)
+    hipLaunchKernelGGL(mark_kernel, dim3((n_exact + 255) / 256), dim3(256), 0, s, exact, n_exact, mask, n_rows);
+  hipLaunchKernelGGL(compact_kernel, dim3(1), dim3(1024), 0, s, mask, n_rows, fill_rows, n_fill);
+  return hipGetLastError();
+}
+
+hipError_t launch_validate(const int32_t* rows, int n, int n_rows, int ascending, const int32_t* positions,
+                           int max_pos, const int32_t* slots, int n_slots, int32_t* flag, hipStream_t s) {
+  hipLaunchKernelGGL(clear_kernel, dim3(1), dim3(256), 0, s, flag, 1);
+  if (n > 0)
+    hipLaunchKernelGGL(validate_kernel, dim3((n + 255) / 256), dim3(256), 0, s, rows, n, n_rows, ascending,
+                       positions, max_pos, slots, n_slots, flag);
+  return hipGetLastError();
+}
+
+}  // namespace rf

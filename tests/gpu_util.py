@@ -1,0 +1,151 @@
+"""Helpers for the GPU tests: upload a workload, run the library, compare.
+
+Inputs come from ``workloads``; expected values come from ``oracle``; the
+device results come from librf through ``late_layer_kv_amd.binding``.
+"""
+from __future__ import annotations
+
+import numpy as np
+import torch
+
+import oracle
+from late_layer_kv_amd import binding as B
+
+CANARY = 0x7FC1          # a bf16 NaN pattern the fill never produces
+FRO_TOL = 5e-3           # Frobenius relative error bound per layer, K and V separately
+MAXEL_TOL = 3e-2         # max element error, floored by the reference head vector's RMS
+BF16_ONE = 0x3F80
+
+
+def t16(a: np.ndarray) -> torch.Tensor:
+    return torch.from_numpy(np.ascontiguousarray(a).view(np.int16))
+
+
+def i32(a) -> torch.Tensor:
+    return torch.from_numpy(np.ascontiguousarray(np.asarray(a, dtype=np.int32)))
+
+
+def bits_to_f64(t: torch.Tensor) -> np.ndarray:
+    return oracle.bf16_bits_to_f64(t.cpu().numpy().view(np.uint16))
+
+
+class DeviceInputs:
+    """A workload's inputs in device memory (maps in pinned host memory if asked)."""
+
+    def __init__(self, w, maps_on_host: bool = None, device: str = "cuda:0"):
+        s = w.spec
+        self.w = w
+        self.device = device
+        host = s.maps_on_host if maps_on_host is None else maps_on_host
+        self.maps_on_host = host
+        self.x = t16(w.x).to(device)
+        if host:
+            self.map_a = [t16(a).pin_memory() for a in w.map_a]
+            self.map_b = [t16(b).pin_memory() for b in w.map_b]
+        else:
+            self.map_a = [t16(a).to(device) for a in w.map_a]
+            self.map_b = [t16(b).to(device) for b in w.map_b]
+        self.gamma = [t16(g).to(device) for g in w.gamma]
+        self.w_k = [t16(a).to(device) for a in w.w_k]
+        self.w_v = [t16(a).to(device) for a in w.w_v]
+        self.positions = i32(w.positions).to(device)
+        self.exact = i32(w.exact_rows).to(device)
+
+    def caches(self):
+        s = self.w.spec
+        mk = lambda: [torch.full((s.n_rows, s.kv_width), CANARY, dtype=torch.int16, device=self.device)
+                      for _ in range(s.n_late)]
+        return mk(), mk()
+
+
+def plan_for(w, **kw) -> B.Plan:
+    return B.Plan.for_spec(w.spec, **kw)
+
+
+def gpu_fill_rows(plan, di: DeviceInputs, exact: torch.Tensor = None):
+    s = di.w.spec
+    ex = di.exact if exact is None else exact
+    out = torch.full((max(s.n_rows, 1),), -7, dtype=torch.int32, device=di.device)
+    nf = torch.zeros(1, dtype=torch.int32, device=di.device)
+    ws = torch.empty(B.fill_rows_workspace_bytes(s.n_rows), dtype=torch.uint8, device=di.device)
+    B.fill_rows(plan, ex, out, nf, ws)
+    torch.cuda.synchronize()
+    n = int(nf.item())
+    return out[:n].clone(), n
+
+
+def gpu_fill(plan, di: DeviceInputs, rows: torch.Tensor, n_fill: int, caches=None, layers_per_launch=None,
+             map_a=None, map_b=None, rope=None, slots=None):
+    s = di.w.spec
+    kc, vc = di.caches() if caches is None else caches
+    g = s.n_late if layers_per_launch is None else layers_per_launch
+    ws = torch.empty(max(plan.fill_workspace_bytes(n_fill, g), 256), dtype=torch.uint8, device=di.device)
+    B.fill(plan, di.x, rows, n_fill, di.positions, slots, di.map_a if map_a is None else map_a,
+           di.map_b if map_b is None else map_b, di.gamma, di.w_k, di.w_v, rope, kc, vc, ws)
+    torch.cuda.synchronize()
+    return kc, vc
+
+
+def gpu_kv_project(plan, di: DeviceInputs, layer_in, rows: torch.Tensor, n: int, caches=None, slots=None):
+    s = di.w.spec
+    kc, vc = di.caches() if caches is None else caches
+    ws = torch.empty(plan.kv_project_workspace_bytes(s.n_late), dtype=torch.uint8, device=di.device)
+    B.kv_project(plan, layer_in, rows, n, di.positions, slots, di.gamma, di.w_k, di.w_v, None, kc, vc, ws)
+    torch.cuda.synchronize()
+    return kc, vc
+
+
+def kv_errors(got: np.ndarray, ref: np.ndarray, head_dim: int):
+    """(Frobenius relative, max floored element, inf-norm ratio) of got vs ref."""
+    n, width = ref.shape
+    d = got - ref
+    fro = np.linalg.norm(d) / np.linalg.norm(ref)
+    rh = ref.reshape(n, width // head_dim, head_dim)
+    rms = np.sqrt(np.mean(rh * rh, axis=2, keepdims=True))
+    floor = np.maximum(np.abs(rh), rms)
+    maxel = float(np.max(np.abs(d.reshape(rh.shape)) / floor))
+    inf = float(np.max(np.abs(d)) / np.max(np.abs(ref)))
+    return float(fro), maxel, inf
+
+
+def check_values(kc, vc, ref: dict, rows: np.ndarray, head_dim: int, slots: np.ndarray = None):
+    """Compare cache rows at slot(rows) with the oracle, per layer, K and V."""
+    sl = rows if slots is None else slots[rows]
+    idx = torch.from_numpy(np.asarray(sl, dtype=np.int64)).to(kc[0].device)
+    worst = {"fro": 0.0, "maxel": 0.0, "inf": 0.0}
+    for l, (rk, rv) in ref.items():
+        for name, cache, r in (("K", kc, rk), ("V", vc, rv)):
+            got = bits_to_f64(cache[l].index_select(0, idx))
+            fro, maxel, inf = kv_errors(got, r, head_dim)
+            worst["fro"] = max(worst["fro"], fro)
+            worst["maxel"] = max(worst["maxel"], maxel)
+            worst["inf"] = max(worst["inf"], inf)
+            assert fro <= FRO_TOL, f"layer {l} {name}: Frobenius relative error {fro:.3e}"
+            assert maxel <= MAXEL_TOL, f"layer {l} {name}: max element error {maxel:.3e}"
+    return worst
+
+
+def check_placement(kc, vc, fill_rows: np.ndarray, n_slots: int, slots: np.ndarray = None):
+    """Bit-exact placement: written slots are exactly slot(fill rows); every
+    other slot still holds the canary in every byte."""
+    filled = np.zeros(n_slots, dtype=bool)
+    filled[fill_rows if slots is None else slots[fill_rows]] = True
+    want = torch.from_numpy(filled).to(kc[0].device)
+    for l in range(len(kc)):
+        for name, cache in (("K", kc), ("V", vc)):
+            eq = cache[l] == CANARY
+            untouched = eq.all(dim=1)
+            anyc = eq.any(dim=1)
+            assert torch.equal(untouched, ~want), f"layer {l} {name}: slots outside the fill set were written"
+            assert not torch.any(anyc & want), f"layer {l} {name}: a filled slot still holds canary bytes"
+
+
+def identity_maps(di: DeviceInputs):
+    """A = I, b = 0 for every late layer, on the device."""
+    s = di.w.spec
+    eye = torch.zeros((s.d_out, s.d_in), dtype=torch.int16)
+    k = min(s.d_in, s.d_out)
+    eye[torch.arange(k), torch.arange(k)] = BF16_ONE
+    a = [eye.to(di.device) for _ in range(s.n_late)]
+    b = [torch.zeros(s.d_out, dtype=torch.int16, device=di.device) for _ in range(s.n_late)]
+    return a, b

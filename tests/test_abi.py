@@ -1,0 +1,164 @@
+"""C-ABI library checks that need no GPU: symbols, host-side errors, host ridge."""
+import ctypes as C
+import os
+import re
+
+import numpy as np
+import pytest
+
+import oracle
+from late_layer_kv_amd import binding as B
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "rf.h")
+
+
+def _declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    names = set(re.findall(r"\b(rf_[a-z_0-9]+)\s*\(", src))
+    return sorted(names)
+
+
+def test_header_and_binding_agree():
+    assert sorted(B.EXPORTS) == _declared_functions()
+
+
+def test_library_exports_every_declared_symbol():
+    L = B.lib()
+    for name in _declared_functions():
+        assert hasattr(L, name), name
+
+
+def _shape(**kw):
+    base = dict(d_in=256, d_out=256, n_late=4, n_kv=2, head_dim=64, rms_eps=1e-5, rope_theta=1e4,
+                n_rows=512, n_slots=512, max_pos=512)
+    base.update(kw)
+    return base
+
+
+@pytest.mark.parametrize("bad,status", [
+    (dict(d_in=100), -2), (dict(d_out=320), -2), (dict(n_late=0), -2), (dict(head_dim=96), -2),
+    (dict(n_kv=1), -2), (dict(rope_theta=1.0), -2), (dict(max_pos=0), -2), (dict(rms_eps=-1.0), -2),
+])
+def test_plan_rejects_bad_shapes(bad, status):
+    with pytest.raises(B.RfError) as e:
+        B.Plan(**_shape(**bad))
+    assert e.value.status == status
+    assert B.last_error()
+
+
+def test_plan_rejects_unknown_flags():
+    L = B.lib()
+    sh = B.Shape(*_shape().values())
+    h = C.c_void_p()
+    assert L.rf_plan_create(C.byref(sh), 8, C.byref(h)) == -1
+    assert L.rf_plan_create(None, 0, C.byref(h)) == -1
+
+
+def test_fill_argument_errors_before_any_device_work():
+    """Every check here fails on the host, before a HIP call, so it runs without a GPU."""
+    p = B.Plan(**_shape())
+    L = B.lib()
+    nl = 4
+    fake = C.c_void_p(0x1000)  # never dereferenced: the call must fail first
+    arr = (C.c_void_p * nl)(*([0x1000] * nl))
+    null_arr = (C.c_void_p * nl)(*([0x1000] * (nl - 1) + [0]))
+    ws = 1 << 40
+
+    def call(x=fake, ld=256, rows=fake, n=10, pos=fake, maps=arr, gam=arr, ws_ptr=C.c_void_p(0x10000), ws_b=ws):
+        return L.rf_fill(p.handle, x, ld, rows, n, pos, None, maps, arr, gam, arr, arr, None, arr, arr,
+                         ws_ptr, ws_b, None)
+    assert call(n=-1) == -1
+    assert call(n=513) == -1
+    assert call(x=None) == -1
+    assert call(x=C.c_void_p(0x1008)) == -1       # misaligned
+    assert call(ld=100) == -1
+    assert call(ld=260) == -1                      # ld not a multiple of 8
+    assert call(rows=None) == -1
+    assert call(pos=None) == -1
+    assert call(maps=null_arr) == -1
+    assert call(gam=None) == -1
+    assert call(ws_ptr=C.c_void_p(0x10010)) == -4  # workspace misaligned
+    assert call(ws_b=16) == -4
+    assert "workspace" in B.last_error()
+    p.close()
+
+
+def test_workspace_sizes():
+    p = B.Plan(**_shape())
+    assert p.fill_workspace_bytes(448, 1) > 0
+    assert p.fill_workspace_bytes(448, 4) > p.fill_workspace_bytes(448, 1)
+    assert p.fill_workspace_bytes(448, 5) == 0   # more layers than the plan has
+    assert p.fill_workspace_bytes(-1, 1) == 0
+    # rope table + flag + prepared weights + Y, each rounded to 256 bytes
+    rope = 512 * 32 * 8
+    prep = 2 * 128 * 256 * 2
+    y = 448 * 256 * 2
+    assert p.fill_workspace_bytes(448, 1) == rope + 256 + prep + y
+    assert p.kv_project_workspace_bytes(2) == rope + 256 + 2 * prep
+    assert B.fill_rows_workspace_bytes(1000) == 4096
+    p.close()
+
+
+# ---- host ridge (float64 inside the library) against the fp64 oracle
+
+
+def _data(seed, n, d_in, d_out, noise=0.3):
+    g = np.random.default_rng(seed)
+    x = (g.standard_normal((n, d_in)) * g.uniform(0.5, 2.0, d_in) + g.standard_normal(d_in)).astype(np.float32)
+    m = g.standard_normal((d_out, d_in))
+    y = (x @ m.T + g.standard_normal(d_out) + noise * g.standard_normal((n, d_out))).astype(np.float32)
+    return x, y
+
+
+@pytest.mark.parametrize("lam", [0.03, 1e-3, 1.0])
+def test_ridge_fit_matches_oracle(lam):
+    x, y = _data(1, 400, 24, 16)
+    a, b = B.ridge_fit(x, y, lam)
+    ar, br = oracle.ridge_fit(x.astype(np.float64), y.astype(np.float64), lam)
+    assert np.allclose(a, ar, rtol=1e-5, atol=1e-6)
+    assert np.allclose(b, br, rtol=1e-5, atol=1e-5)
+
+
+def test_ridge_raw_matches_oracle():
+    x, y = _data(2, 300, 20, 8)
+    a, b = B.ridge_fit(x, y, 2.5, raw=True)
+    ar, br = oracle.ridge_fit_raw(x.astype(np.float64), y.astype(np.float64), 2.5)
+    assert np.allclose(a, ar, rtol=1e-5, atol=1e-6)
+    assert np.array_equal(b, np.zeros_like(b))
+
+
+def test_ridge_running_sums_and_new_lambda():
+    x, y = _data(3, 500, 16, 12)
+    acc = B.RidgeAccumulator(16, 12)
+    for a0, a1 in ((0, 1), (1, 200), (200, 500)):
+        acc.add(x[a0:a1], y[a0:a1])
+    for lam in (0.03, 0.3):
+        a1, b1 = acc.solve(lam)
+        a2, b2 = B.ridge_fit(x, y, lam)
+        assert np.allclose(a1, a2, rtol=1e-6, atol=1e-7)
+        assert np.allclose(b1, b2, rtol=1e-6, atol=1e-6)
+    acc.close()
+
+
+def test_ridge_recovers_map_as_lambda_vanishes():
+    x, y = _data(4, 300, 12, 6, noise=0.0)
+    ar, br = oracle.ridge_fit(x.astype(np.float64), y.astype(np.float64), 1e-12)
+    a, b = B.ridge_fit(x, y, 1e-12)
+    assert np.allclose(a, ar, rtol=1e-4, atol=1e-5)
+
+
+def test_ridge_errors():
+    with pytest.raises(B.RfError) as e:
+        B.RidgeAccumulator(0, 3)
+    assert e.value.status == -1
+    acc = B.RidgeAccumulator(4, 2)
+    with pytest.raises(B.RfError):
+        acc.solve(0.1)   # nothing accumulated
+    acc.add(np.zeros((3, 4), np.float32), np.zeros((3, 2), np.float32))
+    with pytest.raises(B.RfError) as e:
+        acc.solve(0.0)   # singular without a penalty
+    assert e.value.status == -6
+    with pytest.raises(B.RfError):
+        acc.solve(-1.0)
