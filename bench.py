@@ -1,0 +1,189 @@
+#!/usr/bin/env python3
+"""Throughput of the late-layer cache fill on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+
+A step is one pass of the whole fill path over one batch of synthetic input:
+rf_fill_rows (the fill-row set from the exact rows) and rf_fill (map
+contraction, RMSNorm, K/V projections, RoPE and cache scatter for every late
+layer; for the streamed workload also the host->device map copies).  Inputs
+are resident in device memory (pinned host memory for streamed maps) before
+the timed region starts.  W untimed steps, then K timed steps bracketed by
+device synchronisation; one JSON line goes to stdout, progress to stderr.
+
+``value`` is filled rows per second over all late layers.  The roofline entry
+is the dominant kernel (the map contraction): algorithmic flops per launch,
+2 d_in d_out per filled row per layer times the rows and layers one launch
+processes, divided by its mean launch time from HIP events recorded around
+every launch on the stream it runs on.  ``cpu_baseline`` is the fp64 numpy
+oracle timed on a bounded sample of the same workload on the host cores.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+import workloads
+
+PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA, published
+PEAK_HBM_GBS = 8000.0
+
+# layers per launch used by the benchmark (divides the late-layer count)
+GROUP = {"tiny": 4, "8b": 22, "27b": 6, "27b_120k": 6, "8b_ragged_host": 1}
+# rows of the oracle's timed sample (None: every fill row)
+CPU_SAMPLE = {"tiny": None, "8b": 512, "27b": 256, "27b_120k": 256, "8b_ragged_host": 512}
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def t16(a, dev, pinned=False):
+    import torch
+    t = torch.from_numpy(np.ascontiguousarray(a).view(np.int16))
+    return t.pin_memory() if pinned else t.to(dev)
+
+
+def flops_per_row_layer(s):
+    """Algorithmic flops of one filled row in one late layer: the map
+    (2 d_in d_out) and the key and value projections (2 * 2 d_out w)."""
+    return 2 * s.d_in * s.d_out, 4 * s.d_out * s.kv_width
+
+
+def cpu_baseline(w, fill, name):
+    import oracle
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([i.get("num_threads", 1) for i in threadpool_info()] or [os.cpu_count() or 1])
+    except Exception:
+        cores = os.cpu_count() or 1
+    n = CPU_SAMPLE[name]
+    rows = fill if n is None or n >= len(fill) else \
+        np.sort(np.random.default_rng(0).choice(fill, size=n, replace=False)).astype(np.int32)
+    t0 = time.perf_counter()
+    oracle.fill_workload(w, rows=rows)
+    dt = time.perf_counter() - t0
+    return {"value": len(rows) / dt, "unit": "rows/s", "cores": int(cores), "kind": "oracle",
+            "sample": f"{len(rows)} fill rows x all {w.spec.n_late} late layers, fp64 numpy, {dt:.1f} s"}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="27b_120k", choices=workloads.CONFIG_ORDER)
+    ap.add_argument("--layers-per-launch", type=int, default=None)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only (--gpus {args.gpus} asked): the fill runs on a single MI355X "
+              "in this build; see the sharding notes in DESIGN.md", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from late_layer_kv_amd import binding as B
+
+    name = args.workload
+    s = workloads.spec(name)
+    dev = "cuda:0"
+    log(f"[bench] {name}: drawing inputs")
+    t0 = time.perf_counter()
+    w = workloads.make(s)
+    log(f"[bench] {name}: inputs drawn in {time.perf_counter() - t0:.1f} s; uploading")
+    host_maps = s.maps_on_host
+    x = t16(w.x, dev)
+    map_a = [t16(a, dev, host_maps) for a in w.map_a]
+    map_b = [t16(b, dev, host_maps) for b in w.map_b]
+    gamma = [t16(g, dev) for g in w.gamma]
+    w_k = [t16(a, dev) for a in w.w_k]
+    w_v = [t16(a, dev) for a in w.w_v]
+    positions = torch.from_numpy(w.positions).to(dev)
+    exact = torch.from_numpy(w.exact_rows).to(dev)
+    n_fill = s.n_rows - len(np.unique(w.exact_rows))
+    kc = [torch.empty((s.n_rows, s.kv_width), dtype=torch.int16, device=dev) for _ in range(s.n_late)]
+    vc = [torch.empty((s.n_rows, s.kv_width), dtype=torch.int16, device=dev) for _ in range(s.n_late)]
+
+    plan = B.Plan.for_spec(s)
+    g = args.layers_per_launch or GROUP[name]
+    ws = torch.empty(plan.fill_workspace_bytes(n_fill, g), dtype=torch.uint8, device=dev)
+    fill_rows = torch.empty(s.n_rows, dtype=torch.int32, device=dev)
+    n_fill_dev = torch.empty(1, dtype=torch.int32, device=dev)
+    rows_ws = torch.empty(B.fill_rows_workspace_bytes(s.n_rows), dtype=torch.uint8, device=dev)
+    torch.cuda.synchronize()
+
+    def step():
+        B.fill_rows(plan, exact, fill_rows, n_fill_dev, rows_ws)
+        B.fill(plan, x, fill_rows, n_fill, positions, None, map_a, map_b, gamma, w_k, w_v, None, kc, vc, ws)
+
+    log(f"[bench] {name}: n_fill={n_fill}, {s.n_late} late layers, {g} per launch; warmup {args.warmup}")
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    assert int(n_fill_dev.item()) == n_fill
+
+    log(f"[bench] {name}: timing {args.steps} steps")
+    plan.profile(True)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record()
+    for _ in range(args.steps):
+        step()
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / args.steps
+    prof = plan.profile_read()
+    plan.profile(False)
+
+    f_map, f_kv = flops_per_row_layer(s)
+    step_flops = n_fill * s.n_late * (f_map + f_kv)
+    map_ms, map_n = prof["map"]
+    kv_ms, kv_n = prof["kv"]
+    map_launch_flops = n_fill * s.n_late * f_map * args.steps / max(map_n, 1)
+    map_avg_ms = map_ms / max(map_n, 1)
+    map_tflops = map_launch_flops / (map_avg_ms * 1e-3) / 1e12
+    kv_tflops = n_fill * s.n_late * f_kv * args.steps / (kv_ms * 1e-3) / 1e12 if kv_ms else None
+    kernels = {k: {"ms_per_step": v[0] / args.steps, "launches_per_step": v[1] / args.steps}
+               for k, v in prof.items() if v[1]}
+    log(f"[bench] {name}: {ms:.3f} ms/step, map {map_avg_ms:.3f} ms/launch ({map_tflops:.0f} TFLOP/s), "
+        f"kv {kv_tflops and round(kv_tflops)} TFLOP/s")
+
+    out = {
+        "metric": "filled rows/s (all late layers)",
+        "value": n_fill / (ms * 1e-3),
+        "unit": "rows/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": name, "d_in": s.d_in, "d_out": s.d_out, "late_layers": s.n_late,
+                   "kv_heads": s.n_kv, "head_dim": s.head_dim, "rows": s.n_rows, "fill_rows": n_fill,
+                   "prompts": list(s.prompt_lens), "maps": "pinned host, streamed" if host_maps else "HBM",
+                   "layers_per_launch": 1 if host_maps else g},
+        "tflops": step_flops / (ms * 1e-3) / 1e12,
+        "frac_of_bf16_peak": step_flops / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS,
+        "roofline": {"bound": "mfma", "kernel": "map_gemm", "achieved": map_tflops, "peak": PEAK_BF16_TFLOPS,
+                     "unit": "TFLOP/s", "frac": map_tflops / PEAK_BF16_TFLOPS, "traffic": None,
+                     "flops_per_launch": map_launch_flops, "ms_per_launch": map_avg_ms},
+        "kernels": kernels,
+        "kv_gemm_tflops": kv_tflops,
+    }
+    if not args.no_cpu_baseline:
+        log(f"[bench] {name}: timing the fp64 oracle on a sample")
+        f = np.setdiff1d(np.arange(s.n_rows), w.exact_rows).astype(np.int32)
+        out["cpu_baseline"] = cpu_baseline(w, f, name)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

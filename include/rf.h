@@ -122,15 +122,14 @@ rf_status rf_rope_table(const rf_plan* plan, float* table, void* hip_stream);
  *               *n_fill entries (the rest is left untouched)
  *   n_fill      [1] int32 out (device)
  *   workspace   >= rf_fill_rows_workspace_bytes(n_rows) bytes, 256-byte aligned
- * Out-of-range exact rows are ignored by the kernels (RF_VALIDATE reports them). */
+ * Out-of-range exact rows are ignored. */
 size_t rf_fill_rows_workspace_bytes(int32_t n_rows);
-rf_status rf_fill_rows(const rf_plan* plan, const int32_t* exact_rows, int32_t n_exact,
+rf_status rf_fill_rows(rf_plan* plan, const int32_t* exact_rows, int32_t n_exact,
                        int32_t* fill_rows, int32_t* n_fill,
                        void* workspace, size_t ws_bytes, void* hip_stream);
 
 /* The fill (steps 1-5 above) for n_fill rows and every late layer.
- *   x              [n_rows][ld_x] bf16, ld_x >= d_in, ld_x % 8 == 0, 16-byte aligned;
- *                  n_rows*ld_x*2 must be below 2^32 bytes
+ *   x              [n_rows][ld_x] bf16, ld_x >= d_in, ld_x % 8 == 0, 16-byte aligned
  *   fill_rows      [n_fill] int32, ascending, unique, in [0, n_rows)
  *   positions      [n_rows] int32, RoPE position of each row, in [0, max_pos)
  *   slot_of_row    [n_rows] int32 cache slot of each row in [0, n_slots), or
@@ -191,6 +190,28 @@ void rf_ridge_acc_destroy(rf_ridge_acc* acc);
 /* create + add + solve + destroy in one call */
 rf_status rf_ridge_fit(const float* x, const float* y, int64_t n, int32_t d_in, int32_t d_out,
                        double lambda, int32_t flags, float* a, float* b);
+
+/* ---- Kernel timing -------------------------------------------------------
+ * With profiling on, every launch and map copy the plan issues is bracketed
+ * by a pair of HIP events recorded on the stream it runs on (the caller's
+ * stream, or the side stream for map copies).  rf_plan_profile_read waits for
+ * the recorded events, adds up their elapsed times per kind and clears them.
+ * Turning profiling on or off discards unread records. */
+enum {
+  RF_K_MAP = 0,       /* map contraction (map_gemm)                  */
+  RF_K_KV = 1,        /* norm + K/V contraction with RoPE and scatter */
+  RF_K_PREP = 2,      /* gamma folded into [W_k|W_v]                 */
+  RF_K_ROPE = 3,      /* RoPE table                                  */
+  RF_K_ROWS = 4,      /* fill-row compaction                         */
+  RF_K_COPY = 5,      /* host -> device map copy (RF_MAPS_HOST)      */
+  RF_K_COUNT = 6
+};
+typedef struct rf_profile {
+  double ms[RF_K_COUNT];        /* summed event time per kind, milliseconds */
+  int64_t launches[RF_K_COUNT]; /* launches (or copies) per kind            */
+} rf_profile;
+rf_status rf_plan_profile(rf_plan* plan, int32_t enable);
+rf_status rf_plan_profile_read(rf_plan* plan, rf_profile* out);
 
 /* Thread-local message for the last non-OK status of this thread ("" if none). */
 const char* rf_last_error(void);

@@ -29,8 +29,10 @@ EXPORTS = [
     "rf_plan_create", "rf_plan_destroy", "rf_fill_workspace_bytes", "rf_kv_project_workspace_bytes",
     "rf_rope_table", "rf_fill_rows_workspace_bytes", "rf_fill_rows", "rf_fill", "rf_kv_project",
     "rf_ridge_acc_create", "rf_ridge_acc_add", "rf_ridge_solve", "rf_ridge_acc_destroy", "rf_ridge_fit",
-    "rf_last_error",
+    "rf_plan_profile", "rf_plan_profile_read", "rf_last_error",
 ]
+
+KERNEL_KINDS = ["map", "kv", "prep", "rope", "rows", "copy"]
 
 
 class RfError(RuntimeError):
@@ -43,6 +45,10 @@ class Shape(C.Structure):
     _fields_ = [("d_in", C.c_int32), ("d_out", C.c_int32), ("n_late", C.c_int32), ("n_kv", C.c_int32),
                 ("head_dim", C.c_int32), ("rms_eps", C.c_float), ("rope_theta", C.c_double),
                 ("n_rows", C.c_int32), ("n_slots", C.c_int32), ("max_pos", C.c_int32)]
+
+
+class Profile(C.Structure):
+    _fields_ = [("ms", C.c_double * 6), ("launches", C.c_int64 * 6)]
 
 
 _lib = None
@@ -74,6 +80,8 @@ def lib():
         "rf_ridge_solve": (i32, [P, dbl, i32, P, P]),
         "rf_ridge_acc_destroy": (None, [P]),
         "rf_ridge_fit": (i32, [P, P, i64, i32, i32, dbl, i32, P, P]),
+        "rf_plan_profile": (i32, [P, i32]),
+        "rf_plan_profile_read": (i32, [P, C.POINTER(Profile)]),
         "rf_last_error": (C.c_char_p, []),
     }
     for name, (res, args) in sig.items():
@@ -149,6 +157,16 @@ class Plan:
 
     def kv_project_workspace_bytes(self, layers_per_launch: int = 1) -> int:
         return int(lib().rf_kv_project_workspace_bytes(self.handle, layers_per_launch))
+
+    def profile(self, enable: bool) -> None:
+        """Bracket every launch of this plan with HIP events (rf_plan_profile)."""
+        _check("rf_plan_profile", lib().rf_plan_profile(self.handle, 1 if enable else 0))
+
+    def profile_read(self) -> dict:
+        """{kind: (milliseconds, launches)} since the last read (rf_plan_profile_read)."""
+        pr = Profile()
+        _check("rf_plan_profile_read", lib().rf_plan_profile_read(self.handle, C.byref(pr)))
+        return {k: (pr.ms[i], int(pr.launches[i])) for i, k in enumerate(KERNEL_KINDS)}
 
 
 def fill_rows_workspace_bytes(n_rows: int) -> int:

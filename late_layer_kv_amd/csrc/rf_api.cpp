@@ -7,6 +7,7 @@
 #include <cstdio>
 #include <cstring>
 #include <string>
+#include <vector>
 
 #include "../../include/rf.h"
 #include "rf_error.h"
@@ -49,7 +50,60 @@ struct rf_plan {
   uint16_t* mapbuf[2] = {nullptr, nullptr};  // [d_out][d_in] then [d_out], per buffer
   size_t map_elems = 0;
   size_t bias_off = 0;  // element offset of b inside a buffer
+  // kernel timing (rf_plan_profile)
+  struct Rec {
+    int kind;
+    hipEvent_t a, b;
+  };
+  bool prof = false;
+  std::vector<Rec> recs;
+  std::vector<hipEvent_t> pool;
+  hipEvent_t take_event() {
+    hipEvent_t e = nullptr;
+    if (!pool.empty()) {
+      e = pool.back();
+      pool.pop_back();
+    } else if (hipEventCreate(&e) != hipSuccess) {
+      e = nullptr;
+    }
+    return e;
+  }
+  void drop_records() {
+    for (auto& r : recs) {
+      pool.push_back(r.a);
+      pool.push_back(r.b);
+    }
+    recs.clear();
+  }
 };
+
+namespace {
+
+// Brackets one launch (or copy) with an event pair when profiling is on.
+class Timed {
+ public:
+  Timed(rf_plan* p, int kind, hipStream_t s) : p_(p), kind_(kind), s_(s) {
+    if (p_ && p_->prof && (a_ = p_->take_event())) (void)hipEventRecord(a_, s_);
+  }
+  ~Timed() {
+    if (!a_) return;
+    hipEvent_t b = p_->take_event();
+    if (b && hipEventRecord(b, s_) == hipSuccess) {
+      p_->recs.push_back({kind_, a_, b});
+    } else {
+      p_->pool.push_back(a_);
+      if (b) p_->pool.push_back(b);
+    }
+  }
+
+ private:
+  rf_plan* p_;
+  int kind_;
+  hipStream_t s_;
+  hipEvent_t a_ = nullptr;
+};
+
+}  // namespace
 
 namespace {
 
@@ -152,7 +206,34 @@ void rf_plan_destroy(rf_plan* p) {
   }
   if (p->ev_start) (void)hipEventDestroy(p->ev_start);
   if (p->side) (void)hipStreamDestroy(p->side);
+  p->drop_records();
+  for (hipEvent_t e : p->pool) (void)hipEventDestroy(e);
   delete p;
+}
+
+rf_status rf_plan_profile(rf_plan* p, int32_t enable) {
+  if (!p) return fail(RF_E_ARG, "plan is null");
+  p->drop_records();
+  p->prof = enable != 0;
+  return RF_OK;
+}
+
+rf_status rf_plan_profile_read(rf_plan* p, rf_profile* out) {
+  if (!p || !out) return fail(RF_E_ARG, "null argument");
+  *out = rf_profile{};
+  for (const auto& r : p->recs) {
+    float ms = 0.0f;
+    hipError_t e = hipEventSynchronize(r.b);
+    if (e == hipSuccess) e = hipEventElapsedTime(&ms, r.a, r.b);
+    if (e != hipSuccess) {
+      p->drop_records();
+      return hip_fail(e, "profile read");
+    }
+    out->ms[r.kind] += ms;
+    out->launches[r.kind] += 1;
+  }
+  p->drop_records();
+  return RF_OK;
 }
 
 size_t rf_fill_workspace_bytes(const rf_plan* p, int32_t n_fill, int32_t g) {
@@ -181,7 +262,7 @@ rf_status rf_rope_table(const rf_plan* p, float* table, void* stream) {
   return e == hipSuccess ? RF_OK : hip_fail(e, "rope table launch");
 }
 
-rf_status rf_fill_rows(const rf_plan* p, const int32_t* exact_rows, int32_t n_exact, int32_t* fill_rows,
+rf_status rf_fill_rows(rf_plan* p, const int32_t* exact_rows, int32_t n_exact, int32_t* fill_rows,
                        int32_t* n_fill, void* ws, size_t ws_bytes, void* stream) {
   if (!p) return fail(RF_E_ARG, "plan is null");
   if (n_exact < 0 || (n_exact > 0 && !exact_rows)) return fail(RF_E_ARG, "bad exact rows");
@@ -189,6 +270,7 @@ rf_status rf_fill_rows(const rf_plan* p, const int32_t* exact_rows, int32_t n_ex
   if (!ws || (reinterpret_cast<uintptr_t>(ws) % kAlign) || ws_bytes < rf_fill_rows_workspace_bytes(p->s.n_rows))
     return fail(RF_E_WORKSPACE, "workspace needs %zu bytes, 256-byte aligned",
                 rf_fill_rows_workspace_bytes(p->s.n_rows));
+  Timed tm(p, RF_K_ROWS, static_cast<hipStream_t>(stream));
   hipError_t e = rf::launch_fill_rows(exact_rows, n_exact, p->s.n_rows, static_cast<int32_t*>(ws), fill_rows,
                                       n_fill, static_cast<hipStream_t>(stream));
   return e == hipSuccess ? RF_OK : hip_fail(e, "fill-row launch");
@@ -241,6 +323,7 @@ rf_status rf_fill(rf_plan* p, const uint16_t* x, int64_t ld_x, const int32_t* fi
   if (p->flags & RF_VALIDATE)
     if ((st = run_validate(p, fill_rows, n_fill, 1, positions, slot_of_row, flag, hs)) != RF_OK) return st;
   if (!rope) {
+    Timed tm(p, RF_K_ROPE, hs);
     if ((e = rf::launch_rope_table(rope_ws, s.max_pos, s.head_dim, s.rope_theta, hs)) != hipSuccess)
       return hip_fail(e, "rope table launch");
     rope = rope_ws;
@@ -297,24 +380,34 @@ rf_status rf_fill(rf_plan* p, const uint16_t* x, int64_t ld_x, const int32_t* fi
       const int buf = l & 1;
       if (l >= 2 && (e = hipStreamWaitEvent(p->side, p->ev_consumed[buf], 0)) != hipSuccess)
         return hip_fail(e, "stream wait");
-      if ((e = hipMemcpyAsync(p->mapbuf[buf], map_a[l], a_bytes, hipMemcpyHostToDevice, p->side)) != hipSuccess ||
-          (e = hipMemcpyAsync(p->mapbuf[buf] + p->bias_off, map_b[l], b_bytes, hipMemcpyHostToDevice, p->side)) !=
-              hipSuccess)
-        return hip_fail(e, "map copy");
+      {
+        Timed tm(p, RF_K_COPY, p->side);
+        if ((e = hipMemcpyAsync(p->mapbuf[buf], map_a[l], a_bytes, hipMemcpyHostToDevice, p->side)) != hipSuccess ||
+            (e = hipMemcpyAsync(p->mapbuf[buf] + p->bias_off, map_b[l], b_bytes, hipMemcpyHostToDevice,
+                                p->side)) != hipSuccess)
+          return hip_fail(e, "map copy");
+      }
       if ((e = hipEventRecord(p->ev_copied[buf], p->side)) != hipSuccess) return hip_fail(e, "event record");
 
       pp.gamma[0] = gamma[l];
       pp.wk[0] = w_k[l];
       pp.wv[0] = w_v[l];
-      if ((e = rf::launch_prep(pp, 1, hs)) != hipSuccess) return hip_fail(e, "prep launch");
+      {
+        Timed tm(p, RF_K_PREP, hs);
+        if ((e = rf::launch_prep(pp, 1, hs)) != hipSuccess) return hip_fail(e, "prep launch");
+      }
       if ((e = hipStreamWaitEvent(hs, p->ev_copied[buf], 0)) != hipSuccess) return hip_fail(e, "stream wait");
       mp.a[0] = p->mapbuf[buf];
       mp.b[0] = p->mapbuf[buf] + p->bias_off;
-      if ((e = rf::launch_map(mp, 1, hs)) != hipSuccess) return hip_fail(e, "map launch");
+      {
+        Timed tm(p, RF_K_MAP, hs);
+        if ((e = rf::launch_map(mp, 1, hs)) != hipSuccess) return hip_fail(e, "map launch");
+      }
       if ((e = hipEventRecord(p->ev_consumed[buf], hs)) != hipSuccess) return hip_fail(e, "event record");
       kp.in[0] = ybuf;
       kp.kc[0] = k_cache[l];
       kp.vc[0] = v_cache[l];
+      Timed tm(p, RF_K_KV, hs);
       if ((e = rf::launch_kv(kp, 1, hs)) != hipSuccess) return hip_fail(e, "kv launch");
     }
     return RF_OK;
@@ -332,9 +425,18 @@ rf_status rf_fill(rf_plan* p, const uint16_t* x, int64_t ld_x, const int32_t* fi
       kp.kc[i] = k_cache[l0 + i];
       kp.vc[i] = v_cache[l0 + i];
     }
-    if ((e = rf::launch_prep(pp, g, hs)) != hipSuccess) return hip_fail(e, "prep launch");
-    if ((e = rf::launch_map(mp, g, hs)) != hipSuccess) return hip_fail(e, "map launch");
-    if ((e = rf::launch_kv(kp, g, hs)) != hipSuccess) return hip_fail(e, "kv launch");
+    {
+      Timed tm(p, RF_K_PREP, hs);
+      if ((e = rf::launch_prep(pp, g, hs)) != hipSuccess) return hip_fail(e, "prep launch");
+    }
+    {
+      Timed tm(p, RF_K_MAP, hs);
+      if ((e = rf::launch_map(mp, g, hs)) != hipSuccess) return hip_fail(e, "map launch");
+    }
+    {
+      Timed tm(p, RF_K_KV, hs);
+      if ((e = rf::launch_kv(kp, g, hs)) != hipSuccess) return hip_fail(e, "kv launch");
+    }
   }
   return RF_OK;
 }
@@ -379,6 +481,7 @@ rf_status rf_kv_project(rf_plan* p, const uint16_t* const* layer_in, int64_t ld_
   if (p->flags & RF_VALIDATE)
     if ((st = run_validate(p, rows, n, 0, positions, slot_of_row, flag, hs)) != RF_OK) return st;
   if (!rope) {
+    Timed tm(p, RF_K_ROPE, hs);
     if ((e = rf::launch_rope_table(rope_ws, s.max_pos, s.head_dim, s.rope_theta, hs)) != hipSuccess)
       return hip_fail(e, "rope table launch");
     rope = rope_ws;
@@ -417,8 +520,14 @@ rf_status rf_kv_project(rf_plan* p, const uint16_t* const* layer_in, int64_t ld_
       kp.kc[i] = k_cache[l0 + i];
       kp.vc[i] = v_cache[l0 + i];
     }
-    if ((e = rf::launch_prep(pp, g, hs)) != hipSuccess) return hip_fail(e, "prep launch");
-    if ((e = rf::launch_kv(kp, g, hs)) != hipSuccess) return hip_fail(e, "kv launch");
+    {
+      Timed tm(p, RF_K_PREP, hs);
+      if ((e = rf::launch_prep(pp, g, hs)) != hipSuccess) return hip_fail(e, "prep launch");
+    }
+    {
+      Timed tm(p, RF_K_KV, hs);
+      if ((e = rf::launch_kv(kp, g, hs)) != hipSuccess) return hip_fail(e, "kv launch");
+    }
   }
   return RF_OK;
 }
