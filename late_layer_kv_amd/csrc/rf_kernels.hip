@@ -18,11 +18,21 @@
 // the stores therefore all stay inside one lane.
 //
 // Operand tiles stream global -> LDS with global_load_lds_dwordx4 (no VGPR
-// staging), two 64 KB stages (128 KB of the 160 KB LDS).  Rows are 128 bytes
-// (64 bf16) in LDS; the 16-byte chunk at column c of row r sits at chunk
-// position c ^ (r & 7) so that the MFMA fragment reads of 8 consecutive rows hit
-// distinct banks.  The epilogue reuses the LDS as a 256x256 bf16 staging tile so
-// that every global store is a 16-byte, row-contiguous write.
+// staging) through a ring of kStages stages of 32 contraction columns (32 KB
+// each, 160 KB of LDS in all), so kStages - 1 stages of loads are in flight
+// while one is consumed.  Within a stage the MFMA operand fragments of the next
+// 16-column slice are read into a second register set while the current
+// slice's MFMAs run, and the one workgroup barrier per stage sits between the
+// two slices, where the MFMA pipe still has the first slice queued.  The
+// barrier is issued without a memory fence: the fence would make every wave
+// wait for all in-flight prefetches.  Each wave instead waits (vmcnt) for its
+// own loads of the next stage only; the barrier then publishes them.
+//
+// LDS rows are 64 bytes (32 bf16).  gfx950's LDS has 64 banks (256 bytes per
+// cycle, 16 lanes of a 16-byte read per pass), so the 16-byte chunk c of row r
+// is stored at chunk position c ^ ((r >> 2) & 3): the 16 rows one pass reads
+// then cover all 64 banks.  The epilogue reuses the LDS as a 256x256 bf16
+// staging tile so that every global store is a 16-byte, row-contiguous write.
 //
 // Reduction order is fixed by the tile shape alone (no split-K, no atomics on
 // values), so results are bitwise reproducible and independent of which other
@@ -43,12 +53,20 @@ typedef __attribute__((address_space(3))) void lds_ptr_t;
 typedef const __attribute__((address_space(1))) void gbl_ptr_t;
 
 constexpr int kThreads = 256;
-constexpr int kRowBytes = kTileK * 2;                 // 128 B per LDS row
-constexpr int kOperandBytes = 256 * kRowBytes;        // 32 KB per operand tile
-constexpr int kStageBytes = 2 * kOperandBytes;        // 64 KB
-constexpr int kLdsBytes = 2 * kStageBytes;            // 128 KB
+constexpr int kBK = 32;                               // contraction columns per stage
+constexpr int kStages = 5;
+constexpr int kRowBytes = kBK * 2;                    // 64 B per LDS row
+constexpr int kOperandBytes = 256 * kRowBytes;        // 16 KB per operand tile
+constexpr int kStageBytes = 2 * kOperandBytes;        // 32 KB
+constexpr int kLoadsPerStage = 8;                     // global_load_lds per wave per stage
 constexpr int kStageRowBytes = kTileN * 2;            // 512 B per staged output row
-static_assert(kTileM * kStageRowBytes <= kLdsBytes, "staging tile must fit in LDS");
+constexpr int kStagingBytes = kTileM * kStageRowBytes;  // 128 KB
+constexpr int kSlotOffset = kStagingBytes;            // 256 int32 slot ids after the staging tile
+constexpr int kLdsBytes = (kStages * kStageBytes > kStagingBytes + 1024) ? kStages * kStageBytes
+                                                                         : kStagingBytes + 1024;
+static_assert(kTileK % kBK == 0, "host contraction granule must be a multiple of the stage depth");
+static_assert(kLdsBytes <= 160 * 1024, "LDS budget of gfx950");
+static_assert(kStages >= 3 && kStages <= 5, "wait_loads covers 0..3 stages in flight");
 
 __device__ __forceinline__ float bf16_to_f32(uint16_t b) {
   return __uint_as_float(static_cast<uint32_t>(b) << 16);
@@ -91,46 +109,94 @@ __device__ __forceinline__ TileCoord tile_coord(int t, int tiles_m, int tiles_n)
   return c;
 }
 
-__device__ __forceinline__ void wait_vm_and_barrier() {
-  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-  __syncthreads();
+// Wait until at most `groups` stages of this wave's loads are still in flight
+// (loads complete in issue order for the vmcnt counter).
+__device__ __forceinline__ void wait_loads(int groups) {
+  switch (groups) {
+    case 0: asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); break;
+    case 1: asm volatile("s_waitcnt vmcnt(8)" ::: "memory"); break;
+    case 2: asm volatile("s_waitcnt vmcnt(16)" ::: "memory"); break;
+    default: asm volatile("s_waitcnt vmcnt(24)" ::: "memory"); break;
+  }
 }
+static_assert(kLoadsPerStage == 8, "wait_loads immediates assume 8 loads per stage");
 
-// One k-step (64 columns) of both operand tiles for this wave: 8 rows per
-// instruction, 8 instructions per operand.  src[j] already points at this
-// lane's 16-byte chunk of column block 0; the LDS destination of instruction j
-// is wave_base + j * 1 KB and lane i lands at + 16 i (row i / 8, chunk
-// position i % 8).
-__device__ __forceinline__ void issue_stage(const char* const (&wsrc)[8], const char* const (&xsrc)[8],
+// Workgroup barrier without a memory fence (see the file comment).  The
+// "memory" clobber keeps the compiler from moving LDS accesses across it; the
+// hardware ordering the loop relies on is stated where it is used.
+__device__ __forceinline__ void barrier() { asm volatile("s_barrier" ::: "memory"); }
+
+// One stage (32 contraction columns) of both operand tiles for this wave:
+// 16 rows per instruction, 4 instructions per operand.  src[j] points at this
+// lane's 16-byte chunk of column block 0; instruction j of wave w writes LDS
+// bytes [(4w + j) KB, +1 KB) of its operand tile and lane i lands at + 16 i
+// (row 16 (4w + j) + i / 4, chunk position i % 4).
+__device__ __forceinline__ void issue_stage(const char* const (&wsrc)[4], const char* const (&xsrc)[4],
                                             size_t kbyte, char* wdst, char* xdst) {
 #pragma unroll
-  for (int j = 0; j < 8; ++j)
+  for (int j = 0; j < 4; ++j)
     __builtin_amdgcn_global_load_lds((gbl_ptr_t*)(wsrc[j] + kbyte), (lds_ptr_t*)(wdst + j * 1024), 16, 0, 0);
 #pragma unroll
-  for (int j = 0; j < 8; ++j)
+  for (int j = 0; j < 4; ++j)
     __builtin_amdgcn_global_load_lds((gbl_ptr_t*)(xsrc[j] + kbyte), (lds_ptr_t*)(xdst + j * 1024), 16, 0, 0);
+}
+
+struct Frags {
+  bf16x8 a[4], b[4];
+};
+
+__device__ __forceinline__ void read_frags(Frags& f, const char* st, int aoff, int boff) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) f.a[i] = *reinterpret_cast<const bf16x8*>(st + aoff + i * 32 * kRowBytes);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) f.b[i] = *reinterpret_cast<const bf16x8*>(st + boff + i * 32 * kRowBytes);
+}
+
+template <bool SUMSQ>
+__device__ __forceinline__ void mma_slice(const Frags& f, f32x16 (&acc)[4][4], float (&ss)[4]) {
+  if constexpr (SUMSQ) {
+#pragma unroll
+    for (int mb = 0; mb < 4; ++mb) {
+      ss[mb] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(f.b[mb], f.b[mb], 0, 1),
+                                               __builtin_shufflevector(f.b[mb], f.b[mb], 0, 1), ss[mb], false);
+      ss[mb] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(f.b[mb], f.b[mb], 2, 3),
+                                               __builtin_shufflevector(f.b[mb], f.b[mb], 2, 3), ss[mb], false);
+      ss[mb] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(f.b[mb], f.b[mb], 4, 5),
+                                               __builtin_shufflevector(f.b[mb], f.b[mb], 4, 5), ss[mb], false);
+      ss[mb] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(f.b[mb], f.b[mb], 6, 7),
+                                               __builtin_shufflevector(f.b[mb], f.b[mb], 6, 7), ss[mb], false);
+    }
+  }
+#pragma unroll
+  for (int nb = 0; nb < 4; ++nb)
+#pragma unroll
+    for (int mb = 0; mb < 4; ++mb)
+      acc[nb][mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.a[nb], f.b[mb], acc[nb][mb], 0, 0, 0);
 }
 
 // Main loop shared by both contractions.  On return acc[nb][mb] holds the
 // 32x32 block (features nb, rows mb) of this wave and, with SUMSQ, ss[mb] the
-// sum of squares of this lane's half of the contraction for row mb.
+// sum of squares of this lane's half of the contraction for row mb.  The
+// contraction runs in ascending 16-column slices, which fixes the order of
+// every sum.
 template <bool SUMSQ>
-__device__ __forceinline__ void mainloop(const char* const (&wsrc)[8], const char* const (&xsrc)[8], int nk,
+__device__ __forceinline__ void mainloop(const char* const (&wsrc)[4], const char* const (&xsrc)[4], int nk,
                                          char* smem, f32x16 (&acc)[4][4], float (&ss)[4]) {
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int wn = wave & 1, wm = wave >> 1;
   const int r31 = lane & 31, hsel = lane >> 5;
 
-  char* const wdst = smem + wave * 8 * 1024;
-  char* const xdst = smem + kOperandBytes + wave * 8 * 1024;
+  char* const wdst = smem + wave * 4 * 1024;
+  char* const xdst = smem + kOperandBytes + wave * 4 * 1024;
 
   // Fragment offsets inside a stage.  Row r of a 32-row block is lane & 31;
-  // its 16-byte chunk for contraction slice kk is 2 kk + (lane >> 5).
-  int aoff[4], boff[4];
+  // its 16-byte chunk for slice kk is 2 kk + (lane >> 5), stored at position
+  // chunk ^ ((r >> 2) & 3).
+  int aoff[2], boff[2];
 #pragma unroll
-  for (int kk = 0; kk < 4; ++kk) {
-    const int pos = ((2 * kk + hsel) ^ (r31 & 7)) << 4;
+  for (int kk = 0; kk < 2; ++kk) {
+    const int pos = ((2 * kk + hsel) ^ ((r31 >> 2) & 3)) << 4;
     aoff[kk] = (wn * 128 + r31) * kRowBytes + pos;
     boff[kk] = kOperandBytes + (wm * 128 + r31) * kRowBytes + pos;
   }
@@ -142,51 +208,82 @@ __device__ __forceinline__ void mainloop(const char* const (&wsrc)[8], const cha
     for (int j = 0; j < 4; ++j) acc[i][j] = f32x16{};
   }
 
-  issue_stage(wsrc, xsrc, 0, wdst, xdst);
-  wait_vm_and_barrier();
+  // Prologue: stages 0 .. kStages-2 in flight, wait for stage 0.
+#pragma unroll
+  for (int s = 0; s < kStages - 1; ++s)
+    if (s < nk)
+      issue_stage(wsrc, xsrc, static_cast<size_t>(s) * kRowBytes, wdst + s * kStageBytes, xdst + s * kStageBytes);
+  wait_loads(min(kStages - 2, nk - 1));
+  barrier();
 
-  for (int t = 0; t < nk; ++t) {
-    const int cur = t & 1;
-    if (t + 1 < nk) {
-      const int nxt = cur ^ 1;
-      issue_stage(wsrc, xsrc, static_cast<size_t>(t + 1) * kRowBytes, wdst + nxt * kStageBytes,
-                  xdst + nxt * kStageBytes);
+  // Step t reads stage slot t % kStages.  In step t: slice 0's MFMAs run
+  // while slice 1's fragments are read; then each wave waits for its own
+  // loads of step t+1 and the barrier publishes them (it also proves every
+  // wave has consumed step t-1, whose slot takes the loads of step
+  // t + kStages - 1); slice 1's MFMAs then run while those loads are issued
+  // and the fragments of step t+1's slice 0 are read.
+  Frags fa, fb;
+  read_frags(fa, smem, aoff[0], boff[0]);
+  int t = 0, cur = 0;
+  auto next_slot = [](int s) { return (s + 1 == kStages) ? 0 : s + 1; };
+  // steady state: loads still to issue
+  for (; t + kStages - 1 < nk; ++t) {
+    const int nxt = next_slot(cur);
+    const int fill = (cur == 0) ? kStages - 1 : cur - 1;
+    // slice 0: MFMAs on fa, one fragment read of slice 1 after each of the first 8
+    read_frags(fb, smem + cur * kStageBytes, aoff[1], boff[1]);
+    mma_slice<SUMSQ>(fa, acc, ss);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // DS read
     }
-    const char* st = smem + cur * kStageBytes;
+    __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);
+    __builtin_amdgcn_sched_barrier(0);
+    wait_loads(kStages - 3);
+    barrier();
+    __builtin_amdgcn_sched_barrier(0);
+    // slice 1: MFMAs on fb, interleaved with the reads of step t+1's slice 0
+    // and the loads of step t + kStages - 1
+    read_frags(fa, smem + nxt * kStageBytes, aoff[0], boff[0]);
+    issue_stage(wsrc, xsrc, static_cast<size_t>(t + kStages - 1) * kRowBytes, wdst + fill * kStageBytes,
+                xdst + fill * kStageBytes);
+    mma_slice<SUMSQ>(fb, acc, ss);
 #pragma unroll
-    for (int kk = 0; kk < 4; ++kk) {
-      bf16x8 a[4], b[4];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) a[i] = *reinterpret_cast<const bf16x8*>(st + aoff[kk] + i * 32 * kRowBytes);
-#pragma unroll
-      for (int i = 0; i < 4; ++i) b[i] = *reinterpret_cast<const bf16x8*>(st + boff[kk] + i * 32 * kRowBytes);
-      if constexpr (SUMSQ) {
-#pragma unroll
-        for (int mb = 0; mb < 4; ++mb) {
-          ss[mb] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(b[mb], b[mb], 0, 1),
-                                                   __builtin_shufflevector(b[mb], b[mb], 0, 1), ss[mb], false);
-          ss[mb] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(b[mb], b[mb], 2, 3),
-                                                   __builtin_shufflevector(b[mb], b[mb], 2, 3), ss[mb], false);
-          ss[mb] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(b[mb], b[mb], 4, 5),
-                                                   __builtin_shufflevector(b[mb], b[mb], 4, 5), ss[mb], false);
-          ss[mb] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(b[mb], b[mb], 6, 7),
-                                                   __builtin_shufflevector(b[mb], b[mb], 6, 7), ss[mb], false);
-        }
-      }
-#pragma unroll
-      for (int nb = 0; nb < 4; ++nb)
-#pragma unroll
-        for (int mb = 0; mb < 4; ++mb)
-          acc[nb][mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[nb], b[mb], acc[nb][mb], 0, 0, 0);
+    for (int i = 0; i < 8; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 1);  // MFMA
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 1);  // DS read
     }
-    wait_vm_and_barrier();
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 1);  // MFMA
+      __builtin_amdgcn_sched_group_barrier(0x020, 1, 1);  // VMEM read (LDS DMA)
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    cur = nxt;
   }
+  // drain: every load issued; t + 1 < nk
+  for (; t + 1 < nk; ++t) {
+    const int nxt = next_slot(cur);
+    read_frags(fb, smem + cur * kStageBytes, aoff[1], boff[1]);
+    mma_slice<SUMSQ>(fa, acc, ss);
+    wait_loads(nk - 2 - t);
+    barrier();
+    read_frags(fa, smem + nxt * kStageBytes, aoff[0], boff[0]);
+    mma_slice<SUMSQ>(fb, acc, ss);
+    cur = nxt;
+  }
+  // last step
+  read_frags(fb, smem + cur * kStageBytes, aoff[1], boff[1]);
+  mma_slice<SUMSQ>(fa, acc, ss);
+  mma_slice<SUMSQ>(fb, acc, ss);
 }
 
-// Per-lane source pointers for the 8 load instructions of one operand.  Local
-// row of instruction j is wave * 64 + j * 8 + lane / 8; its LDS chunk position
-// is lane % 8, which holds column chunk (lane % 8) ^ (local row & 7).
-__device__ __forceinline__ int load_chunk(int lane) { return (lane & 7) ^ ((lane >> 3) & 7); }
+// Per-lane source pointers for the 4 load instructions of one operand.  Local
+// row of instruction j is wave * 64 + j * 16 + lane / 4; its LDS chunk
+// position is lane % 4, which holds column chunk (lane % 4) ^ ((row >> 2) & 3)
+// = (lane % 4) ^ ((lane >> 4) & 3).
+__device__ __forceinline__ int load_chunk(int lane) { return (lane & 3) ^ ((lane >> 4) & 3); }
 
 // The staging tile: row r (0..255) of 512 bytes, 16-byte chunk c stored at
 // chunk position c ^ (r & 31).
@@ -202,15 +299,15 @@ __global__ void __launch_bounds__(kThreads) map_gemm_kernel(const MapParams p) {
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
 
-  const char* wsrc[8];
-  const char* xsrc[8];
+  const char* wsrc[4];
+  const char* xsrc[4];
   {
     const int chunk = load_chunk(lane);
     const char* abase = reinterpret_cast<const char*>(p.a[c.g]);
     const char* xbase = reinterpret_cast<const char*>(p.x);
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const int lr = wave * 64 + j * 8 + (lane >> 3);
+    for (int j = 0; j < 4; ++j) {
+      const int lr = wave * 64 + j * 16 + (lane >> 2);
       wsrc[j] = abase + (static_cast<size_t>(n0 + lr) * p.K + chunk * 8) * 2;
       int m = min(m0 + lr, p.M - 1);
       int row = p.rows[m];
@@ -221,7 +318,7 @@ __global__ void __launch_bounds__(kThreads) map_gemm_kernel(const MapParams p) {
 
   f32x16 acc[4][4];
   float ss[4];
-  mainloop<false>(wsrc, xsrc, p.K / kTileK, smem, acc, ss);
+  mainloop<false>(wsrc, xsrc, p.K / kBK, smem, acc, ss);
 
   // Epilogue: + b, round to bf16, stage, 16-byte row stores into Y_g.
   const int wn = wave & 1, wm = wave >> 1, r31 = lane & 31, hsel = lane >> 5;
@@ -263,22 +360,22 @@ __global__ void __launch_bounds__(kThreads) map_gemm_kernel(const MapParams p) {
 template <int HD>
 __global__ void __launch_bounds__(kThreads) kv_gemm_kernel(const KvParams p) {
   __shared__ __attribute__((aligned(1024))) char smem[kLdsBytes];
-  __shared__ int slot_of[kTileM];
+  int* const slot_of = reinterpret_cast<int*>(smem + kSlotOffset);
   const int t = xcd_remap(blockIdx.x, gridDim.x);
   const TileCoord c = tile_coord(t, p.tiles_m, p.tiles_n);
   const int m0 = c.tm * kTileM, n0 = c.tn * kTileN;
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
 
-  const char* wsrc[8];
-  const char* xsrc[8];
+  const char* wsrc[4];
+  const char* xsrc[4];
   {
     const int chunk = load_chunk(lane);
     const char* wbase = reinterpret_cast<const char*>(p.wkv + static_cast<size_t>(c.g) * 2 * p.w * p.K);
     const char* xbase = reinterpret_cast<const char*>(p.in[c.g]);
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const int lr = wave * 64 + j * 8 + (lane >> 3);
+    for (int j = 0; j < 4; ++j) {
+      const int lr = wave * 64 + j * 16 + (lane >> 2);
       wsrc[j] = wbase + (static_cast<size_t>(n0 + lr) * p.K + chunk * 8) * 2;
       const int m = min(m0 + lr, p.M - 1);
       int row = p.in_rows ? p.in_rows[m] : m;
@@ -289,12 +386,12 @@ __global__ void __launch_bounds__(kThreads) kv_gemm_kernel(const KvParams p) {
 
   f32x16 acc[4][4];
   float ss[4];
-  mainloop<true>(wsrc, xsrc, p.K / kTileK, smem, acc, ss);
+  mainloop<true>(wsrc, xsrc, p.K / kBK, smem, acc, ss);
 
   const int wn = wave & 1, wm = wave >> 1, r31 = lane & 31, hsel = lane >> 5;
   const float inv_k = 1.0f / static_cast<float>(p.K);
   float rs[4];
-  int pos[4];
+  int pos[4], slot_r[4];
 #pragma unroll
   for (int mb = 0; mb < 4; ++mb) {
     const float tot = ss[mb] + __shfl_xor(ss[mb], 32);
@@ -314,7 +411,7 @@ __global__ void __launch_bounds__(kThreads) kv_gemm_kernel(const KvParams p) {
       }
     }
     pos[mb] = ps;
-    if (wn == 0 && hsel == 0) slot_of[lr] = slot;
+    slot_r[mb] = slot;
   }
 
   const int fw = n0 + wn * 128;  // first feature of this wave; a whole wave is key or value
@@ -359,7 +456,11 @@ __global__ void __launch_bounds__(kThreads) kv_gemm_kernel(const KvParams p) {
         for (int v = 0; v < 16; ++v) acc[nb][mb][v] *= rs[mb];
   }
 
-  __syncthreads();  // operand stages free; slot_of visible
+  __syncthreads();  // every wave is done reading the operand stages
+  if (wn == 0 && hsel == 0) {
+#pragma unroll
+    for (int mb = 0; mb < 4; ++mb) slot_of[wm * 128 + mb * 32 + r31] = slot_r[mb];
+  }
 #pragma unroll
   for (int nb = 0; nb < 4; ++nb) {
 #pragma unroll
