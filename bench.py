@@ -35,8 +35,10 @@ PEAK_HBM_GBS = 8000.0
 
 # layers per launch used by the benchmark (divides the late-layer count)
 GROUP = {"tiny": 4, "8b": 22, "27b": 6, "27b_120k": 6, "8b_ragged_host": 1}
-# rows of the oracle's timed sample (None: every fill row)
-CPU_SAMPLE = {"tiny": None, "8b": 512, "27b": 256, "27b_120k": 256, "8b_ragged_host": 512}
+# rows of the oracle's timed sample (None: every fill row), sized for 10-30 s
+CPU_SAMPLE = {"tiny": None, "8b": 8192, "27b": 4096, "27b_120k": 4096, "8b_ragged_host": 8192}
+ROOT = os.path.dirname(os.path.abspath(__file__))
+KERNEL_SOURCE = os.path.join(ROOT, "late_layer_kv_amd", "csrc", "rf_kernels.hip")
 
 
 def log(*a):
@@ -53,6 +55,84 @@ def flops_per_row_layer(s):
     """Algorithmic flops of one filled row in one late layer: the map
     (2 d_in d_out) and the key and value projections (2 * 2 d_out w)."""
     return 2 * s.d_in * s.d_out, 4 * s.d_out * s.kv_width
+
+
+def kernel_source_hash() -> str:
+    import hashlib
+    with open(KERNEL_SOURCE, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()
+
+
+def traffic_path(name: str) -> str:
+    return os.path.join(ROOT, "profiles", f"traffic_map_gemm_{name}.json")
+
+
+def measured_traffic(name: str):
+    """HBM bytes per map_gemm launch from the PMC runs, if taken on this kernel source."""
+    try:
+        with open(traffic_path(name)) as f:
+            t = json.load(f)
+    except (OSError, ValueError):
+        return None
+    return t["traffic_bytes_per_launch"] if t.get("kernel_source_sha256") == kernel_source_hash() else None
+
+
+def summarize_pmc(fetch_csv: str, write_csv: str, name: str, calib_bytes: int) -> dict:
+    """Traffic per launch from two rocprofv3 --pmc CSVs (FETCH_SIZE, WRITE_SIZE),
+    each scaled by what the same counter reads for a device copy of known size."""
+    import csv
+
+    def per_kernel(path, counter):
+        sums, n = {}, {}
+        copy = []
+        for r in csv.DictReader(open(path)):
+            if r["Counter_Name"] != counter:
+                continue
+            k, v = r["Kernel_Name"], float(r["Counter_Value"])
+            if "map_gemm" in k or "kv_gemm" in k:
+                kk = "map_gemm" if "map_gemm" in k else "kv_gemm"
+                sums[kk] = sums.get(kk, 0.0) + v
+                n[kk] = n.get(kk, 0) + 1
+            elif "copyBuffer" in k or "copy" in k.lower():
+                copy.append((int(r["Grid_Size"]), v))
+        copy_kib = max(copy)[1] if copy else None
+        return {k: sums[k] / n[k] for k in sums}, copy_kib
+
+    f, fc = per_kernel(fetch_csv, "FETCH_SIZE")
+    w, wc = per_kernel(write_csv, "WRITE_SIZE")
+    kf = calib_bytes / (fc * 1024.0) if fc else 1.0
+    kw = calib_bytes / (wc * 1024.0) if wc else 1.0
+    out = {"workload": name, "kernel_source_sha256": kernel_source_hash(),
+           "copy_calibration": {"bytes": calib_bytes, "fetch_kib": fc, "write_kib": wc,
+                                "fetch_factor": kf, "write_factor": kw},
+           "kernels": {k: {"fetch_kib_per_launch": f[k], "write_kib_per_launch": w.get(k),
+                           "bytes_per_launch": f[k] * 1024 * kf + w.get(k, 0.0) * 1024 * kw} for k in f},
+           "source": {"fetch_csv": fetch_csv, "write_csv": write_csv}}
+    out["traffic_bytes_per_launch"] = out["kernels"]["map_gemm"]["bytes_per_launch"]
+    return out
+
+
+def blas_reference(s, steps):
+    """torch.matmul (hipBLASLt) on the fill's two contraction shapes, bf16."""
+    import torch
+    n_fill = s.n_rows - len(workloads.exact_row_list(s))
+    out = {}
+    for label, (m, n, k) in (("map", (n_fill, s.d_out, s.d_in)), ("kv", (n_fill, 2 * s.kv_width, s.d_out))):
+        a = torch.randn(m, k, device="cuda:0", dtype=torch.bfloat16)
+        b = torch.randn(n, k, device="cuda:0", dtype=torch.bfloat16)
+        for _ in range(3):
+            c = a @ b.t()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record()
+        for _ in range(steps):
+            c = a @ b.t()
+        e1.record()
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / steps
+        out[label] = {"m": m, "n": n, "k": k, "ms": ms, "tflops": 2 * m * n * k / (ms * 1e-3) / 1e12}
+        del a, b, c
+    print(json.dumps({"blas_reference": out, "workload": s.name}), flush=True)
 
 
 def cpu_baseline(w, fill, name):
@@ -80,7 +160,22 @@ def main():
     ap.add_argument("--workload", default="27b_120k", choices=workloads.CONFIG_ORDER)
     ap.add_argument("--layers-per-launch", type=int, default=None)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
+                    help="after timing, copy MIB mebibytes device-to-device once (PMC calibration)")
+    ap.add_argument("--blas-reference", action="store_true",
+                    help="time torch.matmul (hipBLASLt) on the two contraction shapes of --workload and exit; "
+                         "a reference point for the roofline, not part of the fill")
+    ap.add_argument("--pmc-summary", nargs=3, metavar=("FETCH_CSV", "WRITE_CSV", "CALIB_MIB"),
+                    help="write the traffic summary for --workload from two rocprofv3 --pmc CSVs and exit")
     args = ap.parse_args()
+    if args.pmc_summary:
+        t = summarize_pmc(args.pmc_summary[0], args.pmc_summary[1], args.workload,
+                          int(args.pmc_summary[2]) << 20)
+        os.makedirs(os.path.dirname(traffic_path(args.workload)), exist_ok=True)
+        with open(traffic_path(args.workload), "w") as f:
+            json.dump(t, f, indent=1)
+        print(json.dumps(t))
+        return
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (--gpus {args.gpus} asked): the fill runs on a single MI355X "
               "in this build; see the sharding notes in DESIGN.md", file=sys.stderr)
@@ -88,6 +183,10 @@ def main():
 
     import torch
     from late_layer_kv_amd import binding as B
+
+    if args.blas_reference:
+        blas_reference(workloads.spec(args.workload), args.steps)
+        return
 
     name = args.workload
     s = workloads.spec(name)
@@ -139,6 +238,14 @@ def main():
     ms = e0.elapsed_time(e1) / args.steps
     prof = plan.profile_read()
     plan.profile(False)
+    if args.calibrate_copy:
+        n16 = (args.calibrate_copy << 20) // 2
+        src = torch.ones(n16, dtype=torch.int16, device=dev)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
 
     f_map, f_kv = flops_per_row_layer(s)
     step_flops = n_fill * s.n_late * (f_map + f_kv)
@@ -147,6 +254,9 @@ def main():
     map_launch_flops = n_fill * s.n_late * f_map * args.steps / max(map_n, 1)
     map_avg_ms = map_ms / max(map_n, 1)
     map_tflops = map_launch_flops / (map_avg_ms * 1e-3) / 1e12
+    rows_per_launch = n_fill * s.n_late / max(map_n / args.steps, 1)
+    map_launch_bytes = (rows_per_launch / n_fill) * (s.d_out * s.d_in + s.d_out) * 2 \
+        + n_fill * s.d_in * 2 + rows_per_launch * s.d_out * 2
     kv_tflops = n_fill * s.n_late * f_kv * args.steps / (kv_ms * 1e-3) / 1e12 if kv_ms else None
     kernels = {k: {"ms_per_step": v[0] / args.steps, "launches_per_step": v[1] / args.steps}
                for k, v in prof.items() if v[1]}
@@ -173,7 +283,8 @@ def main():
         "tflops": step_flops / (ms * 1e-3) / 1e12,
         "frac_of_bf16_peak": step_flops / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS,
         "roofline": {"bound": "mfma", "kernel": "map_gemm", "achieved": map_tflops, "peak": PEAK_BF16_TFLOPS,
-                     "unit": "TFLOP/s", "frac": map_tflops / PEAK_BF16_TFLOPS, "traffic": None,
+                     "unit": "TFLOP/s", "frac": map_tflops / PEAK_BF16_TFLOPS,
+                     "traffic": measured_traffic(name), "algorithmic_bytes_per_launch": map_launch_bytes,
                      "flops_per_launch": map_launch_flops, "ms_per_launch": map_avg_ms},
         "kernels": kernels,
         "kv_gemm_tflops": kv_tflops,

@@ -91,10 +91,12 @@ struct TileCoord {
 };
 
 // Logical tile -> (layer, row tile, feature tile).  Inside a layer tiles go
-// down groups of 8 row tiles for one feature tile before moving on, so the 32
-// workgroups an XCD runs at once cover about 8 row strips x 4 weight strips.
+// down groups of GM row tiles for one feature tile before moving on, so the
+// 32 workgroups an XCD runs at once cover GM row strips x 32/GM weight strips
+// (measured best: 8 for the map contraction with 16-20 feature tiles, 4 for
+// the key/value contraction with its 8 feature tiles).
+template <int GM>
 __device__ __forceinline__ TileCoord tile_coord(int t, int tiles_m, int tiles_n) {
-  constexpr int GM = 8;
   const int per_layer = tiles_m * tiles_n;
   TileCoord c;
   c.g = t / per_layer;
@@ -294,7 +296,7 @@ __device__ __forceinline__ int stage_off(int row, int chunk) {
 __global__ void __launch_bounds__(kThreads) map_gemm_kernel(const MapParams p) {
   __shared__ __attribute__((aligned(1024))) char smem[kLdsBytes];
   const int t = xcd_remap(blockIdx.x, gridDim.x);
-  const TileCoord c = tile_coord(t, p.tiles_m, p.tiles_n);
+  const TileCoord c = tile_coord<8>(t, p.tiles_m, p.tiles_n);
   const int m0 = c.tm * kTileM, n0 = c.tn * kTileN;
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
@@ -362,7 +364,7 @@ __global__ void __launch_bounds__(kThreads) kv_gemm_kernel(const KvParams p) {
   __shared__ __attribute__((aligned(1024))) char smem[kLdsBytes];
   int* const slot_of = reinterpret_cast<int*>(smem + kSlotOffset);
   const int t = xcd_remap(blockIdx.x, gridDim.x);
-  const TileCoord c = tile_coord(t, p.tiles_m, p.tiles_n);
+  const TileCoord c = tile_coord<4>(t, p.tiles_m, p.tiles_n);
   const int m0 = c.tm * kTileM, n0 = c.tn * kTileN;
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
