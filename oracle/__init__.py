@@ -23,6 +23,10 @@ some pin fails for each.  No function here is "parity unpinned".
 from .fill import (  # noqa: F401
     bf16_bits_to_f64, fill_row_set, predicted_input, rms_norm, project,
     rope_inv_freq, rope, layer_kv, fill_layer, fill_workload, exact_kv_workload,
+    map_matrix,
 )
 from .ridge import RidgeSums, ridge_fit, ridge_fit_raw  # noqa: F401
 from .ceiling import layer_ceiling, mac_ceiling  # noqa: F401
+from .quant import (  # noqa: F401
+    dequantize_q8, dequantize_q8_bf16, f64_to_bf16_bits, quantize_q8,
+)

@@ -109,6 +109,18 @@ def _rows(w, rows: Optional[np.ndarray]) -> np.ndarray:
     return fill_row_set(w.spec.n_rows, w.exact_rows) if rows is None else np.asarray(rows)
 
 
+def map_matrix(w, l: int) -> np.ndarray:
+    """Layer l's map A_l [d_out][d_in] in float64, from bf16 or int8 storage.
+
+    int8 maps (section 2.2 "Size and cost", section 4.2) are dequantized
+    exactly: code times the bf16 scale of its 128-weight block.
+    """
+    if w.map_q is not None:
+        from .quant import dequantize_q8
+        return dequantize_q8(w.map_q[l], w.map_scale[l])
+    return bf16_bits_to_f64(w.map_a[l])
+
+
 def fill_workload(w, rows: Optional[np.ndarray] = None,
                   layers: Optional[List[int]] = None) -> Dict[int, Tuple[np.ndarray, np.ndarray]]:
     """fp64 K and V of every late layer for the given rows of a workload.
@@ -122,7 +134,7 @@ def fill_workload(w, rows: Optional[np.ndarray] = None,
     pos = w.positions[r]
     out = {}
     for l in (range(s.n_late) if layers is None else layers):
-        out[l] = fill_layer(xs, bf16_bits_to_f64(w.map_a[l]), bf16_bits_to_f64(w.map_b[l]),
+        out[l] = fill_layer(xs, map_matrix(w, l), bf16_bits_to_f64(w.map_b[l]),
                             bf16_bits_to_f64(w.gamma[l]), bf16_bits_to_f64(w.w_k[l]),
                             bf16_bits_to_f64(w.w_v[l]), pos, s.rope_theta, s.head_dim,
                             s.rms_eps)

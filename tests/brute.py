@@ -51,3 +51,63 @@ def filled_row(x_bits, a_bits, b_bits, g_bits, wk_bits, wv_bits, pos, theta, hd,
             out[base + j] = p * c - q * s
             out[base + j + half] = q * c + p * s
     return out, vv
+
+
+# ---------------------------------------------------------------- int8 maps
+# Written from the format's description (RidgeFill, section 2.2 "Size and
+# cost": int8 codes, one bf16 scale per 128 weights of each row), with
+# Python floats and struct only.
+
+def _f32(v):
+    """Nearest fp32 value of a Python float (struct rounds to nearest even)."""
+    import struct
+    return struct.unpack("<f", struct.pack("<f", v))[0]
+
+
+def _bf16_nearest(v):
+    """bf16 bit pattern nearest a finite fp32-representable value, ties to the
+    even pattern, found by comparing the two bracketing bf16 values."""
+    import struct
+    u = struct.unpack("<I", struct.pack("<f", v))[0]
+    lo = u >> 16
+    cands = [lo, lo + 1]
+    vals = [_f(c) for c in cands]
+    d0, d1 = abs(vals[0] - v), abs(vals[1] - v)
+    if d0 < d1:
+        return cands[0]
+    if d1 < d0:
+        return cands[1]
+    return cands[0] if cands[0] % 2 == 0 else cands[1]
+
+
+def dequant_q8(q_rows, scale_bits_rows):
+    """w[o][k] = q[o][k] * scale[o][k // 128], as nested lists of floats."""
+    out = []
+    for o, row in enumerate(q_rows):
+        out.append([int(row[k]) * _f(scale_bits_rows[o][k // 128]) for k in range(len(row))])
+    return out
+
+
+def quantize_q8(a_rows):
+    """Absmax int8 codes and bf16 scale bits per 128-weight block of each row."""
+    q_rows, s_rows = [], []
+    for row in a_rows:
+        qr, sr = [], []
+        for b0 in range(0, len(row), 128):
+            blk = [float(v) for v in row[b0:b0 + 128]]
+            m = 0.0
+            for v in blk:
+                m = max(m, abs(v))
+            sb = _bf16_nearest(_f32(m / 127.0))
+            s = _f(sb)
+            sr.append(sb)
+            for v in blk:
+                if s == 0.0:
+                    qr.append(0)
+                    continue
+                t = v / s
+                n = round(t)  # Python rounds halves to even
+                qr.append(max(-127, min(127, n)))
+        q_rows.append(qr)
+        s_rows.append(sr)
+    return q_rows, s_rows

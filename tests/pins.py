@@ -320,6 +320,124 @@ def pin_ridge_raw_form(o):
     assert np.allclose(a2.T, np.linalg.solve(x.T @ x + 5.0 * np.eye(6), x.T @ y), rtol=1e-12)
 
 
+# ---------------------------------------------------------------- int8 maps
+
+def _q8_case(seed, d_out, d_in, max_code=True):
+    """Random codes (each block's largest |code| = 127 when max_code) and
+    random positive bf16 scales."""
+    g = _rng(seed)
+    q = g.integers(-60, 61, size=(d_out, d_in)).astype(np.int8)
+    if max_code:
+        for o in range(d_out):
+            for b in range(d_in // 128):
+                k = b * 128 + int(g.integers(0, 128))
+                q[o, k] = 127 if g.integers(0, 2) else -127
+    s = _bits(np.exp(g.uniform(-9.0, 1.0, size=(d_out, d_in // 128))))
+    return q, s
+
+
+def pin_q8_dequant_closed_form(o):
+    """Section 2.2 ("Size and cost"): a weight is its int8 code times the bf16
+    scale of its 128-weight block in the same row."""
+    q = np.zeros((2, 256), dtype=np.int8)
+    q[0, 0], q[0, 127], q[0, 128], q[0, 255] = 3, -5, 7, 127
+    q[1, 64], q[1, 200] = -128, 1
+    s = np.array([[0x3F00, 0x4000], [0x3E80, 0xC040]], dtype=np.uint16)  # 0.5, 2, 0.25, -3
+    w = o.dequantize_q8(q, s)
+    want = np.zeros((2, 256))
+    want[0, 0], want[0, 127], want[0, 128], want[0, 255] = 1.5, -2.5, 14.0, 254.0
+    want[1, 64], want[1, 200] = -32.0, -3.0
+    assert w.dtype == np.float64 and np.array_equal(w, want), np.argwhere(w != want)
+
+
+def pin_q8_dequant_brute(o):
+    """The same definition written as plain loops (tests/brute.py)."""
+    q, s = _q8_case(11, 3, 384)
+    w = o.dequantize_q8(q, s)
+    ref = np.array(brute.dequant_q8(q.tolist(), s.tolist()))
+    assert np.array_equal(w, ref)
+
+
+def pin_q8_grid_fixpoint(o):
+    """A map already on the int8 grid, whose blocks each reach code +-127,
+    quantizes back to the same codes and scales: 127*s/127 = s exactly and
+    q*s/s = q exactly."""
+    q, s = _q8_case(12, 8, 512)
+    a = o.dequantize_q8(q, s).astype(np.float32)
+    assert np.array_equal(a.astype(np.float64), o.dequantize_q8(q, s)), "grid values must be fp32-exact"
+    q2, s2 = o.quantize_q8(a)
+    assert q2.dtype == np.int8 and s2.dtype == np.uint16
+    assert np.array_equal(s2, s) and np.array_equal(q2, q)
+    q3, s3 = o.quantize_q8(-a)
+    assert np.array_equal(s3, s) and np.array_equal(q3, -q), "the format is symmetric"
+
+
+def pin_q8_quantize_bounds(o):
+    """Absmax quantization: every weight is within half a step of its code
+    times the scale, each block's largest weight gets code +-127 with its sign,
+    and the scale is the block's largest |weight| / 127 to bf16 precision."""
+    g = _rng(13)
+    d = 256
+    a = (np.eye(d) + 0.01 * g.standard_normal((d, d))).astype(np.float32)
+    a[5, :128] *= 1e4                           # a block of large weights
+    a[7, 128:] = g.standard_t(2, size=128)      # heavy tails
+    a[9, :128] = 0.0                            # an all-zero block
+    q, sb = o.quantize_q8(a)
+    s = o.dequantize_q8(np.ones_like(q), sb)    # per-weight scale
+    err = np.abs(a.astype(np.float64) - q * s)
+    assert np.all(err <= 0.5 * s * (1 + 1e-12)), float(np.max(err / np.where(s > 0, s, 1)))
+    blocks = np.abs(a.astype(np.float64)).reshape(d, 2, 128)
+    m = blocks.max(axis=2)
+    arg = blocks.argmax(axis=2)
+    for r in range(d):
+        for b in range(2):
+            k = b * 128 + arg[r, b]
+            if m[r, b] == 0:
+                assert sb[r, b] == 0 and not q[r, b * 128:(b + 1) * 128].any()
+                continue
+            assert abs(int(q[r, k])) == 127 and np.sign(q[r, k]) == np.sign(a[r, k]), (r, b)
+            sv = o.bf16_bits_to_f64(sb[r, b])
+            assert abs(sv - m[r, b] / 127) <= 2.0 ** -8 * m[r, b] / 127, (r, b)
+
+
+def pin_q8_quantize_ties(o):
+    """Codes round to the nearest integer with halves to even: with scale 0.5
+    (block max 63.5), 1.25 -> 2, 1.75 -> 4, -0.25 -> 0, -0.75 -> -2."""
+    a = np.zeros((1, 128), dtype=np.float32)
+    a[0, :5] = [63.5, 1.25, 1.75, -0.25, -0.75]
+    q, s = o.quantize_q8(a)
+    assert s[0, 0] == 0x3F00, hex(int(s[0, 0]))
+    assert q[0, :5].tolist() == [127, 2, 4, 0, -2], q[0, :5]
+
+
+def pin_q8_quantize_brute(o):
+    """The quantizer against plain loops (tests/brute.py)."""
+    g = _rng(14)
+    a = (g.standard_normal((4, 256)) * np.exp(g.uniform(-6, 6, size=(4, 1)))).astype(np.float32)
+    a[2, 128:] = 0.0
+    q, s = o.quantize_q8(a)
+    qb, sbr = brute.quantize_q8(a.tolist())
+    assert np.array_equal(q, np.array(qb)) and np.array_equal(s, np.array(sbr))
+
+
+def pin_bf16_rounding_library(o):
+    """One rounding to bf16, nearest even, as torch's float32 -> bfloat16 cast
+    does, on random values and on exact halfway points."""
+    import torch
+    g = _rng(15)
+    v = np.concatenate([g.standard_normal(4000) * np.exp(g.uniform(-20, 20, 4000)),
+                        [1 + 2.0 ** -8, 1 + 3 * 2.0 ** -8, -(1 + 2.0 ** -8), 3 * 2.0 ** -9, 0.0]])
+    v = v.astype(np.float32).astype(np.float64)
+    got = o.f64_to_bf16_bits(v)
+    ref = torch.from_numpy(v.astype(np.float32)).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    assert np.array_equal(got, ref)
+    assert o.f64_to_bf16_bits(np.array([1 + 2.0 ** -8, 1 + 3 * 2.0 ** -8])).tolist() == [0x3F80, 0x3F82]
+    q, s = _q8_case(16, 2, 256)
+    r = o.dequantize_q8_bf16(q, s)
+    assert np.array_equal(r, ref_q := torch.from_numpy(o.dequantize_q8(q, s).astype(np.float32))
+                          .to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)), ref_q
+
+
 # ---------------------------------------------------------------- ceilings
 
 def pin_printed_ceilings(o):
@@ -341,4 +459,7 @@ FILL_PINS = [pin_fill_rows_partition, pin_identity_map_is_exact_kv, pin_map_orie
 RIDGE_PINS = [pin_ridge_recovers_linear_map, pin_ridge_svd_form, pin_ridge_running_sums,
               pin_ridge_penalty_scale, pin_ridge_raw_form]
 CEILING_PINS = [pin_printed_ceilings]
-ALL_PINS = FILL_PINS + RIDGE_PINS + CEILING_PINS
+QUANT_PINS = [pin_q8_dequant_closed_form, pin_q8_dequant_brute, pin_q8_grid_fixpoint,
+              pin_q8_quantize_bounds, pin_q8_quantize_ties, pin_q8_quantize_brute,
+              pin_bf16_rounding_library]
+ALL_PINS = FILL_PINS + RIDGE_PINS + CEILING_PINS + QUANT_PINS

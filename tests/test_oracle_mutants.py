@@ -12,7 +12,7 @@ import pytest
 from tests import pins
 
 ORACLE_DIR = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "oracle")
-FILES = ("fill.py", "ridge.py", "ceiling.py")
+FILES = ("fill.py", "ridge.py", "ceiling.py", "quant.py")
 
 MUTANTS = {
     # the map
@@ -53,9 +53,21 @@ MUTANTS = {
     # the ceilings
     "ceiling_prefix_denominator": ("ceiling.py", [("* tail / n_rows", "* tail / (n_rows - tail)")]),
     "ceiling_mac_sign": ("ceiling.py", [("1.0 / (1.0 - skipped_share)", "1.0 / (1.0 + skipped_share)")]),
+    # the int8 map format
+    "q8_scale_tiled_not_repeated": ("quant.py", [("np.repeat(s, BLOCK, axis=1)", "np.tile(s, (1, BLOCK))")]),
+    "q8_block_64": ("quant.py", [("BLOCK = 128", "BLOCK = 64")]),
+    "q8_code_abs": ("quant.py", [("return q.astype(np.float64) * np.repeat", "return np.abs(q.astype(np.float64)) * np.repeat")]),
+    "q8_absmax_over_128": ("quant.py", [("(m / 127.0)", "(m / 128.0)")]),
+    "q8_round_floor": ("quant.py", [("q = np.rint(blocks / safe)", "q = np.floor(blocks / safe)")]),
+    "q8_round_half_away": ("quant.py", [("q = np.rint(blocks / safe)", "q = np.trunc(blocks / safe + 0.5 * np.sign(blocks))")]),
+    "q8_scale_truncated": ("quant.py", [("((u + 0x7FFF + ((u >> 16) & 1)) >> 16)", "(u >> 16)")]),
+    "q8_max_over_rows": ("quant.py", [("m = np.abs(blocks).max(axis=2)", "m = np.abs(blocks).max(axis=2).max(axis=0, keepdims=True) + 0 * blocks[:, :, 0]")]),
+    "bf16_round_truncates": ("quant.py", [("return ((u + 0x7FFF + lsb) >> 16)", "return ((u) >> 16)")]),
+    "bf16_round_ties_up": ("quant.py", [("return ((u + 0x7FFF + lsb) >> 16)", "return ((u + 0x8000) >> 16)")]),
 }
 
-PINS_FOR = {"fill.py": pins.FILL_PINS, "ridge.py": pins.RIDGE_PINS, "ceiling.py": pins.CEILING_PINS}
+PINS_FOR = {"fill.py": pins.FILL_PINS, "ridge.py": pins.RIDGE_PINS, "ceiling.py": pins.CEILING_PINS,
+            "quant.py": pins.QUANT_PINS}
 
 
 def _load(target, edits):

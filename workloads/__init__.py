@@ -21,6 +21,13 @@ value projections):
   the identity is placed on the leading diagonal when d_in != d_out);
 * b_l ~ N(0, bias_sigma^2), gamma_l ~ 1 + N(0, gamma_sigma^2);
 * W_k, W_v ~ N(0, 1/d_out), stored [n_kv * head_dim][d_out];
+* int8 maps (``map_format="q8"``, the 27B deployment's format: int8 codes
+  and one bf16 scale per 128 weights of each row) are drawn directly in that
+  format with the same value distribution: a block holding the identity's
+  diagonal gets scale ~ (1 + N(0, map_sigma^2)) / 127 and diagonal code 127,
+  any other block scale ~ map_sigma * (2.8 + 0.4 |N(0, 1)|) / 127; the other
+  codes are N(0, map_sigma^2) / scale rounded to integers and clipped to
+  [-127, 127];
 * positions restart at 0 for every prompt of a batch;
 * the exact set is the last ``tail`` rows of every prompt plus ``n_spans``
   disjoint spans of ``span_len`` rows drawn uniformly inside the first
@@ -42,7 +49,8 @@ __all__ = [
 
 # seed-sequence "kind" tags
 _K_X, _K_OUTLIER, _K_LAYER, _K_SPANS = 1, 2, 3, 4
-_L_MAP, _L_BIAS, _L_GAMMA, _L_WK, _L_WV = 0, 1, 2, 3, 4
+_L_MAP, _L_BIAS, _L_GAMMA, _L_WK, _L_WV, _L_QSCALE = 0, 1, 2, 3, 4, 5
+Q8_BLOCK = 128  # weights per bf16 scale along each row of an int8 map
 _X_BLOCK = 8192  # rows per independently seeded block of x_S
 
 
@@ -67,6 +75,7 @@ class Spec:
     n_outliers: int = 4
     outlier_scale: float = 20.0
     maps_on_host: bool = False
+    map_format: str = "bf16"   # "bf16" or "q8"
     seed: int = 0
 
     @property
@@ -140,7 +149,7 @@ class Workload:
     """bf16 bit patterns (uint16) for every input of one fill call."""
     spec: Spec
     x: np.ndarray                 # [n_rows][d_in]
-    map_a: List[np.ndarray]       # n_late x [d_out][d_in]
+    map_a: List[Optional[np.ndarray]]  # n_late x [d_out][d_in] (None for q8 maps)
     map_b: List[np.ndarray]       # n_late x [d_out]
     gamma: List[np.ndarray]       # n_late x [d_out]
     w_k: List[np.ndarray]         # n_late x [n_kv*head_dim][d_out]
@@ -148,6 +157,8 @@ class Workload:
     positions: np.ndarray         # int32 [n_rows]
     exact_rows: np.ndarray        # int32, ascending, unique
     outlier_channels: np.ndarray  # int64 [n_outliers]
+    map_q: Optional[List[np.ndarray]] = None      # q8 only: n_late x int8 [d_out][d_in]
+    map_scale: Optional[List[np.ndarray]] = None  # q8 only: n_late x bf16 [d_out][d_in/128]
     extra: dict = field(default_factory=dict)
 
 
@@ -190,16 +201,45 @@ def _gen_x_block(s: Spec, x: np.ndarray, blk: int, outliers: np.ndarray) -> None
     x[r0:r1] = f32_to_bf16_bits(v)
 
 
-def _gen_layer(s: Spec, l: int):
-    a = _normal((s.seed, _K_LAYER, l, _L_MAP), (s.d_out, s.d_in), s.map_sigma)
+def _gen_q8_map(s: Spec, l: int):
+    if s.d_in % Q8_BLOCK:
+        raise ValueError(f"d_in={s.d_in} is not a multiple of {Q8_BLOCK}")
+    nb = s.d_in // Q8_BLOCK
     k = min(s.d_in, s.d_out)
-    a[np.arange(k), np.arange(k)] += np.float32(1.0)
+    z = _normal((s.seed, _K_LAYER, l, _L_QSCALE), (s.d_out, nb))
+    scale = np.float32(s.map_sigma) * (np.float32(2.8) + np.float32(0.4) * np.abs(z))
+    diag_rows = np.arange(k)
+    scale[diag_rows, diag_rows // Q8_BLOCK] = np.float32(1.0) + np.float32(s.map_sigma) * z[diag_rows, diag_rows // Q8_BLOCK]
+    scale /= np.float32(127.0)
+    s_bits = f32_to_bf16_bits(scale)
+    s_val = (s_bits.astype(np.uint32) << 16).view(np.float32)
+    q = _normal((s.seed, _K_LAYER, l, _L_MAP), (s.d_out, s.d_in), s.map_sigma)
+    q /= np.repeat(s_val, Q8_BLOCK, axis=1)
+    np.rint(q, out=q)
+    np.clip(q, -127, 127, out=q)
+    q = q.astype(np.int8)
+    q[diag_rows, diag_rows] = 127
+    return q, s_bits
+
+
+def _gen_layer(s: Spec, l: int):
+    if s.map_format == "q8":
+        a = None
+    else:
+        a = _normal((s.seed, _K_LAYER, l, _L_MAP), (s.d_out, s.d_in), s.map_sigma)
+        k = min(s.d_in, s.d_out)
+        a[np.arange(k), np.arange(k)] += np.float32(1.0)
     b = _normal((s.seed, _K_LAYER, l, _L_BIAS), (s.d_out,), s.bias_sigma)
     g = _normal((s.seed, _K_LAYER, l, _L_GAMMA), (s.d_out,), s.gamma_sigma, 1.0)
     wsig = 1.0 / np.sqrt(s.d_out)
     wk = _normal((s.seed, _K_LAYER, l, _L_WK), (s.kv_width, s.d_out), wsig)
     wv = _normal((s.seed, _K_LAYER, l, _L_WV), (s.kv_width, s.d_out), wsig)
-    return tuple(f32_to_bf16_bits(t) for t in (a, b, g, wk, wv))
+    out = tuple(None if t is None else f32_to_bf16_bits(t) for t in (a, b, g, wk, wv))
+    if s.map_format == "q8":
+        out += _gen_q8_map(s, l)
+    else:
+        out += (None, None)
+    return out
 
 
 def make(s: Spec, layers: Optional[List[int]] = None) -> Workload:
@@ -219,4 +259,6 @@ def make(s: Spec, layers: Optional[List[int]] = None) -> Workload:
         map_a=[t[0] for t in lay], map_b=[t[1] for t in lay], gamma=[t[2] for t in lay],
         w_k=[t[3] for t in lay], w_v=[t[4] for t in lay],
         positions=_positions(s), exact_rows=exact_row_list(s),
-        outlier_channels=outliers)
+        outlier_channels=outliers,
+        map_q=[t[5] for t in lay] if s.map_format == "q8" else None,
+        map_scale=[t[6] for t in lay] if s.map_format == "q8" else None)
