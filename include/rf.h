@@ -68,8 +68,11 @@ enum {
                        streamed to the GPU one layer at a time on a side stream,
                        overlapped with the previous layer's fill (section 4.2:
                        maps resident or streamed, identical outputs)          */
-  RF_VALIDATE = 2   /* rf_fill / rf_kv_project check their row indices on the
+  RF_VALIDATE = 2,  /* rf_fill / rf_kv_project check their row indices on the
                        device and synchronise the stream before launching     */
+  RF_MAPS_Q8 = 4    /* maps are int8 with bf16 block scales and are passed to
+                       rf_fill_q8 instead of rf_fill; d_in % 128 == 0 (see the
+                       int8 map section below)                                 */
 };
 
 /* rf_ridge_solve / rf_ridge_fit flags */
@@ -93,18 +96,20 @@ typedef struct rf_shape {
 typedef struct rf_plan rf_plan;
 
 /* Create a plan for one shape.  Validates the shape (RF_E_SHAPE / RF_E_ARG).
- * With RF_MAPS_HOST the plan owns two device map buffers, one side stream and
- * four events; these are allocated here, on the current device, and released
- * by rf_plan_destroy.  Without it the plan allocates nothing on the device. */
+ * With RF_MAPS_HOST the plan owns two device map buffers (sized for bf16 maps,
+ * or for int8 maps with RF_MAPS_Q8), one side stream and four events; these
+ * are allocated here, on the current device, and released by rf_plan_destroy.
+ * Without it the plan allocates nothing on the device. */
 rf_status rf_plan_create(const rf_shape* shape, int32_t flags, rf_plan** out);
 void rf_plan_destroy(rf_plan* plan);
 
-/* Workspace bytes rf_fill needs for n_fill rows when `layers_per_launch` late
- * layers are processed per launch (1 .. n_late; larger means fewer, wider
- * launches).  rf_fill uses the widest grouping the given workspace allows, so
- * any size >= rf_fill_workspace_bytes(plan, n_fill, 1) works.  The figure
- * includes the RoPE table that rf_fill builds when none is passed.
- * Returns 0 for a bad argument. */
+/* Workspace bytes rf_fill (or rf_fill_q8 for an RF_MAPS_Q8 plan) needs for
+ * n_fill rows when `layers_per_launch` late layers are processed per launch
+ * (1 .. n_late; larger means fewer, wider launches).  The call uses the widest
+ * grouping the given workspace allows, so any size >=
+ * rf_fill_workspace_bytes(plan, n_fill, 1) works.  The figure includes the
+ * RoPE table built when none is passed and, for RF_MAPS_Q8 plans, the bf16
+ * image of each launch's maps.  Returns 0 for a bad argument. */
 size_t rf_fill_workspace_bytes(const rf_plan* plan, int32_t n_fill, int32_t layers_per_launch);
 
 /* Workspace bytes rf_kv_project needs (one prepared [W_k|W_v] copy per layer
@@ -155,6 +160,46 @@ rf_status rf_fill(rf_plan* plan,
                   uint16_t* const* k_cache, uint16_t* const* v_cache,
                   void* workspace, size_t ws_bytes, void* hip_stream);
 
+/* ---- int8 maps -----------------------------------------------------------
+ * Section 2.2 ("Size and cost") and section 4.2: the 27B deployment stores
+ * each map as int8 codes with one bf16 scale per 128 weights of each row, half
+ * the bytes of a bf16 map.  The weight is w[o][k] = q[o][k] * s[o][k / 128]:
+ *    map_q      [d_out][d_in] int8 codes, 16-byte aligned
+ *    map_scale  [d_out][d_in / 128] bf16 scales
+ * rf_fill_q8 is rf_fill for a plan created with RF_MAPS_Q8: before each launch
+ * group's map contraction it expands the group's maps into a bf16 image in the
+ * workspace, rounding each product q * s once to bf16 (nearest even; the exact
+ * product has at most 16 significant bits), and then runs rf_fill's kernels on
+ * that image.  Its output is therefore bitwise equal to rf_fill given
+ * map_a[l] = rf_map_dequantize_q8(map_q[l], map_scale[l]).  With RF_MAPS_HOST
+ * map_q, map_scale and map_b are pinned HOST pointers; the copies move half
+ * the bytes of bf16 maps.  Other arguments and rules as for rf_fill.
+ * RF_E_ARG if the plan's RF_MAPS_Q8 flag does not match the call. */
+rf_status rf_fill_q8(rf_plan* plan,
+                     const uint16_t* x, int64_t ld_x,
+                     const int32_t* fill_rows, int32_t n_fill,
+                     const int32_t* positions, const int32_t* slot_of_row,
+                     const int8_t* const* map_q, const uint16_t* const* map_scale,
+                     const uint16_t* const* map_b,
+                     const uint16_t* const* gamma,
+                     const uint16_t* const* w_k, const uint16_t* const* w_v,
+                     const float* rope_cos_sin,
+                     uint16_t* const* k_cache, uint16_t* const* v_cache,
+                     void* workspace, size_t ws_bytes, void* hip_stream);
+
+/* Expand one int8 map into bf16 (device to device): w[o][k] = bf16(q[o][k] *
+ * s[o][k / 128]), nearest even.  d_in % 128 == 0, d_out >= 1; q and w 16-byte
+ * aligned.  The kernel rf_fill_q8 runs before each map contraction. */
+rf_status rf_map_dequantize_q8(const int8_t* q, const uint16_t* scale, int32_t d_out, int32_t d_in,
+                               uint16_t* w, void* hip_stream);
+
+/* Quantize an fp32 map (HOST, [d_out][d_in], d_in % 128 == 0) to the int8
+ * format, absmax per 128-weight block: s = bf16 (nearest even) of the fp32
+ * value nearest max|a| / 127, q = a / s rounded to nearest (ties to even) in
+ * double precision and clipped to [-127, 127]; an all-zero block gets s = 0,
+ * q = 0.  Outputs q [d_out][d_in] and scale [d_out][d_in / 128], HOST. */
+rf_status rf_map_quantize_q8(const float* a, int32_t d_out, int32_t d_in, int8_t* q, uint16_t* scale);
+
 /* The exact cache write of each late layer from given true inputs: steps 2-5
  * only (no map).  Section 2.1: exact rows and the tail run the layer from its
  * exact input; with every layer_in[l] = x and A_l = I, b_l = 0, rf_fill gives
@@ -204,7 +249,8 @@ enum {
   RF_K_ROPE = 3,      /* RoPE table                                  */
   RF_K_ROWS = 4,      /* fill-row compaction                         */
   RF_K_COPY = 5,      /* host -> device map copy (RF_MAPS_HOST)      */
-  RF_K_COUNT = 6
+  RF_K_DEQUANT = 6,   /* int8 map -> bf16 image (RF_MAPS_Q8)         */
+  RF_K_COUNT = 7
 };
 typedef struct rf_profile {
   double ms[RF_K_COUNT];        /* summed event time per kind, milliseconds */

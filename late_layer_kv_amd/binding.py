@@ -19,7 +19,9 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "librf.so")
 
 RF_MAPS_HOST = 1
 RF_VALIDATE = 2
+RF_MAPS_Q8 = 4
 RF_RIDGE_RAW = 1
+Q8_BLOCK = 128
 
 STATUS = {0: "RF_OK", -1: "RF_E_ARG", -2: "RF_E_SHAPE", -3: "RF_E_ROWS", -4: "RF_E_WORKSPACE",
           -5: "RF_E_HIP", -6: "RF_E_LINALG"}
@@ -30,9 +32,10 @@ EXPORTS = [
     "rf_rope_table", "rf_fill_rows_workspace_bytes", "rf_fill_rows", "rf_fill", "rf_kv_project",
     "rf_ridge_acc_create", "rf_ridge_acc_add", "rf_ridge_solve", "rf_ridge_acc_destroy", "rf_ridge_fit",
     "rf_plan_profile", "rf_plan_profile_read", "rf_last_error",
+    "rf_fill_q8", "rf_map_dequantize_q8", "rf_map_quantize_q8",
 ]
 
-KERNEL_KINDS = ["map", "kv", "prep", "rope", "rows", "copy"]
+KERNEL_KINDS = ["map", "kv", "prep", "rope", "rows", "copy", "dequant"]
 
 
 class RfError(RuntimeError):
@@ -48,7 +51,7 @@ class Shape(C.Structure):
 
 
 class Profile(C.Structure):
-    _fields_ = [("ms", C.c_double * 6), ("launches", C.c_int64 * 6)]
+    _fields_ = [("ms", C.c_double * 7), ("launches", C.c_int64 * 7)]
 
 
 _lib = None
@@ -83,6 +86,9 @@ def lib():
         "rf_plan_profile": (i32, [P, i32]),
         "rf_plan_profile_read": (i32, [P, C.POINTER(Profile)]),
         "rf_last_error": (C.c_char_p, []),
+        "rf_fill_q8": (i32, [P, P, i64, P, i32, P, P, PP, PP, PP, PP, PP, PP, P, PP, PP, P, sz, P]),
+        "rf_map_dequantize_q8": (i32, [P, P, i32, i32, P, P]),
+        "rf_map_quantize_q8": (i32, [P, i32, i32, P, P]),
     }
     for name, (res, args) in sig.items():
         f = getattr(L, name)
@@ -127,9 +133,10 @@ class Plan:
 
     def __init__(self, d_in: int, d_out: int, n_late: int, n_kv: int, head_dim: int, rms_eps: float,
                  rope_theta: float, n_rows: int, n_slots: int, max_pos: int,
-                 maps_on_host: bool = False, validate: bool = False):
+                 maps_on_host: bool = False, validate: bool = False, maps_q8: bool = False):
         self.shape = Shape(d_in, d_out, n_late, n_kv, head_dim, rms_eps, rope_theta, n_rows, n_slots, max_pos)
-        self.flags = (RF_MAPS_HOST if maps_on_host else 0) | (RF_VALIDATE if validate else 0)
+        self.flags = ((RF_MAPS_HOST if maps_on_host else 0) | (RF_VALIDATE if validate else 0)
+                      | (RF_MAPS_Q8 if maps_q8 else 0))
         h = C.c_void_p()
         _check("rf_plan_create", lib().rf_plan_create(C.byref(self.shape), self.flags, C.byref(h)))
         self.handle = h
@@ -138,6 +145,7 @@ class Plan:
     def for_spec(cls, s, **kw) -> "Plan":
         """Plan for a workloads.Spec."""
         kw.setdefault("maps_on_host", s.maps_on_host)
+        kw.setdefault("maps_q8", s.map_format == "q8")
         return cls(s.d_in, s.d_out, s.n_late, s.n_kv, s.head_dim, s.rms_eps, s.rope_theta,
                    s.n_rows, s.n_rows, s.max_pos, **kw)
 
@@ -195,6 +203,36 @@ def fill(plan: Plan, x, fill_rows_t, n_fill: int, positions, slot_of_row, map_a:
         _ptr_array(map_a), _ptr_array(map_b), _ptr_array(gamma), _ptr_array(w_k), _ptr_array(w_v),
         _ptr(rope), _ptr_array(k_cache), _ptr_array(v_cache), _ptr(workspace),
         workspace.numel() * workspace.element_size(), _stream(stream)))
+
+
+def fill_q8(plan: Plan, x, fill_rows_t, n_fill: int, positions, slot_of_row, map_q: Sequence,
+            map_scale: Sequence, map_b: Sequence, gamma: Sequence, w_k: Sequence, w_v: Sequence, rope,
+            k_cache: Sequence, v_cache: Sequence, workspace, stream=None, ld_x: Optional[int] = None) -> None:
+    """rf_fill_q8: the fill with int8 maps (codes + bf16 block scales) for a
+    plan made with maps_q8; pinned host tensors for a plan with maps_on_host."""
+    ld = x.stride(0) if ld_x is None else ld_x
+    _check("rf_fill_q8", lib().rf_fill_q8(
+        plan.handle, _ptr(x), ld, _ptr(fill_rows_t), n_fill, _ptr(positions), _ptr(slot_of_row),
+        _ptr_array(map_q), _ptr_array(map_scale), _ptr_array(map_b), _ptr_array(gamma), _ptr_array(w_k),
+        _ptr_array(w_v), _ptr(rope), _ptr_array(k_cache), _ptr_array(v_cache), _ptr(workspace),
+        workspace.numel() * workspace.element_size(), _stream(stream)))
+
+
+def map_dequantize_q8(q, scale, w_out, stream=None) -> None:
+    """rf_map_dequantize_q8: w_out[o][k] = bf16(q[o][k] * scale[o][k // 128]) on the device."""
+    d_out, d_in = q.shape
+    _check("rf_map_dequantize_q8", lib().rf_map_dequantize_q8(_ptr(q), _ptr(scale), d_out, d_in, _ptr(w_out),
+                                                              _stream(stream)))
+
+
+def map_quantize_q8(a: np.ndarray):
+    """rf_map_quantize_q8 on the host: (int8 codes [d_out][d_in], bf16 scale bits [d_out][d_in/128])."""
+    a = _f32(a)
+    d_out, d_in = a.shape
+    q = np.empty((d_out, d_in), dtype=np.int8)
+    s = np.empty((d_out, max(d_in // Q8_BLOCK, 1)), dtype=np.uint16)
+    _check("rf_map_quantize_q8", lib().rf_map_quantize_q8(a.ctypes.data, d_out, d_in, q.ctypes.data, s.ctypes.data))
+    return q, s
 
 
 def kv_project(plan: Plan, layer_in: Sequence, rows, n: int, positions, slot_of_row, gamma: Sequence,

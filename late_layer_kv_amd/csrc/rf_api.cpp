@@ -47,9 +47,13 @@ struct rf_plan {
   hipEvent_t ev_start = nullptr;
   hipEvent_t ev_copied[2] = {nullptr, nullptr};
   hipEvent_t ev_consumed[2] = {nullptr, nullptr};
-  uint16_t* mapbuf[2] = {nullptr, nullptr};  // [d_out][d_in] then [d_out], per buffer
-  size_t map_elems = 0;
-  size_t bias_off = 0;  // element offset of b inside a buffer
+  // One streamed layer per buffer: the map (bf16 [d_out][d_in], or int8 codes
+  // [d_out][d_in] then bf16 scales [d_out][d_in/128]) and then b [d_out].
+  char* mapbuf[2] = {nullptr, nullptr};
+  size_t map_bytes = 0;    // bf16 map, or int8 codes
+  size_t scale_off = 0;    // byte offset of the scales (int8 maps)
+  size_t scale_bytes = 0;
+  size_t bias_off = 0;     // byte offset of b
   // kernel timing (rf_plan_profile)
   struct Rec {
     int kind;
@@ -115,11 +119,17 @@ size_t prep_bytes(const rf_shape& s, int g) {
 size_t y_bytes(const rf_shape& s, int n_fill, int g) {
   return up(static_cast<size_t>(g) * n_fill * s.d_out * 2);
 }
+// bf16 image of the int8 maps of one launch group (RF_MAPS_Q8 plans only)
+size_t dq_bytes(const rf_shape& s, int32_t flags, int g) {
+  return (flags & RF_MAPS_Q8) ? up(static_cast<size_t>(g) * s.d_out * s.d_in * 2) : 0;
+}
 constexpr size_t kFlagBytes = kAlign;
 
 rf_status check_shape(const rf_shape* s, int32_t flags) {
   if (!s) return fail(RF_E_ARG, "shape is null");
-  if (flags & ~(RF_MAPS_HOST | RF_VALIDATE)) return fail(RF_E_ARG, "unknown flag bits 0x%x", flags);
+  if (flags & ~(RF_MAPS_HOST | RF_VALIDATE | RF_MAPS_Q8)) return fail(RF_E_ARG, "unknown flag bits 0x%x", flags);
+  if ((flags & RF_MAPS_Q8) && s->d_in % rf::kQ8Block)
+    return fail(RF_E_SHAPE, "d_in=%d must be a multiple of %d for int8 maps", s->d_in, rf::kQ8Block);
   if (s->d_in <= 0 || s->d_in % rf::kTileK)
     return fail(RF_E_SHAPE, "d_in=%d must be a positive multiple of %d", s->d_in, rf::kTileK);
   if (s->d_out <= 0 || s->d_out % rf::kTileN)
@@ -178,9 +188,17 @@ rf_status rf_plan_create(const rf_shape* shape, int32_t flags, rf_plan** out) {
   p->flags = flags;
   hipError_t e = hipSuccess;
   if (flags & RF_MAPS_HOST) {
-    p->map_elems = static_cast<size_t>(shape->d_out) * shape->d_in;
-    p->bias_off = (p->map_elems + 127) / 128 * 128;
-    const size_t bytes = (p->bias_off + shape->d_out) * 2;
+    const size_t elems = static_cast<size_t>(shape->d_out) * shape->d_in;
+    if (flags & RF_MAPS_Q8) {
+      p->map_bytes = elems;
+      p->scale_off = up(p->map_bytes);
+      p->scale_bytes = static_cast<size_t>(shape->d_out) * (shape->d_in / rf::kQ8Block) * 2;
+      p->bias_off = p->scale_off + up(p->scale_bytes);
+    } else {
+      p->map_bytes = elems * 2;
+      p->bias_off = up(p->map_bytes);
+    }
+    const size_t bytes = p->bias_off + static_cast<size_t>(shape->d_out) * 2;
     for (int i = 0; i < 2 && e == hipSuccess; ++i) e = hipMalloc(reinterpret_cast<void**>(&p->mapbuf[i]), bytes);
     if (e == hipSuccess) e = hipStreamCreateWithFlags(&p->side, hipStreamNonBlocking);
     if (e == hipSuccess) e = hipEventCreateWithFlags(&p->ev_start, hipEventDisableTiming);
@@ -240,7 +258,7 @@ size_t rf_fill_workspace_bytes(const rf_plan* p, int32_t n_fill, int32_t g) {
   if (!p || n_fill < 0 || g < 1 || g > p->s.n_late) return 0;
   g = std::min(g, rf::kMaxGroup);
   if (p->flags & RF_MAPS_HOST) g = 1;
-  return rope_bytes(p->s) + kFlagBytes + prep_bytes(p->s, g) + y_bytes(p->s, n_fill, g);
+  return rope_bytes(p->s) + kFlagBytes + prep_bytes(p->s, g) + y_bytes(p->s, n_fill, g) + dq_bytes(p->s, p->flags, g);
 }
 
 size_t rf_kv_project_workspace_bytes(const rf_plan* p, int32_t g) {
@@ -276,14 +294,29 @@ rf_status rf_fill_rows(rf_plan* p, const int32_t* exact_rows, int32_t n_exact, i
   return e == hipSuccess ? RF_OK : hip_fail(e, "fill-row launch");
 }
 
-rf_status rf_fill(rf_plan* p, const uint16_t* x, int64_t ld_x, const int32_t* fill_rows, int32_t n_fill,
-                  const int32_t* positions, const int32_t* slot_of_row, const uint16_t* const* map_a,
-                  const uint16_t* const* map_b, const uint16_t* const* gamma, const uint16_t* const* w_k,
-                  const uint16_t* const* w_v, const float* rope, uint16_t* const* k_cache,
-                  uint16_t* const* v_cache, void* ws, size_t ws_bytes, void* stream) {
-  if (!p) return fail(RF_E_ARG, "plan is null");
+}  // extern "C"
+
+namespace {
+
+// Where a call's maps come from: bf16 matrices, or int8 codes with bf16 block scales.
+struct MapSrc {
+  const uint16_t* const* a = nullptr;      // bf16 [d_out][d_in]
+  const int8_t* const* q = nullptr;        // int8 [d_out][d_in]
+  const uint16_t* const* scale = nullptr;  // bf16 [d_out][d_in/128]
+  const uint16_t* const* b = nullptr;      // bf16 [d_out]
+};
+
+rf_status fill_impl(rf_plan* p, const char* fn, const uint16_t* x, int64_t ld_x, const int32_t* fill_rows,
+                    int32_t n_fill, const int32_t* positions, const int32_t* slot_of_row, const MapSrc& maps,
+                    const uint16_t* const* gamma, const uint16_t* const* w_k, const uint16_t* const* w_v,
+                    const float* rope, uint16_t* const* k_cache, uint16_t* const* v_cache, void* ws,
+                    size_t ws_bytes, void* stream) {
   const rf_shape& s = p->s;
   const int L = s.n_late;
+  const bool q8 = p->flags & RF_MAPS_Q8;
+  if (q8 != (maps.q != nullptr || maps.scale != nullptr))
+    return fail(RF_E_ARG, "%s: plan %s RF_MAPS_Q8 (int8 maps go to rf_fill_q8, bf16 maps to rf_fill)", fn,
+                q8 ? "has" : "lacks");
   if (n_fill < 0 || n_fill > s.n_rows) return fail(RF_E_ARG, "n_fill=%d outside [0, n_rows=%d]", n_fill, s.n_rows);
   if (!x || !aligned16(x)) return fail(RF_E_ARG, "x is null or not 16-byte aligned");
   if (ld_x < s.d_in || ld_x % 8) return fail(RF_E_ARG, "ld_x=%lld must be >= d_in and a multiple of 8", (long long)ld_x);
@@ -291,8 +324,14 @@ rf_status rf_fill(rf_plan* p, const uint16_t* x, int64_t ld_x, const int32_t* fi
   if (!positions) return fail(RF_E_ARG, "positions is null");
   rf_status st;
   const bool host_maps = p->flags & RF_MAPS_HOST;
-  if ((st = check_layer_ptrs(reinterpret_cast<const void* const*>(map_a), L, "map_a", !host_maps)) != RF_OK) return st;
-  if ((st = check_layer_ptrs(reinterpret_cast<const void* const*>(map_b), L, "map_b", !host_maps)) != RF_OK) return st;
+  if (q8) {
+    if ((st = check_layer_ptrs(reinterpret_cast<const void* const*>(maps.q), L, "map_q", !host_maps)) != RF_OK) return st;
+    if ((st = check_layer_ptrs(reinterpret_cast<const void* const*>(maps.scale), L, "map_scale", false)) != RF_OK)
+      return st;
+  } else if ((st = check_layer_ptrs(reinterpret_cast<const void* const*>(maps.a), L, "map_a", !host_maps)) != RF_OK) {
+    return st;
+  }
+  if ((st = check_layer_ptrs(reinterpret_cast<const void* const*>(maps.b), L, "map_b", !host_maps)) != RF_OK) return st;
   if ((st = check_layer_ptrs(reinterpret_cast<const void* const*>(gamma), L, "gamma")) != RF_OK) return st;
   if ((st = check_layer_ptrs(reinterpret_cast<const void* const*>(w_k), L, "w_k")) != RF_OK) return st;
   if ((st = check_layer_ptrs(reinterpret_cast<const void* const*>(w_v), L, "w_v")) != RF_OK) return st;
@@ -318,6 +357,9 @@ rf_status rf_fill(rf_plan* p, const uint16_t* x, int64_t ld_x, const int32_t* fi
   int32_t* flag = reinterpret_cast<int32_t*>(w0 + rope_bytes(s));
   uint16_t* prep = reinterpret_cast<uint16_t*>(w0 + rope_bytes(s) + kFlagBytes);
   uint16_t* ybuf = reinterpret_cast<uint16_t*>(w0 + rope_bytes(s) + kFlagBytes + prep_bytes(s, G));
+  uint16_t* dq = reinterpret_cast<uint16_t*>(w0 + rope_bytes(s) + kFlagBytes + prep_bytes(s, G) +
+                                             y_bytes(s, n_fill, G));
+  const size_t map_elems = static_cast<size_t>(s.d_out) * s.d_in;
 
   hipError_t e;
   if (p->flags & RF_VALIDATE)
@@ -367,25 +409,34 @@ rf_status rf_fill(rf_plan* p, const uint16_t* x, int64_t ld_x, const int32_t* fi
   pp.w = w;
   pp.out = prep;
 
+  rf::DequantParams dp{};
+  dp.d_out = s.d_out;
+  dp.d_in = s.d_in;
+
   const size_t y_layer = static_cast<size_t>(n_fill) * s.d_out;
   if (host_maps) {
-    // Double-buffered stream of (A_l, b_l) over the side stream.  Copy l waits
-    // until the map kernel of layer l-2 (same buffer) has run; the map kernel
-    // of layer l waits for copy l.  The first copies also wait for the work
-    // already on the caller's stream, which may still read the buffers.
-    const size_t a_bytes = p->map_elems * 2, b_bytes = static_cast<size_t>(s.d_out) * 2;
+    // Double-buffered stream of each layer's map and b over the side stream.
+    // Copy l waits until the map kernel of layer l-2 (same buffer) has run; the
+    // kernels of layer l that read the buffer wait for copy l.  The first copies
+    // also wait for the work already on the caller's stream, which may still
+    // read the buffers.
+    const size_t b_bytes = static_cast<size_t>(s.d_out) * 2;
     if ((e = hipEventRecord(p->ev_start, hs)) != hipSuccess) return hip_fail(e, "event record");
     if ((e = hipStreamWaitEvent(p->side, p->ev_start, 0)) != hipSuccess) return hip_fail(e, "stream wait");
     for (int l = 0; l < L; ++l) {
       const int buf = l & 1;
+      char* mb = p->mapbuf[buf];
       if (l >= 2 && (e = hipStreamWaitEvent(p->side, p->ev_consumed[buf], 0)) != hipSuccess)
         return hip_fail(e, "stream wait");
       {
         Timed tm(p, RF_K_COPY, p->side);
-        if ((e = hipMemcpyAsync(p->mapbuf[buf], map_a[l], a_bytes, hipMemcpyHostToDevice, p->side)) != hipSuccess ||
-            (e = hipMemcpyAsync(p->mapbuf[buf] + p->bias_off, map_b[l], b_bytes, hipMemcpyHostToDevice,
-                                p->side)) != hipSuccess)
-          return hip_fail(e, "map copy");
+        const void* msrc = q8 ? static_cast<const void*>(maps.q[l]) : static_cast<const void*>(maps.a[l]);
+        e = hipMemcpyAsync(mb, msrc, p->map_bytes, hipMemcpyHostToDevice, p->side);
+        if (e == hipSuccess && q8)
+          e = hipMemcpyAsync(mb + p->scale_off, maps.scale[l], p->scale_bytes, hipMemcpyHostToDevice, p->side);
+        if (e == hipSuccess)
+          e = hipMemcpyAsync(mb + p->bias_off, maps.b[l], b_bytes, hipMemcpyHostToDevice, p->side);
+        if (e != hipSuccess) return hip_fail(e, "map copy");
       }
       if ((e = hipEventRecord(p->ev_copied[buf], p->side)) != hipSuccess) return hip_fail(e, "event record");
 
@@ -397,8 +448,15 @@ rf_status rf_fill(rf_plan* p, const uint16_t* x, int64_t ld_x, const int32_t* fi
         if ((e = rf::launch_prep(pp, 1, hs)) != hipSuccess) return hip_fail(e, "prep launch");
       }
       if ((e = hipStreamWaitEvent(hs, p->ev_copied[buf], 0)) != hipSuccess) return hip_fail(e, "stream wait");
-      mp.a[0] = p->mapbuf[buf];
-      mp.b[0] = p->mapbuf[buf] + p->bias_off;
+      if (q8) {
+        dp.q[0] = reinterpret_cast<const int8_t*>(mb);
+        dp.s[0] = reinterpret_cast<const uint16_t*>(mb + p->scale_off);
+        dp.w[0] = dq;
+        Timed tm(p, RF_K_DEQUANT, hs);
+        if ((e = rf::launch_dequant(dp, 1, hs)) != hipSuccess) return hip_fail(e, "dequant launch");
+      }
+      mp.a[0] = q8 ? dq : reinterpret_cast<const uint16_t*>(mb);
+      mp.b[0] = reinterpret_cast<const uint16_t*>(mb + p->bias_off);
       {
         Timed tm(p, RF_K_MAP, hs);
         if ((e = rf::launch_map(mp, 1, hs)) != hipSuccess) return hip_fail(e, "map launch");
@@ -419,8 +477,15 @@ rf_status rf_fill(rf_plan* p, const uint16_t* x, int64_t ld_x, const int32_t* fi
       pp.gamma[i] = gamma[l0 + i];
       pp.wk[i] = w_k[l0 + i];
       pp.wv[i] = w_v[l0 + i];
-      mp.a[i] = map_a[l0 + i];
-      mp.b[i] = map_b[l0 + i];
+      if (q8) {
+        dp.q[i] = maps.q[l0 + i];
+        dp.s[i] = maps.scale[l0 + i];
+        dp.w[i] = dq + i * map_elems;
+        mp.a[i] = dq + i * map_elems;
+      } else {
+        mp.a[i] = maps.a[l0 + i];
+      }
+      mp.b[i] = maps.b[l0 + i];
       kp.in[i] = ybuf + i * y_layer;
       kp.kc[i] = k_cache[l0 + i];
       kp.vc[i] = v_cache[l0 + i];
@@ -428,6 +493,10 @@ rf_status rf_fill(rf_plan* p, const uint16_t* x, int64_t ld_x, const int32_t* fi
     {
       Timed tm(p, RF_K_PREP, hs);
       if ((e = rf::launch_prep(pp, g, hs)) != hipSuccess) return hip_fail(e, "prep launch");
+    }
+    if (q8) {
+      Timed tm(p, RF_K_DEQUANT, hs);
+      if ((e = rf::launch_dequant(dp, g, hs)) != hipSuccess) return hip_fail(e, "dequant launch");
     }
     {
       Timed tm(p, RF_K_MAP, hs);
@@ -439,6 +508,54 @@ rf_status rf_fill(rf_plan* p, const uint16_t* x, int64_t ld_x, const int32_t* fi
     }
   }
   return RF_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+rf_status rf_fill(rf_plan* p, const uint16_t* x, int64_t ld_x, const int32_t* fill_rows, int32_t n_fill,
+                  const int32_t* positions, const int32_t* slot_of_row, const uint16_t* const* map_a,
+                  const uint16_t* const* map_b, const uint16_t* const* gamma, const uint16_t* const* w_k,
+                  const uint16_t* const* w_v, const float* rope, uint16_t* const* k_cache,
+                  uint16_t* const* v_cache, void* ws, size_t ws_bytes, void* stream) {
+  if (!p) return fail(RF_E_ARG, "plan is null");
+  MapSrc m;
+  m.a = map_a;
+  m.b = map_b;
+  return fill_impl(p, "rf_fill", x, ld_x, fill_rows, n_fill, positions, slot_of_row, m, gamma, w_k, w_v, rope,
+                   k_cache, v_cache, ws, ws_bytes, stream);
+}
+
+rf_status rf_fill_q8(rf_plan* p, const uint16_t* x, int64_t ld_x, const int32_t* fill_rows, int32_t n_fill,
+                     const int32_t* positions, const int32_t* slot_of_row, const int8_t* const* map_q,
+                     const uint16_t* const* map_scale, const uint16_t* const* map_b, const uint16_t* const* gamma,
+                     const uint16_t* const* w_k, const uint16_t* const* w_v, const float* rope,
+                     uint16_t* const* k_cache, uint16_t* const* v_cache, void* ws, size_t ws_bytes, void* stream) {
+  if (!p) return fail(RF_E_ARG, "plan is null");
+  if (!map_q || !map_scale) return fail(RF_E_ARG, "map_q or map_scale array is null");
+  MapSrc m;
+  m.q = map_q;
+  m.scale = map_scale;
+  m.b = map_b;
+  return fill_impl(p, "rf_fill_q8", x, ld_x, fill_rows, n_fill, positions, slot_of_row, m, gamma, w_k, w_v, rope,
+                   k_cache, v_cache, ws, ws_bytes, stream);
+}
+
+rf_status rf_map_dequantize_q8(const int8_t* q, const uint16_t* scale, int32_t d_out, int32_t d_in, uint16_t* w,
+                               void* stream) {
+  if (!q || !scale || !w) return fail(RF_E_ARG, "null argument");
+  if (!aligned16(q) || !aligned16(w)) return fail(RF_E_ARG, "q and w must be 16-byte aligned");
+  if (d_out < 1 || d_in < 1 || d_in % rf::kQ8Block)
+    return fail(RF_E_SHAPE, "d_out must be >= 1 and d_in a positive multiple of %d", rf::kQ8Block);
+  rf::DequantParams dp{};
+  dp.d_out = d_out;
+  dp.d_in = d_in;
+  dp.q[0] = q;
+  dp.s[0] = scale;
+  dp.w[0] = w;
+  hipError_t e = rf::launch_dequant(dp, 1, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? RF_OK : hip_fail(e, "dequant launch");
 }
 
 rf_status rf_kv_project(rf_plan* p, const uint16_t* const* layer_in, int64_t ld_in, const int32_t* rows, int32_t n,

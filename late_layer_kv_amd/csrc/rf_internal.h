@@ -66,7 +66,17 @@ struct PrepParams {
   const uint16_t* wv[kMaxGroup];
 };
 
+// int8 map -> bf16 image: w_g[o][k] = bf16(q_g[o][k] * s_g[o][k / 128]), nearest even.
+constexpr int kQ8Block = 128;
+struct DequantParams {
+  int32_t d_out, d_in;
+  const int8_t* q[kMaxGroup];     // [d_out][d_in]
+  const uint16_t* s[kMaxGroup];   // [d_out][d_in / 128]
+  uint16_t* w[kMaxGroup];         // [d_out][d_in]
+};
+
 hipError_t launch_map(const MapParams& p, int n_layers, hipStream_t s);
+hipError_t launch_dequant(const DequantParams& p, int n_layers, hipStream_t s);
 hipError_t launch_kv(const KvParams& p, int n_layers, hipStream_t s);
 hipError_t launch_prep(const PrepParams& p, int n_layers, hipStream_t s);
 hipError_t launch_rope_table(float* table, int max_pos, int head_dim, double theta, hipStream_t s);

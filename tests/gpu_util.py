@@ -39,12 +39,15 @@ class DeviceInputs:
         host = s.maps_on_host if maps_on_host is None else maps_on_host
         self.maps_on_host = host
         self.x = t16(w.x).to(device)
-        if host:
-            self.map_a = [t16(a).pin_memory() for a in w.map_a]
-            self.map_b = [t16(b).pin_memory() for b in w.map_b]
+        place = (lambda t: t.pin_memory()) if host else (lambda t: t.to(device))
+        self.q8 = w.map_q is not None
+        if self.q8:
+            self.map_a = None
+            self.map_q = [place(torch.from_numpy(np.ascontiguousarray(q))) for q in w.map_q]
+            self.map_scale = [place(t16(sc)) for sc in w.map_scale]
         else:
-            self.map_a = [t16(a).to(device) for a in w.map_a]
-            self.map_b = [t16(b).to(device) for b in w.map_b]
+            self.map_a = [place(t16(a)) for a in w.map_a]
+        self.map_b = [place(t16(b)) for b in w.map_b]
         self.gamma = [t16(g).to(device) for g in w.gamma]
         self.w_k = [t16(a).to(device) for a in w.w_k]
         self.w_v = [t16(a).to(device) for a in w.w_v]
@@ -80,8 +83,12 @@ def gpu_fill(plan, di: DeviceInputs, rows: torch.Tensor, n_fill: int, caches=Non
     kc, vc = di.caches() if caches is None else caches
     g = s.n_late if layers_per_launch is None else layers_per_launch
     ws = torch.empty(max(plan.fill_workspace_bytes(n_fill, g), 256), dtype=torch.uint8, device=di.device)
-    B.fill(plan, di.x, rows, n_fill, di.positions, slots, di.map_a if map_a is None else map_a,
-           di.map_b if map_b is None else map_b, di.gamma, di.w_k, di.w_v, rope, kc, vc, ws)
+    if di.q8 and map_a is None:
+        B.fill_q8(plan, di.x, rows, n_fill, di.positions, slots, di.map_q, di.map_scale,
+                  di.map_b if map_b is None else map_b, di.gamma, di.w_k, di.w_v, rope, kc, vc, ws)
+    else:
+        B.fill(plan, di.x, rows, n_fill, di.positions, slots, di.map_a if map_a is None else map_a,
+               di.map_b if map_b is None else map_b, di.gamma, di.w_k, di.w_v, rope, kc, vc, ws)
     torch.cuda.synchronize()
     return kc, vc
 

@@ -162,3 +162,99 @@ def test_ridge_errors():
     assert e.value.status == -6
     with pytest.raises(B.RfError):
         acc.solve(-1.0)
+
+
+# ---- int8 maps: host checks and the host quantizer
+
+
+def test_q8_plan_needs_d_in_multiple_of_128():
+    with pytest.raises(B.RfError) as e:
+        B.Plan(**_shape(d_in=192), maps_q8=True)
+    assert e.value.status == -2
+    B.Plan(**_shape(d_in=192)).close()   # fine for bf16 maps
+
+
+def test_q8_flag_must_match_the_call():
+    L = B.lib()
+    nl = 4
+    fake = C.c_void_p(0x1000)
+    arr = (C.c_void_p * nl)(*([0x1000] * nl))
+    ws, ws_b = C.c_void_p(0x10000), 1 << 40
+    p8 = B.Plan(**_shape(), maps_q8=True)
+    pb = B.Plan(**_shape())
+    # bf16 entry point on an int8 plan, and the reverse
+    assert L.rf_fill(p8.handle, fake, 256, fake, 10, fake, None, arr, arr, arr, arr, arr, None, arr, arr,
+                     ws, ws_b, None) == -1
+    assert "RF_MAPS_Q8" in B.last_error()
+    assert L.rf_fill_q8(pb.handle, fake, 256, fake, 10, fake, None, arr, arr, arr, arr, arr, arr, None, arr,
+                        arr, ws, ws_b, None) == -1
+    null_arr = (C.c_void_p * nl)(*([0x1000] * (nl - 1) + [0]))
+    mis_arr = (C.c_void_p * nl)(*([0x1000] * (nl - 1) + [0x1004]))
+
+    def call8(q=arr, s=arr, b=arr, ws_b=ws_b):
+        return L.rf_fill_q8(p8.handle, fake, 256, fake, 10, fake, None, q, s, b, arr, arr, arr, None, arr, arr,
+                            ws, ws_b, None)
+    assert call8(q=None) == -1
+    assert call8(s=None) == -1
+    assert call8(q=null_arr) == -1
+    assert call8(s=null_arr) == -1
+    assert call8(q=mis_arr) == -1        # codes must be 16-byte aligned
+    assert call8(b=null_arr) == -1
+    assert call8(ws_b=16) == -4
+    p8.close()
+    pb.close()
+
+
+def test_q8_workspace_adds_the_bf16_image():
+    p8 = B.Plan(**_shape(), maps_q8=True)
+    pb = B.Plan(**_shape())
+    image = 256 * 256 * 2
+    for g in (1, 2, 4):
+        assert p8.fill_workspace_bytes(448, g) == pb.fill_workspace_bytes(448, g) + g * image
+    assert p8.kv_project_workspace_bytes(2) == pb.kv_project_workspace_bytes(2)
+    for p in (p8, pb):
+        p.close()
+
+
+def test_dequantize_argument_errors_before_any_device_work():
+    L = B.lib()
+    f = C.c_void_p(0x1000)
+    assert L.rf_map_dequantize_q8(None, f, 4, 128, f, None) == -1
+    assert L.rf_map_dequantize_q8(f, None, 4, 128, f, None) == -1
+    assert L.rf_map_dequantize_q8(f, f, 4, 128, None, None) == -1
+    assert L.rf_map_dequantize_q8(C.c_void_p(0x1001), f, 4, 128, f, None) == -1
+    assert L.rf_map_dequantize_q8(f, f, 4, 128, C.c_void_p(0x1002), None) == -1
+    assert L.rf_map_dequantize_q8(f, f, 4, 100, f, None) == -2
+    assert L.rf_map_dequantize_q8(f, f, 0, 128, f, None) == -2
+
+
+def _quant_inputs():
+    import workloads
+    w = workloads.make(workloads.spec("tiny"), layers=[0])
+    g = np.random.default_rng(21)
+    a_map = oracle.bf16_bits_to_f64(w.map_a[0]).astype(np.float32)          # an I + noise map
+    heavy = (g.standard_t(2, size=(64, 384)) * np.exp(g.uniform(-30, 30, size=(64, 1)))).astype(np.float32)
+    heavy[3, 128:256] = 0.0                                                   # all-zero block
+    heavy[5, :128] = 0.0
+    heavy[5, :4] = [63.5, 1.25, 1.75, -0.75]                                  # exact ties at scale 0.5
+    tiny = (g.standard_normal((8, 128)) * 1e-38).astype(np.float32)           # subnormal range
+    return [a_map, heavy, tiny]
+
+
+@pytest.mark.parametrize("case", range(3))
+def test_host_quantizer_matches_oracle_bitwise(case):
+    a = _quant_inputs()[case]
+    q, s = B.map_quantize_q8(a)
+    qr, sr = oracle.quantize_q8(a)
+    assert np.array_equal(s, sr) and np.array_equal(q, qr)
+
+
+def test_host_quantizer_errors():
+    with pytest.raises(B.RfError) as e:
+        B.map_quantize_q8(np.ones((2, 100), np.float32))
+    assert e.value.status == -2
+    a = np.ones((2, 128), np.float32)
+    a[1, 7] = np.nan
+    with pytest.raises(B.RfError) as e:
+        B.map_quantize_q8(a)
+    assert e.value.status == -1
