@@ -159,6 +159,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="27b_120k", choices=workloads.CONFIG_ORDER)
     ap.add_argument("--layers-per-launch", type=int, default=None)
+    ap.add_argument("--maps", default="bf16", choices=["bf16", "q8"],
+                    help="map storage: bf16, or int8 codes with one bf16 scale per 128 weights of each row")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="after timing, copy MIB mebibytes device-to-device once (PMC calibration)")
@@ -189,7 +191,8 @@ def main():
         return
 
     name = args.workload
-    s = workloads.spec(name)
+    s = workloads.spec(name, map_format=args.maps)
+    q8 = args.maps == "q8"
     dev = "cuda:0"
     log(f"[bench] {name}: drawing inputs")
     t0 = time.perf_counter()
@@ -197,7 +200,12 @@ def main():
     log(f"[bench] {name}: inputs drawn in {time.perf_counter() - t0:.1f} s; uploading")
     host_maps = s.maps_on_host
     x = t16(w.x, dev)
-    map_a = [t16(a, dev, host_maps) for a in w.map_a]
+    if q8:
+        place = (lambda t: t.pin_memory()) if host_maps else (lambda t: t.to(dev))
+        map_q = [place(torch.from_numpy(np.ascontiguousarray(q))) for q in w.map_q]
+        map_s = [t16(sc, dev, host_maps) for sc in w.map_scale]
+    else:
+        map_a = [t16(a, dev, host_maps) for a in w.map_a]
     map_b = [t16(b, dev, host_maps) for b in w.map_b]
     gamma = [t16(g, dev) for g in w.gamma]
     w_k = [t16(a, dev) for a in w.w_k]
@@ -218,7 +226,11 @@ def main():
 
     def step():
         B.fill_rows(plan, exact, fill_rows, n_fill_dev, rows_ws)
-        B.fill(plan, x, fill_rows, n_fill, positions, None, map_a, map_b, gamma, w_k, w_v, None, kc, vc, ws)
+        if q8:
+            B.fill_q8(plan, x, fill_rows, n_fill, positions, None, map_q, map_s, map_b, gamma, w_k, w_v, None,
+                      kc, vc, ws)
+        else:
+            B.fill(plan, x, fill_rows, n_fill, positions, None, map_a, map_b, gamma, w_k, w_v, None, kc, vc, ws)
 
     log(f"[bench] {name}: n_fill={n_fill}, {s.n_late} late layers, {g} per launch; warmup {args.warmup}")
     for _ in range(args.warmup):
@@ -279,6 +291,7 @@ def main():
         "config": {"workload": name, "d_in": s.d_in, "d_out": s.d_out, "late_layers": s.n_late,
                    "kv_heads": s.n_kv, "head_dim": s.head_dim, "rows": s.n_rows, "fill_rows": n_fill,
                    "prompts": list(s.prompt_lens), "maps": "pinned host, streamed" if host_maps else "HBM",
+                   "map_format": "int8 + bf16 scale per 128 weights of a row" if q8 else "bf16",
                    "layers_per_launch": 1 if host_maps else g},
         "tflops": step_flops / (ms * 1e-3) / 1e12,
         "frac_of_bf16_peak": step_flops / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS,
@@ -289,6 +302,15 @@ def main():
         "kernels": kernels,
         "kv_gemm_tflops": kv_tflops,
     }
+    if q8 and prof["dequant"][1]:
+        dq_ms, dq_n = prof["dequant"]
+        layers_per_dq = s.n_late * args.steps / dq_n
+        dq_bytes = layers_per_dq * s.d_out * s.d_in * (1 + 2 + 2 / workloads.Q8_BLOCK)
+        dq_avg = dq_ms / dq_n
+        out["dequant_roofline"] = {"bound": "hbm", "kernel": "dequant", "achieved": dq_bytes / (dq_avg * 1e-3) / 1e9,
+                                   "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                                   "frac": dq_bytes / (dq_avg * 1e-3) / 1e9 / PEAK_HBM_GBS,
+                                   "algorithmic_bytes_per_launch": dq_bytes, "ms_per_launch": dq_avg}
     if not args.no_cpu_baseline:
         log(f"[bench] {name}: timing the fp64 oracle on a sample")
         f = np.setdiff1d(np.arange(s.n_rows), w.exact_rows).astype(np.int32)

@@ -40,10 +40,13 @@ def sample_rows(fill: np.ndarray, exact: np.ndarray, positions: np.ndarray, n: i
     return np.array(sorted(pick), dtype=np.int32)
 
 
-@pytest.mark.parametrize("name", workloads.CONFIG_ORDER)
-def test_full_size(name):
-    s = workloads.spec(name)
-    print(f"[full] {name}: generating inputs", flush=True)
+FULL_CASES = [(n, "bf16") for n in workloads.CONFIG_ORDER] + [("27b_120k", "q8"), ("8b_ragged_host", "q8")]
+
+
+@pytest.mark.parametrize("name,fmt", FULL_CASES, ids=[f"{n}-{f}" for n, f in FULL_CASES])
+def test_full_size(name, fmt):
+    s = workloads.spec(name, map_format=fmt)
+    print(f"[full] {name} ({fmt} maps): generating inputs", flush=True)
     w = workloads.make(s)
     di = U.DeviceInputs(w)
     plan = B.Plan.for_spec(s)
