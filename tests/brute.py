@@ -111,3 +111,31 @@ def quantize_q8(a_rows):
         q_rows.append(qr)
         s_rows.append(sr)
     return q_rows, s_rows
+
+
+# ---------------------------------------------------------------- value rescale
+# Written from the description of the value rescale (RidgeFill, section 2.3):
+# per head, the exact value norm over the predicted one, averaged over the
+# calibration rows of one request.
+
+def value_scale(v_exact_rows, v_pred_rows, groups, n_groups, head_dim):
+    """Nested lists: scale[g][h] = mean over rows of group g of |ve_h| / |vp_h|."""
+    width = len(v_exact_rows[0])
+    n_heads = width // head_dim
+    out = []
+    for g in range(n_groups):
+        row = []
+        for h in range(n_heads):
+            tot, cnt = 0.0, 0
+            for ve, vp, gr in zip(v_exact_rows, v_pred_rows, groups):
+                if gr != g:
+                    continue
+                se = sum(ve[h * head_dim + j] ** 2 for j in range(head_dim)) ** 0.5
+                sp = sum(vp[h * head_dim + j] ** 2 for j in range(head_dim)) ** 0.5
+                if sp == 0.0:
+                    continue
+                tot += se / sp
+                cnt += 1
+            row.append(tot / cnt if cnt else 1.0)
+        out.append(row)
+    return out

@@ -438,6 +438,123 @@ def pin_bf16_rounding_library(o):
                           .to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)), ref_q
 
 
+# ---------------------------------------------------------------- value rescale
+
+def pin_rescale_closed_form(o):
+    """Section 2.3 ("Value rescale"), worked by hand.  W_v = I, gain 1, eps 0,
+    two heads of 2: an input row (3, 0, 0, 4) normalises to (1.2, 0, 0, 1.6),
+    one of all ones to itself, so the head norms are (1.2, 1.6) and
+    (sqrt 2, sqrt 2).  Request 0 has two rows, request 1 one; scales are
+    means of per-row ratios, not ratios of mean norms."""
+    s2 = math.sqrt(2.0)
+    v_ex = np.array([[1.2, 0.0, 0.0, 1.6], [1.0, 1.0, 1.0, 1.0], [0.0, 3.0, 4.0, 0.0]])
+    v_pr = np.array([[1.0, 1.0, 1.0, 1.0], [2.0, 0.0, 0.0, 1.0], [0.6, 0.8, 0.0, 2.0]])
+    got = o.scales_from_values(v_ex, v_pr, np.array([0, 0, 1]), 2, 2)
+    want = np.array([[(1.2 / s2 + s2 / 2.0) / 2, (1.6 / s2 + s2 / 1.0) / 2],
+                     [3.0 / 1.0, 4.0 / 2.0]])
+    assert np.allclose(got, want, rtol=1e-14, atol=0), (got, want)
+    # a request with no rows, and a zero predicted head, keep scale 1
+    got = o.scales_from_values(v_ex[:1], np.array([[0.0, 0.0, 3.0, 4.0]]), np.array([1]), 3, 2)
+    assert np.allclose(got, [[1, 1], [1, 1.6 / 5.0], [1, 1]], rtol=1e-14)
+    # the normalisation on the way in
+    h = o.rms_norm(np.array([[3.0, 0.0, 0.0, 4.0]]), np.ones(4), 0.0)
+    assert np.allclose(h, [[1.2, 0.0, 0.0, 1.6]], rtol=1e-15)
+    # the rescale multiplies each head of each row by its request's scale
+    sc = np.array([[2.0, 3.0], [5.0, 7.0]])
+    r = o.rescale_values(np.ones((2, 4)), sc, np.array([1, 0]), 2)
+    assert np.array_equal(r, [[5, 5, 7, 7], [2, 2, 3, 3]])
+
+
+def _rescale_case(o, seed=30):
+    s = workloads.spec("tiny", prompt_lens=(200, 120, 80), tail=40, seed=seed)
+    w = workloads.make(s)
+    rows, grp = workloads.calibration_row_list(s, 16)
+    truth = workloads.make_layer_truth(s, len(rows), outliers=w.outlier_channels)
+    return s, w, rows, grp, truth
+
+
+def pin_rescale_identity_and_invariances(o):
+    """True input = predicted input gives scale 1 exactly and leaves values
+    unchanged; the norm removes any positive scaling of the true inputs
+    (eps = 0); row order inside a request and other requests' rows do not
+    matter."""
+    s, w, rows, grp, truth = _rescale_case(o)
+    xs = o.bf16_bits_to_f64(w.x[rows])
+    g = o.bf16_bits_to_f64(w.gamma[0])
+    wv = o.bf16_bits_to_f64(w.w_v[0])
+    y_pred = o.predicted_input(xs, o.map_matrix(w, 0), o.bf16_bits_to_f64(w.map_b[0]))
+    v_pred = o.project(o.rms_norm(y_pred, g, 0.0), wv)
+    one = o.scales_from_values(v_pred, v_pred, grp, 3, s.head_dim)
+    assert np.array_equal(one, np.ones_like(one))
+    v = np.arange(8.0).reshape(2, 4) + 1
+    assert np.array_equal(o.rescale_values(v, np.ones((3, 2)), np.array([2, 0]), 2), v)
+    yt = o.bf16_bits_to_f64(truth[0])
+    ve = o.project(o.rms_norm(yt, g, 0.0), wv)
+    ve3 = o.project(o.rms_norm(3.5 * yt, g, 0.0), wv)
+    a = o.scales_from_values(ve, v_pred, grp, 3, s.head_dim)
+    b = o.scales_from_values(ve3, v_pred, grp, 3, s.head_dim)
+    assert np.allclose(a, b, rtol=1e-12) and not np.allclose(a, 1.0, rtol=1e-3)
+    perm = np.random.default_rng(1).permutation(len(rows))
+    c = o.scales_from_values(ve[perm], v_pred[perm], grp[perm], 3, s.head_dim)
+    assert np.allclose(a, c, rtol=1e-12)
+    ve2 = ve.copy()
+    ve2[grp == 1] *= 4.0
+    d = o.scales_from_values(ve2, v_pred, grp, 3, s.head_dim)
+    assert np.array_equal(d[[0, 2]], a[[0, 2]]) and np.allclose(d[1], 4.0 * a[1], rtol=1e-12)
+
+
+def pin_rescale_brute(o):
+    """value_scales against plain loops over the same projections (tests/brute.py)."""
+    s, w, rows, grp, truth = _rescale_case(o, seed=31)
+    sc = o.value_scales(w, truth, rows, grp, 3, layers=[1])
+    g = o.bf16_bits_to_f64(w.gamma[1])
+    wv = o.bf16_bits_to_f64(w.w_v[1])
+    xs = o.bf16_bits_to_f64(w.x[rows])
+    a = o.bf16_bits_to_f64(w.map_a[1])
+    b = o.bf16_bits_to_f64(w.map_b[1])
+    vp = (rms_ref(xs @ a.T + b, g, s.rms_eps)) @ wv.T
+    ve = rms_ref(o.bf16_bits_to_f64(truth[1]), g, s.rms_eps) @ wv.T
+    ref = np.array(brute.value_scale(ve.tolist(), vp.tolist(), grp.tolist(), 3, s.head_dim))
+    assert np.allclose(sc[1], ref, rtol=1e-12), (sc[1], ref)
+
+
+def rms_ref(y, g, eps):
+    return g * y / np.sqrt((y * y).sum(axis=1, keepdims=True) / y.shape[1] + eps)
+
+
+def pin_calibration_rows(o):
+    """The first c rows of every request's tail: 4 ragged prompts, c below,
+    at and above the tail length; the workload generator's list agrees."""
+    lens, tail = (30, 9, 20, 5), 8
+    rows, grp = o.calibration_rows(lens, tail, 3)
+    assert rows.tolist() == [22, 23, 24, 31, 32, 33, 51, 52, 53, 59, 60, 61]
+    assert grp.tolist() == [0, 0, 0, 1, 1, 1, 2, 2, 2, 3, 3, 3]
+    rows, grp = o.calibration_rows(lens, tail, 50)
+    assert rows.tolist() == list(range(22, 30)) + list(range(31, 39)) + list(range(51, 59)) + list(range(59, 64))
+    for name in ("27b_120k", "8b_ragged_host"):
+        s = workloads.spec(name)
+        r1, g1 = o.calibration_rows(s.prompt_lens, s.tail, 512)
+        r2, g2 = workloads.calibration_row_list(s, 512)
+        assert np.array_equal(r1, r2) and np.array_equal(g1, g2)
+        assert set(r1.tolist()) <= set(workloads.exact_row_list(s).tolist()), "calibration rows are tail rows"
+
+
+def pin_rescaled_fill(o):
+    """The rescaled fill keeps the keys and multiplies each value head by the
+    scale of its row's request."""
+    s, w, rows, grp, truth = _rescale_case(o, seed=32)
+    fill = o.fill_row_set(s.n_rows, w.exact_rows)[::7]
+    g_of_row = workloads.prompt_of_row(s)
+    sc = {l: np.array([[1.5, 0.5], [2.0, 1.0], [0.25, 4.0]]) for l in range(s.n_late)}
+    base = o.fill_workload(w, rows=fill)
+    res = o.fill_workload_rescaled(w, sc, g_of_row, fill)
+    for l in range(s.n_late):
+        assert np.array_equal(res[l][0], base[l][0])
+        f = sc[l][g_of_row[fill]]
+        want = base[l][1] * np.repeat(f, s.head_dim, axis=1)
+        assert np.array_equal(res[l][1], want)
+
+
 # ---------------------------------------------------------------- ceilings
 
 def pin_printed_ceilings(o):
@@ -462,4 +579,6 @@ CEILING_PINS = [pin_printed_ceilings]
 QUANT_PINS = [pin_q8_dequant_closed_form, pin_q8_dequant_brute, pin_q8_grid_fixpoint,
               pin_q8_quantize_bounds, pin_q8_quantize_ties, pin_q8_quantize_brute,
               pin_bf16_rounding_library]
-ALL_PINS = FILL_PINS + RIDGE_PINS + CEILING_PINS + QUANT_PINS
+RESCALE_PINS = [pin_rescale_closed_form, pin_rescale_identity_and_invariances, pin_rescale_brute,
+                pin_calibration_rows, pin_rescaled_fill]
+ALL_PINS = FILL_PINS + RIDGE_PINS + CEILING_PINS + QUANT_PINS + RESCALE_PINS

@@ -12,7 +12,7 @@ import pytest
 from tests import pins
 
 ORACLE_DIR = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "oracle")
-FILES = ("fill.py", "ridge.py", "ceiling.py", "quant.py")
+FILES = ("fill.py", "ridge.py", "ceiling.py", "quant.py", "rescale.py")
 
 MUTANTS = {
     # the map
@@ -64,10 +64,24 @@ MUTANTS = {
     "q8_max_over_rows": ("quant.py", [("m = np.abs(blocks).max(axis=2)", "m = np.abs(blocks).max(axis=2).max(axis=0, keepdims=True) + 0 * blocks[:, :, 0]")]),
     "bf16_round_truncates": ("quant.py", [("return ((u + 0x7FFF + lsb) >> 16)", "return ((u) >> 16)")]),
     "bf16_round_ties_up": ("quant.py", [("return ((u + 0x7FFF + lsb) >> 16)", "return ((u + 0x8000) >> 16)")]),
+    # the value rescale
+    "rescale_ratio_of_means": ("rescale.py", [("np.mean(ne[ok, h] / npr[ok, h])", "np.mean(ne[ok, h]) / np.mean(npr[ok, h])")]),
+    "rescale_inverted": ("rescale.py", [("np.mean(ne[ok, h] / npr[ok, h])", "np.mean(npr[ok, h] / ne[ok, h])")]),
+    "rescale_squared_norms": ("rescale.py", [("return np.linalg.norm(v.reshape(n, width // head_dim, head_dim), axis=2)",
+                                              "return np.sum(v.reshape(n, width // head_dim, head_dim) ** 2, axis=2)")]),
+    "rescale_groups_ignored": ("rescale.py", [("sel = np.asarray(group) == g", "sel = np.ones(len(group), dtype=bool)")]),
+    "rescale_last_c_rows": ("rescale.py", [("rows.extend(range(first, first + k))", "rows.extend(range(start + n - k, start + n))")]),
+    "rescale_exact_not_normed": ("rescale.py", [("v_exact = project(rms_norm(bf16_bits_to_f64(layer_true[l]), g, s.rms_eps), wv)",
+                                                 "v_exact = project(bf16_bits_to_f64(layer_true[l]), wv)")]),
+    "rescale_keys_too": ("rescale.py", [("return {l: (k, rescale_values(v, scales[l], g, w.spec.head_dim))",
+                                         "return {l: (rescale_values(k, scales[l], g, w.spec.head_dim), rescale_values(v, scales[l], g, w.spec.head_dim))")]),
+    "rescale_heads_interleaved": ("rescale.py", [("np.repeat(scale[np.asarray(group_of_rows)], head_dim, axis=1)",
+                                                  "np.tile(scale[np.asarray(group_of_rows)], (1, head_dim))")]),
+    "rescale_zero_rows_counted": ("rescale.py", [("ok = sel & (npr[:, h] > 0)", "ok = sel")]),
 }
 
 PINS_FOR = {"fill.py": pins.FILL_PINS, "ridge.py": pins.RIDGE_PINS, "ceiling.py": pins.CEILING_PINS,
-            "quant.py": pins.QUANT_PINS}
+            "quant.py": pins.QUANT_PINS, "rescale.py": pins.RESCALE_PINS}
 
 
 def _load(target, edits):
@@ -79,10 +93,13 @@ def _load(target, edits):
             for old, new in edits:
                 assert src.count(old) >= 1, f"mutation anchor not found in {fn}: {old!r}"
                 src = src.replace(old, new, 1)
-        mod = types.ModuleType("oracle_mutant_" + fn[:-3])
+        mod = types.ModuleType("oracle.mutant_" + fn[:-3])
+        mod.__package__ = "oracle"  # relative imports resolve to the unmutated oracle
         exec(compile(src, os.path.join(ORACLE_DIR, fn), "exec"), mod.__dict__)
         for k, v in vars(mod).items():
-            if not k.startswith("_"):
+            # a name a later file imports from an earlier one keeps the earlier
+            # (possibly mutated) definition
+            if not k.startswith("_") and not hasattr(ns, k):
                 setattr(ns, k, v)
     return ns
 

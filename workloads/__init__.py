@@ -44,11 +44,11 @@ import numpy as np
 
 __all__ = [
     "Spec", "Workload", "SPECS", "CONFIG_ORDER", "spec", "make",
-    "f32_to_bf16_bits", "exact_row_list",
+    "f32_to_bf16_bits", "exact_row_list", "prompt_of_row", "calibration_row_list", "make_layer_truth",
 ]
 
 # seed-sequence "kind" tags
-_K_X, _K_OUTLIER, _K_LAYER, _K_SPANS = 1, 2, 3, 4
+_K_X, _K_OUTLIER, _K_LAYER, _K_SPANS, _K_TRUTH = 1, 2, 3, 4, 5
 _L_MAP, _L_BIAS, _L_GAMMA, _L_WK, _L_WV, _L_QSCALE = 0, 1, 2, 3, 4, 5
 Q8_BLOCK = 128  # weights per bf16 scale along each row of an int8 map
 _X_BLOCK = 8192  # rows per independently seeded block of x_S
@@ -186,6 +186,39 @@ def exact_row_list(s: Spec) -> np.ndarray:
         for a, b in taken:
             rows.extend(range(a, b))
     return np.array(sorted(set(rows)), dtype=np.int32)
+
+
+def prompt_of_row(s: Spec) -> np.ndarray:
+    """Index of the prompt (request) each row belongs to, int32 [n_rows]."""
+    return np.concatenate([np.full(n, p, dtype=np.int32) for p, n in enumerate(s.prompt_lens)])
+
+
+def calibration_row_list(s: Spec, c: int):
+    """The first min(c, tail) rows of every prompt's tail and their prompt
+    index: the rows a value rescale measures (int32 arrays, ascending)."""
+    rows, grp = [], []
+    start = 0
+    for p, n in enumerate(s.prompt_lens):
+        t = min(s.tail, n)
+        k = min(c, t)
+        rows.extend(range(start + n - t, start + n - t + k))
+        grp.extend([p] * k)
+        start += n
+    return np.array(rows, dtype=np.int32), np.array(grp, dtype=np.int32)
+
+
+def make_layer_truth(s: Spec, n: int, layers: Optional[List[int]] = None,
+                     outliers: Optional[np.ndarray] = None) -> List[np.ndarray]:
+    """Stand-ins for the true inputs of the late layers on n rows (bf16 bits
+    [n][d_out] per layer): drawn like x_S, N(0, 1) with the outlier channels
+    scaled, independently per layer."""
+    out = []
+    for l in (range(s.n_late) if layers is None else layers):
+        v = _normal((s.seed, _K_TRUTH, l), (n, s.d_out))
+        if outliers is not None and len(outliers):
+            v[:, outliers[outliers < s.d_out]] *= np.float32(s.outlier_scale)
+        out.append(f32_to_bf16_bits(v))
+    return out
 
 
 def _positions(s: Spec) -> np.ndarray:
