@@ -133,6 +133,20 @@ rf_status rf_fill_rows(rf_plan* plan, const int32_t* exact_rows, int32_t n_exact
                        int32_t* fill_rows, int32_t* n_fill,
                        void* workspace, size_t ws_bytes, void* hip_stream);
 
+/* Value rescale applied by the fill (section 2.3, "Value rescale"; see
+ * rf_value_scales below).  With a non-NULL rf_vscale, value head h of filled
+ * row r in late layer l is multiplied by
+ *     scale[(l * n_groups + group_of_row[r]) * n_kv + h]
+ * in fp32, together with the norm's factor, before rounding to bf16; keys are
+ * not touched.  Rows whose group is outside [0, n_groups) are skipped (not
+ * written), like rows with an out-of-range slot.  A NULL rf_vscale, or all
+ * scales 1, gives exactly the unscaled bytes. */
+typedef struct rf_vscale {
+  const float* scale;           /* device fp32 [n_late][n_groups][n_kv], 4-byte aligned */
+  const int32_t* group_of_row;  /* device int32 [n_rows]: request (group) of each row    */
+  int32_t n_groups;             /* >= 1                                                    */
+} rf_vscale;
+
 /* The fill (steps 1-5 above) for n_fill rows and every late layer.
  *   x              [n_rows][ld_x] bf16, ld_x >= d_in, ld_x % 8 == 0, 16-byte aligned
  *   fill_rows      [n_fill] int32, ascending, unique, in [0, n_rows)
@@ -144,6 +158,7 @@ rf_status rf_fill_rows(rf_plan* plan, const int32_t* exact_rows, int32_t n_exact
  *                  pinned maps alive until the stream has completed)
  *   gamma, w_k, w_v, k_cache, v_cache   HOST arrays of n_late device pointers
  *   rope_cos_sin   table from rf_rope_table, or NULL (built in the workspace)
+ *   vscale         HOST pointer to an rf_vscale, or NULL for no value rescale
  *   workspace      >= rf_fill_workspace_bytes(plan, n_fill, 1), 256-byte aligned
  * Rows whose position or slot is out of range are skipped by the kernels
  * (RF_VALIDATE turns them into RF_E_ROWS).  n_fill == 0 enqueues nothing and
@@ -158,6 +173,7 @@ rf_status rf_fill(rf_plan* plan,
                   const uint16_t* const* w_k, const uint16_t* const* w_v,
                   const float* rope_cos_sin,
                   uint16_t* const* k_cache, uint16_t* const* v_cache,
+                  const rf_vscale* vscale,
                   void* workspace, size_t ws_bytes, void* hip_stream);
 
 /* ---- int8 maps -----------------------------------------------------------
@@ -185,6 +201,7 @@ rf_status rf_fill_q8(rf_plan* plan,
                      const uint16_t* const* w_k, const uint16_t* const* w_v,
                      const float* rope_cos_sin,
                      uint16_t* const* k_cache, uint16_t* const* v_cache,
+                     const rf_vscale* vscale,
                      void* workspace, size_t ws_bytes, void* hip_stream);
 
 /* Expand one int8 map into bf16 (device to device): w[o][k] = bf16(q[o][k] *
@@ -199,6 +216,46 @@ rf_status rf_map_dequantize_q8(const int8_t* q, const uint16_t* scale, int32_t d
  * double precision and clipped to [-127, 127]; an all-zero block gets s = 0,
  * q = 0.  Outputs q [d_out][d_in] and scale [d_out][d_in / 128], HOST. */
 rf_status rf_map_quantize_q8(const float* a, int32_t d_out, int32_t d_in, int8_t* q, uint16_t* scale);
+
+/* ---- Value rescale measurement --------------------------------------------
+ * Section 2.3 ("Value rescale"), on for the 27B deployment with c = 512
+ * (section 4.2): in each late layer, the first c rows of each request's tail
+ * are projected to values twice, from their true input and from the map's
+ * prediction; per request g and key-value head h the scale is the mean over
+ * the request's rows of ||v_exact_h|| / ||v_pred_h|| (Euclidean norms over the
+ * head's head_dim values).  Rows whose predicted head norm is zero are left
+ * out; a (request, head) with no rows gets scale 1.
+ *   x              split state, as for rf_fill
+ *   layer_in       HOST array of n_late device pointers; layer_in[l] is bf16
+ *                  [n_calib][ld_in]: the true input of layer l for each
+ *                  calibration row, in calibration order (ld_in >= d_out, % 8)
+ *   calib_rows     [n_calib] int32 rows of x (the calibration rows)
+ *   calib_group    [n_calib] int32 request of each calibration row
+ *   n_groups       requests (>= 1); scale[l][g][h] is written for every g
+ *   map_*, gamma, w_v   as for rf_fill / rf_fill_q8 (RF_MAPS_HOST streams)
+ *   scale          device fp32 [n_late][n_groups][n_kv] out, 4-byte aligned
+ *   workspace      >= rf_value_scales_workspace_bytes(plan, n_calib, 1)
+ * Both value vectors go through the fill's own kernels (map contraction, norm
+ * and value projection, bf16 rounding); the norms, ratios and means are fp32
+ * with a fixed summation order.  The result feeds rf_fill's rf_vscale. */
+size_t rf_value_scales_workspace_bytes(const rf_plan* plan, int32_t n_calib, int32_t layers_per_launch);
+rf_status rf_value_scales(rf_plan* plan,
+                          const uint16_t* x, int64_t ld_x,
+                          const uint16_t* const* layer_in, int64_t ld_in,
+                          const int32_t* calib_rows, const int32_t* calib_group,
+                          int32_t n_calib, int32_t n_groups,
+                          const uint16_t* const* map_a, const uint16_t* const* map_b,
+                          const uint16_t* const* gamma, const uint16_t* const* w_v,
+                          float* scale, void* workspace, size_t ws_bytes, void* hip_stream);
+rf_status rf_value_scales_q8(rf_plan* plan,
+                             const uint16_t* x, int64_t ld_x,
+                             const uint16_t* const* layer_in, int64_t ld_in,
+                             const int32_t* calib_rows, const int32_t* calib_group,
+                             int32_t n_calib, int32_t n_groups,
+                             const int8_t* const* map_q, const uint16_t* const* map_scale,
+                             const uint16_t* const* map_b,
+                             const uint16_t* const* gamma, const uint16_t* const* w_v,
+                             float* scale, void* workspace, size_t ws_bytes, void* hip_stream);
 
 /* The exact cache write of each late layer from given true inputs: steps 2-5
  * only (no map).  Section 2.1: exact rows and the tail run the layer from its
@@ -250,7 +307,8 @@ enum {
   RF_K_ROWS = 4,      /* fill-row compaction                         */
   RF_K_COPY = 5,      /* host -> device map copy (RF_MAPS_HOST)      */
   RF_K_DEQUANT = 6,   /* int8 map -> bf16 image (RF_MAPS_Q8)         */
-  RF_K_COUNT = 7
+  RF_K_SCALE = 7,     /* value-rescale ratios and means              */
+  RF_K_COUNT = 8
 };
 typedef struct rf_profile {
   double ms[RF_K_COUNT];        /* summed event time per kind, milliseconds */

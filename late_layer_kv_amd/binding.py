@@ -33,9 +33,10 @@ EXPORTS = [
     "rf_ridge_acc_create", "rf_ridge_acc_add", "rf_ridge_solve", "rf_ridge_acc_destroy", "rf_ridge_fit",
     "rf_plan_profile", "rf_plan_profile_read", "rf_last_error",
     "rf_fill_q8", "rf_map_dequantize_q8", "rf_map_quantize_q8",
+    "rf_value_scales_workspace_bytes", "rf_value_scales", "rf_value_scales_q8",
 ]
 
-KERNEL_KINDS = ["map", "kv", "prep", "rope", "rows", "copy", "dequant"]
+KERNEL_KINDS = ["map", "kv", "prep", "rope", "rows", "copy", "dequant", "scale"]
 
 
 class RfError(RuntimeError):
@@ -51,7 +52,12 @@ class Shape(C.Structure):
 
 
 class Profile(C.Structure):
-    _fields_ = [("ms", C.c_double * 7), ("launches", C.c_int64 * 7)]
+    _fields_ = [("ms", C.c_double * 8), ("launches", C.c_int64 * 8)]
+
+
+class VScale(C.Structure):
+    """rf_vscale: per-request value scales applied by the fill."""
+    _fields_ = [("scale", C.c_void_p), ("group_of_row", C.c_void_p), ("n_groups", C.c_int32)]
 
 
 _lib = None
@@ -76,7 +82,7 @@ def lib():
         "rf_rope_table": (i32, [P, P, P]),
         "rf_fill_rows_workspace_bytes": (sz, [i32]),
         "rf_fill_rows": (i32, [P, P, i32, P, P, P, sz, P]),
-        "rf_fill": (i32, [P, P, i64, P, i32, P, P, PP, PP, PP, PP, PP, P, PP, PP, P, sz, P]),
+        "rf_fill": (i32, [P, P, i64, P, i32, P, P, PP, PP, PP, PP, PP, P, PP, PP, P, P, sz, P]),
         "rf_kv_project": (i32, [P, PP, i64, P, i32, P, P, PP, PP, PP, P, PP, PP, P, sz, P]),
         "rf_ridge_acc_create": (i32, [i32, i32, C.POINTER(P)]),
         "rf_ridge_acc_add": (i32, [P, P, P, i64]),
@@ -86,7 +92,10 @@ def lib():
         "rf_plan_profile": (i32, [P, i32]),
         "rf_plan_profile_read": (i32, [P, C.POINTER(Profile)]),
         "rf_last_error": (C.c_char_p, []),
-        "rf_fill_q8": (i32, [P, P, i64, P, i32, P, P, PP, PP, PP, PP, PP, PP, P, PP, PP, P, sz, P]),
+        "rf_fill_q8": (i32, [P, P, i64, P, i32, P, P, PP, PP, PP, PP, PP, PP, P, PP, PP, P, P, sz, P]),
+        "rf_value_scales_workspace_bytes": (sz, [P, i32, i32]),
+        "rf_value_scales": (i32, [P, P, i64, PP, i64, P, P, i32, i32, PP, PP, PP, PP, P, P, sz, P]),
+        "rf_value_scales_q8": (i32, [P, P, i64, PP, i64, P, P, i32, i32, PP, PP, PP, PP, PP, P, P, sz, P]),
         "rf_map_dequantize_q8": (i32, [P, P, i32, i32, P, P]),
         "rf_map_quantize_q8": (i32, [P, i32, i32, P, P]),
     }
@@ -163,6 +172,9 @@ class Plan:
     def fill_workspace_bytes(self, n_fill: int, layers_per_launch: int = 1) -> int:
         return int(lib().rf_fill_workspace_bytes(self.handle, n_fill, layers_per_launch))
 
+    def value_scales_workspace_bytes(self, n_calib: int, layers_per_launch: int = 1) -> int:
+        return int(lib().rf_value_scales_workspace_bytes(self.handle, n_calib, layers_per_launch))
+
     def kv_project_workspace_bytes(self, layers_per_launch: int = 1) -> int:
         return int(lib().rf_kv_project_workspace_bytes(self.handle, layers_per_launch))
 
@@ -192,30 +204,60 @@ def fill_rows(plan: Plan, exact_rows, fill_rows_out, n_fill_out, workspace, stre
                                               workspace.element_size(), _stream(stream)))
 
 
+def _vscale(vscale):
+    """(scale tensor, group_of_row tensor, n_groups) -> rf_vscale by reference, or None."""
+    if vscale is None:
+        return None
+    scale, group_of_row, n_groups = vscale
+    return C.byref(VScale(scale.data_ptr(), group_of_row.data_ptr(), n_groups))
+
+
 def fill(plan: Plan, x, fill_rows_t, n_fill: int, positions, slot_of_row, map_a: Sequence, map_b: Sequence,
          gamma: Sequence, w_k: Sequence, w_v: Sequence, rope, k_cache: Sequence, v_cache: Sequence,
-         workspace, stream=None, ld_x: Optional[int] = None) -> None:
+         workspace, stream=None, ld_x: Optional[int] = None, vscale=None) -> None:
     """rf_fill.  map_a/map_b are device tensors, or pinned host tensors for a
-    plan made with maps_on_host."""
+    plan made with maps_on_host.  vscale = (scale [n_late][n_groups][n_kv] fp32,
+    group_of_row [n_rows] int32, n_groups) applies a value rescale."""
     ld = x.stride(0) if ld_x is None else ld_x
     _check("rf_fill", lib().rf_fill(
         plan.handle, _ptr(x), ld, _ptr(fill_rows_t), n_fill, _ptr(positions), _ptr(slot_of_row),
         _ptr_array(map_a), _ptr_array(map_b), _ptr_array(gamma), _ptr_array(w_k), _ptr_array(w_v),
-        _ptr(rope), _ptr_array(k_cache), _ptr_array(v_cache), _ptr(workspace),
+        _ptr(rope), _ptr_array(k_cache), _ptr_array(v_cache), _vscale(vscale), _ptr(workspace),
         workspace.numel() * workspace.element_size(), _stream(stream)))
 
 
 def fill_q8(plan: Plan, x, fill_rows_t, n_fill: int, positions, slot_of_row, map_q: Sequence,
             map_scale: Sequence, map_b: Sequence, gamma: Sequence, w_k: Sequence, w_v: Sequence, rope,
-            k_cache: Sequence, v_cache: Sequence, workspace, stream=None, ld_x: Optional[int] = None) -> None:
+            k_cache: Sequence, v_cache: Sequence, workspace, stream=None, ld_x: Optional[int] = None,
+            vscale=None) -> None:
     """rf_fill_q8: the fill with int8 maps (codes + bf16 block scales) for a
     plan made with maps_q8; pinned host tensors for a plan with maps_on_host."""
     ld = x.stride(0) if ld_x is None else ld_x
     _check("rf_fill_q8", lib().rf_fill_q8(
         plan.handle, _ptr(x), ld, _ptr(fill_rows_t), n_fill, _ptr(positions), _ptr(slot_of_row),
         _ptr_array(map_q), _ptr_array(map_scale), _ptr_array(map_b), _ptr_array(gamma), _ptr_array(w_k),
-        _ptr_array(w_v), _ptr(rope), _ptr_array(k_cache), _ptr_array(v_cache), _ptr(workspace),
+        _ptr_array(w_v), _ptr(rope), _ptr_array(k_cache), _ptr_array(v_cache), _vscale(vscale), _ptr(workspace),
         workspace.numel() * workspace.element_size(), _stream(stream)))
+
+
+def value_scales(plan: Plan, x, layer_in: Sequence, calib_rows, calib_group, n_groups: int, map_a: Sequence,
+                 map_b: Sequence, gamma: Sequence, w_v: Sequence, scale_out, workspace, stream=None,
+                 ld_x: Optional[int] = None, ld_in: Optional[int] = None, map_scale: Sequence = None) -> None:
+    """rf_value_scales (bf16 maps) or rf_value_scales_q8 (map_a holds int8 codes
+    and map_scale their bf16 block scales): per request, layer and kv head,
+    the mean ratio of exact to predicted value norms over the calibration rows."""
+    ld = x.stride(0) if ld_x is None else ld_x
+    ldi = layer_in[0].stride(0) if ld_in is None else ld_in
+    n = calib_rows.numel()
+    common = (plan.handle, _ptr(x), ld, _ptr_array(layer_in), ldi, _ptr(calib_rows), _ptr(calib_group), n,
+              n_groups)
+    tail = (_ptr_array(gamma), _ptr_array(w_v), _ptr(scale_out), _ptr(workspace),
+            workspace.numel() * workspace.element_size(), _stream(stream))
+    if map_scale is None:
+        _check("rf_value_scales", lib().rf_value_scales(*common, _ptr_array(map_a), _ptr_array(map_b), *tail))
+    else:
+        _check("rf_value_scales_q8", lib().rf_value_scales_q8(*common, _ptr_array(map_a), _ptr_array(map_scale),
+                                                              _ptr_array(map_b), *tail))
 
 
 def map_dequantize_q8(q, scale, w_out, stream=None) -> None:

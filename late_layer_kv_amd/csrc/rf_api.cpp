@@ -306,24 +306,14 @@ struct MapSrc {
   const uint16_t* const* b = nullptr;      // bf16 [d_out]
 };
 
-rf_status fill_impl(rf_plan* p, const char* fn, const uint16_t* x, int64_t ld_x, const int32_t* fill_rows,
-                    int32_t n_fill, const int32_t* positions, const int32_t* slot_of_row, const MapSrc& maps,
-                    const uint16_t* const* gamma, const uint16_t* const* w_k, const uint16_t* const* w_v,
-                    const float* rope, uint16_t* const* k_cache, uint16_t* const* v_cache, void* ws,
-                    size_t ws_bytes, void* stream) {
-  const rf_shape& s = p->s;
-  const int L = s.n_late;
+rf_status check_maps(const rf_plan* p, const char* fn, const MapSrc& maps) {
+  const int L = p->s.n_late;
   const bool q8 = p->flags & RF_MAPS_Q8;
-  if (q8 != (maps.q != nullptr || maps.scale != nullptr))
-    return fail(RF_E_ARG, "%s: plan %s RF_MAPS_Q8 (int8 maps go to rf_fill_q8, bf16 maps to rf_fill)", fn,
-                q8 ? "has" : "lacks");
-  if (n_fill < 0 || n_fill > s.n_rows) return fail(RF_E_ARG, "n_fill=%d outside [0, n_rows=%d]", n_fill, s.n_rows);
-  if (!x || !aligned16(x)) return fail(RF_E_ARG, "x is null or not 16-byte aligned");
-  if (ld_x < s.d_in || ld_x % 8) return fail(RF_E_ARG, "ld_x=%lld must be >= d_in and a multiple of 8", (long long)ld_x);
-  if (n_fill > 0 && !fill_rows) return fail(RF_E_ARG, "fill_rows is null");
-  if (!positions) return fail(RF_E_ARG, "positions is null");
-  rf_status st;
   const bool host_maps = p->flags & RF_MAPS_HOST;
+  if (q8 != (maps.q != nullptr || maps.scale != nullptr))
+    return fail(RF_E_ARG, "%s: plan %s RF_MAPS_Q8 (int8 maps go to the _q8 entry points, bf16 maps to the others)",
+                fn, q8 ? "has" : "lacks");
+  rf_status st;
   if (q8) {
     if ((st = check_layer_ptrs(reinterpret_cast<const void* const*>(maps.q), L, "map_q", !host_maps)) != RF_OK) return st;
     if ((st = check_layer_ptrs(reinterpret_cast<const void* const*>(maps.scale), L, "map_scale", false)) != RF_OK)
@@ -331,12 +321,137 @@ rf_status fill_impl(rf_plan* p, const char* fn, const uint16_t* x, int64_t ld_x,
   } else if ((st = check_layer_ptrs(reinterpret_cast<const void* const*>(maps.a), L, "map_a", !host_maps)) != RF_OK) {
     return st;
   }
-  if ((st = check_layer_ptrs(reinterpret_cast<const void* const*>(maps.b), L, "map_b", !host_maps)) != RF_OK) return st;
+  return check_layer_ptrs(reinterpret_cast<const void* const*>(maps.b), L, "map_b", !host_maps);
+}
+
+// Hands the map kernel device bf16 maps, one launch group at a time.  Resident
+// bf16 maps are used as given; resident int8 maps are expanded into the image
+// `dq` first; streamed maps (RF_MAPS_HOST) go through the plan's two device
+// buffers on the side stream, one layer per group: copy l waits until the map
+// kernel of layer l-2 (same buffer) has run, and the kernels of layer l that
+// read the buffer wait for copy l.  The first copies also wait for the work
+// already on the caller's stream, which may still read the buffers.
+class MapFeeder {
+ public:
+  MapFeeder(rf_plan* p, const MapSrc& maps, uint16_t* dq, hipStream_t hs)
+      : p_(p), maps_(maps), dq_(dq), hs_(hs), q8_(p->flags & RF_MAPS_Q8), host_(p->flags & RF_MAPS_HOST) {
+    dp_.d_out = p->s.d_out;
+    dp_.d_in = p->s.d_in;
+  }
+  bool streamed() const { return host_; }
+
+  rf_status begin() {
+    if (!host_) return RF_OK;
+    hipError_t e;
+    if ((e = hipEventRecord(p_->ev_start, hs_)) != hipSuccess) return hip_fail(e, "event record");
+    if ((e = hipStreamWaitEvent(p_->side, p_->ev_start, 0)) != hipSuccess) return hip_fail(e, "stream wait");
+    return RF_OK;
+  }
+
+  // Points mp.a[0..g) and mp.b[0..g) at device bf16 maps of layers l0 .. l0+g-1.
+  rf_status load(int l0, int g, rf::MapParams& mp) {
+    const size_t elems = static_cast<size_t>(p_->s.d_out) * p_->s.d_in;
+    hipError_t e;
+    if (!host_) {
+      for (int i = 0; i < g; ++i) {
+        if (q8_) {
+          dp_.q[i] = maps_.q[l0 + i];
+          dp_.s[i] = maps_.scale[l0 + i];
+          dp_.w[i] = dq_ + i * elems;
+          mp.a[i] = dq_ + i * elems;
+        } else {
+          mp.a[i] = maps_.a[l0 + i];
+        }
+        mp.b[i] = maps_.b[l0 + i];
+      }
+      if (q8_) {
+        Timed tm(p_, RF_K_DEQUANT, hs_);
+        if ((e = rf::launch_dequant(dp_, g, hs_)) != hipSuccess) return hip_fail(e, "dequant launch");
+      }
+      return RF_OK;
+    }
+    const int l = l0, buf = l & 1;
+    char* mb = p_->mapbuf[buf];
+    if (l >= 2 && (e = hipStreamWaitEvent(p_->side, p_->ev_consumed[buf], 0)) != hipSuccess)
+      return hip_fail(e, "stream wait");
+    {
+      Timed tm(p_, RF_K_COPY, p_->side);
+      const void* msrc = q8_ ? static_cast<const void*>(maps_.q[l]) : static_cast<const void*>(maps_.a[l]);
+      e = hipMemcpyAsync(mb, msrc, p_->map_bytes, hipMemcpyHostToDevice, p_->side);
+      if (e == hipSuccess && q8_)
+        e = hipMemcpyAsync(mb + p_->scale_off, maps_.scale[l], p_->scale_bytes, hipMemcpyHostToDevice, p_->side);
+      if (e == hipSuccess)
+        e = hipMemcpyAsync(mb + p_->bias_off, maps_.b[l], static_cast<size_t>(p_->s.d_out) * 2, hipMemcpyHostToDevice,
+                           p_->side);
+      if (e != hipSuccess) return hip_fail(e, "map copy");
+    }
+    if ((e = hipEventRecord(p_->ev_copied[buf], p_->side)) != hipSuccess) return hip_fail(e, "event record");
+    if ((e = hipStreamWaitEvent(hs_, p_->ev_copied[buf], 0)) != hipSuccess) return hip_fail(e, "stream wait");
+    if (q8_) {
+      dp_.q[0] = reinterpret_cast<const int8_t*>(mb);
+      dp_.s[0] = reinterpret_cast<const uint16_t*>(mb + p_->scale_off);
+      dp_.w[0] = dq_;
+      Timed tm(p_, RF_K_DEQUANT, hs_);
+      if ((e = rf::launch_dequant(dp_, 1, hs_)) != hipSuccess) return hip_fail(e, "dequant launch");
+    }
+    mp.a[0] = q8_ ? dq_ : reinterpret_cast<const uint16_t*>(mb);
+    mp.b[0] = reinterpret_cast<const uint16_t*>(mb + p_->bias_off);
+    return RF_OK;
+  }
+
+  // Call after the map kernel of group l0 is enqueued.
+  rf_status consumed(int l0) {
+    if (!host_) return RF_OK;
+    hipError_t e = hipEventRecord(p_->ev_consumed[l0 & 1], hs_);
+    return e == hipSuccess ? RF_OK : hip_fail(e, "event record");
+  }
+
+ private:
+  rf_plan* p_;
+  const MapSrc& maps_;
+  uint16_t* dq_;
+  hipStream_t hs_;
+  bool q8_, host_;
+  rf::DequantParams dp_{};
+};
+
+// Largest layer group (<= kMaxGroup) whose workspace fits; 1 for streamed maps.
+template <class F>
+int pick_group(const rf_plan* p, size_t ws_bytes, F bytes_for) {
+  if (p->flags & RF_MAPS_HOST) return 1;
+  for (int g = max_group(p); g > 1; --g)
+    if (bytes_for(g) <= ws_bytes) return g;
+  return 1;
+}
+
+rf_status check_vscale(const rf_plan* p, const rf_vscale* vs) {
+  if (!vs) return RF_OK;
+  if (!vs->scale || !vs->group_of_row) return fail(RF_E_ARG, "vscale has a null scale or group_of_row");
+  if (vs->n_groups < 1) return fail(RF_E_ARG, "vscale n_groups=%d must be >= 1", vs->n_groups);
+  if (reinterpret_cast<uintptr_t>(vs->scale) & 3) return fail(RF_E_ARG, "vscale scale is not 4-byte aligned");
+  return RF_OK;
+}
+
+rf_status fill_impl(rf_plan* p, const char* fn, const uint16_t* x, int64_t ld_x, const int32_t* fill_rows,
+                    int32_t n_fill, const int32_t* positions, const int32_t* slot_of_row, const MapSrc& maps,
+                    const uint16_t* const* gamma, const uint16_t* const* w_k, const uint16_t* const* w_v,
+                    const float* rope, uint16_t* const* k_cache, uint16_t* const* v_cache, const rf_vscale* vscale,
+                    void* ws, size_t ws_bytes, void* stream) {
+  const rf_shape& s = p->s;
+  const int L = s.n_late;
+  rf_status st;
+  if ((st = check_maps(p, fn, maps)) != RF_OK) return st;
+  if (n_fill < 0 || n_fill > s.n_rows) return fail(RF_E_ARG, "n_fill=%d outside [0, n_rows=%d]", n_fill, s.n_rows);
+  if (!x || !aligned16(x)) return fail(RF_E_ARG, "x is null or not 16-byte aligned");
+  if (ld_x < s.d_in || ld_x % 8) return fail(RF_E_ARG, "ld_x=%lld must be >= d_in and a multiple of 8", (long long)ld_x);
+  if (n_fill > 0 && !fill_rows) return fail(RF_E_ARG, "fill_rows is null");
+  if (!positions) return fail(RF_E_ARG, "positions is null");
   if ((st = check_layer_ptrs(reinterpret_cast<const void* const*>(gamma), L, "gamma")) != RF_OK) return st;
   if ((st = check_layer_ptrs(reinterpret_cast<const void* const*>(w_k), L, "w_k")) != RF_OK) return st;
   if ((st = check_layer_ptrs(reinterpret_cast<const void* const*>(w_v), L, "w_v")) != RF_OK) return st;
   if ((st = check_layer_ptrs(reinterpret_cast<const void* const*>(k_cache), L, "k_cache")) != RF_OK) return st;
   if ((st = check_layer_ptrs(reinterpret_cast<const void* const*>(v_cache), L, "v_cache")) != RF_OK) return st;
+  if ((st = check_vscale(p, vscale)) != RF_OK) return st;
   if (rope && !aligned16(rope)) return fail(RF_E_ARG, "rope table is not 16-byte aligned");
   const size_t need1 = rf_fill_workspace_bytes(p, n_fill, 1);
   if (!ws || (reinterpret_cast<uintptr_t>(ws) % kAlign) || ws_bytes < need1)
@@ -344,13 +459,7 @@ rf_status fill_impl(rf_plan* p, const char* fn, const uint16_t* x, int64_t ld_x,
   if (n_fill == 0) return RF_OK;
 
   hipStream_t hs = static_cast<hipStream_t>(stream);
-  int G = 1;
-  if (!host_maps)
-    for (int g = max_group(p); g > 1; --g)
-      if (rf_fill_workspace_bytes(p, n_fill, g) <= ws_bytes) {
-        G = g;
-        break;
-      }
+  const int G = pick_group(p, ws_bytes, [&](int g) { return rf_fill_workspace_bytes(p, n_fill, g); });
 
   char* w0 = static_cast<char*>(ws);
   float* rope_ws = reinterpret_cast<float*>(w0);
@@ -359,7 +468,6 @@ rf_status fill_impl(rf_plan* p, const char* fn, const uint16_t* x, int64_t ld_x,
   uint16_t* ybuf = reinterpret_cast<uint16_t*>(w0 + rope_bytes(s) + kFlagBytes + prep_bytes(s, G));
   uint16_t* dq = reinterpret_cast<uint16_t*>(w0 + rope_bytes(s) + kFlagBytes + prep_bytes(s, G) +
                                              y_bytes(s, n_fill, G));
-  const size_t map_elems = static_cast<size_t>(s.d_out) * s.d_in;
 
   hipError_t e;
   if (p->flags & RF_VALIDATE)
@@ -403,110 +511,200 @@ rf_status fill_impl(rf_plan* p, const char* fn, const uint16_t* x, int64_t ld_x,
   kp.max_pos = s.max_pos;
   kp.rope = rope;
   kp.eps = s.rms_eps;
+  kp.n_kv = s.n_kv;
+  kp.n_groups = vscale ? vscale->n_groups : 0;
+  kp.group_of_row = vscale ? vscale->group_of_row : nullptr;
 
   rf::PrepParams pp{};
   pp.d = s.d_out;
   pp.w = w;
   pp.out = prep;
 
-  rf::DequantParams dp{};
-  dp.d_out = s.d_out;
-  dp.d_in = s.d_in;
-
   const size_t y_layer = static_cast<size_t>(n_fill) * s.d_out;
-  if (host_maps) {
-    // Double-buffered stream of each layer's map and b over the side stream.
-    // Copy l waits until the map kernel of layer l-2 (same buffer) has run; the
-    // kernels of layer l that read the buffer wait for copy l.  The first copies
-    // also wait for the work already on the caller's stream, which may still
-    // read the buffers.
-    const size_t b_bytes = static_cast<size_t>(s.d_out) * 2;
-    if ((e = hipEventRecord(p->ev_start, hs)) != hipSuccess) return hip_fail(e, "event record");
-    if ((e = hipStreamWaitEvent(p->side, p->ev_start, 0)) != hipSuccess) return hip_fail(e, "stream wait");
-    for (int l = 0; l < L; ++l) {
-      const int buf = l & 1;
-      char* mb = p->mapbuf[buf];
-      if (l >= 2 && (e = hipStreamWaitEvent(p->side, p->ev_consumed[buf], 0)) != hipSuccess)
-        return hip_fail(e, "stream wait");
-      {
-        Timed tm(p, RF_K_COPY, p->side);
-        const void* msrc = q8 ? static_cast<const void*>(maps.q[l]) : static_cast<const void*>(maps.a[l]);
-        e = hipMemcpyAsync(mb, msrc, p->map_bytes, hipMemcpyHostToDevice, p->side);
-        if (e == hipSuccess && q8)
-          e = hipMemcpyAsync(mb + p->scale_off, maps.scale[l], p->scale_bytes, hipMemcpyHostToDevice, p->side);
-        if (e == hipSuccess)
-          e = hipMemcpyAsync(mb + p->bias_off, maps.b[l], b_bytes, hipMemcpyHostToDevice, p->side);
-        if (e != hipSuccess) return hip_fail(e, "map copy");
-      }
-      if ((e = hipEventRecord(p->ev_copied[buf], p->side)) != hipSuccess) return hip_fail(e, "event record");
-
-      pp.gamma[0] = gamma[l];
-      pp.wk[0] = w_k[l];
-      pp.wv[0] = w_v[l];
-      {
-        Timed tm(p, RF_K_PREP, hs);
-        if ((e = rf::launch_prep(pp, 1, hs)) != hipSuccess) return hip_fail(e, "prep launch");
-      }
-      if ((e = hipStreamWaitEvent(hs, p->ev_copied[buf], 0)) != hipSuccess) return hip_fail(e, "stream wait");
-      if (q8) {
-        dp.q[0] = reinterpret_cast<const int8_t*>(mb);
-        dp.s[0] = reinterpret_cast<const uint16_t*>(mb + p->scale_off);
-        dp.w[0] = dq;
-        Timed tm(p, RF_K_DEQUANT, hs);
-        if ((e = rf::launch_dequant(dp, 1, hs)) != hipSuccess) return hip_fail(e, "dequant launch");
-      }
-      mp.a[0] = q8 ? dq : reinterpret_cast<const uint16_t*>(mb);
-      mp.b[0] = reinterpret_cast<const uint16_t*>(mb + p->bias_off);
-      {
-        Timed tm(p, RF_K_MAP, hs);
-        if ((e = rf::launch_map(mp, 1, hs)) != hipSuccess) return hip_fail(e, "map launch");
-      }
-      if ((e = hipEventRecord(p->ev_consumed[buf], hs)) != hipSuccess) return hip_fail(e, "event record");
-      kp.in[0] = ybuf;
-      kp.kc[0] = k_cache[l];
-      kp.vc[0] = v_cache[l];
-      Timed tm(p, RF_K_KV, hs);
-      if ((e = rf::launch_kv(kp, 1, hs)) != hipSuccess) return hip_fail(e, "kv launch");
-    }
-    return RF_OK;
-  }
-
+  const size_t vs_layer = vscale ? static_cast<size_t>(vscale->n_groups) * s.n_kv : 0;
+  MapFeeder feed(p, maps, dq, hs);
+  if ((st = feed.begin()) != RF_OK) return st;
   for (int l0 = 0; l0 < L; l0 += G) {
     const int g = std::min(G, L - l0);
     for (int i = 0; i < g; ++i) {
       pp.gamma[i] = gamma[l0 + i];
       pp.wk[i] = w_k[l0 + i];
       pp.wv[i] = w_v[l0 + i];
-      if (q8) {
-        dp.q[i] = maps.q[l0 + i];
-        dp.s[i] = maps.scale[l0 + i];
-        dp.w[i] = dq + i * map_elems;
-        mp.a[i] = dq + i * map_elems;
-      } else {
-        mp.a[i] = maps.a[l0 + i];
-      }
-      mp.b[i] = maps.b[l0 + i];
       kp.in[i] = ybuf + i * y_layer;
       kp.kc[i] = k_cache[l0 + i];
       kp.vc[i] = v_cache[l0 + i];
+      kp.vscale[i] = vscale ? vscale->scale + (l0 + i) * vs_layer : nullptr;
     }
     {
       Timed tm(p, RF_K_PREP, hs);
       if ((e = rf::launch_prep(pp, g, hs)) != hipSuccess) return hip_fail(e, "prep launch");
     }
-    if (q8) {
-      Timed tm(p, RF_K_DEQUANT, hs);
-      if ((e = rf::launch_dequant(dp, g, hs)) != hipSuccess) return hip_fail(e, "dequant launch");
-    }
+    if ((st = feed.load(l0, g, mp)) != RF_OK) return st;
     {
       Timed tm(p, RF_K_MAP, hs);
       if ((e = rf::launch_map(mp, g, hs)) != hipSuccess) return hip_fail(e, "map launch");
     }
+    if ((st = feed.consumed(l0)) != RF_OK) return st;
     {
       Timed tm(p, RF_K_KV, hs);
       if ((e = rf::launch_kv(kp, g, hs)) != hipSuccess) return hip_fail(e, "kv launch");
     }
   }
+  return RF_OK;
+}
+
+// Workspace of the value-scale measurement, in carve order.
+struct ScaleWs {
+  size_t prep, y, dq, v, ratio, pos, total;
+};
+ScaleWs scale_ws(const rf_plan* p, int n, int g) {
+  const rf_shape& s = p->s;
+  ScaleWs r{};
+  r.prep = prep_bytes(s, g);
+  r.y = y_bytes(s, n, g);
+  r.dq = dq_bytes(s, p->flags, g);
+  r.v = up(static_cast<size_t>(g) * n * kv_width(s) * 2);
+  r.ratio = up(static_cast<size_t>(s.n_late) * n * s.n_kv * 4);
+  r.pos = up(static_cast<size_t>(std::max(n, 1)) * 4);
+  r.total = kFlagBytes + r.prep + r.y + r.dq + 2 * r.v + r.ratio + r.pos;
+  return r;
+}
+
+rf_status value_scales_impl(rf_plan* p, const char* fn, const uint16_t* x, int64_t ld_x,
+                            const uint16_t* const* layer_in, int64_t ld_in, const int32_t* calib_rows,
+                            const int32_t* calib_group, int32_t n, int32_t n_groups, const MapSrc& maps,
+                            const uint16_t* const* gamma, const uint16_t* const* w_v, float* scale, void* ws,
+                            size_t ws_bytes, void* stream) {
+  const rf_shape& s = p->s;
+  const int L = s.n_late;
+  rf_status st;
+  if ((st = check_maps(p, fn, maps)) != RF_OK) return st;
+  if (n < 0 || n > s.n_rows) return fail(RF_E_ARG, "n_calib=%d outside [0, n_rows=%d]", n, s.n_rows);
+  if (n_groups < 1) return fail(RF_E_ARG, "n_groups=%d must be >= 1", n_groups);
+  if (!x || !aligned16(x)) return fail(RF_E_ARG, "x is null or not 16-byte aligned");
+  if (ld_x < s.d_in || ld_x % 8) return fail(RF_E_ARG, "ld_x=%lld must be >= d_in and a multiple of 8", (long long)ld_x);
+  if (ld_in < s.d_out || ld_in % 8)
+    return fail(RF_E_ARG, "ld_in=%lld must be >= d_out and a multiple of 8", (long long)ld_in);
+  if (n > 0 && (!calib_rows || !calib_group)) return fail(RF_E_ARG, "calib_rows or calib_group is null");
+  if (!scale || (reinterpret_cast<uintptr_t>(scale) & 3)) return fail(RF_E_ARG, "scale is null or misaligned");
+  if ((st = check_layer_ptrs(reinterpret_cast<const void* const*>(layer_in), L, "layer_in")) != RF_OK) return st;
+  if ((st = check_layer_ptrs(reinterpret_cast<const void* const*>(gamma), L, "gamma")) != RF_OK) return st;
+  if ((st = check_layer_ptrs(reinterpret_cast<const void* const*>(w_v), L, "w_v")) != RF_OK) return st;
+  const size_t need1 = rf_value_scales_workspace_bytes(p, n, 1);
+  if (!ws || (reinterpret_cast<uintptr_t>(ws) % kAlign) || ws_bytes < need1)
+    return fail(RF_E_WORKSPACE, "workspace of %zu bytes given, %zu needed (256-byte aligned)", ws_bytes, need1);
+
+  hipStream_t hs = static_cast<hipStream_t>(stream);
+  const int G = pick_group(p, ws_bytes, [&](int g) { return rf_value_scales_workspace_bytes(p, n, g); });
+  const ScaleWs sw = scale_ws(p, n, G);
+  char* c = static_cast<char*>(ws) + kFlagBytes;
+  uint16_t* prep = reinterpret_cast<uint16_t*>(c);
+  uint16_t* ybuf = reinterpret_cast<uint16_t*>(c += sw.prep);
+  uint16_t* dq = reinterpret_cast<uint16_t*>(c += sw.y);
+  uint16_t* ve = reinterpret_cast<uint16_t*>(c += sw.dq);
+  uint16_t* vp = reinterpret_cast<uint16_t*>(c += sw.v);
+  float* ratio = reinterpret_cast<float*>(c += sw.v);
+  int32_t* zero_pos = reinterpret_cast<int32_t*>(c += sw.ratio);
+
+  hipError_t e;
+  const int w = kv_width(s);
+  if (n > 0) {
+    rf::MapParams mp{};
+    mp.x = x;
+    mp.ld_x = ld_x;
+    mp.rows = calib_rows;
+    mp.n_rows = s.n_rows;
+    mp.M = n;
+    mp.K = s.d_in;
+    mp.N = s.d_out;
+    mp.tiles_m = (n + rf::kTileM - 1) / rf::kTileM;
+    mp.tiles_n = s.d_out / rf::kTileN;
+    mp.y = ybuf;
+
+    // Value half only, row m of the call stored densely at row m (slot = row,
+    // rows numbered 0..n-1 for this launch; positions are not used by values).
+    if ((e = rf::launch_zero_i32(zero_pos, n, hs)) != hipSuccess) return hip_fail(e, "clear launch");
+    rf::KvParams kp{};
+    kp.in_rows = nullptr;
+    kp.n_in_rows = n;
+    kp.out_rows = nullptr;
+    kp.M = n;
+    kp.K = s.d_out;
+    kp.w = w;
+    kp.head_dim = s.head_dim;
+    kp.tiles_m = mp.tiles_m;
+    kp.tiles_n = (2 * w - w / rf::kTileN * rf::kTileN) / rf::kTileN;
+    kp.wkv = prep;
+    kp.positions = zero_pos;
+    kp.n_rows = n;
+    kp.n_slots = n;
+    kp.max_pos = s.max_pos;
+    kp.eps = s.rms_eps;
+    kp.n_kv = s.n_kv;
+    kp.v_only = 1;
+
+    rf::PrepParams pp{};
+    pp.d = s.d_out;
+    pp.w = w;
+    pp.out = prep;
+
+    rf::RatioParams rp{};
+    rp.n = n;
+    rp.n_kv = s.n_kv;
+    rp.head_dim = s.head_dim;
+
+    const size_t y_layer = static_cast<size_t>(n) * s.d_out;
+    const size_t v_layer = static_cast<size_t>(n) * w;
+    MapFeeder feed(p, maps, dq, hs);
+    if ((st = feed.begin()) != RF_OK) return st;
+    for (int l0 = 0; l0 < L; l0 += G) {
+      const int g = std::min(G, L - l0);
+      for (int i = 0; i < g; ++i) {
+        pp.gamma[i] = gamma[l0 + i];
+        pp.wk[i] = w_v[l0 + i];  // the key half of the prepared weights is not used
+        pp.wv[i] = w_v[l0 + i];
+        rp.ve[i] = ve + i * v_layer;
+        rp.vp[i] = vp + i * v_layer;
+        rp.ratio[i] = ratio + static_cast<size_t>(l0 + i) * n * s.n_kv;
+      }
+      {
+        Timed tm(p, RF_K_PREP, hs);
+        if ((e = rf::launch_prep(pp, g, hs)) != hipSuccess) return hip_fail(e, "prep launch");
+      }
+      if ((st = feed.load(l0, g, mp)) != RF_OK) return st;
+      {
+        Timed tm(p, RF_K_MAP, hs);
+        if ((e = rf::launch_map(mp, g, hs)) != hipSuccess) return hip_fail(e, "map launch");
+      }
+      if ((st = feed.consumed(l0)) != RF_OK) return st;
+      // predicted values from the map's output, exact values from the true inputs
+      kp.ld_in = s.d_out;
+      for (int i = 0; i < g; ++i) {
+        kp.in[i] = ybuf + i * y_layer;
+        kp.vc[i] = vp + i * v_layer;
+      }
+      {
+        Timed tm(p, RF_K_KV, hs);
+        if ((e = rf::launch_kv(kp, g, hs)) != hipSuccess) return hip_fail(e, "kv launch");
+      }
+      kp.ld_in = ld_in;
+      for (int i = 0; i < g; ++i) {
+        kp.in[i] = layer_in[l0 + i];
+        kp.vc[i] = ve + i * v_layer;
+      }
+      {
+        Timed tm(p, RF_K_KV, hs);
+        if ((e = rf::launch_kv(kp, g, hs)) != hipSuccess) return hip_fail(e, "kv launch");
+      }
+      {
+        Timed tm(p, RF_K_SCALE, hs);
+        if ((e = rf::launch_head_ratio(rp, g, hs)) != hipSuccess) return hip_fail(e, "ratio launch");
+      }
+    }
+  }
+  Timed tm(p, RF_K_SCALE, hs);
+  if ((e = rf::launch_scale_mean(ratio, calib_group, n, s.n_kv, n_groups, L, scale, hs)) != hipSuccess)
+    return hip_fail(e, "scale launch");
   return RF_OK;
 }
 
@@ -518,20 +716,21 @@ rf_status rf_fill(rf_plan* p, const uint16_t* x, int64_t ld_x, const int32_t* fi
                   const int32_t* positions, const int32_t* slot_of_row, const uint16_t* const* map_a,
                   const uint16_t* const* map_b, const uint16_t* const* gamma, const uint16_t* const* w_k,
                   const uint16_t* const* w_v, const float* rope, uint16_t* const* k_cache,
-                  uint16_t* const* v_cache, void* ws, size_t ws_bytes, void* stream) {
+                  uint16_t* const* v_cache, const rf_vscale* vscale, void* ws, size_t ws_bytes, void* stream) {
   if (!p) return fail(RF_E_ARG, "plan is null");
   MapSrc m;
   m.a = map_a;
   m.b = map_b;
   return fill_impl(p, "rf_fill", x, ld_x, fill_rows, n_fill, positions, slot_of_row, m, gamma, w_k, w_v, rope,
-                   k_cache, v_cache, ws, ws_bytes, stream);
+                   k_cache, v_cache, vscale, ws, ws_bytes, stream);
 }
 
 rf_status rf_fill_q8(rf_plan* p, const uint16_t* x, int64_t ld_x, const int32_t* fill_rows, int32_t n_fill,
                      const int32_t* positions, const int32_t* slot_of_row, const int8_t* const* map_q,
                      const uint16_t* const* map_scale, const uint16_t* const* map_b, const uint16_t* const* gamma,
                      const uint16_t* const* w_k, const uint16_t* const* w_v, const float* rope,
-                     uint16_t* const* k_cache, uint16_t* const* v_cache, void* ws, size_t ws_bytes, void* stream) {
+                     uint16_t* const* k_cache, uint16_t* const* v_cache, const rf_vscale* vscale, void* ws,
+                     size_t ws_bytes, void* stream) {
   if (!p) return fail(RF_E_ARG, "plan is null");
   if (!map_q || !map_scale) return fail(RF_E_ARG, "map_q or map_scale array is null");
   MapSrc m;
@@ -539,7 +738,42 @@ rf_status rf_fill_q8(rf_plan* p, const uint16_t* x, int64_t ld_x, const int32_t*
   m.scale = map_scale;
   m.b = map_b;
   return fill_impl(p, "rf_fill_q8", x, ld_x, fill_rows, n_fill, positions, slot_of_row, m, gamma, w_k, w_v, rope,
-                   k_cache, v_cache, ws, ws_bytes, stream);
+                   k_cache, v_cache, vscale, ws, ws_bytes, stream);
+}
+
+size_t rf_value_scales_workspace_bytes(const rf_plan* p, int32_t n_calib, int32_t g) {
+  if (!p || n_calib < 0 || g < 1 || g > p->s.n_late) return 0;
+  g = std::min(g, rf::kMaxGroup);
+  if (p->flags & RF_MAPS_HOST) g = 1;
+  return scale_ws(p, n_calib, g).total;
+}
+
+rf_status rf_value_scales(rf_plan* p, const uint16_t* x, int64_t ld_x, const uint16_t* const* layer_in,
+                          int64_t ld_in, const int32_t* calib_rows, const int32_t* calib_group, int32_t n_calib,
+                          int32_t n_groups, const uint16_t* const* map_a, const uint16_t* const* map_b,
+                          const uint16_t* const* gamma, const uint16_t* const* w_v, float* scale, void* ws,
+                          size_t ws_bytes, void* stream) {
+  if (!p) return fail(RF_E_ARG, "plan is null");
+  MapSrc m;
+  m.a = map_a;
+  m.b = map_b;
+  return value_scales_impl(p, "rf_value_scales", x, ld_x, layer_in, ld_in, calib_rows, calib_group, n_calib,
+                           n_groups, m, gamma, w_v, scale, ws, ws_bytes, stream);
+}
+
+rf_status rf_value_scales_q8(rf_plan* p, const uint16_t* x, int64_t ld_x, const uint16_t* const* layer_in,
+                             int64_t ld_in, const int32_t* calib_rows, const int32_t* calib_group, int32_t n_calib,
+                             int32_t n_groups, const int8_t* const* map_q, const uint16_t* const* map_scale,
+                             const uint16_t* const* map_b, const uint16_t* const* gamma,
+                             const uint16_t* const* w_v, float* scale, void* ws, size_t ws_bytes, void* stream) {
+  if (!p) return fail(RF_E_ARG, "plan is null");
+  if (!map_q || !map_scale) return fail(RF_E_ARG, "map_q or map_scale array is null");
+  MapSrc m;
+  m.q = map_q;
+  m.scale = map_scale;
+  m.b = map_b;
+  return value_scales_impl(p, "rf_value_scales_q8", x, ld_x, layer_in, ld_in, calib_rows, calib_group, n_calib,
+                           n_groups, m, gamma, w_v, scale, ws, ws_bytes, stream);
 }
 
 rf_status rf_map_dequantize_q8(const int8_t* q, const uint16_t* scale, int32_t d_out, int32_t d_in, uint16_t* w,

@@ -50,9 +50,20 @@ struct KvParams {
   int32_t n_rows, n_slots, max_pos;
   const float* rope;        // [max_pos][head_dim/2][2]
   float eps;
+  // Value rescale (when group_of_row is set; then every vscale[g] of the launch
+  // must be set): value head h of row r is multiplied by
+  // vscale_g[group_of_row[r] * n_kv + h] before rounding.  Rows whose group is
+  // outside [0, n_groups) are skipped like bad slots.
+  const int32_t* group_of_row;  // [n_rows] or null
+  int32_t n_groups, n_kv;
+  // v_only: tiles start at the 256-feature tile holding feature w (tiles_n =
+  // (2w - that offset) / 256); only value features are stored, keys are
+  // neither rotated nor written (kc may be null).
+  int32_t v_only;
   const uint16_t* in[kMaxGroup];
   uint16_t* kc[kMaxGroup];  // [n_slots][w]
   uint16_t* vc[kMaxGroup];
+  const float* vscale[kMaxGroup];  // [n_groups][n_kv] per layer, or null
 };
 
 // Prepared projection weights: out_g[f][k] = bf16(W[f][k] * gamma_g[k]),
@@ -77,6 +88,22 @@ struct DequantParams {
 
 hipError_t launch_map(const MapParams& p, int n_layers, hipStream_t s);
 hipError_t launch_dequant(const DequantParams& p, int n_layers, hipStream_t s);
+
+// Value-rescale measurement: per layer, ratio[m][h] = ||ve[m][h]|| / ||vp[m][h]|| over the
+// head's hd values (-1 when the predicted norm is zero), then per (layer, group, head)
+// the mean of the non-negative ratios of the rows of that group, in row order (1 if none).
+struct RatioParams {
+  int32_t n, n_kv, head_dim;
+  const uint16_t* ve[kMaxGroup];  // [n][n_kv * head_dim]
+  const uint16_t* vp[kMaxGroup];
+  float* ratio[kMaxGroup];        // [n][n_kv]
+};
+hipError_t launch_head_ratio(const RatioParams& p, int n_layers, hipStream_t s);
+// p[0..n) = 0 (a fill kernel: no memset node if the caller captures the stream)
+hipError_t launch_zero_i32(int32_t* p, int n, hipStream_t s);
+// ratio [n_late][n][n_kv] -> scale [n_late][n_groups][n_kv]
+hipError_t launch_scale_mean(const float* ratio, const int32_t* group, int n, int n_kv, int n_groups,
+                             int n_late, float* scale, hipStream_t s);
 hipError_t launch_kv(const KvParams& p, int n_layers, hipStream_t s);
 hipError_t launch_prep(const PrepParams& p, int n_layers, hipStream_t s);
 hipError_t launch_rope_table(float* table, int max_pos, int head_dim, double theta, hipStream_t s);

@@ -359,13 +359,15 @@ __global__ void __launch_bounds__(kThreads) map_gemm_kernel(const MapParams p) {
   }
 }
 
-template <int HD>
+// VSCALE: the value rescale is applied (a separate instantiation, so the plain
+// fill's epilogue keeps its register budget).
+template <int HD, bool VSCALE>
 __global__ void __launch_bounds__(kThreads) kv_gemm_kernel(const KvParams p) {
   __shared__ __attribute__((aligned(1024))) char smem[kLdsBytes];
   int* const slot_of = reinterpret_cast<int*>(smem + kSlotOffset);
   const int t = xcd_remap(blockIdx.x, gridDim.x);
   const TileCoord c = tile_coord<4>(t, p.tiles_m, p.tiles_n);
-  const int m0 = c.tm * kTileM, n0 = c.tn * kTileN;
+  const int m0 = c.tm * kTileM, n0 = c.tn * kTileN + (p.v_only ? p.w / kTileN * kTileN : 0);
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
 
@@ -392,32 +394,47 @@ __global__ void __launch_bounds__(kThreads) kv_gemm_kernel(const KvParams p) {
 
   const int wn = wave & 1, wm = wave >> 1, r31 = lane & 31, hsel = lane >> 5;
   const float inv_k = 1.0f / static_cast<float>(p.K);
-  float rs[4];
+  const int fw = n0 + wn * 128;  // first feature of this wave; a whole wave is key or value
+  // (with v_only, a tile may start inside the keys when w is not a multiple of
+  // 256; those key waves are neither rotated nor stored)
+  const bool is_key = fw < p.w && !p.v_only;
+  // Value waves of a rescaled fill: the request's value scale for the wave's
+  // first head (and, for heads of 64, the second head, blocks 2-3) is folded
+  // into the norm's per-row factor; without a rescale the factor is exactly
+  // the norm's scale.
+  const float* const vsw = (VSCALE && !is_key) ? p.vscale[c.g] + (fw - p.w) / HD : nullptr;
+  float rs[4], rs2[4];
   int pos[4], slot_r[4];
 #pragma unroll
   for (int mb = 0; mb < 4; ++mb) {
     const float tot = ss[mb] + __shfl_xor(ss[mb], 32);
     rs[mb] = rsqrtf(tot * inv_k + p.eps);
+    rs2[mb] = rs[mb];
     const int lr = wm * 128 + mb * 32 + r31;
     const int m = m0 + lr;
-    int ps = 0, slot = -1;
+    int ps = 0, slot = -1, grp = 0;
     if (m < p.M) {
       const int r = p.out_rows ? p.out_rows[m] : m;
       if (r >= 0 && r < p.n_rows) {
         ps = p.positions[r];
         slot = p.slots ? p.slots[r] : r;
-        if (ps < 0 || ps >= p.max_pos || slot < 0 || slot >= p.n_slots) {
+        if (VSCALE) grp = p.group_of_row[r];
+        if (ps < 0 || ps >= p.max_pos || slot < 0 || slot >= p.n_slots || (VSCALE && (grp < 0 || grp >= p.n_groups))) {
           slot = -1;
           ps = 0;
+          grp = 0;
         }
       }
+    }
+    if (VSCALE && vsw) {
+      const float* sg = vsw + grp * p.n_kv;
+      if (HD == 64) rs2[mb] = rs[mb] * sg[1];
+      rs[mb] = rs[mb] * sg[0];
     }
     pos[mb] = ps;
     slot_r[mb] = slot;
   }
 
-  const int fw = n0 + wn * 128;  // first feature of this wave; a whole wave is key or value
-  const bool is_key = fw < p.w;
   if (is_key) {
     // RoPE, rotate-half: feature j < hd/2 of a head pairs with j + hd/2.  A
     // wave spans 128 features = one head of 128 or two heads of 64, so the
@@ -455,7 +472,7 @@ __global__ void __launch_bounds__(kThreads) kv_gemm_kernel(const KvParams p) {
 #pragma unroll
       for (int mb = 0; mb < 4; ++mb)
 #pragma unroll
-        for (int v = 0; v < 16; ++v) acc[nb][mb][v] *= rs[mb];
+        for (int v = 0; v < 16; ++v) acc[nb][mb][v] *= (HD == 64 && nb >= 2) ? rs2[mb] : rs[mb];
   }
 
   __syncthreads();  // every wave is done reading the operand stages
@@ -482,12 +499,13 @@ __global__ void __launch_bounds__(kThreads) kv_gemm_kernel(const KvParams p) {
   __syncthreads();
   const int chunk = threadIdx.x & 31;
   const int f = n0 + chunk * 8;
+  const bool store = !(p.v_only && f < p.w);
   uint16_t* dst_base = (f < p.w) ? p.kc[c.g] + f : p.vc[c.g] + (f - p.w);
 #pragma unroll 4
   for (int it = 0; it < 32; ++it) {
     const int row = it * 8 + (threadIdx.x >> 5);
     const int slot = slot_of[row];
-    if (slot >= 0) {
+    if (slot >= 0 && store) {
       const uint4 v = *reinterpret_cast<const uint4*>(smem + stage_off(row, chunk));
       *reinterpret_cast<uint4*>(dst_base + static_cast<size_t>(slot) * p.w) = v;
     }
@@ -596,10 +614,18 @@ hipError_t launch_map(const MapParams& p, int n_layers, hipStream_t s) {
 
 hipError_t launch_kv(const KvParams& p, int n_layers, hipStream_t s) {
   const int grid = n_layers * p.tiles_m * p.tiles_n;
-  if (p.head_dim == 128)
-    hipLaunchKernelGGL(kv_gemm_kernel<128>, dim3(grid), dim3(kThreads), 0, s, p);
-  else
-    hipLaunchKernelGGL(kv_gemm_kernel<64>, dim3(grid), dim3(kThreads), 0, s, p);
+  const bool vscale = p.group_of_row != nullptr;
+  if (p.head_dim == 128) {
+    if (vscale)
+      hipLaunchKernelGGL((kv_gemm_kernel<128, true>), dim3(grid), dim3(kThreads), 0, s, p);
+    else
+      hipLaunchKernelGGL((kv_gemm_kernel<128, false>), dim3(grid), dim3(kThreads), 0, s, p);
+  } else {
+    if (vscale)
+      hipLaunchKernelGGL((kv_gemm_kernel<64, true>), dim3(grid), dim3(kThreads), 0, s, p);
+    else
+      hipLaunchKernelGGL((kv_gemm_kernel<64, false>), dim3(grid), dim3(kThreads), 0, s, p);
+  }
   return hipGetLastError();
 }
 

@@ -78,17 +78,17 @@ def gpu_fill_rows(plan, di: DeviceInputs, exact: torch.Tensor = None):
 
 
 def gpu_fill(plan, di: DeviceInputs, rows: torch.Tensor, n_fill: int, caches=None, layers_per_launch=None,
-             map_a=None, map_b=None, rope=None, slots=None):
+             map_a=None, map_b=None, rope=None, slots=None, vscale=None):
     s = di.w.spec
     kc, vc = di.caches() if caches is None else caches
     g = s.n_late if layers_per_launch is None else layers_per_launch
     ws = torch.empty(max(plan.fill_workspace_bytes(n_fill, g), 256), dtype=torch.uint8, device=di.device)
     if di.q8 and map_a is None:
         B.fill_q8(plan, di.x, rows, n_fill, di.positions, slots, di.map_q, di.map_scale,
-                  di.map_b if map_b is None else map_b, di.gamma, di.w_k, di.w_v, rope, kc, vc, ws)
+                  di.map_b if map_b is None else map_b, di.gamma, di.w_k, di.w_v, rope, kc, vc, ws, vscale=vscale)
     else:
         B.fill(plan, di.x, rows, n_fill, di.positions, slots, di.map_a if map_a is None else map_a,
-               di.map_b if map_b is None else map_b, di.gamma, di.w_k, di.w_v, rope, kc, vc, ws)
+               di.map_b if map_b is None else map_b, di.gamma, di.w_k, di.w_v, rope, kc, vc, ws, vscale=vscale)
     torch.cuda.synchronize()
     return kc, vc
 

@@ -66,9 +66,10 @@ def test_fill_argument_errors_before_any_device_work():
     null_arr = (C.c_void_p * nl)(*([0x1000] * (nl - 1) + [0]))
     ws = 1 << 40
 
-    def call(x=fake, ld=256, rows=fake, n=10, pos=fake, maps=arr, gam=arr, ws_ptr=C.c_void_p(0x10000), ws_b=ws):
+    def call(x=fake, ld=256, rows=fake, n=10, pos=fake, maps=arr, gam=arr, ws_ptr=C.c_void_p(0x10000), ws_b=ws,
+             vs=None):
         return L.rf_fill(p.handle, x, ld, rows, n, pos, None, maps, arr, gam, arr, arr, None, arr, arr,
-                         ws_ptr, ws_b, None)
+                         vs, ws_ptr, ws_b, None)
     assert call(n=-1) == -1
     assert call(n=513) == -1
     assert call(x=None) == -1
@@ -82,6 +83,10 @@ def test_fill_argument_errors_before_any_device_work():
     assert call(ws_ptr=C.c_void_p(0x10010)) == -4  # workspace misaligned
     assert call(ws_b=16) == -4
     assert "workspace" in B.last_error()
+    assert call(vs=C.byref(B.VScale(None, 0x1000, 1))) == -1   # null scale
+    assert call(vs=C.byref(B.VScale(0x1000, None, 1))) == -1   # null groups
+    assert call(vs=C.byref(B.VScale(0x1000, 0x1000, 0))) == -1  # no groups
+    assert call(vs=C.byref(B.VScale(0x1002, 0x1000, 1))) == -1  # misaligned scale
     p.close()
 
 
@@ -184,16 +189,16 @@ def test_q8_flag_must_match_the_call():
     pb = B.Plan(**_shape())
     # bf16 entry point on an int8 plan, and the reverse
     assert L.rf_fill(p8.handle, fake, 256, fake, 10, fake, None, arr, arr, arr, arr, arr, None, arr, arr,
-                     ws, ws_b, None) == -1
+                     None, ws, ws_b, None) == -1
     assert "RF_MAPS_Q8" in B.last_error()
     assert L.rf_fill_q8(pb.handle, fake, 256, fake, 10, fake, None, arr, arr, arr, arr, arr, arr, None, arr,
-                        arr, ws, ws_b, None) == -1
+                        arr, None, ws, ws_b, None) == -1
     null_arr = (C.c_void_p * nl)(*([0x1000] * (nl - 1) + [0]))
     mis_arr = (C.c_void_p * nl)(*([0x1000] * (nl - 1) + [0x1004]))
 
     def call8(q=arr, s=arr, b=arr, ws_b=ws_b):
         return L.rf_fill_q8(p8.handle, fake, 256, fake, 10, fake, None, q, s, b, arr, arr, arr, None, arr, arr,
-                            ws, ws_b, None)
+                            None, ws, ws_b, None)
     assert call8(q=None) == -1
     assert call8(s=None) == -1
     assert call8(q=null_arr) == -1
@@ -258,3 +263,40 @@ def test_host_quantizer_errors():
     with pytest.raises(B.RfError) as e:
         B.map_quantize_q8(a)
     assert e.value.status == -1
+
+
+# ---- value rescale: host checks
+
+
+def test_value_scales_argument_errors_and_workspace():
+    p = B.Plan(**_shape())
+    L = B.lib()
+    nl = 4
+    f = C.c_void_p(0x1000)
+    arr = (C.c_void_p * nl)(*([0x1000] * nl))
+    ws, ws_b = C.c_void_p(0x10000), 1 << 40
+
+    def call(n=16, groups=2, x=f, ld_in=256, rows=f, grp=f, scale=f, lay=arr, ws_b=ws_b):
+        return L.rf_value_scales(p.handle, x, 256, lay, ld_in, rows, grp, n, groups, arr, arr, arr, arr, scale,
+                                 ws, ws_b, None)
+    assert call(n=-1) == -1
+    assert call(n=513) == -1
+    assert call(groups=0) == -1
+    assert call(x=None) == -1
+    assert call(ld_in=100) == -1
+    assert call(rows=None) == -1
+    assert call(grp=None) == -1
+    assert call(scale=None) == -1
+    assert call(scale=C.c_void_p(0x1002)) == -1
+    assert call(lay=None) == -1
+    assert call(ws_b=16) == -4
+    # int8 entry point on a bf16 plan
+    assert L.rf_value_scales_q8(p.handle, f, 256, arr, 256, f, f, 16, 2, arr, arr, arr, arr, arr, f, ws, ws_b,
+                                None) == -1
+    # workspace: flag + prepared weights + Y + two value buffers + ratios + zero positions
+    n, w, d = 40, 128, 256
+    up = lambda v: (v + 255) // 256 * 256
+    want = 256 + 2 * w * d * 2 + up(n * d * 2) + 2 * up(n * w * 2) + up(4 * n * 2 * 4) + up(n * 4)
+    assert p.value_scales_workspace_bytes(n, 1) == want
+    assert p.value_scales_workspace_bytes(n, 5) == 0
+    p.close()
