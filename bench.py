@@ -159,6 +159,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="27b_120k", choices=workloads.CONFIG_ORDER)
     ap.add_argument("--layers-per-launch", type=int, default=None)
+    ap.add_argument("--value-rescale", type=int, default=0, metavar="C",
+                    help="include the value rescale measured on the first C tail rows of each prompt")
     ap.add_argument("--maps", default="bf16", choices=["bf16", "q8"],
                     help="map storage: bf16, or int8 codes with one bf16 scale per 128 weights of each row")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -219,6 +221,16 @@ def main():
     plan = B.Plan.for_spec(s)
     g = args.layers_per_launch or GROUP[name]
     ws = torch.empty(plan.fill_workspace_bytes(n_fill, g), dtype=torch.uint8, device=dev)
+    vscale = None
+    if args.value_rescale:
+        c_rows, c_grp = workloads.calibration_row_list(s, args.value_rescale)
+        truth = [t16(t, dev) for t in workloads.make_layer_truth(s, len(c_rows), outliers=w.outlier_channels)]
+        c_rows_d = torch.from_numpy(c_rows).to(dev)
+        c_grp_d = torch.from_numpy(c_grp).to(dev)
+        n_groups = len(s.prompt_lens)
+        scales = torch.empty((s.n_late, n_groups, s.n_kv), dtype=torch.float32, device=dev)
+        ws_scale = torch.empty(plan.value_scales_workspace_bytes(len(c_rows), g), dtype=torch.uint8, device=dev)
+        vscale = (scales, torch.from_numpy(workloads.prompt_of_row(s)).to(dev), n_groups)
     fill_rows = torch.empty(s.n_rows, dtype=torch.int32, device=dev)
     n_fill_dev = torch.empty(1, dtype=torch.int32, device=dev)
     rows_ws = torch.empty(B.fill_rows_workspace_bytes(s.n_rows), dtype=torch.uint8, device=dev)
@@ -226,11 +238,19 @@ def main():
 
     def step():
         B.fill_rows(plan, exact, fill_rows, n_fill_dev, rows_ws)
+        if vscale is not None:
+            if q8:
+                B.value_scales(plan, x, truth, c_rows_d, c_grp_d, n_groups, map_q, map_b, gamma, w_v, scales,
+                               ws_scale, map_scale=map_s)
+            else:
+                B.value_scales(plan, x, truth, c_rows_d, c_grp_d, n_groups, map_a, map_b, gamma, w_v, scales,
+                               ws_scale)
         if q8:
             B.fill_q8(plan, x, fill_rows, n_fill, positions, None, map_q, map_s, map_b, gamma, w_k, w_v, None,
-                      kc, vc, ws)
+                      kc, vc, ws, vscale=vscale)
         else:
-            B.fill(plan, x, fill_rows, n_fill, positions, None, map_a, map_b, gamma, w_k, w_v, None, kc, vc, ws)
+            B.fill(plan, x, fill_rows, n_fill, positions, None, map_a, map_b, gamma, w_k, w_v, None, kc, vc, ws,
+                   vscale=vscale)
 
     log(f"[bench] {name}: n_fill={n_fill}, {s.n_late} late layers, {g} per launch; warmup {args.warmup}")
     for _ in range(args.warmup):
@@ -292,6 +312,7 @@ def main():
                    "kv_heads": s.n_kv, "head_dim": s.head_dim, "rows": s.n_rows, "fill_rows": n_fill,
                    "prompts": list(s.prompt_lens), "maps": "pinned host, streamed" if host_maps else "HBM",
                    "map_format": "int8 + bf16 scale per 128 weights of a row" if q8 else "bf16",
+                   "value_rescale_rows": args.value_rescale or None,
                    "layers_per_launch": 1 if host_maps else g},
         "tflops": step_flops / (ms * 1e-3) / 1e12,
         "frac_of_bf16_peak": step_flops / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS,

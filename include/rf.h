@@ -307,7 +307,8 @@ enum {
   RF_K_ROWS = 4,      /* fill-row compaction                         */
   RF_K_COPY = 5,      /* host -> device map copy (RF_MAPS_HOST)      */
   RF_K_DEQUANT = 6,   /* int8 map -> bf16 image (RF_MAPS_Q8)         */
-  RF_K_SCALE = 7,     /* value-rescale ratios and means              */
+  RF_K_SCALE = 7,     /* every launch of rf_value_scales(_q8) except
+                         the int8 expansion (kind RF_K_DEQUANT)      */
   RF_K_COUNT = 8
 };
 typedef struct rf_profile {

@@ -668,12 +668,12 @@ rf_status value_scales_impl(rf_plan* p, const char* fn, const uint16_t* x, int64
         rp.ratio[i] = ratio + static_cast<size_t>(l0 + i) * n * s.n_kv;
       }
       {
-        Timed tm(p, RF_K_PREP, hs);
+        Timed tm(p, RF_K_SCALE, hs);
         if ((e = rf::launch_prep(pp, g, hs)) != hipSuccess) return hip_fail(e, "prep launch");
       }
       if ((st = feed.load(l0, g, mp)) != RF_OK) return st;
       {
-        Timed tm(p, RF_K_MAP, hs);
+        Timed tm(p, RF_K_SCALE, hs);
         if ((e = rf::launch_map(mp, g, hs)) != hipSuccess) return hip_fail(e, "map launch");
       }
       if ((st = feed.consumed(l0)) != RF_OK) return st;
@@ -684,7 +684,7 @@ rf_status value_scales_impl(rf_plan* p, const char* fn, const uint16_t* x, int64
         kp.vc[i] = vp + i * v_layer;
       }
       {
-        Timed tm(p, RF_K_KV, hs);
+        Timed tm(p, RF_K_SCALE, hs);
         if ((e = rf::launch_kv(kp, g, hs)) != hipSuccess) return hip_fail(e, "kv launch");
       }
       kp.ld_in = ld_in;
@@ -693,7 +693,7 @@ rf_status value_scales_impl(rf_plan* p, const char* fn, const uint16_t* x, int64
         kp.vc[i] = ve + i * v_layer;
       }
       {
-        Timed tm(p, RF_K_KV, hs);
+        Timed tm(p, RF_K_SCALE, hs);
         if ((e = rf::launch_kv(kp, g, hs)) != hipSuccess) return hip_fail(e, "kv launch");
       }
       {
