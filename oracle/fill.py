@@ -14,7 +14,10 @@ where they are taken:
 * projections are stored [out][in] and applied as h W^T;
 * "rotary embedding as usual" is the rotate-half form: within every head,
   dimension j < hd/2 is paired with j + hd/2 and the pair is turned by the
-  angle pos * theta^(-2j/hd), with no frequency scaling.
+  angle pos * theta^(-2j/hd), with no frequency scaling;
+* QK-norm (layers that normalise their keys) is an RMSNorm over each key head
+  with a per-dimension gain shared by the heads and the layer's eps, applied
+  after the key projection and before the rotation.
 """
 from __future__ import annotations
 
@@ -84,25 +87,49 @@ def rope(k: np.ndarray, positions: np.ndarray, theta: float, head_dim: int) -> n
     return out.reshape(n, width)
 
 
+def qk_norm(k: np.ndarray, k_gamma: np.ndarray, eps: float, head_dim: int) -> np.ndarray:
+    """QK-norm on keys (section 6.6 and section 7: the Qwen models normalise
+    each query and key before attention): every head of every row is scaled to
+    unit RMS, RMSNorm over its head_dim values with eps inside the root, then
+    multiplied by the per-dimension gain k_gamma [head_dim] shared by the heads.
+
+    k: [n][n_heads * head_dim].
+    """
+    n, width = k.shape
+    kh = k.reshape(n, width // head_dim, head_dim)
+    ms = np.mean(kh * kh, axis=2, keepdims=True)
+    return (kh / np.sqrt(ms + eps) * k_gamma).reshape(n, width)
+
+
 def layer_kv(h_in: np.ndarray, gamma: np.ndarray, w_k: np.ndarray, w_v: np.ndarray,
-             positions: np.ndarray, theta: float, head_dim: int, eps: float
-             ) -> Tuple[np.ndarray, np.ndarray]:
+             positions: np.ndarray, theta: float, head_dim: int, eps: float,
+             k_gamma: Optional[np.ndarray] = None) -> Tuple[np.ndarray, np.ndarray]:
     """What a late attention layer writes to its cache from an input row.
 
     Section 2.1: from its input a late layer computes only the keys and values
     that later tokens read; section 2.2: the input goes through the layer's own
     normalization and projections and the keys get their rotary embedding.
+    With ``k_gamma`` the layer normalises its keys (QK-norm) before the
+    rotation, as the Qwen layers do.
     """
     h = rms_norm(h_in, gamma, eps)
-    k = rope(project(h, w_k), positions, theta, head_dim)
+    k = project(h, w_k)
+    if k_gamma is not None:
+        k = qk_norm(k, k_gamma, eps, head_dim)
+    k = rope(k, positions, theta, head_dim)
     v = project(h, w_v)
     return k, v
 
 
-def fill_layer(x_s, a, b, gamma, w_k, w_v, positions, theta, head_dim, eps):
+def fill_layer(x_s, a, b, gamma, w_k, w_v, positions, theta, head_dim, eps, k_gamma=None):
     """One late layer's filled K/V: the map's prediction through layer_kv."""
     return layer_kv(predicted_input(x_s, a, b), gamma, w_k, w_v, positions,
-                    theta, head_dim, eps)
+                    theta, head_dim, eps, k_gamma)
+
+
+def _k_gamma(w, l):
+    kn = getattr(w, "k_norm", None)
+    return None if kn is None else bf16_bits_to_f64(kn[l])
 
 
 def _rows(w, rows: Optional[np.ndarray]) -> np.ndarray:
@@ -137,7 +164,7 @@ def fill_workload(w, rows: Optional[np.ndarray] = None,
         out[l] = fill_layer(xs, map_matrix(w, l), bf16_bits_to_f64(w.map_b[l]),
                             bf16_bits_to_f64(w.gamma[l]), bf16_bits_to_f64(w.w_k[l]),
                             bf16_bits_to_f64(w.w_v[l]), pos, s.rope_theta, s.head_dim,
-                            s.rms_eps)
+                            s.rms_eps, _k_gamma(w, l))
     return out
 
 
@@ -156,5 +183,6 @@ def exact_kv_workload(w, layer_inputs: np.ndarray, rows: np.ndarray,
     out = {}
     for l in (range(s.n_late) if layers is None else layers):
         out[l] = layer_kv(h, bf16_bits_to_f64(w.gamma[l]), bf16_bits_to_f64(w.w_k[l]),
-                          bf16_bits_to_f64(w.w_v[l]), pos, s.rope_theta, s.head_dim, s.rms_eps)
+                          bf16_bits_to_f64(w.w_v[l]), pos, s.rope_theta, s.head_dim, s.rms_eps,
+                          _k_gamma(w, l))
     return out

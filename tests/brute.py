@@ -12,8 +12,10 @@ def _f(bits):
     return struct.unpack("<f", struct.pack("<I", int(bits) << 16))[0]
 
 
-def filled_row(x_bits, a_bits, b_bits, g_bits, wk_bits, wv_bits, pos, theta, hd, eps):
-    """K and V (lists of floats) that one late layer stores for one filled row."""
+def filled_row(x_bits, a_bits, b_bits, g_bits, wk_bits, wv_bits, pos, theta, hd, eps, kg_bits=None):
+    """K and V (lists of floats) that one late layer stores for one filled row.
+    With kg_bits (a key-norm gain of hd values) each key head is RMS-normalised
+    and scaled by the gain before its rotation."""
     d_out = len(a_bits)
     d_in = len(a_bits[0])
     x = [_f(v) for v in x_bits]
@@ -40,6 +42,16 @@ def filled_row(x_bits, a_bits, b_bits, g_bits, wk_bits, wv_bits, pos, theta, hd,
             sv += _f(wv_bits[c][n]) * h[n]
         kk.append(sk)
         vv.append(sv)
+    if kg_bits is not None:
+        for head in range(width // hd):
+            base = head * hd
+            ms = 0.0
+            for j in range(hd):
+                ms += kk[base + j] ** 2
+            ms /= hd
+            f = 1.0 / math.sqrt(ms + eps)
+            for j in range(hd):
+                kk[base + j] = kk[base + j] * f * _f(kg_bits[j])
     out = list(kk)
     half = hd // 2
     for head in range(width // hd):

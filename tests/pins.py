@@ -438,6 +438,64 @@ def pin_bf16_rounding_library(o):
                           .to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)), ref_q
 
 
+# ---------------------------------------------------------------- QK-norm
+
+def pin_qk_norm_closed_form(o):
+    """Sections 6.6-7: layers with QK-norm normalise each key head.  Worked by
+    hand: heads of 2, gain (1, 2), eps 0; head (3, 4) has mean square 12.5,
+    head (0, 2) has 2."""
+    k = np.array([[3.0, 4.0, 0.0, 2.0]])
+    got = o.qk_norm(k, np.array([1.0, 2.0]), 0.0, 2)
+    r1, r2 = math.sqrt(12.5), math.sqrt(2.0)
+    want = np.array([[3 / r1, 2 * 4 / r1, 0.0, 2 * 2 / r2]])
+    assert np.allclose(got, want, rtol=1e-15, atol=0), got
+    # eps sits inside the root
+    got = o.qk_norm(np.array([[1.0, 1.0]]), np.array([1.0, 1.0]), 3.0, 2)
+    assert np.allclose(got, [[0.5, 0.5]], rtol=1e-15)
+
+
+def pin_qk_norm_invariants(o):
+    """Unit gain and eps 0 give every head RMS 1; scaling a row changes
+    nothing; heads are normalised independently."""
+    g = _rng(33)
+    k = g.standard_normal((5, 4 * 16)) * np.exp(g.uniform(-3, 3, (5, 1)))
+    u = o.qk_norm(k, np.ones(16), 0.0, 16)
+    rms = np.sqrt(np.mean(u.reshape(5, 4, 16) ** 2, axis=2))
+    assert np.allclose(rms, 1.0, rtol=1e-13)
+    assert np.allclose(o.qk_norm(7.5 * k, np.ones(16), 0.0, 16), u, rtol=1e-13)
+    k2 = k.copy()
+    k2[:, 16:32] *= 100.0
+    k2[:, 48:] = g.standard_normal((5, 16))
+    u2 = o.qk_norm(k2, np.ones(16), 0.0, 16)
+    assert np.array_equal(u2[:, :16], u[:, :16]) and np.array_equal(u2[:, 32:48], u[:, 32:48])
+
+
+def pin_qk_layer_brute(o):
+    """A layer with QK-norm against plain loops (tests/brute.py): norm, key
+    projection, per-head key norm with a non-uniform gain, then the rotation."""
+    g = _rng(34)
+    d, hd, nkv, n = 32, 8, 2, 3
+    bits = lambda a: _bits(a)
+    x = bits(g.standard_normal((n, d)))
+    a = bits(np.eye(d) + 0.05 * g.standard_normal((d, d)))
+    b = bits(0.1 * g.standard_normal(d))
+    gam = bits(1 + 0.1 * g.standard_normal(d))
+    wk = bits(g.standard_normal((nkv * hd, d)) / np.sqrt(d))
+    wv = bits(g.standard_normal((nkv * hd, d)) / np.sqrt(d))
+    kg = bits(1 + 0.3 * g.standard_normal(hd))
+    pos = np.array([0, 5, 77])
+    f = o.bf16_bits_to_f64
+    k, v = o.fill_layer(f(x), f(a), f(b), f(gam), f(wk), f(wv), pos, 1e4, hd, 1e-5, f(kg))
+    for i in range(n):
+        kb, vb = brute.filled_row(x[i], a, b, gam, wk, wv, int(pos[i]), 1e4, hd, 1e-5, kg)
+        assert np.allclose(k[i], kb, rtol=1e-11, atol=1e-12), i
+        assert np.allclose(v[i], vb, rtol=1e-11, atol=1e-12), i
+    # without a gain the layer is the plain one
+    k0, _ = o.fill_layer(f(x), f(a), f(b), f(gam), f(wk), f(wv), pos, 1e4, hd, 1e-5)
+    kb0, _ = brute.filled_row(x[1], a, b, gam, wk, wv, 5, 1e4, hd, 1e-5)
+    assert np.allclose(k0[1], kb0, rtol=1e-11, atol=1e-12)
+
+
 # ---------------------------------------------------------------- value rescale
 
 def pin_rescale_closed_form(o):
@@ -572,7 +630,8 @@ def pin_printed_ceilings(o):
 FILL_PINS = [pin_fill_rows_partition, pin_identity_map_is_exact_kv, pin_map_orientation,
              pin_bias_only_map, pin_rmsnorm_closed_forms, pin_one_hot_layer_kv,
              pin_rope_is_complex_rotation, pin_rope_invariants, pin_brute_force_tiny,
-             pin_fill_row_independence]
+             pin_fill_row_independence, pin_qk_norm_closed_form, pin_qk_norm_invariants,
+             pin_qk_layer_brute]
 RIDGE_PINS = [pin_ridge_recovers_linear_map, pin_ridge_svd_form, pin_ridge_running_sums,
               pin_ridge_penalty_scale, pin_ridge_raw_form]
 CEILING_PINS = [pin_printed_ceilings]

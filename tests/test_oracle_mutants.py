@@ -29,7 +29,7 @@ MUTANTS = {
     "norm_skipped": ("fill.py", [("h = rms_norm(h_in, gamma, eps)", "h = h_in")]),
     # the projections
     "proj_transposed": ("fill.py", [("return h @ w.T", "return h @ w")]),
-    "proj_k_v_swapped": ("fill.py", [("k = rope(project(h, w_k)", "k = rope(project(h, w_v)"),
+    "proj_k_v_swapped": ("fill.py", [("k = project(h, w_k)", "k = project(h, w_v)"),
                                      ("v = project(h, w_v)", "v = project(h, w_k)")]),
     # the rotation
     "rope_freq_exponent": ("fill.py", [("-2.0 * j / head_dim", "-1.0 * j / head_dim")]),
@@ -38,7 +38,18 @@ MUTANTS = {
                                            ("hi = kh[..., half:]", "hi = kh[..., 1::2]")]),
     "rope_position_off_by_one": ("fill.py", [("np.asarray(positions, dtype=np.float64)[:, None]",
                                               "(np.asarray(positions, dtype=np.float64)[:, None] + 1)")]),
-    "rope_on_values_too": ("fill.py", [("v = project(h, w_v)", "v = rope(project(h, w_v), positions, theta, head_dim)")]),
+    "rope_on_values_too": ("fill.py", [("v = project(h, w_v)\n    return k, v", "v = rope(project(h, w_v), positions, theta, head_dim)\n    return k, v")]),
+    # QK-norm
+    "qk_eps_outside_root": ("fill.py", [("return (kh / np.sqrt(ms + eps) * k_gamma)", "return (kh / (np.sqrt(ms) + eps) * k_gamma)")]),
+    "qk_mean_over_row": ("fill.py", [("ms = np.mean(kh * kh, axis=2, keepdims=True)", "ms = np.mean(kh * kh, axis=(1, 2), keepdims=True)")]),
+    "qk_gain_before_norm": ("fill.py", [("return (kh / np.sqrt(ms + eps) * k_gamma)", "return (kh * k_gamma / np.sqrt(np.mean((kh * k_gamma) ** 2, axis=2, keepdims=True) + eps))")]),
+    "qk_after_rope": ("fill.py", [("""    k = project(h, w_k)
+    if k_gamma is not None:
+        k = qk_norm(k, k_gamma, eps, head_dim)
+    k = rope(k, positions, theta, head_dim)""", """    k = rope(project(h, w_k), positions, theta, head_dim)
+    if k_gamma is not None:
+        k = qk_norm(k, k_gamma, eps, head_dim)""")]),
+    "qk_gain_reversed": ("fill.py", [("return (kh / np.sqrt(ms + eps) * k_gamma)", "return (kh / np.sqrt(ms + eps) * k_gamma[::-1])")]),
     # rows and decoding
     "rows_union_not_difference": ("fill.py", [("np.setdiff1d(", "np.union1d(")]),
     "rows_wrong_positions": ("fill.py", [("pos = w.positions[r]\n    out = {}\n    for l in (range(s.n_late) if layers is None else layers):\n        out[l] = fill_layer",

@@ -28,6 +28,8 @@ value projections):
   any other block scale ~ map_sigma * (2.8 + 0.4 |N(0, 1)|) / 127; the other
   codes are N(0, map_sigma^2) / scale rounded to integers and clipped to
   [-127, 127];
+* layers that normalise their keys (``qk_norm=True``) get a key-norm gain
+  k_gamma_l ~ 1 + N(0, gamma_sigma^2) of length head_dim;
 * positions restart at 0 for every prompt of a batch;
 * the exact set is the last ``tail`` rows of every prompt plus ``n_spans``
   disjoint spans of ``span_len`` rows drawn uniformly inside the first
@@ -49,7 +51,7 @@ __all__ = [
 
 # seed-sequence "kind" tags
 _K_X, _K_OUTLIER, _K_LAYER, _K_SPANS, _K_TRUTH = 1, 2, 3, 4, 5
-_L_MAP, _L_BIAS, _L_GAMMA, _L_WK, _L_WV, _L_QSCALE = 0, 1, 2, 3, 4, 5
+_L_MAP, _L_BIAS, _L_GAMMA, _L_WK, _L_WV, _L_QSCALE, _L_KNORM = 0, 1, 2, 3, 4, 5, 6
 Q8_BLOCK = 128  # weights per bf16 scale along each row of an int8 map
 _X_BLOCK = 8192  # rows per independently seeded block of x_S
 
@@ -76,6 +78,7 @@ class Spec:
     outlier_scale: float = 20.0
     maps_on_host: bool = False
     map_format: str = "bf16"   # "bf16" or "q8"
+    qk_norm: bool = False      # keys normalised per head before RoPE
     seed: int = 0
 
     @property
@@ -159,6 +162,7 @@ class Workload:
     outlier_channels: np.ndarray  # int64 [n_outliers]
     map_q: Optional[List[np.ndarray]] = None      # q8 only: n_late x int8 [d_out][d_in]
     map_scale: Optional[List[np.ndarray]] = None  # q8 only: n_late x bf16 [d_out][d_in/128]
+    k_norm: Optional[List[np.ndarray]] = None     # qk_norm only: n_late x bf16 [head_dim]
     extra: dict = field(default_factory=dict)
 
 
@@ -272,6 +276,10 @@ def _gen_layer(s: Spec, l: int):
         out += _gen_q8_map(s, l)
     else:
         out += (None, None)
+    if s.qk_norm:
+        out += (f32_to_bf16_bits(_normal((s.seed, _K_LAYER, l, _L_KNORM), (s.head_dim,), s.gamma_sigma, 1.0)),)
+    else:
+        out += (None,)
     return out
 
 
@@ -294,4 +302,5 @@ def make(s: Spec, layers: Optional[List[int]] = None) -> Workload:
         positions=_positions(s), exact_rows=exact_row_list(s),
         outlier_channels=outliers,
         map_q=[t[5] for t in lay] if s.map_format == "q8" else None,
-        map_scale=[t[6] for t in lay] if s.map_format == "q8" else None)
+        map_scale=[t[6] for t in lay] if s.map_format == "q8" else None,
+        k_norm=[t[7] for t in lay] if s.qk_norm else None)
