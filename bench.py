@@ -161,6 +161,7 @@ def main():
     ap.add_argument("--layers-per-launch", type=int, default=None)
     ap.add_argument("--value-rescale", type=int, default=0, metavar="C",
                     help="include the value rescale measured on the first C tail rows of each prompt")
+    ap.add_argument("--qk-norm", action="store_true", help="layers normalise their keys per head before RoPE")
     ap.add_argument("--maps", default="bf16", choices=["bf16", "q8"],
                     help="map storage: bf16, or int8 codes with one bf16 scale per 128 weights of each row")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -193,7 +194,7 @@ def main():
         return
 
     name = args.workload
-    s = workloads.spec(name, map_format=args.maps)
+    s = workloads.spec(name, map_format=args.maps, qk_norm=args.qk_norm)
     q8 = args.maps == "q8"
     dev = "cuda:0"
     log(f"[bench] {name}: drawing inputs")
@@ -210,6 +211,7 @@ def main():
         map_a = [t16(a, dev, host_maps) for a in w.map_a]
     map_b = [t16(b, dev, host_maps) for b in w.map_b]
     gamma = [t16(g, dev) for g in w.gamma]
+    k_norm = [t16(g, dev) for g in w.k_norm] if w.k_norm is not None else None
     w_k = [t16(a, dev) for a in w.w_k]
     w_v = [t16(a, dev) for a in w.w_v]
     positions = torch.from_numpy(w.positions).to(dev)
@@ -247,10 +249,10 @@ def main():
                                ws_scale)
         if q8:
             B.fill_q8(plan, x, fill_rows, n_fill, positions, None, map_q, map_s, map_b, gamma, w_k, w_v, None,
-                      kc, vc, ws, vscale=vscale)
+                      kc, vc, ws, vscale=vscale, k_norm=k_norm)
         else:
             B.fill(plan, x, fill_rows, n_fill, positions, None, map_a, map_b, gamma, w_k, w_v, None, kc, vc, ws,
-                   vscale=vscale)
+                   vscale=vscale, k_norm=k_norm)
 
     log(f"[bench] {name}: n_fill={n_fill}, {s.n_late} late layers, {g} per launch; warmup {args.warmup}")
     for _ in range(args.warmup):
@@ -313,6 +315,7 @@ def main():
                    "prompts": list(s.prompt_lens), "maps": "pinned host, streamed" if host_maps else "HBM",
                    "map_format": "int8 + bf16 scale per 128 weights of a row" if q8 else "bf16",
                    "value_rescale_rows": args.value_rescale or None,
+                   "qk_norm": bool(args.qk_norm),
                    "layers_per_launch": 1 if host_maps else g},
         "tflops": step_flops / (ms * 1e-3) / 1e12,
         "frac_of_bf16_peak": step_flops / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS,

@@ -147,6 +147,19 @@ typedef struct rf_vscale {
   int32_t n_groups;             /* >= 1                                                    */
 } rf_vscale;
 
+/* Options of a fill (HOST struct; pass NULL for none of them).
+ *   vscale  value rescale (above), or NULL
+ *   k_norm  QK-norm for layers that normalise their keys (RidgeFill section
+ *           6.6 and section 7: the Qwen layers normalise each query and key
+ *           before attention): HOST array of n_late device pointers, each bf16
+ *           [head_dim], 16-byte aligned; or NULL.  Each key head is divided by
+ *           sqrt(mean of its head_dim squares + rms_eps) and multiplied by the
+ *           gain per dimension, after the key projection and before RoPE. */
+typedef struct rf_fill_opts {
+  const rf_vscale* vscale;
+  const uint16_t* const* k_norm;
+} rf_fill_opts;
+
 /* The fill (steps 1-5 above) for n_fill rows and every late layer.
  *   x              [n_rows][ld_x] bf16, ld_x >= d_in, ld_x % 8 == 0, 16-byte aligned
  *   fill_rows      [n_fill] int32, ascending, unique, in [0, n_rows)
@@ -158,7 +171,7 @@ typedef struct rf_vscale {
  *                  pinned maps alive until the stream has completed)
  *   gamma, w_k, w_v, k_cache, v_cache   HOST arrays of n_late device pointers
  *   rope_cos_sin   table from rf_rope_table, or NULL (built in the workspace)
- *   vscale         HOST pointer to an rf_vscale, or NULL for no value rescale
+ *   opts           HOST pointer to rf_fill_opts (value rescale, QK-norm), or NULL
  *   workspace      >= rf_fill_workspace_bytes(plan, n_fill, 1), 256-byte aligned
  * Rows whose position or slot is out of range are skipped by the kernels
  * (RF_VALIDATE turns them into RF_E_ROWS).  n_fill == 0 enqueues nothing and
@@ -173,7 +186,7 @@ rf_status rf_fill(rf_plan* plan,
                   const uint16_t* const* w_k, const uint16_t* const* w_v,
                   const float* rope_cos_sin,
                   uint16_t* const* k_cache, uint16_t* const* v_cache,
-                  const rf_vscale* vscale,
+                  const rf_fill_opts* opts,
                   void* workspace, size_t ws_bytes, void* hip_stream);
 
 /* ---- int8 maps -----------------------------------------------------------
@@ -201,7 +214,7 @@ rf_status rf_fill_q8(rf_plan* plan,
                      const uint16_t* const* w_k, const uint16_t* const* w_v,
                      const float* rope_cos_sin,
                      uint16_t* const* k_cache, uint16_t* const* v_cache,
-                     const rf_vscale* vscale,
+                     const rf_fill_opts* opts,
                      void* workspace, size_t ws_bytes, void* hip_stream);
 
 /* Expand one int8 map into bf16 (device to device): w[o][k] = bf16(q[o][k] *
@@ -264,6 +277,8 @@ rf_status rf_value_scales_q8(rf_plan* plan,
  *   layer_in   HOST array of n_late device pointers, each bf16 [n_rows][ld_in]
  *              (entries may alias), ld_in >= d_out, ld_in % 8 == 0
  *   rows       [n] int32 rows to write, in [0, n_rows), unique
+ *   opts       as for rf_fill, but without a value rescale (RF_E_ARG if
+ *              opts->vscale is set): exact rows are not rescaled
  *   other arguments as for rf_fill. */
 rf_status rf_kv_project(rf_plan* plan,
                         const uint16_t* const* layer_in, int64_t ld_in,
@@ -273,6 +288,7 @@ rf_status rf_kv_project(rf_plan* plan,
                         const uint16_t* const* w_k, const uint16_t* const* w_v,
                         const float* rope_cos_sin,
                         uint16_t* const* k_cache, uint16_t* const* v_cache,
+                        const rf_fill_opts* opts,
                         void* workspace, size_t ws_bytes, void* hip_stream);
 
 /* ---- Closed-form ridge map, HOST memory, float64 inside (validation only) ----

@@ -60,6 +60,11 @@ class VScale(C.Structure):
     _fields_ = [("scale", C.c_void_p), ("group_of_row", C.c_void_p), ("n_groups", C.c_int32)]
 
 
+class FillOpts(C.Structure):
+    """rf_fill_opts: value rescale and QK-norm of a fill."""
+    _fields_ = [("vscale", C.POINTER(VScale)), ("k_norm", C.POINTER(C.c_void_p))]
+
+
 _lib = None
 P = C.c_void_p
 PP = C.POINTER(C.c_void_p)
@@ -83,7 +88,7 @@ def lib():
         "rf_fill_rows_workspace_bytes": (sz, [i32]),
         "rf_fill_rows": (i32, [P, P, i32, P, P, P, sz, P]),
         "rf_fill": (i32, [P, P, i64, P, i32, P, P, PP, PP, PP, PP, PP, P, PP, PP, P, P, sz, P]),
-        "rf_kv_project": (i32, [P, PP, i64, P, i32, P, P, PP, PP, PP, P, PP, PP, P, sz, P]),
+        "rf_kv_project": (i32, [P, PP, i64, P, i32, P, P, PP, PP, PP, P, PP, PP, P, P, sz, P]),
         "rf_ridge_acc_create": (i32, [i32, i32, C.POINTER(P)]),
         "rf_ridge_acc_add": (i32, [P, P, P, i64]),
         "rf_ridge_solve": (i32, [P, dbl, i32, P, P]),
@@ -204,39 +209,52 @@ def fill_rows(plan: Plan, exact_rows, fill_rows_out, n_fill_out, workspace, stre
                                               workspace.element_size(), _stream(stream)))
 
 
-def _vscale(vscale):
-    """(scale tensor, group_of_row tensor, n_groups) -> rf_vscale by reference, or None."""
-    if vscale is None:
-        return None
-    scale, group_of_row, n_groups = vscale
-    return C.byref(VScale(scale.data_ptr(), group_of_row.data_ptr(), n_groups))
+class _Opts:
+    """Keeps an rf_fill_opts and everything it points to alive for one call."""
+
+    def __init__(self, vscale=None, k_norm=None):
+        self.ref = None
+        if vscale is None and k_norm is None:
+            return
+        self.opts = FillOpts()
+        if vscale is not None:
+            scale, group_of_row, n_groups = vscale
+            self.vs = VScale(scale.data_ptr(), group_of_row.data_ptr(), n_groups)
+            self.opts.vscale = C.pointer(self.vs)
+        if k_norm is not None:
+            self.kn = _ptr_array(k_norm)
+            self.opts.k_norm = C.cast(self.kn, C.POINTER(C.c_void_p))
+        self.ref = C.byref(self.opts)
 
 
 def fill(plan: Plan, x, fill_rows_t, n_fill: int, positions, slot_of_row, map_a: Sequence, map_b: Sequence,
          gamma: Sequence, w_k: Sequence, w_v: Sequence, rope, k_cache: Sequence, v_cache: Sequence,
-         workspace, stream=None, ld_x: Optional[int] = None, vscale=None) -> None:
+         workspace, stream=None, ld_x: Optional[int] = None, vscale=None, k_norm: Sequence = None) -> None:
     """rf_fill.  map_a/map_b are device tensors, or pinned host tensors for a
     plan made with maps_on_host.  vscale = (scale [n_late][n_groups][n_kv] fp32,
-    group_of_row [n_rows] int32, n_groups) applies a value rescale."""
+    group_of_row [n_rows] int32, n_groups) applies a value rescale; k_norm (one
+    bf16 [head_dim] gain per late layer) applies QK-norm to the keys."""
     ld = x.stride(0) if ld_x is None else ld_x
+    o = _Opts(vscale, k_norm)
     _check("rf_fill", lib().rf_fill(
         plan.handle, _ptr(x), ld, _ptr(fill_rows_t), n_fill, _ptr(positions), _ptr(slot_of_row),
         _ptr_array(map_a), _ptr_array(map_b), _ptr_array(gamma), _ptr_array(w_k), _ptr_array(w_v),
-        _ptr(rope), _ptr_array(k_cache), _ptr_array(v_cache), _vscale(vscale), _ptr(workspace),
+        _ptr(rope), _ptr_array(k_cache), _ptr_array(v_cache), o.ref, _ptr(workspace),
         workspace.numel() * workspace.element_size(), _stream(stream)))
 
 
 def fill_q8(plan: Plan, x, fill_rows_t, n_fill: int, positions, slot_of_row, map_q: Sequence,
             map_scale: Sequence, map_b: Sequence, gamma: Sequence, w_k: Sequence, w_v: Sequence, rope,
             k_cache: Sequence, v_cache: Sequence, workspace, stream=None, ld_x: Optional[int] = None,
-            vscale=None) -> None:
+            vscale=None, k_norm: Sequence = None) -> None:
     """rf_fill_q8: the fill with int8 maps (codes + bf16 block scales) for a
     plan made with maps_q8; pinned host tensors for a plan with maps_on_host."""
     ld = x.stride(0) if ld_x is None else ld_x
+    o = _Opts(vscale, k_norm)
     _check("rf_fill_q8", lib().rf_fill_q8(
         plan.handle, _ptr(x), ld, _ptr(fill_rows_t), n_fill, _ptr(positions), _ptr(slot_of_row),
         _ptr_array(map_q), _ptr_array(map_scale), _ptr_array(map_b), _ptr_array(gamma), _ptr_array(w_k),
-        _ptr_array(w_v), _ptr(rope), _ptr_array(k_cache), _ptr_array(v_cache), _vscale(vscale), _ptr(workspace),
+        _ptr_array(w_v), _ptr(rope), _ptr_array(k_cache), _ptr_array(v_cache), o.ref, _ptr(workspace),
         workspace.numel() * workspace.element_size(), _stream(stream)))
 
 
@@ -279,13 +297,15 @@ def map_quantize_q8(a: np.ndarray):
 
 def kv_project(plan: Plan, layer_in: Sequence, rows, n: int, positions, slot_of_row, gamma: Sequence,
                w_k: Sequence, w_v: Sequence, rope, k_cache: Sequence, v_cache: Sequence, workspace,
-               stream=None, ld_in: Optional[int] = None) -> None:
+               stream=None, ld_in: Optional[int] = None, k_norm: Sequence = None) -> None:
     """rf_kv_project: the exact cache write of every late layer from given inputs."""
     ld = layer_in[0].stride(0) if ld_in is None else ld_in
+    o = _Opts(None, k_norm)
     _check("rf_kv_project", lib().rf_kv_project(
         plan.handle, _ptr_array(layer_in), ld, _ptr(rows), n, _ptr(positions), _ptr(slot_of_row),
         _ptr_array(gamma), _ptr_array(w_k), _ptr_array(w_v), _ptr(rope), _ptr_array(k_cache),
-        _ptr_array(v_cache), _ptr(workspace), workspace.numel() * workspace.element_size(), _stream(stream)))
+        _ptr_array(v_cache), o.ref, _ptr(workspace), workspace.numel() * workspace.element_size(),
+        _stream(stream)))
 
 
 def _f32(a: np.ndarray) -> np.ndarray:

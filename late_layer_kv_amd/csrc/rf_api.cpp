@@ -424,6 +424,11 @@ int pick_group(const rf_plan* p, size_t ws_bytes, F bytes_for) {
   return 1;
 }
 
+rf_status check_opts(const rf_plan* p, const rf_fill_opts* o) {
+  if (!o || !o->k_norm) return RF_OK;
+  return check_layer_ptrs(reinterpret_cast<const void* const*>(o->k_norm), p->s.n_late, "k_norm");
+}
+
 rf_status check_vscale(const rf_plan* p, const rf_vscale* vs) {
   if (!vs) return RF_OK;
   if (!vs->scale || !vs->group_of_row) return fail(RF_E_ARG, "vscale has a null scale or group_of_row");
@@ -435,9 +440,11 @@ rf_status check_vscale(const rf_plan* p, const rf_vscale* vs) {
 rf_status fill_impl(rf_plan* p, const char* fn, const uint16_t* x, int64_t ld_x, const int32_t* fill_rows,
                     int32_t n_fill, const int32_t* positions, const int32_t* slot_of_row, const MapSrc& maps,
                     const uint16_t* const* gamma, const uint16_t* const* w_k, const uint16_t* const* w_v,
-                    const float* rope, uint16_t* const* k_cache, uint16_t* const* v_cache, const rf_vscale* vscale,
+                    const float* rope, uint16_t* const* k_cache, uint16_t* const* v_cache, const rf_fill_opts* opts,
                     void* ws, size_t ws_bytes, void* stream) {
   const rf_shape& s = p->s;
+  const rf_vscale* vscale = opts ? opts->vscale : nullptr;
+  const uint16_t* const* k_norm = opts ? opts->k_norm : nullptr;
   const int L = s.n_late;
   rf_status st;
   if ((st = check_maps(p, fn, maps)) != RF_OK) return st;
@@ -452,6 +459,7 @@ rf_status fill_impl(rf_plan* p, const char* fn, const uint16_t* x, int64_t ld_x,
   if ((st = check_layer_ptrs(reinterpret_cast<const void* const*>(k_cache), L, "k_cache")) != RF_OK) return st;
   if ((st = check_layer_ptrs(reinterpret_cast<const void* const*>(v_cache), L, "v_cache")) != RF_OK) return st;
   if ((st = check_vscale(p, vscale)) != RF_OK) return st;
+  if ((st = check_opts(p, opts)) != RF_OK) return st;
   if (rope && !aligned16(rope)) return fail(RF_E_ARG, "rope table is not 16-byte aligned");
   const size_t need1 = rf_fill_workspace_bytes(p, n_fill, 1);
   if (!ws || (reinterpret_cast<uintptr_t>(ws) % kAlign) || ws_bytes < need1)
@@ -514,6 +522,7 @@ rf_status fill_impl(rf_plan* p, const char* fn, const uint16_t* x, int64_t ld_x,
   kp.n_kv = s.n_kv;
   kp.n_groups = vscale ? vscale->n_groups : 0;
   kp.group_of_row = vscale ? vscale->group_of_row : nullptr;
+  kp.qk_norm = k_norm != nullptr;
 
   rf::PrepParams pp{};
   pp.d = s.d_out;
@@ -534,6 +543,7 @@ rf_status fill_impl(rf_plan* p, const char* fn, const uint16_t* x, int64_t ld_x,
       kp.kc[i] = k_cache[l0 + i];
       kp.vc[i] = v_cache[l0 + i];
       kp.vscale[i] = vscale ? vscale->scale + (l0 + i) * vs_layer : nullptr;
+      kp.kgamma[i] = k_norm ? k_norm[l0 + i] : nullptr;
     }
     {
       Timed tm(p, RF_K_PREP, hs);
@@ -716,20 +726,20 @@ rf_status rf_fill(rf_plan* p, const uint16_t* x, int64_t ld_x, const int32_t* fi
                   const int32_t* positions, const int32_t* slot_of_row, const uint16_t* const* map_a,
                   const uint16_t* const* map_b, const uint16_t* const* gamma, const uint16_t* const* w_k,
                   const uint16_t* const* w_v, const float* rope, uint16_t* const* k_cache,
-                  uint16_t* const* v_cache, const rf_vscale* vscale, void* ws, size_t ws_bytes, void* stream) {
+                  uint16_t* const* v_cache, const rf_fill_opts* opts, void* ws, size_t ws_bytes, void* stream) {
   if (!p) return fail(RF_E_ARG, "plan is null");
   MapSrc m;
   m.a = map_a;
   m.b = map_b;
   return fill_impl(p, "rf_fill", x, ld_x, fill_rows, n_fill, positions, slot_of_row, m, gamma, w_k, w_v, rope,
-                   k_cache, v_cache, vscale, ws, ws_bytes, stream);
+                   k_cache, v_cache, opts, ws, ws_bytes, stream);
 }
 
 rf_status rf_fill_q8(rf_plan* p, const uint16_t* x, int64_t ld_x, const int32_t* fill_rows, int32_t n_fill,
                      const int32_t* positions, const int32_t* slot_of_row, const int8_t* const* map_q,
                      const uint16_t* const* map_scale, const uint16_t* const* map_b, const uint16_t* const* gamma,
                      const uint16_t* const* w_k, const uint16_t* const* w_v, const float* rope,
-                     uint16_t* const* k_cache, uint16_t* const* v_cache, const rf_vscale* vscale, void* ws,
+                     uint16_t* const* k_cache, uint16_t* const* v_cache, const rf_fill_opts* opts, void* ws,
                      size_t ws_bytes, void* stream) {
   if (!p) return fail(RF_E_ARG, "plan is null");
   if (!map_q || !map_scale) return fail(RF_E_ARG, "map_q or map_scale array is null");
@@ -738,7 +748,7 @@ rf_status rf_fill_q8(rf_plan* p, const uint16_t* x, int64_t ld_x, const int32_t*
   m.scale = map_scale;
   m.b = map_b;
   return fill_impl(p, "rf_fill_q8", x, ld_x, fill_rows, n_fill, positions, slot_of_row, m, gamma, w_k, w_v, rope,
-                   k_cache, v_cache, vscale, ws, ws_bytes, stream);
+                   k_cache, v_cache, opts, ws, ws_bytes, stream);
 }
 
 size_t rf_value_scales_workspace_bytes(const rf_plan* p, int32_t n_calib, int32_t g) {
@@ -795,9 +805,10 @@ rf_status rf_map_dequantize_q8(const int8_t* q, const uint16_t* scale, int32_t d
 rf_status rf_kv_project(rf_plan* p, const uint16_t* const* layer_in, int64_t ld_in, const int32_t* rows, int32_t n,
                         const int32_t* positions, const int32_t* slot_of_row, const uint16_t* const* gamma,
                         const uint16_t* const* w_k, const uint16_t* const* w_v, const float* rope,
-                        uint16_t* const* k_cache, uint16_t* const* v_cache, void* ws, size_t ws_bytes,
-                        void* stream) {
+                        uint16_t* const* k_cache, uint16_t* const* v_cache, const rf_fill_opts* opts, void* ws,
+                        size_t ws_bytes, void* stream) {
   if (!p) return fail(RF_E_ARG, "plan is null");
+  if (opts && opts->vscale) return fail(RF_E_ARG, "rf_kv_project writes exact rows: no value rescale");
   const rf_shape& s = p->s;
   const int L = s.n_late;
   if (n < 0 || n > s.n_rows) return fail(RF_E_ARG, "n=%d outside [0, n_rows=%d]", n, s.n_rows);
@@ -811,6 +822,7 @@ rf_status rf_kv_project(rf_plan* p, const uint16_t* const* layer_in, int64_t ld_
   if ((st = check_layer_ptrs(reinterpret_cast<const void* const*>(w_v), L, "w_v")) != RF_OK) return st;
   if ((st = check_layer_ptrs(reinterpret_cast<const void* const*>(k_cache), L, "k_cache")) != RF_OK) return st;
   if ((st = check_layer_ptrs(reinterpret_cast<const void* const*>(v_cache), L, "v_cache")) != RF_OK) return st;
+  if ((st = check_opts(p, opts)) != RF_OK) return st;
   if (rope && !aligned16(rope)) return fail(RF_E_ARG, "rope table is not 16-byte aligned");
   const size_t need1 = rf_kv_project_workspace_bytes(p, 1);
   if (!ws || (reinterpret_cast<uintptr_t>(ws) % kAlign) || ws_bytes < need1)
@@ -857,6 +869,9 @@ rf_status rf_kv_project(rf_plan* p, const uint16_t* const* layer_in, int64_t ld_
   kp.max_pos = s.max_pos;
   kp.rope = rope;
   kp.eps = s.rms_eps;
+  kp.n_kv = s.n_kv;
+  const uint16_t* const* k_norm = opts ? opts->k_norm : nullptr;
+  kp.qk_norm = k_norm != nullptr;
   rf::PrepParams pp{};
   pp.d = s.d_out;
   pp.w = w;
@@ -870,6 +885,7 @@ rf_status rf_kv_project(rf_plan* p, const uint16_t* const* layer_in, int64_t ld_
       kp.in[i] = layer_in[l0 + i];
       kp.kc[i] = k_cache[l0 + i];
       kp.vc[i] = v_cache[l0 + i];
+      kp.kgamma[i] = k_norm ? k_norm[l0 + i] : nullptr;
     }
     {
       Timed tm(p, RF_K_PREP, hs);

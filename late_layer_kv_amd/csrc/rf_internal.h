@@ -60,10 +60,14 @@ struct KvParams {
   // (2w - that offset) / 256); only value features are stored, keys are
   // neither rotated nor written (kc may be null).
   int32_t v_only;
+  // QK-norm: each key head is divided by sqrt(mean of its squares + eps) and
+  // multiplied by kgamma_g[j] (bf16 [head_dim]) before RoPE.
+  int32_t qk_norm;
   const uint16_t* in[kMaxGroup];
   uint16_t* kc[kMaxGroup];  // [n_slots][w]
   uint16_t* vc[kMaxGroup];
   const float* vscale[kMaxGroup];  // [n_groups][n_kv] per layer, or null
+  const uint16_t* kgamma[kMaxGroup];  // [head_dim] per layer (qk_norm)
 };
 
 // Prepared projection weights: out_g[f][k] = bf16(W[f][k] * gamma_g[k]),

@@ -359,9 +359,10 @@ __global__ void __launch_bounds__(kThreads) map_gemm_kernel(const MapParams p) {
   }
 }
 
-// VSCALE: the value rescale is applied (a separate instantiation, so the plain
-// fill's epilogue keeps its register budget).
-template <int HD, bool VSCALE>
+// VSCALE: the value rescale is applied; QK: keys are RMS-normalised per head
+// with a per-dimension gain before RoPE.  Each option is its own
+// instantiation, so the plain fill's epilogue keeps its register budget.
+template <int HD, bool VSCALE, bool QK>
 __global__ void __launch_bounds__(kThreads) kv_gemm_kernel(const KvParams p) {
   __shared__ __attribute__((aligned(1024))) char smem[kLdsBytes];
   int* const slot_of = reinterpret_cast<int*>(smem + kSlotOffset);
@@ -441,12 +442,26 @@ __global__ void __launch_bounds__(kThreads) kv_gemm_kernel(const KvParams p) {
     // partner is block nb + hd/64 at the same register index.
     constexpr int half = HD / 2;
     constexpr int pstep = half / 32;  // 2 for hd 128, 1 for hd 64
+    constexpr int heads = 128 / HD;   // heads per wave
     const float2* tab = reinterpret_cast<const float2*>(p.rope);
+    // With QK-norm each head is also divided by sqrt(mean over the head of
+    // k^2 + eps) and its dimensions scaled by the gain before the rotation.
+    // The rotation is linear, so the per-row, per-head division is applied
+    // after it: the rotation pass sums the squares of the unrotated values it
+    // reads (a lane holds half of each head's values for its row, the other
+    // half is in lane ^ 32), then a second pass scales.
+    float sq[4][heads];
+#pragma unroll
+    for (int mb = 0; mb < 4; ++mb)
+#pragma unroll
+      for (int h = 0; h < heads; ++h) sq[mb][h] = 0.0f;
+    const uint16_t* kg = QK ? p.kgamma[c.g] : nullptr;
 #pragma unroll
     for (int nb = 0; nb < 4; ++nb) {
       const int jb = (nb * 32) & (HD - 1);
       if (jb >= half) continue;
       const int nb2 = nb + pstep;
+      const int h = nb / (4 / heads);
 #pragma unroll
       for (int mb = 0; mb < 4; ++mb) {
         const float2* trow = tab + static_cast<size_t>(pos[mb]) * half + jb + hsel * 4;
@@ -455,14 +470,43 @@ __global__ void __launch_bounds__(kThreads) kv_gemm_kernel(const KvParams p) {
           const float4 cs01 = *reinterpret_cast<const float4*>(trow + q * 8);
           const float4 cs23 = *reinterpret_cast<const float4*>(trow + q * 8 + 2);
           const float cs[8] = {cs01.x, cs01.y, cs01.z, cs01.w, cs23.x, cs23.y, cs23.z, cs23.w};
+          float g1[4] = {1.0f, 1.0f, 1.0f, 1.0f}, g2[4] = {1.0f, 1.0f, 1.0f, 1.0f};
+          if (QK) {
+            // gains of dimensions j and j + hd/2, four consecutive each
+            const uint2 a = *reinterpret_cast<const uint2*>(kg + jb + q * 8 + hsel * 4);
+            const uint2 b = *reinterpret_cast<const uint2*>(kg + jb + half + q * 8 + hsel * 4);
+            g1[0] = __uint_as_float(a.x << 16), g1[1] = __uint_as_float(a.x & 0xffff0000u);
+            g1[2] = __uint_as_float(a.y << 16), g1[3] = __uint_as_float(a.y & 0xffff0000u);
+            g2[0] = __uint_as_float(b.x << 16), g2[1] = __uint_as_float(b.x & 0xffff0000u);
+            g2[2] = __uint_as_float(b.y << 16), g2[3] = __uint_as_float(b.y & 0xffff0000u);
+          }
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
-            const float x1 = acc[nb][mb][q * 4 + i] * rs[mb];
-            const float x2 = acc[nb2][mb][q * 4 + i] * rs[mb];
+            float x1 = acc[nb][mb][q * 4 + i] * rs[mb];
+            float x2 = acc[nb2][mb][q * 4 + i] * rs[mb];
+            if (QK) {
+              sq[mb][h] += x1 * x1 + x2 * x2;
+              x1 *= g1[i];
+              x2 *= g2[i];
+            }
             const float co = cs[2 * i], si = cs[2 * i + 1];
             acc[nb][mb][q * 4 + i] = x1 * co - x2 * si;
             acc[nb2][mb][q * 4 + i] = x2 * co + x1 * si;
           }
+        }
+      }
+    }
+    if (QK) {
+#pragma unroll
+      for (int mb = 0; mb < 4; ++mb) {
+#pragma unroll
+        for (int h = 0; h < heads; ++h) {
+          const float tot = sq[mb][h] + __shfl_xor(sq[mb][h], 32);
+          const float f = rsqrtf(tot * (1.0f / HD) + p.eps);
+#pragma unroll
+          for (int nb = h * (4 / heads); nb < (h + 1) * (4 / heads); ++nb)
+#pragma unroll
+            for (int v = 0; v < 16; ++v) acc[nb][mb][v] *= f;
         }
       }
     }
@@ -614,17 +658,16 @@ hipError_t launch_map(const MapParams& p, int n_layers, hipStream_t s) {
 
 hipError_t launch_kv(const KvParams& p, int n_layers, hipStream_t s) {
   const int grid = n_layers * p.tiles_m * p.tiles_n;
-  const bool vscale = p.group_of_row != nullptr;
-  if (p.head_dim == 128) {
-    if (vscale)
-      hipLaunchKernelGGL((kv_gemm_kernel<128, true>), dim3(grid), dim3(kThreads), 0, s, p);
-    else
-      hipLaunchKernelGGL((kv_gemm_kernel<128, false>), dim3(grid), dim3(kThreads), 0, s, p);
-  } else {
-    if (vscale)
-      hipLaunchKernelGGL((kv_gemm_kernel<64, true>), dim3(grid), dim3(kThreads), 0, s, p);
-    else
-      hipLaunchKernelGGL((kv_gemm_kernel<64, false>), dim3(grid), dim3(kThreads), 0, s, p);
+  const int variant = (p.head_dim == 128 ? 4 : 0) | (p.group_of_row ? 2 : 0) | (p.qk_norm ? 1 : 0);
+  switch (variant) {
+    case 0: hipLaunchKernelGGL((kv_gemm_kernel<64, false, false>), dim3(grid), dim3(kThreads), 0, s, p); break;
+    case 1: hipLaunchKernelGGL((kv_gemm_kernel<64, false, true>), dim3(grid), dim3(kThreads), 0, s, p); break;
+    case 2: hipLaunchKernelGGL((kv_gemm_kernel<64, true, false>), dim3(grid), dim3(kThreads), 0, s, p); break;
+    case 3: hipLaunchKernelGGL((kv_gemm_kernel<64, true, true>), dim3(grid), dim3(kThreads), 0, s, p); break;
+    case 4: hipLaunchKernelGGL((kv_gemm_kernel<128, false, false>), dim3(grid), dim3(kThreads), 0, s, p); break;
+    case 5: hipLaunchKernelGGL((kv_gemm_kernel<128, false, true>), dim3(grid), dim3(kThreads), 0, s, p); break;
+    case 6: hipLaunchKernelGGL((kv_gemm_kernel<128, true, false>), dim3(grid), dim3(kThreads), 0, s, p); break;
+    default: hipLaunchKernelGGL((kv_gemm_kernel<128, true, true>), dim3(grid), dim3(kThreads), 0, s, p); break;
   }
   return hipGetLastError();
 }

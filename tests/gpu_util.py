@@ -53,6 +53,7 @@ class DeviceInputs:
         self.w_v = [t16(a).to(device) for a in w.w_v]
         self.positions = i32(w.positions).to(device)
         self.exact = i32(w.exact_rows).to(device)
+        self.k_norm = None if w.k_norm is None else [t16(g).to(device) for g in w.k_norm]
 
     def caches(self):
         s = self.w.spec
@@ -85,10 +86,12 @@ def gpu_fill(plan, di: DeviceInputs, rows: torch.Tensor, n_fill: int, caches=Non
     ws = torch.empty(max(plan.fill_workspace_bytes(n_fill, g), 256), dtype=torch.uint8, device=di.device)
     if di.q8 and map_a is None:
         B.fill_q8(plan, di.x, rows, n_fill, di.positions, slots, di.map_q, di.map_scale,
-                  di.map_b if map_b is None else map_b, di.gamma, di.w_k, di.w_v, rope, kc, vc, ws, vscale=vscale)
+                  di.map_b if map_b is None else map_b, di.gamma, di.w_k, di.w_v, rope, kc, vc, ws, vscale=vscale,
+                  k_norm=di.k_norm)
     else:
         B.fill(plan, di.x, rows, n_fill, di.positions, slots, di.map_a if map_a is None else map_a,
-               di.map_b if map_b is None else map_b, di.gamma, di.w_k, di.w_v, rope, kc, vc, ws, vscale=vscale)
+               di.map_b if map_b is None else map_b, di.gamma, di.w_k, di.w_v, rope, kc, vc, ws, vscale=vscale,
+               k_norm=di.k_norm)
     torch.cuda.synchronize()
     return kc, vc
 
@@ -97,7 +100,8 @@ def gpu_kv_project(plan, di: DeviceInputs, layer_in, rows: torch.Tensor, n: int,
     s = di.w.spec
     kc, vc = di.caches() if caches is None else caches
     ws = torch.empty(plan.kv_project_workspace_bytes(s.n_late), dtype=torch.uint8, device=di.device)
-    B.kv_project(plan, layer_in, rows, n, di.positions, slots, di.gamma, di.w_k, di.w_v, None, kc, vc, ws)
+    B.kv_project(plan, layer_in, rows, n, di.positions, slots, di.gamma, di.w_k, di.w_v, None, kc, vc, ws,
+                 k_norm=di.k_norm)
     torch.cuda.synchronize()
     return kc, vc
 

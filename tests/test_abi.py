@@ -83,10 +83,23 @@ def test_fill_argument_errors_before_any_device_work():
     assert call(ws_ptr=C.c_void_p(0x10010)) == -4  # workspace misaligned
     assert call(ws_b=16) == -4
     assert "workspace" in B.last_error()
-    assert call(vs=C.byref(B.VScale(None, 0x1000, 1))) == -1   # null scale
-    assert call(vs=C.byref(B.VScale(0x1000, None, 1))) == -1   # null groups
-    assert call(vs=C.byref(B.VScale(0x1000, 0x1000, 0))) == -1  # no groups
-    assert call(vs=C.byref(B.VScale(0x1002, 0x1000, 1))) == -1  # misaligned scale
+    def opts(vs=None, kn=None):
+        o = B.FillOpts()
+        if vs is not None:
+            o.vscale = C.pointer(vs)
+        if kn is not None:
+            o.k_norm = C.cast(kn, C.POINTER(C.c_void_p))
+        return C.byref(o)
+    assert call(vs=opts(B.VScale(None, 0x1000, 1))) == -1   # null scale
+    assert call(vs=opts(B.VScale(0x1000, None, 1))) == -1   # null groups
+    assert call(vs=opts(B.VScale(0x1000, 0x1000, 0))) == -1  # no groups
+    assert call(vs=opts(B.VScale(0x1002, 0x1000, 1))) == -1  # misaligned scale
+    assert call(vs=opts(kn=null_arr)) == -1                  # a layer without a key-norm gain
+    assert call(vs=opts(kn=(C.c_void_p * nl)(*([0x1000] * (nl - 1) + [0x1008])))) == -1  # misaligned gain
+    # exact rows take no value rescale
+    ws_ptr = C.c_void_p(0x10000)
+    assert L.rf_kv_project(p.handle, arr, 256, fake, 10, fake, None, arr, arr, arr, None, arr, arr,
+                           opts(B.VScale(0x1000, 0x1000, 1)), ws_ptr, ws, None) == -1
     p.close()
 
 

@@ -40,13 +40,14 @@ def sample_rows(fill: np.ndarray, exact: np.ndarray, positions: np.ndarray, n: i
     return np.array(sorted(pick), dtype=np.int32)
 
 
-FULL_CASES = [(n, "bf16") for n in workloads.CONFIG_ORDER] + [("27b_120k", "q8"), ("8b_ragged_host", "q8")]
+FULL_CASES = [(n, "bf16", False) for n in workloads.CONFIG_ORDER] + \
+    [("27b_120k", "q8", False), ("8b_ragged_host", "q8", False), ("27b", "bf16", True)]
 
 
-@pytest.mark.parametrize("name,fmt", FULL_CASES, ids=[f"{n}-{f}" for n, f in FULL_CASES])
-def test_full_size(name, fmt):
-    s = workloads.spec(name, map_format=fmt)
-    print(f"[full] {name} ({fmt} maps): generating inputs", flush=True)
+@pytest.mark.parametrize("name,fmt,qk", FULL_CASES, ids=[f"{n}-{f}{'-qk' if q else ''}" for n, f, q in FULL_CASES])
+def test_full_size(name, fmt, qk):
+    s = workloads.spec(name, map_format=fmt, qk_norm=qk)
+    print(f"[full] {name} ({fmt} maps{', QK-norm' if qk else ''}): generating inputs", flush=True)
     w = workloads.make(s)
     di = U.DeviceInputs(w)
     plan = B.Plan.for_spec(s)
