@@ -135,6 +135,37 @@ def blas_reference(s, steps):
     print(json.dumps({"blas_reference": out, "workload": s.name}), flush=True)
 
 
+PEAK_FP64_TFLOPS = 78.6    # MI355X dense fp64 MFMA, published
+
+
+def capture_bench(s, rows, steps, warmup):
+    """rf_ridge_dev_add on `rows` rows of width d_in -> d_out: fp64 running sums
+    of X^T X (upper half) and X^T Y, section 2.2 "Fitting"."""
+    import torch
+    from late_layer_kv_amd import binding as B
+    g = torch.Generator(device="cuda:0").manual_seed(0)
+    x = torch.randn((rows, s.d_in), generator=g, device="cuda:0").to(torch.bfloat16).view(torch.int16)
+    y = torch.randn((rows, s.d_out), generator=g, device="cuda:0").to(torch.bfloat16).view(torch.int16)
+    dev = B.RidgeDeviceSums(s.d_in, s.d_out)
+    for _ in range(warmup):
+        dev.add(x, y)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record()
+    for _ in range(steps):
+        dev.add(x, y)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / steps
+    flop = 2.0 * rows * s.d_in * (s.d_in / 2 + s.d_out)
+    tf = flop / (ms * 1e-3) / 1e12
+    print(json.dumps({"capture": {"workload": s.name, "rows": rows, "d_in": s.d_in, "d_out": s.d_out,
+                                  "ms_per_call": ms, "rows_per_s": rows / (ms * 1e-3),
+                                  "roofline": {"bound": "mfma", "achieved": tf, "peak": PEAK_FP64_TFLOPS,
+                                               "unit": "TFLOP/s (fp64)", "frac": tf / PEAK_FP64_TFLOPS}}}),
+          flush=True)
+
+
 def cpu_baseline(w, fill, name):
     import oracle
     try:
@@ -170,6 +201,9 @@ def main():
     ap.add_argument("--blas-reference", action="store_true",
                     help="time torch.matmul (hipBLASLt) on the two contraction shapes of --workload and exit; "
                          "a reference point for the roofline, not part of the fill")
+    ap.add_argument("--capture", type=int, default=0, metavar="ROWS",
+                    help="time the device capture of the ridge sums (X^T X, X^T Y) on ROWS rows of --workload's "
+                         "width and exit; a separate JSON line, not the fill")
     ap.add_argument("--pmc-summary", nargs=3, metavar=("FETCH_CSV", "WRITE_CSV", "CALIB_MIB"),
                     help="write the traffic summary for --workload from two rocprofv3 --pmc CSVs and exit")
     args = ap.parse_args()
@@ -191,6 +225,9 @@ def main():
 
     if args.blas_reference:
         blas_reference(workloads.spec(args.workload), args.steps)
+        return
+    if args.capture:
+        capture_bench(workloads.spec(args.workload), args.capture, args.steps, args.warmup)
         return
 
     name = args.workload

@@ -305,9 +305,33 @@ rf_status rf_ridge_acc_add(rf_ridge_acc* acc, const float* x, const float* y, in
 rf_status rf_ridge_solve(const rf_ridge_acc* acc, double lambda, int32_t flags,
                          float* a, float* b);
 void rf_ridge_acc_destroy(rf_ridge_acc* acc);
+/* The running sums themselves (HOST, fp64; any output pointer may be NULL):
+ * sxx [d_in][d_in] (full, symmetric), sxy [d_in][d_out], sx [d_in], sy [d_out], n. */
+rf_status rf_ridge_acc_sums(const rf_ridge_acc* acc, double* sxx, double* sxy, double* sx, double* sy, int64_t* n);
 /* create + add + solve + destroy in one call */
 rf_status rf_ridge_fit(const float* x, const float* y, int64_t n, int32_t d_in, int32_t d_out,
                        double lambda, int32_t flags, float* a, float* b);
+
+/* ---- Device capture of the ridge sums --------------------------------------
+ * Section 2.2 ("Fitting"): the running sums of X^T X, X^T Y, X and Y that the
+ * ridge solve needs, formed on the GPU from calibration activations that are
+ * already there (bf16 split states X [n][ld_x] and layer inputs Y [n][ld_y],
+ * device memory, 16-byte aligned, ld multiples of 8).  bf16 values and their
+ * products are exact in fp64, and the sums are accumulated in fp64 with
+ * matrix instructions, so they equal rf_ridge_acc_add's on the same values up
+ * to the order of the fp64 additions.  X^T X is formed on its upper tiles only.
+ *   create   d_in, d_out positive multiples of 128; allocates the sums
+ *            ((d_in + d_out) * d_in + 64 * max(d_in, d_out) + d_in + d_out
+ *            doubles) on the current device and zeroes them (synchronously)
+ *   add      enqueues on hip_stream; n == 0 is a no-op
+ *   merge    waits for hip_stream, adds the sums into a host accumulator of
+ *            the same d_in, d_out, and clears them; then rf_ridge_solve */
+typedef struct rf_ridge_dev rf_ridge_dev;
+rf_status rf_ridge_dev_create(int32_t d_in, int32_t d_out, rf_ridge_dev** out);
+rf_status rf_ridge_dev_add(rf_ridge_dev* dev, const uint16_t* x, int64_t ld_x, const uint16_t* y, int64_t ld_y,
+                           int64_t n, void* hip_stream);
+rf_status rf_ridge_dev_merge(rf_ridge_dev* dev, rf_ridge_acc* acc, void* hip_stream);
+void rf_ridge_dev_destroy(rf_ridge_dev* dev);
 
 /* ---- Kernel timing -------------------------------------------------------
  * With profiling on, every launch and map copy the plan issues is bracketed

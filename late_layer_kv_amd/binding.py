@@ -34,6 +34,7 @@ EXPORTS = [
     "rf_plan_profile", "rf_plan_profile_read", "rf_last_error",
     "rf_fill_q8", "rf_map_dequantize_q8", "rf_map_quantize_q8",
     "rf_value_scales_workspace_bytes", "rf_value_scales", "rf_value_scales_q8",
+    "rf_ridge_dev_create", "rf_ridge_dev_add", "rf_ridge_dev_merge", "rf_ridge_dev_destroy", "rf_ridge_acc_sums",
 ]
 
 KERNEL_KINDS = ["map", "kv", "prep", "rope", "rows", "copy", "dequant", "scale"]
@@ -99,6 +100,11 @@ def lib():
         "rf_last_error": (C.c_char_p, []),
         "rf_fill_q8": (i32, [P, P, i64, P, i32, P, P, PP, PP, PP, PP, PP, PP, P, PP, PP, P, P, sz, P]),
         "rf_value_scales_workspace_bytes": (sz, [P, i32, i32]),
+        "rf_ridge_dev_create": (i32, [i32, i32, C.POINTER(P)]),
+        "rf_ridge_dev_add": (i32, [P, P, i64, P, i64, i64, P]),
+        "rf_ridge_dev_merge": (i32, [P, P, P]),
+        "rf_ridge_dev_destroy": (None, [P]),
+        "rf_ridge_acc_sums": (i32, [P, P, P, P, P, P]),
         "rf_value_scales": (i32, [P, P, i64, PP, i64, P, P, i32, i32, PP, PP, PP, PP, P, P, sz, P]),
         "rf_value_scales_q8": (i32, [P, P, i64, PP, i64, P, P, i32, i32, PP, PP, PP, PP, PP, P, P, sz, P]),
         "rf_map_dequantize_q8": (i32, [P, P, i32, i32, P, P]),
@@ -333,9 +339,51 @@ class RidgeAccumulator:
                                                       a.ctypes.data, b.ctypes.data))
         return a, b
 
+    def sums(self):
+        """(sxx [d_in][d_in], sxy [d_in][d_out], sx, sy, n) in float64."""
+        sxx = np.empty((self.d_in, self.d_in))
+        sxy = np.empty((self.d_in, self.d_out))
+        sx = np.empty(self.d_in)
+        sy = np.empty(self.d_out)
+        n = C.c_int64()
+        _check("rf_ridge_acc_sums", lib().rf_ridge_acc_sums(self.handle, sxx.ctypes.data, sxy.ctypes.data,
+                                                            sx.ctypes.data, sy.ctypes.data, C.byref(n)))
+        return sxx, sxy, sx, sy, int(n.value)
+
     def close(self):
         if self.handle:
             lib().rf_ridge_acc_destroy(self.handle)
+            self.handle = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+
+class RidgeDeviceSums:
+    """rf_ridge_dev: fp64 running sums of a ridge fit formed on the GPU from
+    device bf16 activations; merge() moves them into a RidgeAccumulator."""
+
+    def __init__(self, d_in: int, d_out: int):
+        h = C.c_void_p()
+        _check("rf_ridge_dev_create", lib().rf_ridge_dev_create(d_in, d_out, C.byref(h)))
+        self.handle, self.d_in, self.d_out = h, d_in, d_out
+
+    def add(self, x, y, stream=None) -> None:
+        """x: device bf16 [n][>= d_in], y: device bf16 [n][>= d_out] (row-major)."""
+        if x.shape[0] != y.shape[0]:
+            raise ValueError("x and y must have the same number of rows")
+        _check("rf_ridge_dev_add", lib().rf_ridge_dev_add(self.handle, _ptr(x), x.stride(0), _ptr(y), y.stride(0),
+                                                          x.shape[0], _stream(stream)))
+
+    def merge(self, acc: "RidgeAccumulator", stream=None) -> None:
+        _check("rf_ridge_dev_merge", lib().rf_ridge_dev_merge(self.handle, acc.handle, _stream(stream)))
+
+    def close(self):
+        if self.handle:
+            lib().rf_ridge_dev_destroy(self.handle)
             self.handle = None
 
     def __del__(self):

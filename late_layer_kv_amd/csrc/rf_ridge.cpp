@@ -8,12 +8,14 @@
 // solve.  The solve is a Cholesky factorisation of the symmetric positive
 // definite matrix Xc^T Xc + alpha I followed by two triangular solves per
 // output column.
+#include <algorithm>
 #include <cmath>
 #include <new>
 #include <vector>
 
 #include "../../include/rf.h"
 #include "rf_error.h"
+#include "rf_ridge_internal.h"
 
 namespace {
 rf_status rfail(rf_status st, const char* msg) {
@@ -27,6 +29,23 @@ struct rf_ridge_acc {
   long long n = 0;
   std::vector<double> sx, sy, sxx, sxy;  // sxx [d_in][d_in], sxy [d_in][d_out]
 };
+
+void rf::ridge_acc_dims(const rf_ridge_acc* a, int* d_in, int* d_out) {
+  *d_in = a->d_in;
+  *d_out = a->d_out;
+}
+
+void rf::ridge_acc_add_sums(rf_ridge_acc* a, const double* sxx, const double* sxy, const double* sx,
+                            const double* sy, int64_t n) {
+  const int di = a->d_in, dout = a->d_out;
+  for (int i = 0; i < di; ++i) {
+    a->sx[i] += sx[i];
+    for (int k = i; k < di; ++k) a->sxx[static_cast<size_t>(i) * di + k] += sxx[static_cast<size_t>(i) * di + k];
+    for (int j = 0; j < dout; ++j) a->sxy[static_cast<size_t>(i) * dout + j] += sxy[static_cast<size_t>(i) * dout + j];
+  }
+  for (int j = 0; j < dout; ++j) a->sy[j] += sy[j];
+  a->n += n;
+}
 
 extern "C" {
 
@@ -70,6 +89,23 @@ rf_status rf_ridge_acc_add(rf_ridge_acc* a, const float* x, const float* y, int6
     for (int j = 0; j < dout; ++j) a->sy[j] += yr[j];
   }
   a->n += n;
+  return RF_OK;
+}
+
+rf_status rf_ridge_acc_sums(const rf_ridge_acc* a, double* sxx, double* sxy, double* sx, double* sy, int64_t* n) {
+  if (!a) return rfail(RF_E_ARG, "accumulator is null");
+  const int di = a->d_in, dout = a->d_out;
+  if (sxx)
+    for (int i = 0; i < di; ++i)
+      for (int k = i; k < di; ++k) {
+        const double v = a->sxx[static_cast<size_t>(i) * di + k];
+        sxx[static_cast<size_t>(i) * di + k] = v;
+        sxx[static_cast<size_t>(k) * di + i] = v;
+      }
+  if (sxy) std::copy(a->sxy.begin(), a->sxy.end(), sxy);
+  if (sx) std::copy(a->sx.begin(), a->sx.end(), sx);
+  if (sy) std::copy(a->sy.begin(), a->sy.end(), sy);
+  if (n) *n = a->n;
   return RF_OK;
 }
 

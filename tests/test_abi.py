@@ -313,3 +313,26 @@ def test_value_scales_argument_errors_and_workspace():
     assert p.value_scales_workspace_bytes(n, 1) == want
     assert p.value_scales_workspace_bytes(n, 5) == 0
     p.close()
+
+
+def test_ridge_device_sums_argument_errors():
+    L = B.lib()
+    h = C.c_void_p()
+    assert L.rf_ridge_dev_create(100, 128, C.byref(h)) == -2
+    assert L.rf_ridge_dev_create(128, 0, C.byref(h)) == -2
+    assert L.rf_ridge_dev_create(128, 128, None) == -1
+    assert L.rf_ridge_dev_add(None, None, 128, None, 128, 4, None) == -1
+    assert L.rf_ridge_dev_merge(None, None, None) == -1
+
+
+def test_ridge_acc_sums_round_trip():
+    x, y = _data(5, 50, 6, 4)
+    acc = B.RidgeAccumulator(6, 4)
+    acc.add(x, y)
+    sxx, sxy, sx, sy, n = acc.sums()
+    ref = oracle.RidgeSums(6, 4)
+    ref.add(x.astype(np.float64), y.astype(np.float64))
+    assert n == 50
+    for a, b in ((sxx, ref.sxx), (sxy, ref.sxy), (sx, ref.sx), (sy, ref.sy)):
+        assert np.allclose(a, b, rtol=1e-12, atol=1e-9)
+    assert np.array_equal(sxx, sxx.T)
