@@ -18,21 +18,26 @@
 // the stores therefore all stay inside one lane.
 //
 // Operand tiles stream global -> LDS with global_load_lds_dwordx4 (no VGPR
-// staging) through a ring of kStages stages of 32 contraction columns (32 KB
-// each, 160 KB of LDS in all), so kStages - 1 stages of loads are in flight
-// while one is consumed.  Within a stage the MFMA operand fragments of the next
-// 16-column slice are read into a second register set while the current
-// slice's MFMAs run, and the one workgroup barrier per stage sits between the
-// two slices, where the MFMA pipe still has the first slice queued.  The
-// barrier is issued without a memory fence: the fence would make every wave
-// wait for all in-flight prefetches.  Each wave instead waits (vmcnt) for its
-// own loads of the next stage only; the barrier then publishes them.
+// staging) in stages of 64 contraction columns, so every operand row of a
+// stage is one full 128-byte line (one L2 request per row per stage; 32-column
+// stages fetched half lines and cost the texture path about 14% of the map
+// contraction's speed).  The 160 KB of LDS is a ring of five 32 KB slots, each
+// holding one operand (256 rows x 128 bytes) of one stage, so about one and a
+// half stages of loads are in flight while one is consumed.  Within a stage
+// the MFMA operand fragments of the next 16-column slice are read into a
+// second register set while the current slice's MFMAs run.  The one
+// workgroup barrier per stage sits before the last slice, where the MFMA pipe
+// still has the third slice queued; it is issued without a memory fence (the
+// fence would make every wave wait for all in-flight prefetches).  Each wave
+// instead waits (vmcnt) for its own loads of the next stage only; the barrier
+// then publishes them and frees the two slots just consumed.
 //
-// LDS rows are 64 bytes (32 bf16).  gfx950's LDS has 64 banks (256 bytes per
-// cycle, 16 lanes of a 16-byte read per pass), so the 16-byte chunk c of row r
-// is stored at chunk position c ^ ((r >> 2) & 3): the 16 rows one pass reads
-// then cover all 64 banks.  The epilogue reuses the LDS as a 256x256 bf16
-// staging tile so that every global store is a 16-byte, row-contiguous write.
+// LDS slot rows are 128 bytes (64 bf16).  gfx950's LDS has 64 banks (256
+// bytes per cycle, 16 lanes of a 16-byte read per pass), so the 16-byte chunk c
+// of row r is stored at chunk position c ^ ((r >> 1) & 7): the 16 rows one
+// pass reads then cover all 64 banks.  The epilogue reuses the LDS as a
+// 256x256 bf16 staging tile so that every global store is a 16-byte,
+// row-contiguous write.
 //
 // Reduction order is fixed by the tile shape alone (no split-K, no atomics on
 // values), so results are bitwise reproducible and independent of which other
@@ -53,20 +58,17 @@ typedef __attribute__((address_space(3))) void lds_ptr_t;
 typedef const __attribute__((address_space(1))) void gbl_ptr_t;
 
 constexpr int kThreads = 256;
-constexpr int kBK = 32;                               // contraction columns per stage
-constexpr int kStages = 5;
-constexpr int kRowBytes = kBK * 2;                    // 64 B per LDS row
-constexpr int kOperandBytes = 256 * kRowBytes;        // 16 KB per operand tile
-constexpr int kStageBytes = 2 * kOperandBytes;        // 32 KB
-constexpr int kLoadsPerStage = 8;                     // global_load_lds per wave per stage
+constexpr int kBK = 64;                               // contraction columns per stage
+constexpr int kRing = 5;                              // LDS slots, one operand of one stage each
+constexpr int kRowBytes = kBK * 2;                    // 128 B per slot row
+constexpr int kSlotBytes = 256 * kRowBytes;           // 32 KB
+constexpr int kLoadsPerSlot = 8;                      // global_load_lds per wave per slot
 constexpr int kStageRowBytes = kTileN * 2;            // 512 B per staged output row
 constexpr int kStagingBytes = kTileM * kStageRowBytes;  // 128 KB
 constexpr int kSlotOffset = kStagingBytes;            // 256 int32 slot ids after the staging tile
-constexpr int kLdsBytes = (kStages * kStageBytes > kStagingBytes + 1024) ? kStages * kStageBytes
-                                                                         : kStagingBytes + 1024;
+constexpr int kLdsBytes = (kRing * kSlotBytes > kStagingBytes + 1024) ? kRing * kSlotBytes : kStagingBytes + 1024;
 static_assert(kTileK % kBK == 0, "host contraction granule must be a multiple of the stage depth");
 static_assert(kLdsBytes <= 160 * 1024, "LDS budget of gfx950");
-static_assert(kStages >= 3 && kStages <= 5, "wait_loads covers 0..3 stages in flight");
 
 __device__ __forceinline__ float bf16_to_f32(uint16_t b) {
   return __uint_as_float(static_cast<uint32_t>(b) << 16);
@@ -111,47 +113,49 @@ __device__ __forceinline__ TileCoord tile_coord(int t, int tiles_m, int tiles_n)
   return c;
 }
 
-// Wait until at most `groups` stages of this wave's loads are still in flight
+// Wait until at most `slots` slots of this wave's loads are still in flight
 // (loads complete in issue order for the vmcnt counter).
-__device__ __forceinline__ void wait_loads(int groups) {
-  switch (groups) {
+__device__ __forceinline__ void wait_slots(int slots) {
+  switch (slots) {
     case 0: asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); break;
     case 1: asm volatile("s_waitcnt vmcnt(8)" ::: "memory"); break;
-    case 2: asm volatile("s_waitcnt vmcnt(16)" ::: "memory"); break;
-    default: asm volatile("s_waitcnt vmcnt(24)" ::: "memory"); break;
+    default: asm volatile("s_waitcnt vmcnt(16)" ::: "memory"); break;
   }
 }
-static_assert(kLoadsPerStage == 8, "wait_loads immediates assume 8 loads per stage");
+static_assert(kLoadsPerSlot == 8, "wait_slots immediates assume 8 loads per slot");
 
 // Workgroup barrier without a memory fence (see the file comment).  The
 // "memory" clobber keeps the compiler from moving LDS accesses across it; the
 // hardware ordering the loop relies on is stated where it is used.
 __device__ __forceinline__ void barrier() { asm volatile("s_barrier" ::: "memory"); }
 
-// One stage (32 contraction columns) of both operand tiles for this wave:
-// 16 rows per instruction, 4 instructions per operand.  src[j] points at this
-// lane's 16-byte chunk of column block 0; instruction j of wave w writes LDS
-// bytes [(4w + j) KB, +1 KB) of its operand tile and lane i lands at + 16 i
-// (row 16 (4w + j) + i / 4, chunk position i % 4).
-__device__ __forceinline__ void issue_stage(const char* const (&wsrc)[4], const char* const (&xsrc)[4],
-                                            size_t kbyte, char* wdst, char* xdst) {
+// LDS position of 16-byte chunk c (0..7) of slot row r.
+__device__ __forceinline__ int slot_pos(int r, int c) { return r * kRowBytes + ((c ^ ((r >> 1) & 7)) << 4); }
+
+// The 8 loads of one slot (one operand of one stage) for this wave:
+// instruction j covers slot rows 64 w + 8 j .. + 7 and lane i lands at LDS byte
+// 1 KB * (8 w + j) + 16 i, i.e. row 64 w + 8 j + i / 8, position i % 8.  src[j]
+// points at that lane's chunk of column block 0 (see load_chunk).
+__device__ __forceinline__ void issue_slot(const char* const (&src)[8], size_t kbyte, char* dst) {
 #pragma unroll
-  for (int j = 0; j < 4; ++j)
-    __builtin_amdgcn_global_load_lds((gbl_ptr_t*)(wsrc[j] + kbyte), (lds_ptr_t*)(wdst + j * 1024), 16, 0, 0);
-#pragma unroll
-  for (int j = 0; j < 4; ++j)
-    __builtin_amdgcn_global_load_lds((gbl_ptr_t*)(xsrc[j] + kbyte), (lds_ptr_t*)(xdst + j * 1024), 16, 0, 0);
+  for (int j = 0; j < kLoadsPerSlot; ++j)
+    __builtin_amdgcn_global_load_lds((gbl_ptr_t*)(src[j] + kbyte), (lds_ptr_t*)(dst + j * 1024), 16, 0, 0);
 }
+
+// Column chunk a lane fetches for instruction j: position i % 8 of row
+// 64 w + 8 j + i / 8 holds chunk (i % 8) ^ ((row >> 1) & 7).  The 8 lanes of a
+// row fetch its 8 chunks, one whole 128-byte line.
+__device__ __forceinline__ int load_chunk(int lane, int j) { return (lane & 7) ^ ((4 * j + (lane >> 4)) & 7); }
 
 struct Frags {
   bf16x8 a[4], b[4];
 };
 
-__device__ __forceinline__ void read_frags(Frags& f, const char* st, int aoff, int boff) {
+__device__ __forceinline__ void read_frags(Frags& f, const char* ws, const char* xs, int aoff, int boff) {
 #pragma unroll
-  for (int i = 0; i < 4; ++i) f.a[i] = *reinterpret_cast<const bf16x8*>(st + aoff + i * 32 * kRowBytes);
+  for (int i = 0; i < 4; ++i) f.a[i] = *reinterpret_cast<const bf16x8*>(ws + aoff + i * 32 * kRowBytes);
 #pragma unroll
-  for (int i = 0; i < 4; ++i) f.b[i] = *reinterpret_cast<const bf16x8*>(st + boff + i * 32 * kRowBytes);
+  for (int i = 0; i < 4; ++i) f.b[i] = *reinterpret_cast<const bf16x8*>(xs + boff + i * 32 * kRowBytes);
 }
 
 template <bool SUMSQ>
@@ -176,33 +180,101 @@ __device__ __forceinline__ void mma_slice(const Frags& f, f32x16 (&acc)[4][4], f
       acc[nb][mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.a[nb], f.b[mb], acc[nb][mb], 0, 0, 0);
 }
 
-// Main loop shared by both contractions.  On return acc[nb][mb] holds the
-// 32x32 block (features nb, rows mb) of this wave and, with SUMSQ, ss[mb] the
-// sum of squares of this lane's half of the contraction for row mb.  The
-// contraction runs in ascending 16-column slices, which fixes the order of
-// every sum.
+__device__ __forceinline__ int ring(int s) { return s >= kRing ? s - kRing : s; }
+
+// One stage t, reading slots sw (weights) and sw + 1 (data rows), that ends by
+// publishing stage t+1.  Slot sequence number u = 0, 1, 2, ... is the weights
+// of stage u / 2 (even u) or its data rows (odd u), in ring slot u % 5.
+//   PEND : during slice 0, load u = 2t+4 (weights of stage t+2) into slot
+//          sw + 4, free since the barrier that opened stage t;
+//   ISSUE: during slice 3, after the barrier, load u = 2t+5 (data rows of
+//          stage t+2) into slot sw, free once every wave has passed it;
+//   WAIT : slots this wave may still have in flight at the barrier (stage t+1
+//          needs u <= 2t+3 landed; u = 2t+4 may still fly).
+// The sched_group_barrier runs pin one fragment read or one load after each
+// MFMA of a slice.
+template <bool SUMSQ, bool PEND, bool ISSUE, int WAIT>
+__device__ __forceinline__ void stage(Frags& fa, Frags& fb, f32x16 (&acc)[4][4], float (&ss)[4], int& sw, int t,
+                                      char* smem, char* mydst, const char* const (&wsrc)[8],
+                                      const char* const (&xsrc)[8], const int (&aoff)[4], const int (&boff)[4]) {
+  const char* ws = smem + sw * kSlotBytes;
+  const char* xs = smem + ring(sw + 1) * kSlotBytes;
+  read_frags(fb, ws, xs, aoff[1], boff[1]);
+  if (PEND) issue_slot(wsrc, static_cast<size_t>(t + 2) * kRowBytes, mydst + ring(sw + 4) * kSlotBytes);
+  mma_slice<SUMSQ>(fa, acc, ss);
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
+    __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // DS read
+  }
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+    if (PEND) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);  // VMEM read (LDS DMA)
+  }
+  __builtin_amdgcn_sched_barrier(0);
+  read_frags(fa, ws, xs, aoff[2], boff[2]);
+  mma_slice<SUMSQ>(fb, acc, ss);
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 1);
+    __builtin_amdgcn_sched_group_barrier(0x100, 1, 1);
+  }
+  __builtin_amdgcn_sched_group_barrier(0x008, 8, 1);
+  __builtin_amdgcn_sched_barrier(0);
+  read_frags(fb, ws, xs, aoff[3], boff[3]);
+  mma_slice<SUMSQ>(fa, acc, ss);
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 2);
+    __builtin_amdgcn_sched_group_barrier(0x100, 1, 2);
+  }
+  __builtin_amdgcn_sched_group_barrier(0x008, 8, 2);
+  __builtin_amdgcn_sched_barrier(0);
+  wait_slots(WAIT);
+  barrier();
+  __builtin_amdgcn_sched_barrier(0);
+  const int nsw = ring(sw + 2);
+  read_frags(fa, smem + nsw * kSlotBytes, smem + ring(nsw + 1) * kSlotBytes, aoff[0], boff[0]);
+  if (ISSUE) issue_slot(xsrc, static_cast<size_t>(t + 2) * kRowBytes, mydst + sw * kSlotBytes);
+  mma_slice<SUMSQ>(fb, acc, ss);
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 3);
+    __builtin_amdgcn_sched_group_barrier(0x100, 1, 3);
+  }
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 3);
+    if (ISSUE) __builtin_amdgcn_sched_group_barrier(0x020, 1, 3);
+  }
+  __builtin_amdgcn_sched_barrier(0);
+  sw = nsw;
+}
+
+// Main loop shared by both contractions over nk stages of 64 columns.  On
+// return acc[nb][mb] holds the 32x32 block (features nb, rows mb) of this wave
+// and, with SUMSQ, ss[mb] the sum of squares of this lane's half of the
+// contraction for row mb.  The contraction runs in ascending 16-column slices,
+// which fixes the order of every sum.
 template <bool SUMSQ>
-__device__ __forceinline__ void mainloop(const char* const (&wsrc)[4], const char* const (&xsrc)[4], int nk,
+__device__ __forceinline__ void mainloop(const char* const (&wsrc)[8], const char* const (&xsrc)[8], int nk,
                                          char* smem, f32x16 (&acc)[4][4], float (&ss)[4]) {
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int wn = wave & 1, wm = wave >> 1;
   const int r31 = lane & 31, hsel = lane >> 5;
+  char* const mydst = smem + wave * kLoadsPerSlot * 1024;
 
-  char* const wdst = smem + wave * 4 * 1024;
-  char* const xdst = smem + kOperandBytes + wave * 4 * 1024;
-
-  // Fragment offsets inside a stage.  Row r of a 32-row block is lane & 31;
-  // its 16-byte chunk for slice kk is 2 kk + (lane >> 5), stored at position
-  // chunk ^ ((r >> 2) & 3).
-  int aoff[2], boff[2];
+  // Fragment offsets inside a slot.  Row r of a 32-row block is lane & 31;
+  // its 16-byte chunk for slice kk is 2 kk + (lane >> 5); 32-row blocks are
+  // 4 KB apart and share the chunk permutation.
+  int aoff[4], boff[4];
 #pragma unroll
-  for (int kk = 0; kk < 2; ++kk) {
-    const int pos = ((2 * kk + hsel) ^ ((r31 >> 2) & 3)) << 4;
-    aoff[kk] = (wn * 128 + r31) * kRowBytes + pos;
-    boff[kk] = kOperandBytes + (wm * 128 + r31) * kRowBytes + pos;
+  for (int kk = 0; kk < 4; ++kk) {
+    aoff[kk] = slot_pos(wn * 128 + r31, 2 * kk + hsel);
+    boff[kk] = slot_pos(wm * 128 + r31, 2 * kk + hsel);
   }
-
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     ss[i] = 0.0f;
@@ -210,82 +282,35 @@ __device__ __forceinline__ void mainloop(const char* const (&wsrc)[4], const cha
     for (int j = 0; j < 4; ++j) acc[i][j] = f32x16{};
   }
 
-  // Prologue: stages 0 .. kStages-2 in flight, wait for stage 0.
+  // Prologue: slots u = 0 .. 3 (stages 0 and 1), wait for stage 0.
+  const int total = 2 * nk;
 #pragma unroll
-  for (int s = 0; s < kStages - 1; ++s)
-    if (s < nk)
-      issue_stage(wsrc, xsrc, static_cast<size_t>(s) * kRowBytes, wdst + s * kStageBytes, xdst + s * kStageBytes);
-  wait_loads(min(kStages - 2, nk - 1));
+  for (int u = 0; u < 4; ++u)
+    if (u < total)
+      issue_slot((u & 1) ? xsrc : wsrc, static_cast<size_t>(u >> 1) * kRowBytes, mydst + u * kSlotBytes);
+  wait_slots(min(4, total) - 2);
   barrier();
-
-  // Step t reads stage slot t % kStages.  In step t: slice 0's MFMAs run
-  // while slice 1's fragments are read; then each wave waits for its own
-  // loads of step t+1 and the barrier publishes them (it also proves every
-  // wave has consumed step t-1, whose slot takes the loads of step
-  // t + kStages - 1); slice 1's MFMAs then run while those loads are issued
-  // and the fragments of step t+1's slice 0 are read.
   Frags fa, fb;
-  read_frags(fa, smem, aoff[0], boff[0]);
-  int t = 0, cur = 0;
-  auto next_slot = [](int s) { return (s + 1 == kStages) ? 0 : s + 1; };
-  // steady state: loads still to issue
-  for (; t + kStages - 1 < nk; ++t) {
-    const int nxt = next_slot(cur);
-    const int fill = (cur == 0) ? kStages - 1 : cur - 1;
-    // slice 0: MFMAs on fa, one fragment read of slice 1 after each of the first 8
-    read_frags(fb, smem + cur * kStageBytes, aoff[1], boff[1]);
-    mma_slice<SUMSQ>(fa, acc, ss);
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
-      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // DS read
-    }
-    __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);
-    __builtin_amdgcn_sched_barrier(0);
-    wait_loads(kStages - 3);
-    barrier();
-    __builtin_amdgcn_sched_barrier(0);
-    // slice 1: MFMAs on fb, interleaved with the reads of step t+1's slice 0
-    // and the loads of step t + kStages - 1
-    read_frags(fa, smem + nxt * kStageBytes, aoff[0], boff[0]);
-    issue_stage(wsrc, xsrc, static_cast<size_t>(t + kStages - 1) * kRowBytes, wdst + fill * kStageBytes,
-                xdst + fill * kStageBytes);
-    mma_slice<SUMSQ>(fb, acc, ss);
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 1);  // MFMA
-      __builtin_amdgcn_sched_group_barrier(0x100, 1, 1);  // DS read
-    }
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 1);  // MFMA
-      __builtin_amdgcn_sched_group_barrier(0x020, 1, 1);  // VMEM read (LDS DMA)
-    }
-    __builtin_amdgcn_sched_barrier(0);
-    cur = nxt;
+  int sw = 0;
+  read_frags(fa, smem, smem + kSlotBytes, aoff[0], boff[0]);
+  int t = 0;
+  // At the barrier of stage t this wave has issued u <= 2t+4.
+  for (; t + 3 <= nk; ++t) stage<SUMSQ, true, true, 1>(fa, fb, acc, ss, sw, t, smem, mydst, wsrc, xsrc, aoff, boff);
+  if (t + 2 == nk) {
+    stage<SUMSQ, false, false, 0>(fa, fb, acc, ss, sw, t, smem, mydst, wsrc, xsrc, aoff, boff);
+    ++t;
   }
-  // drain: every load issued; t + 1 < nk
-  for (; t + 1 < nk; ++t) {
-    const int nxt = next_slot(cur);
-    read_frags(fb, smem + cur * kStageBytes, aoff[1], boff[1]);
-    mma_slice<SUMSQ>(fa, acc, ss);
-    wait_loads(nk - 2 - t);
-    barrier();
-    read_frags(fa, smem + nxt * kStageBytes, aoff[0], boff[0]);
-    mma_slice<SUMSQ>(fb, acc, ss);
-    cur = nxt;
-  }
-  // last step
-  read_frags(fb, smem + cur * kStageBytes, aoff[1], boff[1]);
+  // last stage: nothing left to publish
+  const char* ws = smem + sw * kSlotBytes;
+  const char* xs = smem + ring(sw + 1) * kSlotBytes;
+  read_frags(fb, ws, xs, aoff[1], boff[1]);
+  mma_slice<SUMSQ>(fa, acc, ss);
+  read_frags(fa, ws, xs, aoff[2], boff[2]);
+  mma_slice<SUMSQ>(fb, acc, ss);
+  read_frags(fb, ws, xs, aoff[3], boff[3]);
   mma_slice<SUMSQ>(fa, acc, ss);
   mma_slice<SUMSQ>(fb, acc, ss);
 }
-
-// Per-lane source pointers for the 4 load instructions of one operand.  Local
-// row of instruction j is wave * 64 + j * 16 + lane / 4; its LDS chunk
-// position is lane % 4, which holds column chunk (lane % 4) ^ ((row >> 2) & 3)
-// = (lane % 4) ^ ((lane >> 4) & 3).
-__device__ __forceinline__ int load_chunk(int lane) { return (lane & 3) ^ ((lane >> 4) & 3); }
 
 // The staging tile: row r (0..255) of 512 bytes, 16-byte chunk c stored at
 // chunk position c ^ (r & 31).
@@ -301,15 +326,15 @@ __global__ void __launch_bounds__(kThreads) map_gemm_kernel(const MapParams p) {
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
 
-  const char* wsrc[4];
-  const char* xsrc[4];
+  const char* wsrc[8];
+  const char* xsrc[8];
   {
-    const int chunk = load_chunk(lane);
     const char* abase = reinterpret_cast<const char*>(p.a[c.g]);
     const char* xbase = reinterpret_cast<const char*>(p.x);
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int lr = wave * 64 + j * 16 + (lane >> 2);
+    for (int j = 0; j < 8; ++j) {
+      const int lr = wave * 64 + j * 8 + (lane >> 3);
+      const int chunk = load_chunk(lane, j);
       wsrc[j] = abase + (static_cast<size_t>(n0 + lr) * p.K + chunk * 8) * 2;
       int m = min(m0 + lr, p.M - 1);
       int row = p.rows[m];
@@ -372,15 +397,15 @@ __global__ void __launch_bounds__(kThreads) kv_gemm_kernel(const KvParams p) {
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
 
-  const char* wsrc[4];
-  const char* xsrc[4];
+  const char* wsrc[8];
+  const char* xsrc[8];
   {
-    const int chunk = load_chunk(lane);
     const char* wbase = reinterpret_cast<const char*>(p.wkv + static_cast<size_t>(c.g) * 2 * p.w * p.K);
     const char* xbase = reinterpret_cast<const char*>(p.in[c.g]);
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int lr = wave * 64 + j * 16 + (lane >> 2);
+    for (int j = 0; j < 8; ++j) {
+      const int lr = wave * 64 + j * 8 + (lane >> 3);
+      const int chunk = load_chunk(lane, j);
       wsrc[j] = wbase + (static_cast<size_t>(n0 + lr) * p.K + chunk * 8) * 2;
       const int m = min(m0 + lr, p.M - 1);
       int row = p.in_rows ? p.in_rows[m] : m;
