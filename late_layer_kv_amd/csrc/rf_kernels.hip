@@ -158,19 +158,24 @@ __device__ __forceinline__ void read_frags(Frags& f, const char* ws, const char*
   for (int i = 0; i < 4; ++i) f.b[i] = *reinterpret_cast<const bf16x8*>(xs + boff + i * 32 * kRowBytes);
 }
 
-template <bool SUMSQ>
+template <bool SUMSQ, int HALF = 0>
 __device__ __forceinline__ void mma_slice(const Frags& f, f32x16 (&acc)[4][4], float (&ss)[4]) {
   if constexpr (SUMSQ) {
+    // The two waves that share a row block split its sums: wave column HALF
+    // sums row blocks 2 HALF and 2 HALF + 1 (ss[0..1]); the epilogue swaps halves.
+    constexpr int half = HALF;
 #pragma unroll
-    for (int mb = 0; mb < 4; ++mb) {
-      ss[mb] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(f.b[mb], f.b[mb], 0, 1),
-                                               __builtin_shufflevector(f.b[mb], f.b[mb], 0, 1), ss[mb], false);
-      ss[mb] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(f.b[mb], f.b[mb], 2, 3),
-                                               __builtin_shufflevector(f.b[mb], f.b[mb], 2, 3), ss[mb], false);
-      ss[mb] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(f.b[mb], f.b[mb], 4, 5),
-                                               __builtin_shufflevector(f.b[mb], f.b[mb], 4, 5), ss[mb], false);
-      ss[mb] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(f.b[mb], f.b[mb], 6, 7),
-                                               __builtin_shufflevector(f.b[mb], f.b[mb], 6, 7), ss[mb], false);
+    for (int j = 0; j < 2; ++j) {
+      const int mb = 2 * half + j;
+      float& s_ = ss[j];
+      s_ = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(f.b[mb], f.b[mb], 0, 1),
+                                           __builtin_shufflevector(f.b[mb], f.b[mb], 0, 1), s_, false);
+      s_ = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(f.b[mb], f.b[mb], 2, 3),
+                                           __builtin_shufflevector(f.b[mb], f.b[mb], 2, 3), s_, false);
+      s_ = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(f.b[mb], f.b[mb], 4, 5),
+                                           __builtin_shufflevector(f.b[mb], f.b[mb], 4, 5), s_, false);
+      s_ = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(f.b[mb], f.b[mb], 6, 7),
+                                           __builtin_shufflevector(f.b[mb], f.b[mb], 6, 7), s_, false);
     }
   }
 #pragma unroll
@@ -193,7 +198,7 @@ __device__ __forceinline__ int ring(int s) { return s >= kRing ? s - kRing : s; 
 //          needs u <= 2t+3 landed; u = 2t+4 may still fly).
 // The sched_group_barrier runs pin one fragment read or one load after each
 // MFMA of a slice.
-template <bool SUMSQ, bool PEND, bool ISSUE, int WAIT>
+template <bool SUMSQ, int HALF, bool PEND, bool ISSUE, int WAIT>
 __device__ __forceinline__ void stage(Frags& fa, Frags& fb, f32x16 (&acc)[4][4], float (&ss)[4], int& sw, int t,
                                       char* smem, char* mydst, const char* const (&wsrc)[8],
                                       const char* const (&xsrc)[8], const int (&aoff)[4], const int (&boff)[4]) {
@@ -201,7 +206,7 @@ __device__ __forceinline__ void stage(Frags& fa, Frags& fb, f32x16 (&acc)[4][4],
   const char* xs = smem + ring(sw + 1) * kSlotBytes;
   read_frags(fb, ws, xs, aoff[1], boff[1]);
   if (PEND) issue_slot(wsrc, static_cast<size_t>(t + 2) * kRowBytes, mydst + ring(sw + 4) * kSlotBytes);
-  mma_slice<SUMSQ>(fa, acc, ss);
+  mma_slice<SUMSQ, HALF>(fa, acc, ss);
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
     __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
@@ -214,7 +219,7 @@ __device__ __forceinline__ void stage(Frags& fa, Frags& fb, f32x16 (&acc)[4][4],
   }
   __builtin_amdgcn_sched_barrier(0);
   read_frags(fa, ws, xs, aoff[2], boff[2]);
-  mma_slice<SUMSQ>(fb, acc, ss);
+  mma_slice<SUMSQ, HALF>(fb, acc, ss);
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
     __builtin_amdgcn_sched_group_barrier(0x008, 1, 1);
@@ -223,7 +228,7 @@ __device__ __forceinline__ void stage(Frags& fa, Frags& fb, f32x16 (&acc)[4][4],
   __builtin_amdgcn_sched_group_barrier(0x008, 8, 1);
   __builtin_amdgcn_sched_barrier(0);
   read_frags(fb, ws, xs, aoff[3], boff[3]);
-  mma_slice<SUMSQ>(fa, acc, ss);
+  mma_slice<SUMSQ, HALF>(fa, acc, ss);
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
     __builtin_amdgcn_sched_group_barrier(0x008, 1, 2);
@@ -237,7 +242,7 @@ __device__ __forceinline__ void stage(Frags& fa, Frags& fb, f32x16 (&acc)[4][4],
   const int nsw = ring(sw + 2);
   read_frags(fa, smem + nsw * kSlotBytes, smem + ring(nsw + 1) * kSlotBytes, aoff[0], boff[0]);
   if (ISSUE) issue_slot(xsrc, static_cast<size_t>(t + 2) * kRowBytes, mydst + sw * kSlotBytes);
-  mma_slice<SUMSQ>(fb, acc, ss);
+  mma_slice<SUMSQ, HALF>(fb, acc, ss);
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
     __builtin_amdgcn_sched_group_barrier(0x008, 1, 3);
@@ -254,10 +259,11 @@ __device__ __forceinline__ void stage(Frags& fa, Frags& fb, f32x16 (&acc)[4][4],
 
 // Main loop shared by both contractions over nk stages of 64 columns.  On
 // return acc[nb][mb] holds the 32x32 block (features nb, rows mb) of this wave
-// and, with SUMSQ, ss[mb] the sum of squares of this lane's half of the
-// contraction for row mb.  The contraction runs in ascending 16-column slices,
-// which fixes the order of every sum.
-template <bool SUMSQ>
+// and, with SUMSQ, ss[j] (j = 0, 1) the sum of squares of this lane's half of
+// the contraction for row block 2 HALF + j (the wave column HALF = wave & 1
+// picks which two of the four row blocks this wave sums).  The contraction
+// runs in ascending 16-column slices, which fixes the order of every sum.
+template <bool SUMSQ, int HALF = 0>
 __device__ __forceinline__ void mainloop(const char* const (&wsrc)[8], const char* const (&xsrc)[8], int nk,
                                          char* smem, f32x16 (&acc)[4][4], float (&ss)[4]) {
   const int lane = threadIdx.x & 63;
@@ -295,21 +301,21 @@ __device__ __forceinline__ void mainloop(const char* const (&wsrc)[8], const cha
   read_frags(fa, smem, smem + kSlotBytes, aoff[0], boff[0]);
   int t = 0;
   // At the barrier of stage t this wave has issued u <= 2t+4.
-  for (; t + 3 <= nk; ++t) stage<SUMSQ, true, true, 1>(fa, fb, acc, ss, sw, t, smem, mydst, wsrc, xsrc, aoff, boff);
+  for (; t + 3 <= nk; ++t) stage<SUMSQ, HALF, true, true, 1>(fa, fb, acc, ss, sw, t, smem, mydst, wsrc, xsrc, aoff, boff);
   if (t + 2 == nk) {
-    stage<SUMSQ, false, false, 0>(fa, fb, acc, ss, sw, t, smem, mydst, wsrc, xsrc, aoff, boff);
+    stage<SUMSQ, HALF, false, false, 0>(fa, fb, acc, ss, sw, t, smem, mydst, wsrc, xsrc, aoff, boff);
     ++t;
   }
   // last stage: nothing left to publish
   const char* ws = smem + sw * kSlotBytes;
   const char* xs = smem + ring(sw + 1) * kSlotBytes;
   read_frags(fb, ws, xs, aoff[1], boff[1]);
-  mma_slice<SUMSQ>(fa, acc, ss);
+  mma_slice<SUMSQ, HALF>(fa, acc, ss);
   read_frags(fa, ws, xs, aoff[2], boff[2]);
-  mma_slice<SUMSQ>(fb, acc, ss);
+  mma_slice<SUMSQ, HALF>(fb, acc, ss);
   read_frags(fb, ws, xs, aoff[3], boff[3]);
-  mma_slice<SUMSQ>(fa, acc, ss);
-  mma_slice<SUMSQ>(fb, acc, ss);
+  mma_slice<SUMSQ, HALF>(fa, acc, ss);
+  mma_slice<SUMSQ, HALF>(fb, acc, ss);
 }
 
 // The staging tile: row r (0..255) of 512 bytes, 16-byte chunk c stored at
@@ -416,10 +422,28 @@ __global__ void __launch_bounds__(kThreads) kv_gemm_kernel(const KvParams p) {
 
   f32x16 acc[4][4];
   float ss[4];
-  mainloop<true>(wsrc, xsrc, p.K / kBK, smem, acc, ss);
+  // wave-uniform branch: the two waves of a row half each sum two row blocks
+  if ((wave & 1) == 0)
+    mainloop<true, 0>(wsrc, xsrc, p.K / kBK, smem, acc, ss);
+  else
+    mainloop<true, 1>(wsrc, xsrc, p.K / kBK, smem, acc, ss);
 
   const int wn = wave & 1, wm = wave >> 1, r31 = lane & 31, hsel = lane >> 5;
   const float inv_k = 1.0f / static_cast<float>(p.K);
+  // Sums of squares: this wave holds row blocks 2 wn, 2 wn + 1 in ss[0..1];
+  // the other wave of its row half holds the rest.  Full row sums (both lane
+  // halves) are swapped through LDS once every wave is done with the operands.
+  float* const ss_lds = reinterpret_cast<float*>(smem + kSlotOffset + 1024);
+  __syncthreads();
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    const float tot = ss[j] + __shfl_xor(ss[j], 32);
+    if (hsel == 0) ss_lds[wm * 128 + (2 * wn + j) * 32 + r31] = tot;
+  }
+  __syncthreads();
+  float rowss[4];
+#pragma unroll
+  for (int mb = 0; mb < 4; ++mb) rowss[mb] = ss_lds[wm * 128 + mb * 32 + r31];
   const int fw = n0 + wn * 128;  // first feature of this wave; a whole wave is key or value
   // (with v_only, a tile may start inside the keys when w is not a multiple of
   // 256; those key waves are neither rotated nor stored)
@@ -433,8 +457,7 @@ __global__ void __launch_bounds__(kThreads) kv_gemm_kernel(const KvParams p) {
   int pos[4], slot_r[4];
 #pragma unroll
   for (int mb = 0; mb < 4; ++mb) {
-    const float tot = ss[mb] + __shfl_xor(ss[mb], 32);
-    rs[mb] = rsqrtf(tot * inv_k + p.eps);
+    rs[mb] = rsqrtf(rowss[mb] * inv_k + p.eps);
     rs2[mb] = rs[mb];
     const int lr = wm * 128 + mb * 32 + r31;
     const int m = m0 + lr;
@@ -544,7 +567,7 @@ __global__ void __launch_bounds__(kThreads) kv_gemm_kernel(const KvParams p) {
         for (int v = 0; v < 16; ++v) acc[nb][mb][v] *= (HD == 64 && nb >= 2) ? rs2[mb] : rs[mb];
   }
 
-  __syncthreads();  // every wave is done reading the operand stages
+  // (every wave passed its last operand read before the sums were swapped)
   if (wn == 0 && hsel == 0) {
 #pragma unroll
     for (int mb = 0; mb < 4; ++mb) slot_of[wm * 128 + mb * 32 + r31] = slot_r[mb];
