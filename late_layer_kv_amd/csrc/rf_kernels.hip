@@ -54,6 +54,7 @@ namespace {
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) void lds_ptr_t;
 typedef const __attribute__((address_space(1))) void gbl_ptr_t;
 
@@ -318,6 +319,152 @@ __device__ __forceinline__ void mainloop(const char* const (&wsrc)[8], const cha
   mma_slice<SUMSQ, HALF>(fb, acc, ss);
 }
 
+// ---- 16x16x32 variant of the main loop ------------------------------------
+// Same ring, slots, loads and barrier placement; the wave's 128x128 block is
+// 8x8 blocks of v_mfma_f32_16x16x32_bf16.  Under the part's power limit that
+// instruction sustains a higher clock than the 32x32 one for the same work,
+// so it wins at full MFMA load.  A lane owns row (l & 15) of each 16-row block
+// and features 4 (l >> 4) .. + 3 of each 16-feature block.  A stage is two
+// 32-column steps; the fragments of the next step are read into the second
+// register set while the current step's 64 MFMAs run.
+struct Frags16 {
+  bf16x8 a[8], b[8];
+};
+
+__device__ __forceinline__ void read_frags16(Frags16& f, const char* ws, const char* xs, int aoff, int boff) {
+#pragma unroll
+  for (int i = 0; i < 8; ++i) f.a[i] = *reinterpret_cast<const bf16x8*>(ws + aoff + i * 16 * kRowBytes);
+#pragma unroll
+  for (int i = 0; i < 8; ++i) f.b[i] = *reinterpret_cast<const bf16x8*>(xs + boff + i * 16 * kRowBytes);
+}
+
+// One MFMA 16x16x32 accumulating in place.  Written as inline assembly: the
+// compiler's register allocation of the builtin copies accumulators between
+// AGPRs around every instruction at this block count.  The statement is
+// volatile, so memory operations keep their place relative to it and the
+// fragment reads / operand loads below interleave exactly as written.
+__device__ __forceinline__ void mfma16(f32x4& acc, const bf16x8& a, const bf16x8& b) {
+  asm volatile("v_mfma_f32_16x16x32_bf16 %0, %1, %2, %0" : "+a"(acc) : "v"(a), "v"(b));
+}
+
+// Sum of squares of the wave's 4 row blocks 4 HALF .. + 3 (this lane's chunk).
+template <int HALF>
+__device__ __forceinline__ void sumsq16(const Frags16& f, float (&ss)[4]) {
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const bf16x8& b = f.b[4 * HALF + j];
+    float& s_ = ss[j];
+    s_ = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(b, b, 0, 1), __builtin_shufflevector(b, b, 0, 1), s_, false);
+    s_ = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(b, b, 2, 3), __builtin_shufflevector(b, b, 2, 3), s_, false);
+    s_ = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(b, b, 4, 5), __builtin_shufflevector(b, b, 4, 5), s_, false);
+    s_ = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(b, b, 6, 7), __builtin_shufflevector(b, b, 6, 7), s_, false);
+  }
+}
+
+// The 64 MFMAs of one 32-column step on fragments f.  With READ, the 16
+// fragment reads of the next step (into nf, from slots ws / xs) follow MFMAs
+// 0..15 one each; with LOAD, the 8 operand loads of one slot follow every
+// second MFMA from 16 on.
+template <bool READ, bool LOAD>
+__device__ __forceinline__ void mma_step16(const Frags16& f, f32x4 (&acc)[8][8], Frags16& nf, const char* ws,
+                                           const char* xs, int aoff, int boff, const char* const (&src)[8],
+                                           size_t kbyte, char* dst) {
+#pragma unroll
+  for (int i = 0; i < 64; ++i) {
+    const int nb = i >> 3, mb = i & 7;
+    mfma16(acc[nb][mb], f.a[nb], f.b[mb]);
+    if (READ && i < 8) nf.a[i] = *reinterpret_cast<const bf16x8*>(ws + aoff + i * 16 * kRowBytes);
+    if (READ && i >= 8 && i < 16) nf.b[i - 8] = *reinterpret_cast<const bf16x8*>(xs + boff + (i - 8) * 16 * kRowBytes);
+    if (LOAD && i >= 16 && i < 32 && (i & 1) == 0) {
+      const int j = (i - 16) >> 1;
+      __builtin_amdgcn_global_load_lds((gbl_ptr_t*)(src[j] + kbyte), (lds_ptr_t*)(dst + j * 1024), 16, 0, 0);
+    }
+  }
+}
+
+// One stage t on slots sw (weights) and sw + 1 (data rows); the slot sequence
+// and the PEND / ISSUE / WAIT roles are those of stage() above, with the
+// barrier between the two steps: step 0 reads step 1's fragments, step 1 reads
+// the next stage's step 0.
+template <bool SUMSQ, int HALF, bool PEND, bool ISSUE, int WAIT>
+__device__ __forceinline__ void stage16(Frags16& fa, Frags16& fb, f32x4 (&acc)[8][8], float (&ss)[4], int& sw, int t,
+                                        char* smem, char* mydst, const char* const (&wsrc)[8],
+                                        const char* const (&xsrc)[8], const int (&aoff)[2], const int (&boff)[2]) {
+  const char* ws = smem + sw * kSlotBytes;
+  const char* xs = smem + ring(sw + 1) * kSlotBytes;
+  if (SUMSQ) sumsq16<HALF>(fa, ss);
+  mma_step16<true, PEND>(fa, acc, fb, ws, xs, aoff[1], boff[1], wsrc, static_cast<size_t>(t + 2) * kRowBytes,
+                         mydst + ring(sw + 4) * kSlotBytes);
+  wait_slots(WAIT);
+  barrier();
+  const int nsw = ring(sw + 2);
+  if (SUMSQ) sumsq16<HALF>(fb, ss);
+  mma_step16<true, ISSUE>(fb, acc, fa, smem + nsw * kSlotBytes, smem + ring(nsw + 1) * kSlotBytes, aoff[0], boff[0],
+                          xsrc, static_cast<size_t>(t + 2) * kRowBytes, mydst + sw * kSlotBytes);
+  sw = nsw;
+}
+
+// Main loop over nk stages with 16x16x32 blocks.  On return acc[nb][mb] holds
+// features 16 nb + 4 (l >> 4) + v, row 16 mb + (l & 15) of the wave's block,
+// and with SUMSQ ss[j] this lane's part (its 8-column chunk of every 32) of
+// the sum of squares of row block 4 HALF + j.
+template <bool SUMSQ, int HALF = 0>
+__device__ __forceinline__ void mainloop16(const char* const (&wsrc)[8], const char* const (&xsrc)[8], int nk,
+                                           char* smem, f32x4 (&acc)[8][8], float (&ss)[4]) {
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int wn = wave & 1, wm = wave >> 1;
+  const int r15 = lane & 15, q = lane >> 4;
+  char* const mydst = smem + wave * kLoadsPerSlot * 1024;
+  // Row r of a 16-row block is lane & 15, its chunk for step s is 4 s + q;
+  // 16-row blocks are 2 KB apart and share the chunk permutation.
+  int aoff[2], boff[2];
+#pragma unroll
+  for (int st = 0; st < 2; ++st) {
+    aoff[st] = slot_pos(wn * 128 + r15, 4 * st + q);
+    boff[st] = slot_pos(wm * 128 + r15, 4 * st + q);
+  }
+#pragma unroll
+  for (int i = 0; i < 4; ++i) ss[i] = 0.0f;
+#pragma unroll
+  for (int i = 0; i < 8; ++i)
+#pragma unroll
+    for (int j = 0; j < 8; ++j) acc[i][j] = f32x4{};
+  // accumulator writes land before the first MFMA reads them
+  __builtin_amdgcn_sched_barrier(0);
+  asm volatile("s_nop 4" ::: "memory");
+  __builtin_amdgcn_sched_barrier(0);
+
+  const int total = 2 * nk;
+#pragma unroll
+  for (int u = 0; u < 4; ++u)
+    if (u < total)
+      issue_slot((u & 1) ? xsrc : wsrc, static_cast<size_t>(u >> 1) * kRowBytes, mydst + u * kSlotBytes);
+  wait_slots(min(4, total) - 2);
+  barrier();
+  Frags16 fa, fb;
+  int sw = 0;
+  read_frags16(fa, smem, smem + kSlotBytes, aoff[0], boff[0]);
+  int t = 0;
+  for (; t + 3 <= nk; ++t) stage16<SUMSQ, HALF, true, true, 1>(fa, fb, acc, ss, sw, t, smem, mydst, wsrc, xsrc, aoff, boff);
+  if (t + 2 == nk) {
+    stage16<SUMSQ, HALF, false, false, 0>(fa, fb, acc, ss, sw, t, smem, mydst, wsrc, xsrc, aoff, boff);
+    ++t;
+  }
+  const char* ws = smem + sw * kSlotBytes;
+  const char* xs = smem + ring(sw + 1) * kSlotBytes;
+  if (SUMSQ) sumsq16<HALF>(fa, ss);
+  mma_step16<true, false>(fa, acc, fb, ws, xs, aoff[1], boff[1], wsrc, 0, mydst);
+  if (SUMSQ) sumsq16<HALF>(fb, ss);
+  mma_step16<false, false>(fb, acc, fa, ws, xs, 0, 0, wsrc, 0, mydst);
+  // The compiler does not see the MFMAs in the assembly statements: give the
+  // last ones the wait states an MFMA result needs before other instructions
+  // read its registers (nothing may be scheduled across the nops).
+  __builtin_amdgcn_sched_barrier(0);
+  asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory");
+  __builtin_amdgcn_sched_barrier(0);
+}
+
 // The staging tile: row r (0..255) of 512 bytes, 16-byte chunk c stored at
 // chunk position c ^ (r & 31).
 __device__ __forceinline__ int stage_off(int row, int chunk) {
@@ -349,31 +496,29 @@ __global__ void __launch_bounds__(kThreads) map_gemm_kernel(const MapParams p) {
     }
   }
 
-  f32x16 acc[4][4];
+  f32x4 acc[8][8];
   float ss[4];
-  mainloop<false>(wsrc, xsrc, p.K / kBK, smem, acc, ss);
+  mainloop16<false>(wsrc, xsrc, p.K / kBK, smem, acc, ss);
 
-  // Epilogue: + b, round to bf16, stage, 16-byte row stores into Y_g.
-  const int wn = wave & 1, wm = wave >> 1, r31 = lane & 31, hsel = lane >> 5;
-  const uint16_t* bias = p.b[c.g] + n0 + wn * 128 + hsel * 4;
+  // Epilogue: + b, round to bf16, stage, 16-byte row stores into Y_g.  A lane
+  // holds 4 consecutive features (8 bytes, one half of a staged chunk) of a row.
+  const int wn = wave & 1, wm = wave >> 1, r15 = lane & 15, q = lane >> 4;
+  const uint16_t* bias = p.b[c.g] + n0 + wn * 128 + q * 4;
   __syncthreads();  // every wave is done reading the operand stages
 #pragma unroll
-  for (int nb = 0; nb < 4; ++nb) {
+  for (int nb = 0; nb < 8; ++nb) {
+    const uint2 braw = *reinterpret_cast<const uint2*>(bias + nb * 16);
+    const float b0 = bf16_to_f32(braw.x & 0xffff), b1 = bf16_to_f32(braw.x >> 16);
+    const float b2 = bf16_to_f32(braw.y & 0xffff), b3 = bf16_to_f32(braw.y >> 16);
+    const int chunk = wn * 16 + nb * 2 + (q >> 1);
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const uint2 braw = *reinterpret_cast<const uint2*>(bias + nb * 32 + q * 8);
-      const float b0 = bf16_to_f32(braw.x & 0xffff), b1 = bf16_to_f32(braw.x >> 16);
-      const float b2 = bf16_to_f32(braw.y & 0xffff), b3 = bf16_to_f32(braw.y >> 16);
-      const int chunk = wn * 16 + nb * 4 + q;
-#pragma unroll
-      for (int mb = 0; mb < 4; ++mb) {
-        const int row = wm * 128 + mb * 32 + r31;
-        const f32x16& v = acc[nb][mb];
-        uint2 o;
-        o.x = pack_bf16x2(v[q * 4 + 0] + b0, v[q * 4 + 1] + b1);
-        o.y = pack_bf16x2(v[q * 4 + 2] + b2, v[q * 4 + 3] + b3);
-        *reinterpret_cast<uint2*>(smem + stage_off(row, chunk) + hsel * 8) = o;
-      }
+    for (int mb = 0; mb < 8; ++mb) {
+      const int row = wm * 128 + mb * 16 + r15;
+      const f32x4& v = acc[nb][mb];
+      uint2 o;
+      o.x = pack_bf16x2(v[0] + b0, v[1] + b1);
+      o.y = pack_bf16x2(v[2] + b2, v[3] + b3);
+      *reinterpret_cast<uint2*>(smem + stage_off(row, chunk) + (q & 1) * 8) = o;
     }
   }
   __syncthreads();
