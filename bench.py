@@ -107,7 +107,12 @@ def summarize_pmc(fetch_csv: str, write_csv: str, name: str, calib_bytes: int) -
                                 "fetch_factor": kf, "write_factor": kw},
            "kernels": {k: {"fetch_kib_per_launch": f[k], "write_kib_per_launch": w.get(k),
                            "bytes_per_launch": f[k] * 1024 * kf + w.get(k, 0.0) * 1024 * kw} for k in f},
-           "source": {"fetch_csv": fetch_csv, "write_csv": write_csv}}
+           "source": {pmc: ("cd /tmp && export TMPDIR=/tmp && rocprofv3 --pmc " + pmc + " -f csv -d <out>/" + pmc.split("_")[0].lower()
+                            + " -o " + pmc.split("_")[0].lower() + " -- python3 <repo>/bench.py --workload " + name
+                            + " --steps 1 --warmup 1 --no-cpu-baseline --calibrate-copy " + str(calib_bytes >> 20))
+                      for pmc in ("FETCH_SIZE", "WRITE_SIZE")}}
+    out["source"]["summary"] = (f"python bench.py --workload {name} --pmc-summary <out>/fetch/fetch_counter_collection.csv "
+                                f"<out>/write/write_counter_collection.csv {calib_bytes >> 20}")
     out["traffic_bytes_per_launch"] = out["kernels"]["map_gemm"]["bytes_per_launch"]
     return out
 

@@ -10,12 +10,20 @@
 //
 // Both use one main loop.  A workgroup of 4 waves owns a 256x256 output tile
 // (256 output features x 256 rows); each wave owns 128 features x 128 rows as
-// 4x4 blocks of v_mfma_f32_32x32x16_bf16.  The weight matrix is the MFMA "A"
+// 8x8 blocks of v_mfma_f32_16x16x32_bf16.  The weight matrix is the MFMA "A"
 // operand and the data rows the "B" operand, so in the accumulator every lane
-// holds whole data rows: lane l owns row (l & 31) of each 32-row block and 16
-// features of each 32-feature block (4 runs of 4 consecutive features).  The
-// RoPE partner of a key feature, the row's norm scale and 4-feature packing for
-// the stores therefore all stay inside one lane.
+// holds whole data rows: lane l owns row (l & 15) of each 16-row block and
+// features 4 (l >> 4) .. + 3 of each 16-feature block.  The RoPE partner of a
+// key feature therefore sits in the same lane and register; a row's norm and
+// QK-norm sums reduce over the four lanes l, l ^ 16, l ^ 32, l ^ 48.
+//
+// Why 16x16x32 rather than 32x32x16: both issue the same flops per cycle,
+// but the part runs power-limited at full MFMA load and the 32x32 form draws
+// more per flop (it moves four times the accumulator data per instruction).
+// In a register-only loop on random bf16 data the 16x16 form held 2.07 GHz
+// and 2.04 PFLOP/s against 1.83 GHz and 1.81 PFLOP/s for the 32x32 form; in
+// these kernels the switch gained 7-10%.  The MFMAs are inline assembly (see
+// mfma16) so their accumulators stay in place.
 //
 // Operand tiles stream global -> LDS with global_load_lds_dwordx4 (no VGPR
 // staging) in stages of 64 contraction columns, so every operand row of a
@@ -24,13 +32,13 @@
 // contraction's speed).  The 160 KB of LDS is a ring of five 32 KB slots, each
 // holding one operand (256 rows x 128 bytes) of one stage, so about one and a
 // half stages of loads are in flight while one is consumed.  Within a stage
-// the MFMA operand fragments of the next 16-column slice are read into a
-// second register set while the current slice's MFMAs run.  The one
-// workgroup barrier per stage sits before the last slice, where the MFMA pipe
-// still has the third slice queued; it is issued without a memory fence (the
-// fence would make every wave wait for all in-flight prefetches).  Each wave
-// instead waits (vmcnt) for its own loads of the next stage only; the barrier
-// then publishes them and frees the two slots just consumed.
+// the MFMA operand fragments of the next 32-column step are read into a
+// second register set while the current step's MFMAs run.  The one
+// workgroup barrier per stage sits between the two steps; it is issued
+// without a memory fence (the fence would make every wave wait for all
+// in-flight prefetches).  Each wave instead waits (vmcnt) for its own loads
+// of the next stage only; the barrier then publishes them and frees the two
+// slots just consumed.
 //
 // LDS slot rows are 128 bytes (64 bf16).  gfx950's LDS has 64 banks (256
 // bytes per cycle, 16 lanes of a 16-byte read per pass), so the 16-byte chunk c
@@ -53,7 +61,6 @@ namespace {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
-typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) void lds_ptr_t;
 typedef const __attribute__((address_space(1))) void gbl_ptr_t;
@@ -148,190 +155,19 @@ __device__ __forceinline__ void issue_slot(const char* const (&src)[8], size_t k
 // row fetch its 8 chunks, one whole 128-byte line.
 __device__ __forceinline__ int load_chunk(int lane, int j) { return (lane & 7) ^ ((4 * j + (lane >> 4)) & 7); }
 
-struct Frags {
-  bf16x8 a[4], b[4];
-};
-
-__device__ __forceinline__ void read_frags(Frags& f, const char* ws, const char* xs, int aoff, int boff) {
-#pragma unroll
-  for (int i = 0; i < 4; ++i) f.a[i] = *reinterpret_cast<const bf16x8*>(ws + aoff + i * 32 * kRowBytes);
-#pragma unroll
-  for (int i = 0; i < 4; ++i) f.b[i] = *reinterpret_cast<const bf16x8*>(xs + boff + i * 32 * kRowBytes);
-}
-
-template <bool SUMSQ, int HALF = 0>
-__device__ __forceinline__ void mma_slice(const Frags& f, f32x16 (&acc)[4][4], float (&ss)[4]) {
-  if constexpr (SUMSQ) {
-    // The two waves that share a row block split its sums: wave column HALF
-    // sums row blocks 2 HALF and 2 HALF + 1 (ss[0..1]); the epilogue swaps halves.
-    constexpr int half = HALF;
-#pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      const int mb = 2 * half + j;
-      float& s_ = ss[j];
-      s_ = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(f.b[mb], f.b[mb], 0, 1),
-                                           __builtin_shufflevector(f.b[mb], f.b[mb], 0, 1), s_, false);
-      s_ = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(f.b[mb], f.b[mb], 2, 3),
-                                           __builtin_shufflevector(f.b[mb], f.b[mb], 2, 3), s_, false);
-      s_ = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(f.b[mb], f.b[mb], 4, 5),
-                                           __builtin_shufflevector(f.b[mb], f.b[mb], 4, 5), s_, false);
-      s_ = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(f.b[mb], f.b[mb], 6, 7),
-                                           __builtin_shufflevector(f.b[mb], f.b[mb], 6, 7), s_, false);
-    }
-  }
-#pragma unroll
-  for (int nb = 0; nb < 4; ++nb)
-#pragma unroll
-    for (int mb = 0; mb < 4; ++mb)
-      acc[nb][mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.a[nb], f.b[mb], acc[nb][mb], 0, 0, 0);
-}
-
 __device__ __forceinline__ int ring(int s) { return s >= kRing ? s - kRing : s; }
 
-// One stage t, reading slots sw (weights) and sw + 1 (data rows), that ends by
-// publishing stage t+1.  Slot sequence number u = 0, 1, 2, ... is the weights
-// of stage u / 2 (even u) or its data rows (odd u), in ring slot u % 5.
-//   PEND : during slice 0, load u = 2t+4 (weights of stage t+2) into slot
-//          sw + 4, free since the barrier that opened stage t;
-//   ISSUE: during slice 3, after the barrier, load u = 2t+5 (data rows of
-//          stage t+2) into slot sw, free once every wave has passed it;
-//   WAIT : slots this wave may still have in flight at the barrier (stage t+1
-//          needs u <= 2t+3 landed; u = 2t+4 may still fly).
-// The sched_group_barrier runs pin one fragment read or one load after each
-// MFMA of a slice.
-template <bool SUMSQ, int HALF, bool PEND, bool ISSUE, int WAIT>
-__device__ __forceinline__ void stage(Frags& fa, Frags& fb, f32x16 (&acc)[4][4], float (&ss)[4], int& sw, int t,
-                                      char* smem, char* mydst, const char* const (&wsrc)[8],
-                                      const char* const (&xsrc)[8], const int (&aoff)[4], const int (&boff)[4]) {
-  const char* ws = smem + sw * kSlotBytes;
-  const char* xs = smem + ring(sw + 1) * kSlotBytes;
-  read_frags(fb, ws, xs, aoff[1], boff[1]);
-  if (PEND) issue_slot(wsrc, static_cast<size_t>(t + 2) * kRowBytes, mydst + ring(sw + 4) * kSlotBytes);
-  mma_slice<SUMSQ, HALF>(fa, acc, ss);
-#pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
-    __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // DS read
-  }
-#pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-    if (PEND) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);  // VMEM read (LDS DMA)
-  }
-  __builtin_amdgcn_sched_barrier(0);
-  read_frags(fa, ws, xs, aoff[2], boff[2]);
-  mma_slice<SUMSQ, HALF>(fb, acc, ss);
-#pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    __builtin_amdgcn_sched_group_barrier(0x008, 1, 1);
-    __builtin_amdgcn_sched_group_barrier(0x100, 1, 1);
-  }
-  __builtin_amdgcn_sched_group_barrier(0x008, 8, 1);
-  __builtin_amdgcn_sched_barrier(0);
-  read_frags(fb, ws, xs, aoff[3], boff[3]);
-  mma_slice<SUMSQ, HALF>(fa, acc, ss);
-#pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    __builtin_amdgcn_sched_group_barrier(0x008, 1, 2);
-    __builtin_amdgcn_sched_group_barrier(0x100, 1, 2);
-  }
-  __builtin_amdgcn_sched_group_barrier(0x008, 8, 2);
-  __builtin_amdgcn_sched_barrier(0);
-  wait_slots(WAIT);
-  barrier();
-  __builtin_amdgcn_sched_barrier(0);
-  const int nsw = ring(sw + 2);
-  read_frags(fa, smem + nsw * kSlotBytes, smem + ring(nsw + 1) * kSlotBytes, aoff[0], boff[0]);
-  if (ISSUE) issue_slot(xsrc, static_cast<size_t>(t + 2) * kRowBytes, mydst + sw * kSlotBytes);
-  mma_slice<SUMSQ, HALF>(fb, acc, ss);
-#pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    __builtin_amdgcn_sched_group_barrier(0x008, 1, 3);
-    __builtin_amdgcn_sched_group_barrier(0x100, 1, 3);
-  }
-#pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    __builtin_amdgcn_sched_group_barrier(0x008, 1, 3);
-    if (ISSUE) __builtin_amdgcn_sched_group_barrier(0x020, 1, 3);
-  }
-  __builtin_amdgcn_sched_barrier(0);
-  sw = nsw;
-}
-
-// Main loop shared by both contractions over nk stages of 64 columns.  On
-// return acc[nb][mb] holds the 32x32 block (features nb, rows mb) of this wave
-// and, with SUMSQ, ss[j] (j = 0, 1) the sum of squares of this lane's half of
-// the contraction for row block 2 HALF + j (the wave column HALF = wave & 1
-// picks which two of the four row blocks this wave sums).  The contraction
-// runs in ascending 16-column slices, which fixes the order of every sum.
-template <bool SUMSQ, int HALF = 0>
-__device__ __forceinline__ void mainloop(const char* const (&wsrc)[8], const char* const (&xsrc)[8], int nk,
-                                         char* smem, f32x16 (&acc)[4][4], float (&ss)[4]) {
-  const int lane = threadIdx.x & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int wn = wave & 1, wm = wave >> 1;
-  const int r31 = lane & 31, hsel = lane >> 5;
-  char* const mydst = smem + wave * kLoadsPerSlot * 1024;
-
-  // Fragment offsets inside a slot.  Row r of a 32-row block is lane & 31;
-  // its 16-byte chunk for slice kk is 2 kk + (lane >> 5); 32-row blocks are
-  // 4 KB apart and share the chunk permutation.
-  int aoff[4], boff[4];
-#pragma unroll
-  for (int kk = 0; kk < 4; ++kk) {
-    aoff[kk] = slot_pos(wn * 128 + r31, 2 * kk + hsel);
-    boff[kk] = slot_pos(wm * 128 + r31, 2 * kk + hsel);
-  }
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    ss[i] = 0.0f;
-#pragma unroll
-    for (int j = 0; j < 4; ++j) acc[i][j] = f32x16{};
-  }
-
-  // Prologue: slots u = 0 .. 3 (stages 0 and 1), wait for stage 0.
-  const int total = 2 * nk;
-#pragma unroll
-  for (int u = 0; u < 4; ++u)
-    if (u < total)
-      issue_slot((u & 1) ? xsrc : wsrc, static_cast<size_t>(u >> 1) * kRowBytes, mydst + u * kSlotBytes);
-  wait_slots(min(4, total) - 2);
-  barrier();
-  Frags fa, fb;
-  int sw = 0;
-  read_frags(fa, smem, smem + kSlotBytes, aoff[0], boff[0]);
-  int t = 0;
-  // At the barrier of stage t this wave has issued u <= 2t+4.
-  for (; t + 3 <= nk; ++t) stage<SUMSQ, HALF, true, true, 1>(fa, fb, acc, ss, sw, t, smem, mydst, wsrc, xsrc, aoff, boff);
-  if (t + 2 == nk) {
-    stage<SUMSQ, HALF, false, false, 0>(fa, fb, acc, ss, sw, t, smem, mydst, wsrc, xsrc, aoff, boff);
-    ++t;
-  }
-  // last stage: nothing left to publish
-  const char* ws = smem + sw * kSlotBytes;
-  const char* xs = smem + ring(sw + 1) * kSlotBytes;
-  read_frags(fb, ws, xs, aoff[1], boff[1]);
-  mma_slice<SUMSQ, HALF>(fa, acc, ss);
-  read_frags(fa, ws, xs, aoff[2], boff[2]);
-  mma_slice<SUMSQ, HALF>(fb, acc, ss);
-  read_frags(fb, ws, xs, aoff[3], boff[3]);
-  mma_slice<SUMSQ, HALF>(fa, acc, ss);
-  mma_slice<SUMSQ, HALF>(fb, acc, ss);
-}
-
-// ---- 16x16x32 variant of the main loop ------------------------------------
-// Same ring, slots, loads and barrier placement; the wave's 128x128 block is
-// 8x8 blocks of v_mfma_f32_16x16x32_bf16.  Under the part's power limit that
-// instruction sustains a higher clock than the 32x32 one for the same work,
-// so it wins at full MFMA load.  A lane owns row (l & 15) of each 16-row block
-// and features 4 (l >> 4) .. + 3 of each 16-feature block.  A stage is two
-// 32-column steps; the fragments of the next step are read into the second
-// register set while the current step's 64 MFMAs run.
-struct Frags16 {
+// ---- Main loop -----------------------------------------------------------
+// The wave's 128x128 block is 8x8 blocks of v_mfma_f32_16x16x32_bf16: a lane
+// owns row (l & 15) of each 16-row block and features 4 (l >> 4) .. + 3 of
+// each 16-feature block.  A 64-column stage is two 32-column steps; the
+// fragments of the next step are read into the second register set while the
+// current step's 64 MFMAs run.
+struct Frags {
   bf16x8 a[8], b[8];
 };
 
-__device__ __forceinline__ void read_frags16(Frags16& f, const char* ws, const char* xs, int aoff, int boff) {
+__device__ __forceinline__ void read_frags(Frags& f, const char* ws, const char* xs, int aoff, int boff) {
 #pragma unroll
   for (int i = 0; i < 8; ++i) f.a[i] = *reinterpret_cast<const bf16x8*>(ws + aoff + i * 16 * kRowBytes);
 #pragma unroll
@@ -349,7 +185,7 @@ __device__ __forceinline__ void mfma16(f32x4& acc, const bf16x8& a, const bf16x8
 
 // Sum of squares of the wave's 4 row blocks 4 HALF .. + 3 (this lane's chunk).
 template <int HALF>
-__device__ __forceinline__ void sumsq16(const Frags16& f, float (&ss)[4]) {
+__device__ __forceinline__ void sumsq(const Frags& f, float (&ss)[4]) {
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
     const bf16x8& b = f.b[4 * HALF + j];
@@ -366,7 +202,7 @@ __device__ __forceinline__ void sumsq16(const Frags16& f, float (&ss)[4]) {
 // 0..15 one each; with LOAD, the 8 operand loads of one slot follow every
 // second MFMA from 16 on.
 template <bool READ, bool LOAD>
-__device__ __forceinline__ void mma_step16(const Frags16& f, f32x4 (&acc)[8][8], Frags16& nf, const char* ws,
+__device__ __forceinline__ void mma_step(const Frags& f, f32x4 (&acc)[8][8], Frags& nf, const char* ws,
                                            const char* xs, int aoff, int boff, const char* const (&src)[8],
                                            size_t kbyte, char* dst) {
 #pragma unroll
@@ -382,34 +218,41 @@ __device__ __forceinline__ void mma_step16(const Frags16& f, f32x4 (&acc)[8][8],
   }
 }
 
-// One stage t on slots sw (weights) and sw + 1 (data rows); the slot sequence
-// and the PEND / ISSUE / WAIT roles are those of stage() above, with the
-// barrier between the two steps: step 0 reads step 1's fragments, step 1 reads
-// the next stage's step 0.
+// One stage t on slots sw (weights) and sw + 1 (data rows), ending with stage
+// t+1 published.  Slot sequence number u = 0, 1, 2, ... is the weights of
+// stage u / 2 (even u) or its data rows (odd u), in ring slot u % 5.
+//   PEND : during step 0, load u = 2t+4 (weights of stage t+2) into slot
+//          sw + 4, free since the barrier that opened stage t;
+//   ISSUE: during step 1, after the barrier, load u = 2t+5 (data rows of
+//          stage t+2) into slot sw, free once every wave has passed it;
+//   WAIT : slots this wave may still have in flight at the barrier (stage t+1
+//          needs u <= 2t+3 landed; u = 2t+4 may still fly).
+// Step 0 reads step 1's fragments from the current slots; after the barrier,
+// step 1 reads the next stage's step-0 fragments.
 template <bool SUMSQ, int HALF, bool PEND, bool ISSUE, int WAIT>
-__device__ __forceinline__ void stage16(Frags16& fa, Frags16& fb, f32x4 (&acc)[8][8], float (&ss)[4], int& sw, int t,
+__device__ __forceinline__ void stage(Frags& fa, Frags& fb, f32x4 (&acc)[8][8], float (&ss)[4], int& sw, int t,
                                         char* smem, char* mydst, const char* const (&wsrc)[8],
                                         const char* const (&xsrc)[8], const int (&aoff)[2], const int (&boff)[2]) {
   const char* ws = smem + sw * kSlotBytes;
   const char* xs = smem + ring(sw + 1) * kSlotBytes;
-  if (SUMSQ) sumsq16<HALF>(fa, ss);
-  mma_step16<true, PEND>(fa, acc, fb, ws, xs, aoff[1], boff[1], wsrc, static_cast<size_t>(t + 2) * kRowBytes,
+  if (SUMSQ) sumsq<HALF>(fa, ss);
+  mma_step<true, PEND>(fa, acc, fb, ws, xs, aoff[1], boff[1], wsrc, static_cast<size_t>(t + 2) * kRowBytes,
                          mydst + ring(sw + 4) * kSlotBytes);
   wait_slots(WAIT);
   barrier();
   const int nsw = ring(sw + 2);
-  if (SUMSQ) sumsq16<HALF>(fb, ss);
-  mma_step16<true, ISSUE>(fb, acc, fa, smem + nsw * kSlotBytes, smem + ring(nsw + 1) * kSlotBytes, aoff[0], boff[0],
+  if (SUMSQ) sumsq<HALF>(fb, ss);
+  mma_step<true, ISSUE>(fb, acc, fa, smem + nsw * kSlotBytes, smem + ring(nsw + 1) * kSlotBytes, aoff[0], boff[0],
                           xsrc, static_cast<size_t>(t + 2) * kRowBytes, mydst + sw * kSlotBytes);
   sw = nsw;
 }
 
-// Main loop over nk stages with 16x16x32 blocks.  On return acc[nb][mb] holds
+// Main loop over nk stages, shared by both contractions.  On return acc[nb][mb] holds
 // features 16 nb + 4 (l >> 4) + v, row 16 mb + (l & 15) of the wave's block,
 // and with SUMSQ ss[j] this lane's part (its 8-column chunk of every 32) of
 // the sum of squares of row block 4 HALF + j.
 template <bool SUMSQ, int HALF = 0>
-__device__ __forceinline__ void mainloop16(const char* const (&wsrc)[8], const char* const (&xsrc)[8], int nk,
+__device__ __forceinline__ void mainloop(const char* const (&wsrc)[8], const char* const (&xsrc)[8], int nk,
                                            char* smem, f32x4 (&acc)[8][8], float (&ss)[4]) {
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -442,21 +285,21 @@ __device__ __forceinline__ void mainloop16(const char* const (&wsrc)[8], const c
       issue_slot((u & 1) ? xsrc : wsrc, static_cast<size_t>(u >> 1) * kRowBytes, mydst + u * kSlotBytes);
   wait_slots(min(4, total) - 2);
   barrier();
-  Frags16 fa, fb;
+  Frags fa, fb;
   int sw = 0;
-  read_frags16(fa, smem, smem + kSlotBytes, aoff[0], boff[0]);
+  read_frags(fa, smem, smem + kSlotBytes, aoff[0], boff[0]);
   int t = 0;
-  for (; t + 3 <= nk; ++t) stage16<SUMSQ, HALF, true, true, 1>(fa, fb, acc, ss, sw, t, smem, mydst, wsrc, xsrc, aoff, boff);
+  for (; t + 3 <= nk; ++t) stage<SUMSQ, HALF, true, true, 1>(fa, fb, acc, ss, sw, t, smem, mydst, wsrc, xsrc, aoff, boff);
   if (t + 2 == nk) {
-    stage16<SUMSQ, HALF, false, false, 0>(fa, fb, acc, ss, sw, t, smem, mydst, wsrc, xsrc, aoff, boff);
+    stage<SUMSQ, HALF, false, false, 0>(fa, fb, acc, ss, sw, t, smem, mydst, wsrc, xsrc, aoff, boff);
     ++t;
   }
   const char* ws = smem + sw * kSlotBytes;
   const char* xs = smem + ring(sw + 1) * kSlotBytes;
-  if (SUMSQ) sumsq16<HALF>(fa, ss);
-  mma_step16<true, false>(fa, acc, fb, ws, xs, aoff[1], boff[1], wsrc, 0, mydst);
-  if (SUMSQ) sumsq16<HALF>(fb, ss);
-  mma_step16<false, false>(fb, acc, fa, ws, xs, 0, 0, wsrc, 0, mydst);
+  if (SUMSQ) sumsq<HALF>(fa, ss);
+  mma_step<true, false>(fa, acc, fb, ws, xs, aoff[1], boff[1], wsrc, 0, mydst);
+  if (SUMSQ) sumsq<HALF>(fb, ss);
+  mma_step<false, false>(fb, acc, fa, ws, xs, 0, 0, wsrc, 0, mydst);
   // The compiler does not see the MFMAs in the assembly statements: give the
   // last ones the wait states an MFMA result needs before other instructions
   // read its registers (nothing may be scheduled across the nops).
@@ -498,7 +341,7 @@ __global__ void __launch_bounds__(kThreads) map_gemm_kernel(const MapParams p) {
 
   f32x4 acc[8][8];
   float ss[4];
-  mainloop16<false>(wsrc, xsrc, p.K / kBK, smem, acc, ss);
+  mainloop<false>(wsrc, xsrc, p.K / kBK, smem, acc, ss);
 
   // Epilogue: + b, round to bf16, stage, 16-byte row stores into Y_g.  A lane
   // holds 4 consecutive features (8 bytes, one half of a staged chunk) of a row.
@@ -565,46 +408,48 @@ __global__ void __launch_bounds__(kThreads) kv_gemm_kernel(const KvParams p) {
     }
   }
 
-  f32x16 acc[4][4];
+  f32x4 acc[8][8];
   float ss[4];
-  // wave-uniform branch: the two waves of a row half each sum two row blocks
+  // wave-uniform branch: the two waves of a row half each sum four row blocks
   if ((wave & 1) == 0)
     mainloop<true, 0>(wsrc, xsrc, p.K / kBK, smem, acc, ss);
   else
     mainloop<true, 1>(wsrc, xsrc, p.K / kBK, smem, acc, ss);
 
-  const int wn = wave & 1, wm = wave >> 1, r31 = lane & 31, hsel = lane >> 5;
+  const int wn = wave & 1, wm = wave >> 1, r15 = lane & 15, q = lane >> 4;
   const float inv_k = 1.0f / static_cast<float>(p.K);
-  // Sums of squares: this wave holds row blocks 2 wn, 2 wn + 1 in ss[0..1];
-  // the other wave of its row half holds the rest.  Full row sums (both lane
-  // halves) are swapped through LDS once every wave is done with the operands.
+  // Sums of squares: this wave holds row blocks 4 wn .. 4 wn + 3 in ss[0..3],
+  // each lane one 8-column chunk of every 32; the other wave of its row half
+  // holds the other blocks.  Full row sums (all four lane groups) are swapped
+  // through LDS once every wave is done with the operands.
   float* const ss_lds = reinterpret_cast<float*>(smem + kSlotOffset + 1024);
   __syncthreads();
 #pragma unroll
-  for (int j = 0; j < 2; ++j) {
-    const float tot = ss[j] + __shfl_xor(ss[j], 32);
-    if (hsel == 0) ss_lds[wm * 128 + (2 * wn + j) * 32 + r31] = tot;
+  for (int j = 0; j < 4; ++j) {
+    float tot = ss[j] + __shfl_xor(ss[j], 16);
+    tot += __shfl_xor(tot, 32);
+    if (q == 0) ss_lds[wm * 128 + (4 * wn + j) * 16 + r15] = tot;
   }
   __syncthreads();
-  float rowss[4];
+  float rowss[8];
 #pragma unroll
-  for (int mb = 0; mb < 4; ++mb) rowss[mb] = ss_lds[wm * 128 + mb * 32 + r31];
+  for (int mb = 0; mb < 8; ++mb) rowss[mb] = ss_lds[wm * 128 + mb * 16 + r15];
   const int fw = n0 + wn * 128;  // first feature of this wave; a whole wave is key or value
   // (with v_only, a tile may start inside the keys when w is not a multiple of
   // 256; those key waves are neither rotated nor stored)
   const bool is_key = fw < p.w && !p.v_only;
   // Value waves of a rescaled fill: the request's value scale for the wave's
-  // first head (and, for heads of 64, the second head, blocks 2-3) is folded
+  // first head (and, for heads of 64, the second head, blocks 4-7) is folded
   // into the norm's per-row factor; without a rescale the factor is exactly
   // the norm's scale.
   const float* const vsw = (VSCALE && !is_key) ? p.vscale[c.g] + (fw - p.w) / HD : nullptr;
-  float rs[4], rs2[4];
-  int pos[4], slot_r[4];
+  float rs[8], rs2[8];
+  int pos[8], slot_r[8];
 #pragma unroll
-  for (int mb = 0; mb < 4; ++mb) {
+  for (int mb = 0; mb < 8; ++mb) {
     rs[mb] = rsqrtf(rowss[mb] * inv_k + p.eps);
     rs2[mb] = rs[mb];
-    const int lr = wm * 128 + mb * 32 + r31;
+    const int lr = wm * 128 + mb * 16 + r15;
     const int m = m0 + lr;
     int ps = 0, slot = -1, grp = 0;
     if (m < p.M) {
@@ -632,105 +477,101 @@ __global__ void __launch_bounds__(kThreads) kv_gemm_kernel(const KvParams p) {
   if (is_key) {
     // RoPE, rotate-half: feature j < hd/2 of a head pairs with j + hd/2.  A
     // wave spans 128 features = one head of 128 or two heads of 64, so the
-    // partner is block nb + hd/64 at the same register index.
+    // partner is block nb + hd/32 at the same register index.
     constexpr int half = HD / 2;
-    constexpr int pstep = half / 32;  // 2 for hd 128, 1 for hd 64
+    constexpr int pstep = half / 16;  // 4 for hd 128, 2 for hd 64
     constexpr int heads = 128 / HD;   // heads per wave
+    constexpr int per_head = HD / 16; // 16-feature blocks per head
     const float2* tab = reinterpret_cast<const float2*>(p.rope);
     // With QK-norm each head is also divided by sqrt(mean over the head of
     // k^2 + eps) and its dimensions scaled by the gain before the rotation.
     // The rotation is linear, so the per-row, per-head division is applied
     // after it: the rotation pass sums the squares of the unrotated values it
-    // reads (a lane holds half of each head's values for its row, the other
-    // half is in lane ^ 32), then a second pass scales.
-    float sq[4][heads];
+    // reads (a lane holds a quarter of each head's values for its row, the
+    // rest are in lanes ^ 16, ^ 32, ^ 48), then a second pass scales.
+    float sq[8][heads];
 #pragma unroll
-    for (int mb = 0; mb < 4; ++mb)
+    for (int mb = 0; mb < 8; ++mb)
 #pragma unroll
       for (int h = 0; h < heads; ++h) sq[mb][h] = 0.0f;
     const uint16_t* kg = QK ? p.kgamma[c.g] : nullptr;
 #pragma unroll
-    for (int nb = 0; nb < 4; ++nb) {
-      const int jb = (nb * 32) & (HD - 1);
+    for (int nb = 0; nb < 8; ++nb) {
+      const int jb = (nb * 16) & (HD - 1);
       if (jb >= half) continue;
       const int nb2 = nb + pstep;
-      const int h = nb / (4 / heads);
+      const int h = nb / per_head;
+      float g1[4] = {1.0f, 1.0f, 1.0f, 1.0f}, g2[4] = {1.0f, 1.0f, 1.0f, 1.0f};
+      if (QK) {
+        // gains of dimensions j and j + hd/2, four consecutive each
+        const uint2 a = *reinterpret_cast<const uint2*>(kg + jb + q * 4);
+        const uint2 b = *reinterpret_cast<const uint2*>(kg + jb + half + q * 4);
+        g1[0] = __uint_as_float(a.x << 16), g1[1] = __uint_as_float(a.x & 0xffff0000u);
+        g1[2] = __uint_as_float(a.y << 16), g1[3] = __uint_as_float(a.y & 0xffff0000u);
+        g2[0] = __uint_as_float(b.x << 16), g2[1] = __uint_as_float(b.x & 0xffff0000u);
+        g2[2] = __uint_as_float(b.y << 16), g2[3] = __uint_as_float(b.y & 0xffff0000u);
+      }
 #pragma unroll
-      for (int mb = 0; mb < 4; ++mb) {
-        const float2* trow = tab + static_cast<size_t>(pos[mb]) * half + jb + hsel * 4;
+      for (int mb = 0; mb < 8; ++mb) {
+        const float2* trow = tab + static_cast<size_t>(pos[mb]) * half + jb + q * 4;
+        const float4 cs01 = *reinterpret_cast<const float4*>(trow);
+        const float4 cs23 = *reinterpret_cast<const float4*>(trow + 2);
+        const float cs[8] = {cs01.x, cs01.y, cs01.z, cs01.w, cs23.x, cs23.y, cs23.z, cs23.w};
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const float4 cs01 = *reinterpret_cast<const float4*>(trow + q * 8);
-          const float4 cs23 = *reinterpret_cast<const float4*>(trow + q * 8 + 2);
-          const float cs[8] = {cs01.x, cs01.y, cs01.z, cs01.w, cs23.x, cs23.y, cs23.z, cs23.w};
-          float g1[4] = {1.0f, 1.0f, 1.0f, 1.0f}, g2[4] = {1.0f, 1.0f, 1.0f, 1.0f};
+        for (int i = 0; i < 4; ++i) {
+          float x1 = acc[nb][mb][i] * rs[mb];
+          float x2 = acc[nb2][mb][i] * rs[mb];
           if (QK) {
-            // gains of dimensions j and j + hd/2, four consecutive each
-            const uint2 a = *reinterpret_cast<const uint2*>(kg + jb + q * 8 + hsel * 4);
-            const uint2 b = *reinterpret_cast<const uint2*>(kg + jb + half + q * 8 + hsel * 4);
-            g1[0] = __uint_as_float(a.x << 16), g1[1] = __uint_as_float(a.x & 0xffff0000u);
-            g1[2] = __uint_as_float(a.y << 16), g1[3] = __uint_as_float(a.y & 0xffff0000u);
-            g2[0] = __uint_as_float(b.x << 16), g2[1] = __uint_as_float(b.x & 0xffff0000u);
-            g2[2] = __uint_as_float(b.y << 16), g2[3] = __uint_as_float(b.y & 0xffff0000u);
+            sq[mb][h] += x1 * x1 + x2 * x2;
+            x1 *= g1[i];
+            x2 *= g2[i];
           }
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            float x1 = acc[nb][mb][q * 4 + i] * rs[mb];
-            float x2 = acc[nb2][mb][q * 4 + i] * rs[mb];
-            if (QK) {
-              sq[mb][h] += x1 * x1 + x2 * x2;
-              x1 *= g1[i];
-              x2 *= g2[i];
-            }
-            const float co = cs[2 * i], si = cs[2 * i + 1];
-            acc[nb][mb][q * 4 + i] = x1 * co - x2 * si;
-            acc[nb2][mb][q * 4 + i] = x2 * co + x1 * si;
-          }
+          const float co = cs[2 * i], si = cs[2 * i + 1];
+          acc[nb][mb][i] = x1 * co - x2 * si;
+          acc[nb2][mb][i] = x2 * co + x1 * si;
         }
       }
     }
     if (QK) {
 #pragma unroll
-      for (int mb = 0; mb < 4; ++mb) {
+      for (int mb = 0; mb < 8; ++mb) {
 #pragma unroll
         for (int h = 0; h < heads; ++h) {
-          const float tot = sq[mb][h] + __shfl_xor(sq[mb][h], 32);
+          float tot = sq[mb][h] + __shfl_xor(sq[mb][h], 16);
+          tot += __shfl_xor(tot, 32);
           const float f = rsqrtf(tot * (1.0f / HD) + p.eps);
 #pragma unroll
-          for (int nb = h * (4 / heads); nb < (h + 1) * (4 / heads); ++nb)
+          for (int nb = h * per_head; nb < (h + 1) * per_head; ++nb)
 #pragma unroll
-            for (int v = 0; v < 16; ++v) acc[nb][mb][v] *= f;
+            for (int v = 0; v < 4; ++v) acc[nb][mb][v] *= f;
         }
       }
     }
   } else {
 #pragma unroll
-    for (int nb = 0; nb < 4; ++nb)
+    for (int nb = 0; nb < 8; ++nb)
 #pragma unroll
-      for (int mb = 0; mb < 4; ++mb)
+      for (int mb = 0; mb < 8; ++mb)
 #pragma unroll
-        for (int v = 0; v < 16; ++v) acc[nb][mb][v] *= (HD == 64 && nb >= 2) ? rs2[mb] : rs[mb];
+        for (int v = 0; v < 4; ++v) acc[nb][mb][v] *= (HD == 64 && nb >= 4) ? rs2[mb] : rs[mb];
   }
 
   // (every wave passed its last operand read before the sums were swapped)
-  if (wn == 0 && hsel == 0) {
+  if (wn == 0 && q == 0) {
 #pragma unroll
-    for (int mb = 0; mb < 4; ++mb) slot_of[wm * 128 + mb * 32 + r31] = slot_r[mb];
+    for (int mb = 0; mb < 8; ++mb) slot_of[wm * 128 + mb * 16 + r15] = slot_r[mb];
   }
 #pragma unroll
-  for (int nb = 0; nb < 4; ++nb) {
+  for (int nb = 0; nb < 8; ++nb) {
+    const int chunk = wn * 16 + nb * 2 + (q >> 1);
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const int chunk = wn * 16 + nb * 4 + q;
-#pragma unroll
-      for (int mb = 0; mb < 4; ++mb) {
-        const int row = wm * 128 + mb * 32 + r31;
-        const f32x16& v = acc[nb][mb];
-        uint2 o;
-        o.x = pack_bf16x2(v[q * 4 + 0], v[q * 4 + 1]);
-        o.y = pack_bf16x2(v[q * 4 + 2], v[q * 4 + 3]);
-        *reinterpret_cast<uint2*>(smem + stage_off(row, chunk) + hsel * 8) = o;
-      }
+    for (int mb = 0; mb < 8; ++mb) {
+      const int row = wm * 128 + mb * 16 + r15;
+      const f32x4& v = acc[nb][mb];
+      uint2 o;
+      o.x = pack_bf16x2(v[0], v[1]);
+      o.y = pack_bf16x2(v[2], v[3]);
+      *reinterpret_cast<uint2*>(smem + stage_off(row, chunk) + (q & 1) * 8) = o;
     }
   }
   __syncthreads();
