@@ -183,6 +183,15 @@ __device__ __forceinline__ void mfma16(f32x4& acc, const bf16x8& a, const bf16x8
   asm volatile("v_mfma_f32_16x16x32_bf16 %0, %1, %2, %0" : "+a"(acc) : "v"(a), "v"(b));
 }
 
+// One accumulator value read out of its AGPR where it is used.  The compiler
+// otherwise copies all 256 accumulators into VGPRs at the end of the main
+// loop, which leaves the epilogue no registers for its loads.
+__device__ __forceinline__ float agpr(float a) {
+  float v;
+  asm volatile("v_accvgpr_read_b32 %0, %1" : "=v"(v) : "a"(a));
+  return v;
+}
+
 // Sum of squares of the wave's 4 row blocks 4 HALF .. + 3 (this lane's chunk).
 template <int HALF>
 __device__ __forceinline__ void sumsq(const Frags& f, float (&ss)[4]) {
@@ -339,20 +348,27 @@ __global__ void __launch_bounds__(kThreads) map_gemm_kernel(const MapParams p) {
     }
   }
 
+  // This lane's bias values (4 consecutive features of each 16-feature block),
+  // fetched before the main loop so their latency hides behind it.
+  const int wn = wave & 1, wm = wave >> 1, r15 = lane & 15, q = lane >> 4;
+  uint2 braw[8];
+  {
+    const uint16_t* bias = p.b[c.g] + n0 + wn * 128 + q * 4;
+#pragma unroll
+    for (int nb = 0; nb < 8; ++nb) braw[nb] = *reinterpret_cast<const uint2*>(bias + nb * 16);
+  }
+
   f32x4 acc[8][8];
   float ss[4];
   mainloop<false>(wsrc, xsrc, p.K / kBK, smem, acc, ss);
 
   // Epilogue: + b, round to bf16, stage, 16-byte row stores into Y_g.  A lane
   // holds 4 consecutive features (8 bytes, one half of a staged chunk) of a row.
-  const int wn = wave & 1, wm = wave >> 1, r15 = lane & 15, q = lane >> 4;
-  const uint16_t* bias = p.b[c.g] + n0 + wn * 128 + q * 4;
   __syncthreads();  // every wave is done reading the operand stages
 #pragma unroll
   for (int nb = 0; nb < 8; ++nb) {
-    const uint2 braw = *reinterpret_cast<const uint2*>(bias + nb * 16);
-    const float b0 = bf16_to_f32(braw.x & 0xffff), b1 = bf16_to_f32(braw.x >> 16);
-    const float b2 = bf16_to_f32(braw.y & 0xffff), b3 = bf16_to_f32(braw.y >> 16);
+    const float b0 = bf16_to_f32(braw[nb].x & 0xffff), b1 = bf16_to_f32(braw[nb].x >> 16);
+    const float b2 = bf16_to_f32(braw[nb].y & 0xffff), b3 = bf16_to_f32(braw[nb].y >> 16);
     const int chunk = wn * 16 + nb * 2 + (q >> 1);
 #pragma unroll
     for (int mb = 0; mb < 8; ++mb) {
@@ -408,6 +424,16 @@ __global__ void __launch_bounds__(kThreads) kv_gemm_kernel(const KvParams p) {
     }
   }
 
+  const int wn = wave & 1, wm = wave >> 1, r15 = lane & 15, q = lane >> 4;
+  // Output-row indices of this lane's 8 rows, fetched before the main loop so
+  // their latency hides behind it (indices clamped: every load is in bounds).
+  int orow[8];
+#pragma unroll
+  for (int mb = 0; mb < 8; ++mb) {
+    const int m = min(m0 + wm * 128 + mb * 16 + r15, p.M - 1);
+    orow[mb] = p.out_rows ? p.out_rows[m] : m;
+  }
+
   f32x4 acc[8][8];
   float ss[4];
   // wave-uniform branch: the two waves of a row half each sum four row blocks
@@ -416,7 +442,39 @@ __global__ void __launch_bounds__(kThreads) kv_gemm_kernel(const KvParams p) {
   else
     mainloop<true, 1>(wsrc, xsrc, p.K / kBK, smem, acc, ss);
 
-  const int wn = wave & 1, wm = wave >> 1, r15 = lane & 15, q = lane >> 4;
+  // Row bookkeeping, branch-free so that all loads of a kind issue together:
+  // position, cache slot and (rescale) request of each row; a row that is out
+  // of range anywhere gets slot -1 and is not stored.
+  int pos[8], slot_r[8], grp_r[8];
+  bool ok[8];
+#pragma unroll
+  for (int mb = 0; mb < 8; ++mb) {
+    const int r = orow[mb];
+    ok[mb] = (m0 + wm * 128 + mb * 16 + r15 < p.M) & (r >= 0) & (r < p.n_rows);
+    orow[mb] = ok[mb] ? r : 0;
+  }
+  // (one wave-uniform branch per array, outside the row loops, so that each
+  // array's 8 loads issue back to back)
+#pragma unroll
+  for (int mb = 0; mb < 8; ++mb) pos[mb] = p.positions[orow[mb]];
+  if (p.slots) {
+#pragma unroll
+    for (int mb = 0; mb < 8; ++mb) slot_r[mb] = p.slots[orow[mb]];
+  } else {
+#pragma unroll
+    for (int mb = 0; mb < 8; ++mb) slot_r[mb] = orow[mb];
+  }
+#pragma unroll
+  for (int mb = 0; mb < 8; ++mb) grp_r[mb] = VSCALE ? p.group_of_row[orow[mb]] : 0;
+#pragma unroll
+  for (int mb = 0; mb < 8; ++mb) {
+    const bool good = ok[mb] & (pos[mb] >= 0) & (pos[mb] < p.max_pos) & (slot_r[mb] >= 0) &
+                      (slot_r[mb] < p.n_slots) & (!VSCALE | ((grp_r[mb] >= 0) & (grp_r[mb] < p.n_groups)));
+    slot_r[mb] = good ? slot_r[mb] : -1;
+    pos[mb] = good ? pos[mb] : 0;
+    grp_r[mb] = good ? grp_r[mb] : 0;
+  }
+  __builtin_amdgcn_sched_barrier(0);
   const float inv_k = 1.0f / static_cast<float>(p.K);
   // Sums of squares: this wave holds row blocks 4 wn .. 4 wn + 3 in ss[0..3],
   // each lane one 8-column chunk of every 32; the other wave of its row half
@@ -430,10 +488,11 @@ __global__ void __launch_bounds__(kThreads) kv_gemm_kernel(const KvParams p) {
     tot += __shfl_xor(tot, 32);
     if (q == 0) ss_lds[wm * 128 + (4 * wn + j) * 16 + r15] = tot;
   }
-  __syncthreads();
-  float rowss[8];
+  if (wn == 0 && q == 0) {
 #pragma unroll
-  for (int mb = 0; mb < 8; ++mb) rowss[mb] = ss_lds[wm * 128 + mb * 16 + r15];
+    for (int mb = 0; mb < 8; ++mb) slot_of[wm * 128 + mb * 16 + r15] = slot_r[mb];
+  }
+  __syncthreads();
   const int fw = n0 + wn * 128;  // first feature of this wave; a whole wave is key or value
   // (with v_only, a tile may start inside the keys when w is not a multiple of
   // 256; those key waves are neither rotated nor stored)
@@ -444,36 +503,36 @@ __global__ void __launch_bounds__(kThreads) kv_gemm_kernel(const KvParams p) {
   // the norm's scale.
   const float* const vsw = (VSCALE && !is_key) ? p.vscale[c.g] + (fw - p.w) / HD : nullptr;
   float rs[8], rs2[8];
-  int pos[8], slot_r[8];
 #pragma unroll
   for (int mb = 0; mb < 8; ++mb) {
-    rs[mb] = rsqrtf(rowss[mb] * inv_k + p.eps);
+    rs[mb] = rsqrtf(ss_lds[wm * 128 + mb * 16 + r15] * inv_k + p.eps);
     rs2[mb] = rs[mb];
-    const int lr = wm * 128 + mb * 16 + r15;
-    const int m = m0 + lr;
-    int ps = 0, slot = -1, grp = 0;
-    if (m < p.M) {
-      const int r = p.out_rows ? p.out_rows[m] : m;
-      if (r >= 0 && r < p.n_rows) {
-        ps = p.positions[r];
-        slot = p.slots ? p.slots[r] : r;
-        if (VSCALE) grp = p.group_of_row[r];
-        if (ps < 0 || ps >= p.max_pos || slot < 0 || slot >= p.n_slots || (VSCALE && (grp < 0 || grp >= p.n_groups))) {
-          slot = -1;
-          ps = 0;
-          grp = 0;
-        }
-      }
+  }
+  if (VSCALE && vsw) {  // wave-uniform; the 8 (16) scale loads issue together
+    float sa[8], sb[8];
+#pragma unroll
+    for (int mb = 0; mb < 8; ++mb) {
+      const float* sg = vsw + grp_r[mb] * p.n_kv;
+      sa[mb] = sg[0];
+      sb[mb] = HD == 64 ? sg[1] : 1.0f;
     }
-    if (VSCALE && vsw) {
-      const float* sg = vsw + grp * p.n_kv;
-      if (HD == 64) rs2[mb] = rs[mb] * sg[1];
-      rs[mb] = rs[mb] * sg[0];
+#pragma unroll
+    for (int mb = 0; mb < 8; ++mb) {
+      rs2[mb] = rs[mb] * sb[mb];
+      rs[mb] = rs[mb] * sa[mb];
     }
-    pos[mb] = ps;
-    slot_r[mb] = slot;
   }
 
+  __builtin_amdgcn_sched_barrier(0);
+  // Scale (and for keys rotate), round to bf16 and write each 4-feature run
+  // straight into the staging tile: 8 bytes, one half of a staged chunk.
+  auto stage4 = [&](int nb, int mb, float v0, float v1, float v2, float v3) {
+    const int row = wm * 128 + mb * 16 + r15;
+    uint2 o;
+    o.x = pack_bf16x2(v0, v1);
+    o.y = pack_bf16x2(v2, v3);
+    *reinterpret_cast<uint2*>(smem + stage_off(row, wn * 16 + nb * 2 + (q >> 1)) + (q & 1) * 8) = o;
+  };
   if (is_key) {
     // RoPE, rotate-half: feature j < hd/2 of a head pairs with j + hd/2.  A
     // wave spans 128 features = one head of 128 or two heads of 64, so the
@@ -485,15 +544,33 @@ __global__ void __launch_bounds__(kThreads) kv_gemm_kernel(const KvParams p) {
     const float2* tab = reinterpret_cast<const float2*>(p.rope);
     // With QK-norm each head is also divided by sqrt(mean over the head of
     // k^2 + eps) and its dimensions scaled by the gain before the rotation.
-    // The rotation is linear, so the per-row, per-head division is applied
-    // after it: the rotation pass sums the squares of the unrotated values it
-    // reads (a lane holds a quarter of each head's values for its row, the
-    // rest are in lanes ^ 16, ^ 32, ^ 48), then a second pass scales.
-    float sq[8][heads];
+    // The head sums come first (a lane holds a quarter of each head's values
+    // for its row, the rest are in lanes ^ 16, ^ 32, ^ 48); the division
+    // then folds into the row factor of the rotation pass.
+    float kf[8][heads];
 #pragma unroll
     for (int mb = 0; mb < 8; ++mb)
 #pragma unroll
-      for (int h = 0; h < heads; ++h) sq[mb][h] = 0.0f;
+      for (int h = 0; h < heads; ++h) kf[mb][h] = rs[mb];
+    if (QK) {
+#pragma unroll
+      for (int mb = 0; mb < 8; ++mb) {
+#pragma unroll
+        for (int h = 0; h < heads; ++h) {
+          float sq = 0.0f;
+#pragma unroll
+          for (int nb = h * per_head; nb < (h + 1) * per_head; ++nb)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+              const float x = agpr(acc[nb][mb][i]) * rs[mb];
+              sq += x * x;
+            }
+          sq += __shfl_xor(sq, 16);
+          sq += __shfl_xor(sq, 32);
+          kf[mb][h] = rs[mb] * rsqrtf(sq * (1.0f / HD) + p.eps);
+        }
+      }
+    }
     const uint16_t* kg = QK ? p.kgamma[c.g] : nullptr;
 #pragma unroll
     for (int nb = 0; nb < 8; ++nb) {
@@ -501,6 +578,14 @@ __global__ void __launch_bounds__(kThreads) kv_gemm_kernel(const KvParams p) {
       if (jb >= half) continue;
       const int nb2 = nb + pstep;
       const int h = nb / per_head;
+      // cos/sin of dims jb + 4q .. + 3 for the 8 rows, all requested at once
+      float4 cs[8][2];
+#pragma unroll
+      for (int mb = 0; mb < 8; ++mb) {
+        const float2* trow = tab + static_cast<size_t>(pos[mb]) * half + jb + q * 4;
+        cs[mb][0] = *reinterpret_cast<const float4*>(trow);
+        cs[mb][1] = *reinterpret_cast<const float4*>(trow + 2);
+      }
       float g1[4] = {1.0f, 1.0f, 1.0f, 1.0f}, g2[4] = {1.0f, 1.0f, 1.0f, 1.0f};
       if (QK) {
         // gains of dimensions j and j + hd/2, four consecutive each
@@ -513,65 +598,33 @@ __global__ void __launch_bounds__(kThreads) kv_gemm_kernel(const KvParams p) {
       }
 #pragma unroll
       for (int mb = 0; mb < 8; ++mb) {
-        const float2* trow = tab + static_cast<size_t>(pos[mb]) * half + jb + q * 4;
-        const float4 cs01 = *reinterpret_cast<const float4*>(trow);
-        const float4 cs23 = *reinterpret_cast<const float4*>(trow + 2);
-        const float cs[8] = {cs01.x, cs01.y, cs01.z, cs01.w, cs23.x, cs23.y, cs23.z, cs23.w};
+        const float c4[8] = {cs[mb][0].x, cs[mb][0].y, cs[mb][0].z, cs[mb][0].w,
+                             cs[mb][1].x, cs[mb][1].y, cs[mb][1].z, cs[mb][1].w};
+        float y1[4], y2[4];
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          float x1 = acc[nb][mb][i] * rs[mb];
-          float x2 = acc[nb2][mb][i] * rs[mb];
-          if (QK) {
-            sq[mb][h] += x1 * x1 + x2 * x2;
-            x1 *= g1[i];
-            x2 *= g2[i];
-          }
-          const float co = cs[2 * i], si = cs[2 * i + 1];
-          acc[nb][mb][i] = x1 * co - x2 * si;
-          acc[nb2][mb][i] = x2 * co + x1 * si;
+          const float x1 = agpr(acc[nb][mb][i]) * kf[mb][h] * g1[i];
+          const float x2 = agpr(acc[nb2][mb][i]) * kf[mb][h] * g2[i];
+          const float co = c4[2 * i], si = c4[2 * i + 1];
+          y1[i] = x1 * co - x2 * si;
+          y2[i] = x2 * co + x1 * si;
         }
+        stage4(nb, mb, y1[0], y1[1], y1[2], y1[3]);
+        stage4(nb2, mb, y2[0], y2[1], y2[2], y2[3]);
       }
-    }
-    if (QK) {
-#pragma unroll
-      for (int mb = 0; mb < 8; ++mb) {
-#pragma unroll
-        for (int h = 0; h < heads; ++h) {
-          float tot = sq[mb][h] + __shfl_xor(sq[mb][h], 16);
-          tot += __shfl_xor(tot, 32);
-          const float f = rsqrtf(tot * (1.0f / HD) + p.eps);
-#pragma unroll
-          for (int nb = h * per_head; nb < (h + 1) * per_head; ++nb)
-#pragma unroll
-            for (int v = 0; v < 4; ++v) acc[nb][mb][v] *= f;
-        }
-      }
+      // keep the accumulator reads of later blocks from being hoisted here
+      __builtin_amdgcn_sched_barrier(0);
     }
   } else {
 #pragma unroll
-    for (int nb = 0; nb < 8; ++nb)
+    for (int nb = 0; nb < 8; ++nb) {
 #pragma unroll
-      for (int mb = 0; mb < 8; ++mb)
-#pragma unroll
-        for (int v = 0; v < 4; ++v) acc[nb][mb][v] *= (HD == 64 && nb >= 4) ? rs2[mb] : rs[mb];
-  }
-
-  // (every wave passed its last operand read before the sums were swapped)
-  if (wn == 0 && q == 0) {
-#pragma unroll
-    for (int mb = 0; mb < 8; ++mb) slot_of[wm * 128 + mb * 16 + r15] = slot_r[mb];
-  }
-#pragma unroll
-  for (int nb = 0; nb < 8; ++nb) {
-    const int chunk = wn * 16 + nb * 2 + (q >> 1);
-#pragma unroll
-    for (int mb = 0; mb < 8; ++mb) {
-      const int row = wm * 128 + mb * 16 + r15;
-      const f32x4& v = acc[nb][mb];
-      uint2 o;
-      o.x = pack_bf16x2(v[0], v[1]);
-      o.y = pack_bf16x2(v[2], v[3]);
-      *reinterpret_cast<uint2*>(smem + stage_off(row, chunk) + (q & 1) * 8) = o;
+      for (int mb = 0; mb < 8; ++mb) {
+        const float f = (HD == 64 && nb >= 4) ? rs2[mb] : rs[mb];
+        stage4(nb, mb, agpr(acc[nb][mb][0]) * f, agpr(acc[nb][mb][1]) * f, agpr(acc[nb][mb][2]) * f,
+               agpr(acc[nb][mb][3]) * f);
+      }
+      __builtin_amdgcn_sched_barrier(0);
     }
   }
   __syncthreads();
