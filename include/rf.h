@@ -108,12 +108,14 @@ void rf_plan_destroy(rf_plan* plan);
  * (1 .. n_late; larger means fewer, wider launches).  The call uses the widest
  * grouping the given workspace allows, so any size >=
  * rf_fill_workspace_bytes(plan, n_fill, 1) works.  The figure includes the
- * RoPE table built when none is passed and, for RF_MAPS_Q8 plans, the bf16
- * image of each launch's maps.  Returns 0 for a bad argument. */
+ * RoPE table built when none is passed, the per-row sums of squares and norm
+ * factors of each launch layer's map output and, for RF_MAPS_Q8 plans, the
+ * bf16 image of each launch's maps.  Returns 0 for a bad argument. */
 size_t rf_fill_workspace_bytes(const rf_plan* plan, int32_t n_fill, int32_t layers_per_launch);
 
-/* Workspace bytes rf_kv_project needs (one prepared [W_k|W_v] copy per layer
- * group plus the RoPE table if none is passed); same grouping rule. */
+/* Workspace bytes rf_kv_project needs (one prepared [W_k|W_v] copy and one
+ * fp32 norm factor per plan row for each layer of a group, plus the RoPE table
+ * if none is passed); same grouping rule. */
 size_t rf_kv_project_workspace_bytes(const rf_plan* plan, int32_t layers_per_launch);
 
 /* Fill `table` (device, fp32 [max_pos][head_dim/2][2] = (cos, sin)) with the
@@ -349,7 +351,8 @@ enum {
   RF_K_DEQUANT = 6,   /* int8 map -> bf16 image (RF_MAPS_Q8)         */
   RF_K_SCALE = 7,     /* every launch of rf_value_scales(_q8) except
                          the int8 expansion (kind RF_K_DEQUANT)      */
-  RF_K_COUNT = 8
+  RF_K_NORM = 8,      /* per-row norm factors from the map's row sums */
+  RF_K_COUNT = 9
 };
 typedef struct rf_profile {
   double ms[RF_K_COUNT];        /* summed event time per kind, milliseconds */

@@ -37,7 +37,7 @@ EXPORTS = [
     "rf_ridge_dev_create", "rf_ridge_dev_add", "rf_ridge_dev_merge", "rf_ridge_dev_destroy", "rf_ridge_acc_sums",
 ]
 
-KERNEL_KINDS = ["map", "kv", "prep", "rope", "rows", "copy", "dequant", "scale"]
+KERNEL_KINDS = ["map", "kv", "prep", "rope", "rows", "copy", "dequant", "scale", "norm"]
 
 
 class RfError(RuntimeError):
@@ -53,7 +53,7 @@ class Shape(C.Structure):
 
 
 class Profile(C.Structure):
-    _fields_ = [("ms", C.c_double * 8), ("launches", C.c_int64 * 8)]
+    _fields_ = [("ms", C.c_double * len(KERNEL_KINDS)), ("launches", C.c_int64 * len(KERNEL_KINDS))]
 
 
 class VScale(C.Structure):

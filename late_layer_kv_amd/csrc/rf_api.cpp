@@ -119,6 +119,12 @@ size_t prep_bytes(const rf_shape& s, int g) {
 size_t y_bytes(const rf_shape& s, int n_fill, int g) {
   return up(static_cast<size_t>(g) * n_fill * s.d_out * 2);
 }
+// Per-row norm of each launch layer's Y: the map's per-tile sums of squares,
+// then the factor 1 / sqrt(mean + eps) per row.
+size_t ssq_bytes(const rf_shape& s, int n_fill, int g) {
+  return up(static_cast<size_t>(g) * (s.d_out / rf::kTileN) * n_fill * 4);
+}
+size_t rs_bytes(int n_fill, int g) { return up(static_cast<size_t>(g) * n_fill * 4); }
 // bf16 image of the int8 maps of one launch group (RF_MAPS_Q8 plans only)
 size_t dq_bytes(const rf_shape& s, int32_t flags, int g) {
   return (flags & RF_MAPS_Q8) ? up(static_cast<size_t>(g) * s.d_out * s.d_in * 2) : 0;
@@ -258,13 +264,14 @@ size_t rf_fill_workspace_bytes(const rf_plan* p, int32_t n_fill, int32_t g) {
   if (!p || n_fill < 0 || g < 1 || g > p->s.n_late) return 0;
   g = std::min(g, rf::kMaxGroup);
   if (p->flags & RF_MAPS_HOST) g = 1;
-  return rope_bytes(p->s) + kFlagBytes + prep_bytes(p->s, g) + y_bytes(p->s, n_fill, g) + dq_bytes(p->s, p->flags, g);
+  return rope_bytes(p->s) + kFlagBytes + prep_bytes(p->s, g) + y_bytes(p->s, n_fill, g) + dq_bytes(p->s, p->flags, g) +
+         ssq_bytes(p->s, n_fill, g) + rs_bytes(n_fill, g);
 }
 
 size_t rf_kv_project_workspace_bytes(const rf_plan* p, int32_t g) {
   if (!p || g < 1 || g > p->s.n_late) return 0;
   g = std::min(g, rf::kMaxGroup);
-  return rope_bytes(p->s) + kFlagBytes + prep_bytes(p->s, g);
+  return rope_bytes(p->s) + kFlagBytes + prep_bytes(p->s, g) + rs_bytes(p->s.n_rows, g);
 }
 
 size_t rf_fill_rows_workspace_bytes(int32_t n_rows) {
@@ -476,6 +483,8 @@ rf_status fill_impl(rf_plan* p, const char* fn, const uint16_t* x, int64_t ld_x,
   uint16_t* ybuf = reinterpret_cast<uint16_t*>(w0 + rope_bytes(s) + kFlagBytes + prep_bytes(s, G));
   uint16_t* dq = reinterpret_cast<uint16_t*>(w0 + rope_bytes(s) + kFlagBytes + prep_bytes(s, G) +
                                              y_bytes(s, n_fill, G));
+  float* ssq = reinterpret_cast<float*>(reinterpret_cast<char*>(dq) + dq_bytes(s, p->flags, G));
+  float* rsb = reinterpret_cast<float*>(reinterpret_cast<char*>(ssq) + ssq_bytes(s, n_fill, G));
 
   hipError_t e;
   if (p->flags & RF_VALIDATE)
@@ -499,6 +508,7 @@ rf_status fill_impl(rf_plan* p, const char* fn, const uint16_t* x, int64_t ld_x,
   mp.tiles_m = (n_fill + rf::kTileM - 1) / rf::kTileM;
   mp.tiles_n = s.d_out / rf::kTileN;
   mp.y = ybuf;
+  mp.ssq = ssq;
 
   rf::KvParams kp{};
   kp.ld_in = s.d_out;
@@ -540,6 +550,7 @@ rf_status fill_impl(rf_plan* p, const char* fn, const uint16_t* x, int64_t ld_x,
       pp.wk[i] = w_k[l0 + i];
       pp.wv[i] = w_v[l0 + i];
       kp.in[i] = ybuf + i * y_layer;
+      kp.rs[i] = rsb + static_cast<size_t>(i) * n_fill;
       kp.kc[i] = k_cache[l0 + i];
       kp.vc[i] = v_cache[l0 + i];
       kp.vscale[i] = vscale ? vscale->scale + (l0 + i) * vs_layer : nullptr;
@@ -556,6 +567,11 @@ rf_status fill_impl(rf_plan* p, const char* fn, const uint16_t* x, int64_t ld_x,
     }
     if ((st = feed.consumed(l0)) != RF_OK) return st;
     {
+      Timed tm(p, RF_K_NORM, hs);
+      if ((e = rf::launch_row_scale(ssq, mp.tiles_n, n_fill, g, 1.0f / s.d_out, s.rms_eps, rsb, hs)) != hipSuccess)
+        return hip_fail(e, "row scale launch");
+    }
+    {
       Timed tm(p, RF_K_KV, hs);
       if ((e = rf::launch_kv(kp, g, hs)) != hipSuccess) return hip_fail(e, "kv launch");
     }
@@ -565,7 +581,7 @@ rf_status fill_impl(rf_plan* p, const char* fn, const uint16_t* x, int64_t ld_x,
 
 // Workspace of the value-scale measurement, in carve order.
 struct ScaleWs {
-  size_t prep, y, dq, v, ratio, pos, total;
+  size_t prep, y, dq, v, ratio, pos, ssq, rs, total;
 };
 ScaleWs scale_ws(const rf_plan* p, int n, int g) {
   const rf_shape& s = p->s;
@@ -576,7 +592,9 @@ ScaleWs scale_ws(const rf_plan* p, int n, int g) {
   r.v = up(static_cast<size_t>(g) * n * kv_width(s) * 2);
   r.ratio = up(static_cast<size_t>(s.n_late) * n * s.n_kv * 4);
   r.pos = up(static_cast<size_t>(std::max(n, 1)) * 4);
-  r.total = kFlagBytes + r.prep + r.y + r.dq + 2 * r.v + r.ratio + r.pos;
+  r.ssq = ssq_bytes(s, n, g);
+  r.rs = rs_bytes(n, g);
+  r.total = kFlagBytes + r.prep + r.y + r.dq + 2 * r.v + r.ratio + r.pos + r.ssq + r.rs;
   return r;
 }
 
@@ -615,6 +633,8 @@ rf_status value_scales_impl(rf_plan* p, const char* fn, const uint16_t* x, int64
   uint16_t* vp = reinterpret_cast<uint16_t*>(c += sw.v);
   float* ratio = reinterpret_cast<float*>(c += sw.v);
   int32_t* zero_pos = reinterpret_cast<int32_t*>(c += sw.ratio);
+  float* ssq = reinterpret_cast<float*>(c += sw.pos);
+  float* rsb = reinterpret_cast<float*>(c += sw.ssq);
 
   hipError_t e;
   const int w = kv_width(s);
@@ -630,6 +650,7 @@ rf_status value_scales_impl(rf_plan* p, const char* fn, const uint16_t* x, int64
     mp.tiles_m = (n + rf::kTileM - 1) / rf::kTileM;
     mp.tiles_n = s.d_out / rf::kTileN;
     mp.y = ybuf;
+    mp.ssq = ssq;
 
     // Value half only, row m of the call stored densely at row m (slot = row,
     // rows numbered 0..n-1 for this launch; positions are not used by values).
@@ -687,20 +708,41 @@ rf_status value_scales_impl(rf_plan* p, const char* fn, const uint16_t* x, int64
         if ((e = rf::launch_map(mp, g, hs)) != hipSuccess) return hip_fail(e, "map launch");
       }
       if ((st = feed.consumed(l0)) != RF_OK) return st;
-      // predicted values from the map's output, exact values from the true inputs
+      // predicted values from the map's output (norms from its row sums),
+      // exact values from the true inputs (norms from a pass over them)
+      {
+        Timed tm(p, RF_K_SCALE, hs);
+        if ((e = rf::launch_row_scale(ssq, mp.tiles_n, n, g, 1.0f / s.d_out, s.rms_eps, rsb, hs)) != hipSuccess)
+          return hip_fail(e, "row scale launch");
+      }
       kp.ld_in = s.d_out;
       for (int i = 0; i < g; ++i) {
         kp.in[i] = ybuf + i * y_layer;
         kp.vc[i] = vp + i * v_layer;
+        kp.rs[i] = rsb + static_cast<size_t>(i) * n;
       }
       {
         Timed tm(p, RF_K_SCALE, hs);
         if ((e = rf::launch_kv(kp, g, hs)) != hipSuccess) return hip_fail(e, "kv launch");
       }
+      rf::RmsParams rmp{};
+      rmp.ld_in = ld_in;
+      rmp.n_in_rows = n;
+      rmp.M = n;
+      rmp.K = s.d_out;
+      rmp.inv_k = 1.0f / s.d_out;
+      rmp.eps = s.rms_eps;
+      rmp.rs = rsb;
       kp.ld_in = ld_in;
       for (int i = 0; i < g; ++i) {
         kp.in[i] = layer_in[l0 + i];
         kp.vc[i] = ve + i * v_layer;
+        rmp.in[i] = layer_in[l0 + i];
+      }
+      {
+        // (the same stream: the predicted launch above has read rsb)
+        Timed tm(p, RF_K_SCALE, hs);
+        if ((e = rf::launch_row_rms(rmp, g, hs)) != hipSuccess) return hip_fail(e, "row rms launch");
       }
       {
         Timed tm(p, RF_K_SCALE, hs);
@@ -840,6 +882,7 @@ rf_status rf_kv_project(rf_plan* p, const uint16_t* const* layer_in, int64_t ld_
   float* rope_ws = reinterpret_cast<float*>(w0);
   int32_t* flag = reinterpret_cast<int32_t*>(w0 + rope_bytes(s));
   uint16_t* prep = reinterpret_cast<uint16_t*>(w0 + rope_bytes(s) + kFlagBytes);
+  float* rsb = reinterpret_cast<float*>(w0 + rope_bytes(s) + kFlagBytes + prep_bytes(s, G));
   hipError_t e;
   if (p->flags & RF_VALIDATE)
     if ((st = run_validate(p, rows, n, 0, positions, slot_of_row, flag, hs)) != RF_OK) return st;
@@ -876,6 +919,15 @@ rf_status rf_kv_project(rf_plan* p, const uint16_t* const* layer_in, int64_t ld_
   pp.d = s.d_out;
   pp.w = w;
   pp.out = prep;
+  rf::RmsParams rp{};
+  rp.ld_in = ld_in;
+  rp.in_rows = rows;
+  rp.n_in_rows = s.n_rows;
+  rp.M = n;
+  rp.K = s.d_out;
+  rp.inv_k = 1.0f / s.d_out;
+  rp.eps = s.rms_eps;
+  rp.rs = rsb;
   for (int l0 = 0; l0 < L; l0 += G) {
     const int g = std::min(G, L - l0);
     for (int i = 0; i < g; ++i) {
@@ -883,6 +935,8 @@ rf_status rf_kv_project(rf_plan* p, const uint16_t* const* layer_in, int64_t ld_
       pp.wk[i] = w_k[l0 + i];
       pp.wv[i] = w_v[l0 + i];
       kp.in[i] = layer_in[l0 + i];
+      rp.in[i] = layer_in[l0 + i];
+      kp.rs[i] = rsb + static_cast<size_t>(i) * n;
       kp.kc[i] = k_cache[l0 + i];
       kp.vc[i] = v_cache[l0 + i];
       kp.kgamma[i] = k_norm ? k_norm[l0 + i] : nullptr;
@@ -890,6 +944,10 @@ rf_status rf_kv_project(rf_plan* p, const uint16_t* const* layer_in, int64_t ld_
     {
       Timed tm(p, RF_K_PREP, hs);
       if ((e = rf::launch_prep(pp, g, hs)) != hipSuccess) return hip_fail(e, "prep launch");
+    }
+    {
+      Timed tm(p, RF_K_NORM, hs);
+      if ((e = rf::launch_row_rms(rp, g, hs)) != hipSuccess) return hip_fail(e, "row rms launch");
     }
     {
       Timed tm(p, RF_K_KV, hs);

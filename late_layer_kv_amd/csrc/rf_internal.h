@@ -27,13 +27,18 @@ struct MapParams {
   int32_t N;              // d_out
   int32_t tiles_m, tiles_n;
   uint16_t* y;            // [n_layers][M][N]
+  // Row sums of squares of the stored (bf16) Y, one partial per 256-feature
+  // tile: ssq[(g * tiles_n + tn) * M + m], or null (not written).
+  float* ssq;
   const uint16_t* a[kMaxGroup];  // [N][K]
   const uint16_t* b[kMaxGroup];  // [N]
 };
 
 // Norm + key/value contraction with the RoPE and cache-scatter epilogue:
 //   acc[m][f] = sum_k in_g[src(m)][k] * Wp_g[f][k],  Wp_g = bf16(W_kv * gamma)
-//   out = acc / sqrt(mean_k in^2 + eps), RoPE on key features, bf16 to the cache.
+//   out = acc * rs_g[m], RoPE on key features, bf16 to the cache, where
+//   rs_g[m] = 1 / sqrt(mean_k in_g[src(m)][k]^2 + eps) comes precomputed
+//   (launch_row_scale from the map's row sums, or launch_row_rms).
 struct KvParams {
   int64_t ld_in;
   const int32_t* in_rows;   // [M] gather index into in_g, or null (row m)
@@ -68,6 +73,7 @@ struct KvParams {
   uint16_t* vc[kMaxGroup];
   const float* vscale[kMaxGroup];  // [n_groups][n_kv] per layer, or null
   const uint16_t* kgamma[kMaxGroup];  // [head_dim] per layer (qk_norm)
+  const float* rs[kMaxGroup];  // [M] norm factor of row m of this call, per layer
 };
 
 // Prepared projection weights: out_g[f][k] = bf16(W[f][k] * gamma_g[k]),
@@ -91,6 +97,10 @@ struct DequantParams {
 };
 
 hipError_t launch_map(const MapParams& p, int n_layers, hipStream_t s);
+// rs[g * M + m] = 1 / sqrt(sum_t ssq[(g * tiles + t) * M + m] * inv_k + eps), the
+// map's tile partials summed in tile order.
+hipError_t launch_row_scale(const float* ssq, int tiles, int M, int n_layers, float inv_k, float eps, float* rs,
+                            hipStream_t s);
 hipError_t launch_dequant(const DequantParams& p, int n_layers, hipStream_t s);
 
 // Value-rescale measurement: per layer, ratio[m][h] = ||ve[m][h]|| / ||vp[m][h]|| over the
@@ -109,6 +119,17 @@ hipError_t launch_zero_i32(int32_t* p, int n, hipStream_t s);
 hipError_t launch_scale_mean(const float* ratio, const int32_t* group, int n, int n_kv, int n_groups,
                              int n_late, float* scale, hipStream_t s);
 hipError_t launch_kv(const KvParams& p, int n_layers, hipStream_t s);
+// rs[g * M + m] = 1 / sqrt(mean_k in_g[src(m)][k]^2 + eps) for inputs that do
+// not come from the map contraction (src as in KvParams).
+struct RmsParams {
+  int64_t ld_in;
+  const int32_t* in_rows;  // [M] or null (row m)
+  int32_t n_in_rows, M, K;  // K a multiple of 256
+  float inv_k, eps;        // inv_k = 1.0f / K, as the map path's row_scale is given it
+  float* rs;               // [n_layers][M]
+  const uint16_t* in[kMaxGroup];
+};
+hipError_t launch_row_rms(const RmsParams& p, int n_layers, hipStream_t s);
 hipError_t launch_prep(const PrepParams& p, int n_layers, hipStream_t s);
 hipError_t launch_rope_table(float* table, int max_pos, int head_dim, double theta, hipStream_t s);
 hipError_t launch_fill_rows(const int32_t* exact, int n_exact, int n_rows, int32_t* mask,

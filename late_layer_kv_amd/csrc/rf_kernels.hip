@@ -88,6 +88,19 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
   return __builtin_bit_cast(uint32_t, v);
 }
 
+// Row sums of squares for the norm are formed the same way wherever the row
+// comes from (map epilogue or a pass over given inputs), so that the two give
+// bitwise-equal factors: per 256-feature tile, each of its two 128-feature
+// halves is split into four lane parts (features 16 nb + 4 q + v), each part
+// summed over nb = 0..7 with this pair of bf16 dot products (4 consecutive
+// features packed as two bf16 pairs), then (q0 + q1) + (q2 + q3), then
+// half 0 + half 1; tiles are added in ascending order.
+__device__ __forceinline__ float sq4(float s, uint32_t lo, uint32_t hi) {
+  const bf16x2 a = __builtin_bit_cast(bf16x2, lo), b = __builtin_bit_cast(bf16x2, hi);
+  s = __builtin_amdgcn_fdot2_f32_bf16(a, a, s, false);
+  return __builtin_amdgcn_fdot2_f32_bf16(b, b, s, false);
+}
+
 // Workgroups are dealt round-robin to the 8 XCDs.  Renumber them so that each
 // XCD works on one contiguous range of logical tiles, which the tile order
 // below makes share operand strips in that XCD's L2.
@@ -192,20 +205,6 @@ __device__ __forceinline__ float agpr(float a) {
   return v;
 }
 
-// Sum of squares of the wave's 4 row blocks 4 HALF .. + 3 (this lane's chunk).
-template <int HALF>
-__device__ __forceinline__ void sumsq(const Frags& f, float (&ss)[4]) {
-#pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const bf16x8& b = f.b[4 * HALF + j];
-    float& s_ = ss[j];
-    s_ = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(b, b, 0, 1), __builtin_shufflevector(b, b, 0, 1), s_, false);
-    s_ = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(b, b, 2, 3), __builtin_shufflevector(b, b, 2, 3), s_, false);
-    s_ = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(b, b, 4, 5), __builtin_shufflevector(b, b, 4, 5), s_, false);
-    s_ = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(b, b, 6, 7), __builtin_shufflevector(b, b, 6, 7), s_, false);
-  }
-}
-
 // The 64 MFMAs of one 32-column step on fragments f.  With READ, the 16
 // fragment reads of the next step (into nf, from slots ws / xs) follow MFMAs
 // 0..15 one each; with LOAD, the 8 operand loads of one slot follow every
@@ -238,31 +237,26 @@ __device__ __forceinline__ void mma_step(const Frags& f, f32x4 (&acc)[8][8], Fra
 //          needs u <= 2t+3 landed; u = 2t+4 may still fly).
 // Step 0 reads step 1's fragments from the current slots; after the barrier,
 // step 1 reads the next stage's step-0 fragments.
-template <bool SUMSQ, int HALF, bool PEND, bool ISSUE, int WAIT>
-__device__ __forceinline__ void stage(Frags& fa, Frags& fb, f32x4 (&acc)[8][8], float (&ss)[4], int& sw, int t,
+template <bool PEND, bool ISSUE, int WAIT>
+__device__ __forceinline__ void stage(Frags& fa, Frags& fb, f32x4 (&acc)[8][8], int& sw, int t,
                                         char* smem, char* mydst, const char* const (&wsrc)[8],
                                         const char* const (&xsrc)[8], const int (&aoff)[2], const int (&boff)[2]) {
   const char* ws = smem + sw * kSlotBytes;
   const char* xs = smem + ring(sw + 1) * kSlotBytes;
-  if (SUMSQ) sumsq<HALF>(fa, ss);
   mma_step<true, PEND>(fa, acc, fb, ws, xs, aoff[1], boff[1], wsrc, static_cast<size_t>(t + 2) * kRowBytes,
                          mydst + ring(sw + 4) * kSlotBytes);
   wait_slots(WAIT);
   barrier();
   const int nsw = ring(sw + 2);
-  if (SUMSQ) sumsq<HALF>(fb, ss);
   mma_step<true, ISSUE>(fb, acc, fa, smem + nsw * kSlotBytes, smem + ring(nsw + 1) * kSlotBytes, aoff[0], boff[0],
                           xsrc, static_cast<size_t>(t + 2) * kRowBytes, mydst + sw * kSlotBytes);
   sw = nsw;
 }
 
-// Main loop over nk stages, shared by both contractions.  On return acc[nb][mb] holds
-// features 16 nb + 4 (l >> 4) + v, row 16 mb + (l & 15) of the wave's block,
-// and with SUMSQ ss[j] this lane's part (its 8-column chunk of every 32) of
-// the sum of squares of row block 4 HALF + j.
-template <bool SUMSQ, int HALF = 0>
+// Main loop over nk stages, shared by both contractions.  On return acc[nb][mb]
+// holds features 16 nb + 4 (l >> 4) + v, row 16 mb + (l & 15) of the wave's block.
 __device__ __forceinline__ void mainloop(const char* const (&wsrc)[8], const char* const (&xsrc)[8], int nk,
-                                           char* smem, f32x4 (&acc)[8][8], float (&ss)[4]) {
+                                         char* smem, f32x4 (&acc)[8][8]) {
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int wn = wave & 1, wm = wave >> 1;
@@ -276,8 +270,6 @@ __device__ __forceinline__ void mainloop(const char* const (&wsrc)[8], const cha
     aoff[st] = slot_pos(wn * 128 + r15, 4 * st + q);
     boff[st] = slot_pos(wm * 128 + r15, 4 * st + q);
   }
-#pragma unroll
-  for (int i = 0; i < 4; ++i) ss[i] = 0.0f;
 #pragma unroll
   for (int i = 0; i < 8; ++i)
 #pragma unroll
@@ -298,16 +290,14 @@ __device__ __forceinline__ void mainloop(const char* const (&wsrc)[8], const cha
   int sw = 0;
   read_frags(fa, smem, smem + kSlotBytes, aoff[0], boff[0]);
   int t = 0;
-  for (; t + 3 <= nk; ++t) stage<SUMSQ, HALF, true, true, 1>(fa, fb, acc, ss, sw, t, smem, mydst, wsrc, xsrc, aoff, boff);
+  for (; t + 3 <= nk; ++t) stage<true, true, 1>(fa, fb, acc, sw, t, smem, mydst, wsrc, xsrc, aoff, boff);
   if (t + 2 == nk) {
-    stage<SUMSQ, HALF, false, false, 0>(fa, fb, acc, ss, sw, t, smem, mydst, wsrc, xsrc, aoff, boff);
+    stage<false, false, 0>(fa, fb, acc, sw, t, smem, mydst, wsrc, xsrc, aoff, boff);
     ++t;
   }
   const char* ws = smem + sw * kSlotBytes;
   const char* xs = smem + ring(sw + 1) * kSlotBytes;
-  if (SUMSQ) sumsq<HALF>(fa, ss);
   mma_step<true, false>(fa, acc, fb, ws, xs, aoff[1], boff[1], wsrc, 0, mydst);
-  if (SUMSQ) sumsq<HALF>(fb, ss);
   mma_step<false, false>(fb, acc, fa, ws, xs, 0, 0, wsrc, 0, mydst);
   // The compiler does not see the MFMAs in the assembly statements: give the
   // last ones the wait states an MFMA result needs before other instructions
@@ -359,12 +349,18 @@ __global__ void __launch_bounds__(kThreads) map_gemm_kernel(const MapParams p) {
   }
 
   f32x4 acc[8][8];
-  float ss[4];
-  mainloop<false>(wsrc, xsrc, p.K / kBK, smem, acc, ss);
+  mainloop(wsrc, xsrc, p.K / kBK, smem, acc);
 
   // Epilogue: + b, round to bf16, stage, 16-byte row stores into Y_g.  A lane
   // holds 4 consecutive features (8 bytes, one half of a staged chunk) of a row.
+  // With p.ssq the squares of the stored bf16 values are summed per row as
+  // well (for the norm of the next contraction): per lane over its 32
+  // features, then over the four lanes of the row, then the two waves of the
+  // tile's feature halves meet in LDS.
   __syncthreads();  // every wave is done reading the operand stages
+  float sq[8];
+#pragma unroll
+  for (int mb = 0; mb < 8; ++mb) sq[mb] = 0.0f;
 #pragma unroll
   for (int nb = 0; nb < 8; ++nb) {
     const float b0 = bf16_to_f32(braw[nb].x & 0xffff), b1 = bf16_to_f32(braw[nb].x >> 16);
@@ -378,9 +374,22 @@ __global__ void __launch_bounds__(kThreads) map_gemm_kernel(const MapParams p) {
       o.x = pack_bf16x2(v[0] + b0, v[1] + b1);
       o.y = pack_bf16x2(v[2] + b2, v[3] + b3);
       *reinterpret_cast<uint2*>(smem + stage_off(row, chunk) + (q & 1) * 8) = o;
+      sq[mb] = sq4(sq[mb], o.x, o.y);
+    }
+  }
+  float* const sq_lds = reinterpret_cast<float*>(smem + kSlotOffset);  // [2][256], past the staging tile
+  if (p.ssq) {
+#pragma unroll
+    for (int mb = 0; mb < 8; ++mb) {
+      float t = sq[mb] + __shfl_xor(sq[mb], 16);
+      t += __shfl_xor(t, 32);
+      if (q == 0) sq_lds[wn * 256 + wm * 128 + mb * 16 + r15] = t;
     }
   }
   __syncthreads();
+  if (p.ssq && m0 + static_cast<int>(threadIdx.x) < p.M)
+    p.ssq[(static_cast<size_t>(c.g) * p.tiles_n + c.tn) * p.M + m0 + threadIdx.x] =
+        sq_lds[threadIdx.x] + sq_lds[256 + threadIdx.x];
   uint16_t* y = p.y + static_cast<size_t>(c.g) * p.M * p.N;
   const int chunk = threadIdx.x & 31;
 #pragma unroll 4
@@ -392,6 +401,55 @@ __global__ void __launch_bounds__(kThreads) map_gemm_kernel(const MapParams p) {
       *reinterpret_cast<uint4*>(y + static_cast<size_t>(m) * p.N + n0 + chunk * 8) = v;
     }
   }
+}
+
+// Norm factor per row from the map contraction's per-tile sums of squares,
+// summed in tile order (deterministic).
+__global__ void __launch_bounds__(256) row_scale_kernel(const float* __restrict__ ssq, int tiles, int M,
+                                                        float inv_k, float eps, float* __restrict__ rs) {
+  const int g = blockIdx.y;
+  const int m = blockIdx.x * 256 + threadIdx.x;
+  if (m >= M) return;
+  const float* src = ssq + static_cast<size_t>(g) * tiles * M + m;
+  float t = 0.0f;
+  for (int j = 0; j < tiles; ++j) t += src[static_cast<size_t>(j) * M];
+  rs[static_cast<size_t>(g) * M + m] = rsqrtf(t * inv_k + eps);
+}
+
+// Norm factor of rows that do not come from the map contraction: one wave per
+// row, with the sums formed exactly as the map epilogue and row_scale_kernel
+// form them (see sq4): lane l takes part q = l & 3 of half (l >> 2) & 1 of
+// tile 8 i + (l >> 3) in round i.
+__global__ void __launch_bounds__(256) row_rms_kernel(const RmsParams p) {
+  const int g = blockIdx.y;
+  const int m = blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  if (m >= p.M) return;  // whole waves leave together
+  int row = p.in_rows ? p.in_rows[m] : m;
+  row = (row >= 0 && row < p.n_in_rows) ? row : 0;
+  const uint16_t* src = p.in[g] + static_cast<size_t>(row) * p.ld_in;
+  const int tiles = p.K / kTileN;
+  const int q = lane & 3, half = (lane >> 2) & 1, jj = lane >> 3;
+  float total = 0.0f;
+  for (int i = 0; i * 8 < tiles; ++i) {
+    const int j = min(i * 8 + jj, tiles - 1);  // lanes past the last tile load it again, unused
+    const uint16_t* t0 = src + j * kTileN + half * 128 + q * 4;
+    float s_ = 0.0f;
+#pragma unroll
+    for (int nb = 0; nb < 8; ++nb) {
+      const uint2 v = *reinterpret_cast<const uint2*>(t0 + nb * 16);
+      s_ = sq4(s_, v.x, v.y);
+    }
+    float t = s_ + __shfl_xor(s_, 1);
+    t += __shfl_xor(t, 2);
+    t += __shfl_xor(t, 4);
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      const float v = __shfl(t, k * 8);
+      if (i * 8 + k < tiles) total += v;
+    }
+  }
+  if (lane == 0) p.rs[static_cast<size_t>(g) * p.M + m] = rsqrtf(total * p.inv_k + p.eps);
 }
 
 // VSCALE: the value rescale is applied; QK: keys are RMS-normalised per head
@@ -425,22 +483,20 @@ __global__ void __launch_bounds__(kThreads) kv_gemm_kernel(const KvParams p) {
   }
 
   const int wn = wave & 1, wm = wave >> 1, r15 = lane & 15, q = lane >> 4;
-  // Output-row indices of this lane's 8 rows, fetched before the main loop so
-  // their latency hides behind it (indices clamped: every load is in bounds).
+  // Output-row indices and norm factors of this lane's 8 rows, fetched before
+  // the main loop so their latency hides behind it (indices clamped: every
+  // load is in bounds).
   int orow[8];
+  float rs[8];
 #pragma unroll
   for (int mb = 0; mb < 8; ++mb) {
     const int m = min(m0 + wm * 128 + mb * 16 + r15, p.M - 1);
     orow[mb] = p.out_rows ? p.out_rows[m] : m;
+    rs[mb] = p.rs[c.g][m];
   }
 
   f32x4 acc[8][8];
-  float ss[4];
-  // wave-uniform branch: the two waves of a row half each sum four row blocks
-  if ((wave & 1) == 0)
-    mainloop<true, 0>(wsrc, xsrc, p.K / kBK, smem, acc, ss);
-  else
-    mainloop<true, 1>(wsrc, xsrc, p.K / kBK, smem, acc, ss);
+  mainloop(wsrc, xsrc, p.K / kBK, smem, acc);
 
   // Row bookkeeping, branch-free so that all loads of a kind issue together:
   // position, cache slot and (rescale) request of each row; a row that is out
@@ -475,24 +531,11 @@ __global__ void __launch_bounds__(kThreads) kv_gemm_kernel(const KvParams p) {
     grp_r[mb] = good ? grp_r[mb] : 0;
   }
   __builtin_amdgcn_sched_barrier(0);
-  const float inv_k = 1.0f / static_cast<float>(p.K);
-  // Sums of squares: this wave holds row blocks 4 wn .. 4 wn + 3 in ss[0..3],
-  // each lane one 8-column chunk of every 32; the other wave of its row half
-  // holds the other blocks.  Full row sums (all four lane groups) are swapped
-  // through LDS once every wave is done with the operands.
-  float* const ss_lds = reinterpret_cast<float*>(smem + kSlotOffset + 1024);
-  __syncthreads();
-#pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    float tot = ss[j] + __shfl_xor(ss[j], 16);
-    tot += __shfl_xor(tot, 32);
-    if (q == 0) ss_lds[wm * 128 + (4 * wn + j) * 16 + r15] = tot;
-  }
+  __syncthreads();  // every wave is done with the operand slots
   if (wn == 0 && q == 0) {
 #pragma unroll
     for (int mb = 0; mb < 8; ++mb) slot_of[wm * 128 + mb * 16 + r15] = slot_r[mb];
   }
-  __syncthreads();
   const int fw = n0 + wn * 128;  // first feature of this wave; a whole wave is key or value
   // (with v_only, a tile may start inside the keys when w is not a multiple of
   // 256; those key waves are neither rotated nor stored)
@@ -502,12 +545,9 @@ __global__ void __launch_bounds__(kThreads) kv_gemm_kernel(const KvParams p) {
   // into the norm's per-row factor; without a rescale the factor is exactly
   // the norm's scale.
   const float* const vsw = (VSCALE && !is_key) ? p.vscale[c.g] + (fw - p.w) / HD : nullptr;
-  float rs[8], rs2[8];
+  float rs2[8];
 #pragma unroll
-  for (int mb = 0; mb < 8; ++mb) {
-    rs[mb] = rsqrtf(ss_lds[wm * 128 + mb * 16 + r15] * inv_k + p.eps);
-    rs2[mb] = rs[mb];
-  }
+  for (int mb = 0; mb < 8; ++mb) rs2[mb] = rs[mb];
   if (VSCALE && vsw) {  // wave-uniform; the 8 (16) scale loads issue together
     float sa[8], sb[8];
 #pragma unroll
@@ -740,6 +780,19 @@ __global__ void __launch_bounds__(256) validate_kernel(const int32_t* rows, int 
 hipError_t launch_map(const MapParams& p, int n_layers, hipStream_t s) {
   const int grid = n_layers * p.tiles_m * p.tiles_n;
   hipLaunchKernelGGL(map_gemm_kernel, dim3(grid), dim3(kThreads), 0, s, p);
+  return hipGetLastError();
+}
+
+hipError_t launch_row_scale(const float* ssq, int tiles, int M, int n_layers, float inv_k, float eps, float* rs,
+                            hipStream_t s) {
+  if (M <= 0 || n_layers <= 0) return hipSuccess;
+  hipLaunchKernelGGL(row_scale_kernel, dim3((M + 255) / 256, n_layers), dim3(256), 0, s, ssq, tiles, M, inv_k, eps, rs);
+  return hipGetLastError();
+}
+
+hipError_t launch_row_rms(const RmsParams& p, int n_layers, hipStream_t s) {
+  if (p.M <= 0 || n_layers <= 0) return hipSuccess;
+  hipLaunchKernelGGL(row_rms_kernel, dim3((p.M + 3) / 4, n_layers), dim3(256), 0, s, p);
   return hipGetLastError();
 }
 

@@ -109,12 +109,16 @@ def test_workspace_sizes():
     assert p.fill_workspace_bytes(448, 4) > p.fill_workspace_bytes(448, 1)
     assert p.fill_workspace_bytes(448, 5) == 0   # more layers than the plan has
     assert p.fill_workspace_bytes(-1, 1) == 0
-    # rope table + flag + prepared weights + Y, each rounded to 256 bytes
+    # rope table + flag + prepared weights + Y + per-tile row sums of squares
+    # + per-row norm factors, each rounded to 256 bytes
     rope = 512 * 32 * 8
     prep = 2 * 128 * 256 * 2
     y = 448 * 256 * 2
-    assert p.fill_workspace_bytes(448, 1) == rope + 256 + prep + y
-    assert p.kv_project_workspace_bytes(2) == rope + 256 + 2 * prep
+    ssq = 448 * (256 // 256) * 4
+    rs = 448 * 4
+    assert p.fill_workspace_bytes(448, 1) == rope + 256 + prep + y + ssq + rs
+    assert p.fill_workspace_bytes(448, 2) == rope + 256 + 2 * (prep + y + ssq + rs)
+    assert p.kv_project_workspace_bytes(2) == rope + 256 + 2 * prep + 2 * 512 * 4  # + norm factor per plan row
     assert B.fill_rows_workspace_bytes(1000) == 4096
     p.close()
 
@@ -307,9 +311,11 @@ def test_value_scales_argument_errors_and_workspace():
     assert L.rf_value_scales_q8(p.handle, f, 256, arr, 256, f, f, 16, 2, arr, arr, arr, arr, arr, f, ws, ws_b,
                                 None) == -1
     # workspace: flag + prepared weights + Y + two value buffers + ratios + zero positions
+    # + per-tile row sums of squares + per-row norm factors
     n, w, d = 40, 128, 256
     up = lambda v: (v + 255) // 256 * 256
-    want = 256 + 2 * w * d * 2 + up(n * d * 2) + 2 * up(n * w * 2) + up(4 * n * 2 * 4) + up(n * 4)
+    want = (256 + 2 * w * d * 2 + up(n * d * 2) + 2 * up(n * w * 2) + up(4 * n * 2 * 4) + up(n * 4)
+            + up(n * (d // 256) * 4) + up(n * 4))
     assert p.value_scales_workspace_bytes(n, 1) == want
     assert p.value_scales_workspace_bytes(n, 5) == 0
     p.close()
