@@ -23,7 +23,7 @@ some pin fails for each.  No function here is "parity unpinned".
 from .fill import (  # noqa: F401
     bf16_bits_to_f64, fill_row_set, predicted_input, rms_norm, project,
     rope_inv_freq, rope, layer_kv, fill_layer, fill_workload, exact_kv_workload,
-    map_matrix, qk_norm,
+    map_matrix, qk_norm, indexer_keys, fill_indexer_workload, exact_indexer_workload,
 )
 from .ridge import RidgeSums, ridge_fit, ridge_fit_raw  # noqa: F401
 from .ceiling import layer_ceiling, mac_ceiling  # noqa: F401

@@ -17,7 +17,12 @@ where they are taken:
   angle pos * theta^(-2j/hd), with no frequency scaling;
 * QK-norm (layers that normalise their keys) is an RMSNorm over each key head
   with a per-dimension gain shared by the heads and the layer's eps, applied
-  after the key projection and before the rotation.
+  after the key projection and before the rotation;
+* the sparse-attention indexer's keys that filled rows also write (section 2.1,
+  section 5.1: one 128-wide key head shared by the indexer's query heads) are
+  projected from the same normalised input as the layer's keys and values and
+  rotated the same way; no key norm applies to them (the pages give the
+  indexer no normalization of its own).
 """
 from __future__ import annotations
 
@@ -121,6 +126,17 @@ def layer_kv(h_in: np.ndarray, gamma: np.ndarray, w_k: np.ndarray, w_v: np.ndarr
     return k, v
 
 
+def indexer_keys(h_in: np.ndarray, gamma: np.ndarray, w_idx: np.ndarray, positions: np.ndarray,
+                 theta: float, head_dim: int, eps: float) -> np.ndarray:
+    """The indexer keys a late sparse-attention layer writes from an input row.
+
+    Section 2.1 (filled rows also write the indexer's keys, section 5.1): the
+    layer's normalised input times the indexer key projection W_idx
+    [heads * head_dim][d], each head rotated like the attention keys.
+    """
+    return rope(project(rms_norm(h_in, gamma, eps), w_idx), positions, theta, head_dim)
+
+
 def fill_layer(x_s, a, b, gamma, w_k, w_v, positions, theta, head_dim, eps, k_gamma=None):
     """One late layer's filled K/V: the map's prediction through layer_kv."""
     return layer_kv(predicted_input(x_s, a, b), gamma, w_k, w_v, positions,
@@ -186,3 +202,31 @@ def exact_kv_workload(w, layer_inputs: np.ndarray, rows: np.ndarray,
                           bf16_bits_to_f64(w.w_v[l]), pos, s.rope_theta, s.head_dim, s.rms_eps,
                           _k_gamma(w, l))
     return out
+
+
+def fill_indexer_workload(w, rows: Optional[np.ndarray] = None,
+                          layers: Optional[List[int]] = None) -> Dict[int, np.ndarray]:
+    """fp64 indexer keys of every late layer for the given (filled) rows:
+    {layer: [len(rows)][idx_heads * head_dim]}, unrounded."""
+    s = w.spec
+    r = _rows(w, rows)
+    xs = bf16_bits_to_f64(w.x[r])
+    pos = w.positions[r]
+    out = {}
+    for l in (range(s.n_late) if layers is None else layers):
+        y = predicted_input(xs, map_matrix(w, l), bf16_bits_to_f64(w.map_b[l]))
+        out[l] = indexer_keys(y, bf16_bits_to_f64(w.gamma[l]), bf16_bits_to_f64(w.w_idx[l]), pos,
+                              s.rope_theta, s.head_dim, s.rms_eps)
+    return out
+
+
+def exact_indexer_workload(w, layer_inputs: np.ndarray, rows: np.ndarray,
+                           layers: Optional[List[int]] = None) -> Dict[int, np.ndarray]:
+    """fp64 indexer keys each late layer writes from the given true inputs."""
+    s = w.spec
+    r = np.asarray(rows)
+    h = bf16_bits_to_f64(layer_inputs[r])
+    pos = w.positions[r]
+    return {l: indexer_keys(h, bf16_bits_to_f64(w.gamma[l]), bf16_bits_to_f64(w.w_idx[l]), pos,
+                            s.rope_theta, s.head_dim, s.rms_eps)
+            for l in (range(s.n_late) if layers is None else layers)}

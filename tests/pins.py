@@ -496,6 +496,65 @@ def pin_qk_layer_brute(o):
     assert np.allclose(k0[1], kb0, rtol=1e-11, atol=1e-12)
 
 
+# ---------------------------------------------------------------- indexer keys
+
+def pin_indexer_one_hot(o):
+    """Section 2.1 / 5.1: filled rows also write the indexer's key head.  Worked
+    by hand at position 0 (no rotation): a one-hot projection row c picks
+    gamma_c * y_c / sqrt(mean(y^2) + eps) of the row's input; at position p
+    the pair (j, j + hd/2) of a 2-wide head turns by p * theta^0 = p radians."""
+    y = np.array([[3.0, -4.0, 0.0, 12.0]])          # mean square 169/4
+    gam = np.array([1.0, 2.0, 0.5, 1.0])
+    w = np.zeros((2, 4))
+    w[0, 1] = 1.0                                    # dim 0 <- feature 1
+    w[1, 3] = 1.0                                    # dim 1 <- feature 3
+    r = math.sqrt(169 / 4)
+    got = o.indexer_keys(y, gam, w, np.array([0]), 1e4, 2, 0.0)
+    assert np.allclose(got, [[2 * -4 / r, 12 / r]], rtol=1e-15, atol=0), got
+    got = o.indexer_keys(y, gam, w, np.array([1]), 1e4, 2, 0.0)
+    a, b = -8 / r, 12 / r
+    want = [[a * math.cos(1) - b * math.sin(1), b * math.cos(1) + a * math.sin(1)]]
+    assert np.allclose(got, want, rtol=1e-14, atol=1e-15), got
+
+
+def pin_indexer_brute(o):
+    """Indexer keys of filled rows against plain loops: the map, the norm, the
+    indexer projection and the per-head rotation (tests/brute.py, whose key
+    path is independent of the oracle), for two heads of 8 at three positions."""
+    g = _rng(41)
+    d, hd, n = 32, 8, 3
+    bits = _bits
+    x = bits(g.standard_normal((n, d)))
+    a = bits(np.eye(d) + 0.05 * g.standard_normal((d, d)))
+    b = bits(0.1 * g.standard_normal(d))
+    gam = bits(1 + 0.1 * g.standard_normal(d))
+    wi = bits(g.standard_normal((2 * hd, d)) / np.sqrt(d))
+    pos = np.array([0, 9, 301])
+    f = o.bf16_bits_to_f64
+    got = o.indexer_keys(o.predicted_input(f(x), f(a), f(b)), f(gam), f(wi), pos, 1e4, hd, 1e-5)
+    for i in range(n):
+        kb, _ = brute.filled_row(x[i], a, b, gam, wi, wi, int(pos[i]), 1e4, hd, 1e-5)
+        assert np.allclose(got[i], kb, rtol=1e-11, atol=1e-12), i
+
+
+def pin_indexer_is_a_plain_key_head(o):
+    """With W_idx equal to the first key head's rows the indexer key equals
+    that head of a layer without QK-norm, and a QK-normed layer's gain leaves
+    the indexer key untouched (it has no norm of its own)."""
+    g = _rng(42)
+    d, hd, nkv, n = 48, 16, 3, 4
+    h = g.standard_normal((n, d))
+    gam = 1 + 0.1 * g.standard_normal(d)
+    wk = g.standard_normal((nkv * hd, d)) / np.sqrt(d)
+    wv = g.standard_normal((nkv * hd, d)) / np.sqrt(d)
+    pos = np.array([0, 3, 1000, 65000])
+    k, _ = o.layer_kv(h, gam, wk, wv, pos, 5e5, hd, 1e-5)
+    ik = o.indexer_keys(h, gam, wk[:hd], pos, 5e5, hd, 1e-5)
+    assert np.array_equal(ik, k[:, :hd])
+    kq, _ = o.layer_kv(h, gam, wk, wv, pos, 5e5, hd, 1e-5, 1 + 0.3 * g.standard_normal(hd))
+    assert not np.allclose(kq[:, :hd], ik)
+
+
 # ---------------------------------------------------------------- value rescale
 
 def pin_rescale_closed_form(o):
@@ -631,7 +690,7 @@ FILL_PINS = [pin_fill_rows_partition, pin_identity_map_is_exact_kv, pin_map_orie
              pin_bias_only_map, pin_rmsnorm_closed_forms, pin_one_hot_layer_kv,
              pin_rope_is_complex_rotation, pin_rope_invariants, pin_brute_force_tiny,
              pin_fill_row_independence, pin_qk_norm_closed_form, pin_qk_norm_invariants,
-             pin_qk_layer_brute]
+             pin_qk_layer_brute, pin_indexer_one_hot, pin_indexer_brute, pin_indexer_is_a_plain_key_head]
 RIDGE_PINS = [pin_ridge_recovers_linear_map, pin_ridge_svd_form, pin_ridge_running_sums,
               pin_ridge_penalty_scale, pin_ridge_raw_form]
 CEILING_PINS = [pin_printed_ceilings]

@@ -57,6 +57,17 @@ MUTANTS = {
     "bf16_decode_shift": ("fill.py", [("astype(np.uint32) << 16", "astype(np.uint32) << 15")]),
     # the ridge fit
     "ridge_not_centred": ("ridge.py", [("xc = x - mu_s", "xc = x")]),
+    # indexer keys
+    "idx_no_rope": ("fill.py", [("return rope(project(rms_norm(h_in, gamma, eps), w_idx), positions, theta, head_dim)",
+                                 "return project(rms_norm(h_in, gamma, eps), w_idx)")]),
+    "idx_unnormed": ("fill.py", [("return rope(project(rms_norm(h_in, gamma, eps), w_idx), positions, theta, head_dim)",
+                                  "return rope(project(h_in, w_idx), positions, theta, head_dim)")]),
+    "idx_gain_dropped": ("fill.py", [("return rope(project(rms_norm(h_in, gamma, eps), w_idx), positions, theta, head_dim)",
+                                      "return rope(project(rms_norm(h_in, 1.0, eps), w_idx), positions, theta, head_dim)")]),
+    "idx_half_heads": ("fill.py", [("return rope(project(rms_norm(h_in, gamma, eps), w_idx), positions, theta, head_dim)",
+                                    "return rope(project(rms_norm(h_in, gamma, eps), w_idx), positions, theta, head_dim // 2)")]),
+    "idx_transposed": ("fill.py", [("return rope(project(rms_norm(h_in, gamma, eps), w_idx), positions, theta, head_dim)",
+                                    "return rope(rms_norm(h_in, gamma, eps) @ w_idx, positions, theta, head_dim)")]),
     "ridge_alpha_not_trace_scaled": ("ridge.py", [("alpha = lam * np.trace(gram) / x.shape[1]", "alpha = lam")]),
     "ridge_offset_sign": ("ridge.py", [("b = mu_l - a @ mu_s\n    return a, b", "b = mu_l + a @ mu_s\n    return a, b")]),
     "ridge_sums_not_centred": ("ridge.py", [("cxx = self.sxx - self.n * np.outer(mu_s, mu_s)", "cxx = self.sxx")]),

@@ -30,6 +30,8 @@ value projections):
   [-127, 127];
 * layers that normalise their keys (``qk_norm=True``) get a key-norm gain
   k_gamma_l ~ 1 + N(0, gamma_sigma^2) of length head_dim;
+* layers with a sparse-attention indexer (``idx_heads > 0``) get its key
+  projection W_idx ~ N(0, 1/d_out), stored [idx_heads * head_dim][d_out];
 * positions restart at 0 for every prompt of a batch;
 * the exact set is the last ``tail`` rows of every prompt plus ``n_spans``
   disjoint spans of ``span_len`` rows drawn uniformly inside the first
@@ -51,7 +53,7 @@ __all__ = [
 
 # seed-sequence "kind" tags
 _K_X, _K_OUTLIER, _K_LAYER, _K_SPANS, _K_TRUTH = 1, 2, 3, 4, 5
-_L_MAP, _L_BIAS, _L_GAMMA, _L_WK, _L_WV, _L_QSCALE, _L_KNORM = 0, 1, 2, 3, 4, 5, 6
+_L_MAP, _L_BIAS, _L_GAMMA, _L_WK, _L_WV, _L_QSCALE, _L_KNORM, _L_WIDX = 0, 1, 2, 3, 4, 5, 6, 7
 Q8_BLOCK = 128  # weights per bf16 scale along each row of an int8 map
 _X_BLOCK = 8192  # rows per independently seeded block of x_S
 
@@ -79,6 +81,7 @@ class Spec:
     maps_on_host: bool = False
     map_format: str = "bf16"   # "bf16" or "q8"
     qk_norm: bool = False      # keys normalised per head before RoPE
+    idx_heads: int = 0         # indexer key heads per late layer (head_dim wide each)
     seed: int = 0
 
     @property
@@ -163,6 +166,7 @@ class Workload:
     map_q: Optional[List[np.ndarray]] = None      # q8 only: n_late x int8 [d_out][d_in]
     map_scale: Optional[List[np.ndarray]] = None  # q8 only: n_late x bf16 [d_out][d_in/128]
     k_norm: Optional[List[np.ndarray]] = None     # qk_norm only: n_late x bf16 [head_dim]
+    w_idx: Optional[List[np.ndarray]] = None      # idx_heads only: n_late x bf16 [idx_heads*hd][d_out]
     extra: dict = field(default_factory=dict)
 
 
@@ -280,6 +284,10 @@ def _gen_layer(s: Spec, l: int):
         out += (f32_to_bf16_bits(_normal((s.seed, _K_LAYER, l, _L_KNORM), (s.head_dim,), s.gamma_sigma, 1.0)),)
     else:
         out += (None,)
+    if s.idx_heads:
+        out += (f32_to_bf16_bits(_normal((s.seed, _K_LAYER, l, _L_WIDX), (s.idx_heads * s.head_dim, s.d_out), wsig)),)
+    else:
+        out += (None,)
     return out
 
 
@@ -303,4 +311,5 @@ def make(s: Spec, layers: Optional[List[int]] = None) -> Workload:
         outlier_channels=outliers,
         map_q=[t[5] for t in lay] if s.map_format == "q8" else None,
         map_scale=[t[6] for t in lay] if s.map_format == "q8" else None,
-        k_norm=[t[7] for t in lay] if s.qk_norm else None)
+        k_norm=[t[7] for t in lay] if s.qk_norm else None,
+        w_idx=[t[8] for t in lay] if s.idx_heads else None)
