@@ -53,8 +53,9 @@ def t16(a, dev, pinned=False):
 
 def flops_per_row_layer(s):
     """Algorithmic flops of one filled row in one late layer: the map
-    (2 d_in d_out) and the key and value projections (2 * 2 d_out w)."""
-    return 2 * s.d_in * s.d_out, 4 * s.d_out * s.kv_width
+    (2 d_in d_out) and the key, value and indexer-key projections
+    (2 d_out (2 w + idx_heads hd))."""
+    return 2 * s.d_in * s.d_out, 2 * s.d_out * (2 * s.kv_width + s.idx_heads * s.head_dim)
 
 
 def kernel_source_hash() -> str:
@@ -198,6 +199,8 @@ def main():
     ap.add_argument("--value-rescale", type=int, default=0, metavar="C",
                     help="include the value rescale measured on the first C tail rows of each prompt")
     ap.add_argument("--qk-norm", action="store_true", help="layers normalise their keys per head before RoPE")
+    ap.add_argument("--indexer", type=int, default=0, metavar="HEADS",
+                    help="layers also write HEADS head_dim-wide indexer key heads (sparse-attention layers)")
     ap.add_argument("--maps", default="bf16", choices=["bf16", "q8"],
                     help="map storage: bf16, or int8 codes with one bf16 scale per 128 weights of each row")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -236,7 +239,7 @@ def main():
         return
 
     name = args.workload
-    s = workloads.spec(name, map_format=args.maps, qk_norm=args.qk_norm)
+    s = workloads.spec(name, map_format=args.maps, qk_norm=args.qk_norm, idx_heads=args.indexer)
     q8 = args.maps == "q8"
     dev = "cuda:0"
     log(f"[bench] {name}: drawing inputs")
@@ -254,6 +257,7 @@ def main():
     map_b = [t16(b, dev, host_maps) for b in w.map_b]
     gamma = [t16(g, dev) for g in w.gamma]
     k_norm = [t16(g, dev) for g in w.k_norm] if w.k_norm is not None else None
+    w_idx = [t16(a, dev) for a in w.w_idx] if w.w_idx is not None else None
     w_k = [t16(a, dev) for a in w.w_k]
     w_v = [t16(a, dev) for a in w.w_v]
     positions = torch.from_numpy(w.positions).to(dev)
@@ -261,6 +265,8 @@ def main():
     n_fill = s.n_rows - len(np.unique(w.exact_rows))
     kc = [torch.empty((s.n_rows, s.kv_width), dtype=torch.int16, device=dev) for _ in range(s.n_late)]
     vc = [torch.empty((s.n_rows, s.kv_width), dtype=torch.int16, device=dev) for _ in range(s.n_late)]
+    ic = [torch.empty((s.n_rows, s.idx_heads * s.head_dim), dtype=torch.int16, device=dev)
+          for _ in range(s.n_late)] if w_idx is not None else None
 
     plan = B.Plan.for_spec(s)
     g = args.layers_per_launch or GROUP[name]
@@ -291,10 +297,10 @@ def main():
                                ws_scale)
         if q8:
             B.fill_q8(plan, x, fill_rows, n_fill, positions, None, map_q, map_s, map_b, gamma, w_k, w_v, None,
-                      kc, vc, ws, vscale=vscale, k_norm=k_norm)
+                      kc, vc, ws, vscale=vscale, k_norm=k_norm, w_idx=w_idx, idx_cache=ic)
         else:
             B.fill(plan, x, fill_rows, n_fill, positions, None, map_a, map_b, gamma, w_k, w_v, None, kc, vc, ws,
-                   vscale=vscale, k_norm=k_norm)
+                   vscale=vscale, k_norm=k_norm, w_idx=w_idx, idx_cache=ic)
 
     log(f"[bench] {name}: n_fill={n_fill}, {s.n_late} late layers, {g} per launch; warmup {args.warmup}")
     for _ in range(args.warmup):
@@ -358,6 +364,7 @@ def main():
                    "map_format": "int8 + bf16 scale per 128 weights of a row" if q8 else "bf16",
                    "value_rescale_rows": args.value_rescale or None,
                    "qk_norm": bool(args.qk_norm),
+                   "indexer_key_heads": args.indexer,
                    "layers_per_launch": 1 if host_maps else g},
         "tflops": step_flops / (ms * 1e-3) / 1e12,
         "frac_of_bf16_peak": step_flops / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS,

@@ -91,6 +91,8 @@ typedef struct rf_shape {
   int32_t n_rows;      /* rows of x (all prompts of a batch concatenated)        */
   int32_t n_slots;     /* slots per layer cache                                  */
   int32_t max_pos;     /* every position lies in [0, max_pos)                    */
+  int32_t n_idx;       /* indexer key heads per late layer, head_dim wide each;
+                          0 = none (see rf_fill_opts); 0 .. 8                    */
 } rf_shape;
 
 typedef struct rf_plan rf_plan;
@@ -156,10 +158,21 @@ typedef struct rf_vscale {
  *           before attention): HOST array of n_late device pointers, each bf16
  *           [head_dim], 16-byte aligned; or NULL.  Each key head is divided by
  *           sqrt(mean of its head_dim squares + rms_eps) and multiplied by the
- *           gain per dimension, after the key projection and before RoPE. */
+ *           gain per dimension, after the key projection and before RoPE.
+ *   w_idx, idx_cache  indexer keys, required exactly when the plan's n_idx > 0
+ *           (RidgeFill section 2.1 and section 5.1: in sparse-attention layers
+ *           filled rows also write the indexer's keys, one 128-wide key head
+ *           shared by the indexer's query heads).  HOST arrays of n_late
+ *           device pointers, 16-byte aligned: w_idx bf16 [n_idx*head_dim][d_out]
+ *           (the indexer key projection), idx_cache bf16
+ *           [n_slots][n_idx*head_dim].  Each indexer head is the normalised
+ *           input times W_idx, rotated like the attention keys (same theta and
+ *           pairing), without QK-norm; it is stored at the row's slot like K. */
 typedef struct rf_fill_opts {
   const rf_vscale* vscale;
   const uint16_t* const* k_norm;
+  const uint16_t* const* w_idx;
+  uint16_t* const* idx_cache;
 } rf_fill_opts;
 
 /* The fill (steps 1-5 above) for n_fill rows and every late layer.

@@ -49,7 +49,7 @@ class RfError(RuntimeError):
 class Shape(C.Structure):
     _fields_ = [("d_in", C.c_int32), ("d_out", C.c_int32), ("n_late", C.c_int32), ("n_kv", C.c_int32),
                 ("head_dim", C.c_int32), ("rms_eps", C.c_float), ("rope_theta", C.c_double),
-                ("n_rows", C.c_int32), ("n_slots", C.c_int32), ("max_pos", C.c_int32)]
+                ("n_rows", C.c_int32), ("n_slots", C.c_int32), ("max_pos", C.c_int32), ("n_idx", C.c_int32)]
 
 
 class Profile(C.Structure):
@@ -62,8 +62,9 @@ class VScale(C.Structure):
 
 
 class FillOpts(C.Structure):
-    """rf_fill_opts: value rescale and QK-norm of a fill."""
-    _fields_ = [("vscale", C.POINTER(VScale)), ("k_norm", C.POINTER(C.c_void_p))]
+    """rf_fill_opts: value rescale, QK-norm and indexer keys of a fill."""
+    _fields_ = [("vscale", C.POINTER(VScale)), ("k_norm", C.POINTER(C.c_void_p)),
+                ("w_idx", C.POINTER(C.c_void_p)), ("idx_cache", C.POINTER(C.c_void_p))]
 
 
 _lib = None
@@ -153,8 +154,9 @@ class Plan:
 
     def __init__(self, d_in: int, d_out: int, n_late: int, n_kv: int, head_dim: int, rms_eps: float,
                  rope_theta: float, n_rows: int, n_slots: int, max_pos: int,
-                 maps_on_host: bool = False, validate: bool = False, maps_q8: bool = False):
-        self.shape = Shape(d_in, d_out, n_late, n_kv, head_dim, rms_eps, rope_theta, n_rows, n_slots, max_pos)
+                 maps_on_host: bool = False, validate: bool = False, maps_q8: bool = False, n_idx: int = 0):
+        self.shape = Shape(d_in, d_out, n_late, n_kv, head_dim, rms_eps, rope_theta, n_rows, n_slots, max_pos,
+                           n_idx)
         self.flags = ((RF_MAPS_HOST if maps_on_host else 0) | (RF_VALIDATE if validate else 0)
                       | (RF_MAPS_Q8 if maps_q8 else 0))
         h = C.c_void_p()
@@ -166,6 +168,7 @@ class Plan:
         """Plan for a workloads.Spec."""
         kw.setdefault("maps_on_host", s.maps_on_host)
         kw.setdefault("maps_q8", s.map_format == "q8")
+        kw.setdefault("n_idx", s.idx_heads)
         return cls(s.d_in, s.d_out, s.n_late, s.n_kv, s.head_dim, s.rms_eps, s.rope_theta,
                    s.n_rows, s.n_rows, s.max_pos, **kw)
 
@@ -218,9 +221,9 @@ def fill_rows(plan: Plan, exact_rows, fill_rows_out, n_fill_out, workspace, stre
 class _Opts:
     """Keeps an rf_fill_opts and everything it points to alive for one call."""
 
-    def __init__(self, vscale=None, k_norm=None):
+    def __init__(self, vscale=None, k_norm=None, w_idx=None, idx_cache=None):
         self.ref = None
-        if vscale is None and k_norm is None:
+        if vscale is None and k_norm is None and w_idx is None and idx_cache is None:
             return
         self.opts = FillOpts()
         if vscale is not None:
@@ -230,18 +233,26 @@ class _Opts:
         if k_norm is not None:
             self.kn = _ptr_array(k_norm)
             self.opts.k_norm = C.cast(self.kn, C.POINTER(C.c_void_p))
+        if w_idx is not None:
+            self.wi = _ptr_array(w_idx)
+            self.opts.w_idx = C.cast(self.wi, C.POINTER(C.c_void_p))
+        if idx_cache is not None:
+            self.ic = _ptr_array(idx_cache)
+            self.opts.idx_cache = C.cast(self.ic, C.POINTER(C.c_void_p))
         self.ref = C.byref(self.opts)
 
 
 def fill(plan: Plan, x, fill_rows_t, n_fill: int, positions, slot_of_row, map_a: Sequence, map_b: Sequence,
          gamma: Sequence, w_k: Sequence, w_v: Sequence, rope, k_cache: Sequence, v_cache: Sequence,
-         workspace, stream=None, ld_x: Optional[int] = None, vscale=None, k_norm: Sequence = None) -> None:
+         workspace, stream=None, ld_x: Optional[int] = None, vscale=None, k_norm: Sequence = None,
+         w_idx: Sequence = None, idx_cache: Sequence = None) -> None:
     """rf_fill.  map_a/map_b are device tensors, or pinned host tensors for a
     plan made with maps_on_host.  vscale = (scale [n_late][n_groups][n_kv] fp32,
     group_of_row [n_rows] int32, n_groups) applies a value rescale; k_norm (one
-    bf16 [head_dim] gain per late layer) applies QK-norm to the keys."""
+    bf16 [head_dim] gain per late layer) applies QK-norm to the keys; w_idx /
+    idx_cache (per late layer) write the indexer keys of a plan with n_idx > 0."""
     ld = x.stride(0) if ld_x is None else ld_x
-    o = _Opts(vscale, k_norm)
+    o = _Opts(vscale, k_norm, w_idx, idx_cache)
     _check("rf_fill", lib().rf_fill(
         plan.handle, _ptr(x), ld, _ptr(fill_rows_t), n_fill, _ptr(positions), _ptr(slot_of_row),
         _ptr_array(map_a), _ptr_array(map_b), _ptr_array(gamma), _ptr_array(w_k), _ptr_array(w_v),
@@ -252,11 +263,11 @@ def fill(plan: Plan, x, fill_rows_t, n_fill: int, positions, slot_of_row, map_a:
 def fill_q8(plan: Plan, x, fill_rows_t, n_fill: int, positions, slot_of_row, map_q: Sequence,
             map_scale: Sequence, map_b: Sequence, gamma: Sequence, w_k: Sequence, w_v: Sequence, rope,
             k_cache: Sequence, v_cache: Sequence, workspace, stream=None, ld_x: Optional[int] = None,
-            vscale=None, k_norm: Sequence = None) -> None:
+            vscale=None, k_norm: Sequence = None, w_idx: Sequence = None, idx_cache: Sequence = None) -> None:
     """rf_fill_q8: the fill with int8 maps (codes + bf16 block scales) for a
     plan made with maps_q8; pinned host tensors for a plan with maps_on_host."""
     ld = x.stride(0) if ld_x is None else ld_x
-    o = _Opts(vscale, k_norm)
+    o = _Opts(vscale, k_norm, w_idx, idx_cache)
     _check("rf_fill_q8", lib().rf_fill_q8(
         plan.handle, _ptr(x), ld, _ptr(fill_rows_t), n_fill, _ptr(positions), _ptr(slot_of_row),
         _ptr_array(map_q), _ptr_array(map_scale), _ptr_array(map_b), _ptr_array(gamma), _ptr_array(w_k),
@@ -303,10 +314,11 @@ def map_quantize_q8(a: np.ndarray):
 
 def kv_project(plan: Plan, layer_in: Sequence, rows, n: int, positions, slot_of_row, gamma: Sequence,
                w_k: Sequence, w_v: Sequence, rope, k_cache: Sequence, v_cache: Sequence, workspace,
-               stream=None, ld_in: Optional[int] = None, k_norm: Sequence = None) -> None:
+               stream=None, ld_in: Optional[int] = None, k_norm: Sequence = None, w_idx: Sequence = None,
+               idx_cache: Sequence = None) -> None:
     """rf_kv_project: the exact cache write of every late layer from given inputs."""
     ld = layer_in[0].stride(0) if ld_in is None else ld_in
-    o = _Opts(None, k_norm)
+    o = _Opts(None, k_norm, w_idx, idx_cache)
     _check("rf_kv_project", lib().rf_kv_project(
         plan.handle, _ptr_array(layer_in), ld, _ptr(rows), n, _ptr(positions), _ptr(slot_of_row),
         _ptr_array(gamma), _ptr_array(w_k), _ptr_array(w_v), _ptr(rope), _ptr_array(k_cache),

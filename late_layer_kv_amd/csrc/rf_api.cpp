@@ -112,9 +112,12 @@ class Timed {
 namespace {
 
 int kv_width(const rf_shape& s) { return s.n_kv * s.head_dim; }
+int idx_width(const rf_shape& s) { return s.n_idx * s.head_dim; }
+// prepared-weight rows per layer: keys, values, indexer keys, zero rows up to a whole tile
+int prep_rows(const rf_shape& s) { return (2 * kv_width(s) + idx_width(s) + rf::kTileN - 1) / rf::kTileN * rf::kTileN; }
 size_t rope_bytes(const rf_shape& s) { return up(static_cast<size_t>(s.max_pos) * (s.head_dim / 2) * 8); }
 size_t prep_bytes(const rf_shape& s, int g) {
-  return up(static_cast<size_t>(g) * 2 * kv_width(s) * s.d_out * 2);
+  return up(static_cast<size_t>(g) * prep_rows(s) * s.d_out * 2);
 }
 size_t y_bytes(const rf_shape& s, int n_fill, int g) {
   return up(static_cast<size_t>(g) * n_fill * s.d_out * 2);
@@ -149,6 +152,7 @@ rf_status check_shape(const rf_shape* s, int32_t flags) {
   if (!(s->rope_theta > 1.0)) return fail(RF_E_SHAPE, "rope_theta must be > 1");
   if (s->n_rows < 0 || s->n_slots < 0 || s->max_pos < 1)
     return fail(RF_E_SHAPE, "n_rows, n_slots must be >= 0 and max_pos >= 1");
+  if (s->n_idx < 0 || s->n_idx > 8) return fail(RF_E_SHAPE, "n_idx=%d must be in [0, 8]", s->n_idx);
   return RF_OK;
 }
 
@@ -432,8 +436,18 @@ int pick_group(const rf_plan* p, size_t ws_bytes, F bytes_for) {
 }
 
 rf_status check_opts(const rf_plan* p, const rf_fill_opts* o) {
-  if (!o || !o->k_norm) return RF_OK;
-  return check_layer_ptrs(reinterpret_cast<const void* const*>(o->k_norm), p->s.n_late, "k_norm");
+  const int L = p->s.n_late;
+  rf_status st;
+  if (o && o->k_norm)
+    if ((st = check_layer_ptrs(reinterpret_cast<const void* const*>(o->k_norm), L, "k_norm")) != RF_OK) return st;
+  const bool has_idx = o && (o->w_idx || o->idx_cache);
+  if (p->s.n_idx == 0)
+    return has_idx ? fail(RF_E_ARG, "w_idx / idx_cache given but the plan has n_idx = 0") : RF_OK;
+  if (!o || !o->w_idx || !o->idx_cache)
+    return fail(RF_E_ARG, "the plan has n_idx=%d indexer heads: opts->w_idx and opts->idx_cache are required",
+                p->s.n_idx);
+  if ((st = check_layer_ptrs(reinterpret_cast<const void* const*>(o->w_idx), L, "w_idx")) != RF_OK) return st;
+  return check_layer_ptrs(reinterpret_cast<const void* const*>(o->idx_cache), L, "idx_cache");
 }
 
 rf_status check_vscale(const rf_plan* p, const rf_vscale* vs) {
@@ -520,7 +534,9 @@ rf_status fill_impl(rf_plan* p, const char* fn, const uint16_t* x, int64_t ld_x,
   kp.w = w;
   kp.head_dim = s.head_dim;
   kp.tiles_m = mp.tiles_m;
-  kp.tiles_n = 2 * w / rf::kTileN;
+  kp.tiles_n = prep_rows(s) / rf::kTileN;
+  kp.wrows = prep_rows(s);
+  kp.widx = idx_width(s);
   kp.wkv = prep;
   kp.positions = positions;
   kp.slots = slot_of_row;
@@ -537,6 +553,8 @@ rf_status fill_impl(rf_plan* p, const char* fn, const uint16_t* x, int64_t ld_x,
   rf::PrepParams pp{};
   pp.d = s.d_out;
   pp.w = w;
+  pp.widx = idx_width(s);
+  pp.rows = prep_rows(s);
   pp.out = prep;
 
   const size_t y_layer = static_cast<size_t>(n_fill) * s.d_out;
@@ -549,9 +567,11 @@ rf_status fill_impl(rf_plan* p, const char* fn, const uint16_t* x, int64_t ld_x,
       pp.gamma[i] = gamma[l0 + i];
       pp.wk[i] = w_k[l0 + i];
       pp.wv[i] = w_v[l0 + i];
+      pp.wi[i] = s.n_idx ? opts->w_idx[l0 + i] : nullptr;
       kp.in[i] = ybuf + i * y_layer;
       kp.rs[i] = rsb + static_cast<size_t>(i) * n_fill;
       kp.kc[i] = k_cache[l0 + i];
+      kp.ic[i] = s.n_idx ? opts->idx_cache[l0 + i] : nullptr;
       kp.vc[i] = v_cache[l0 + i];
       kp.vscale[i] = vscale ? vscale->scale + (l0 + i) * vs_layer : nullptr;
       kp.kgamma[i] = k_norm ? k_norm[l0 + i] : nullptr;
@@ -665,6 +685,7 @@ rf_status value_scales_impl(rf_plan* p, const char* fn, const uint16_t* x, int64
     kp.head_dim = s.head_dim;
     kp.tiles_m = mp.tiles_m;
     kp.tiles_n = (2 * w - w / rf::kTileN * rf::kTileN) / rf::kTileN;
+    kp.wrows = 2 * w;  // keys and values only (no indexer rows here)
     kp.wkv = prep;
     kp.positions = zero_pos;
     kp.n_rows = n;
@@ -677,6 +698,7 @@ rf_status value_scales_impl(rf_plan* p, const char* fn, const uint16_t* x, int64
     rf::PrepParams pp{};
     pp.d = s.d_out;
     pp.w = w;
+    pp.rows = 2 * w;
     pp.out = prep;
 
     rf::RatioParams rp{};
@@ -903,7 +925,9 @@ rf_status rf_kv_project(rf_plan* p, const uint16_t* const* layer_in, int64_t ld_
   kp.w = w;
   kp.head_dim = s.head_dim;
   kp.tiles_m = (n + rf::kTileM - 1) / rf::kTileM;
-  kp.tiles_n = 2 * w / rf::kTileN;
+  kp.tiles_n = prep_rows(s) / rf::kTileN;
+  kp.wrows = prep_rows(s);
+  kp.widx = idx_width(s);
   kp.wkv = prep;
   kp.positions = positions;
   kp.slots = slot_of_row;
@@ -918,6 +942,8 @@ rf_status rf_kv_project(rf_plan* p, const uint16_t* const* layer_in, int64_t ld_
   rf::PrepParams pp{};
   pp.d = s.d_out;
   pp.w = w;
+  pp.widx = idx_width(s);
+  pp.rows = prep_rows(s);
   pp.out = prep;
   rf::RmsParams rp{};
   rp.ld_in = ld_in;
@@ -934,10 +960,12 @@ rf_status rf_kv_project(rf_plan* p, const uint16_t* const* layer_in, int64_t ld_
       pp.gamma[i] = gamma[l0 + i];
       pp.wk[i] = w_k[l0 + i];
       pp.wv[i] = w_v[l0 + i];
+      pp.wi[i] = s.n_idx ? opts->w_idx[l0 + i] : nullptr;
       kp.in[i] = layer_in[l0 + i];
       rp.in[i] = layer_in[l0 + i];
       kp.rs[i] = rsb + static_cast<size_t>(i) * n;
       kp.kc[i] = k_cache[l0 + i];
+      kp.ic[i] = s.n_idx ? opts->idx_cache[l0 + i] : nullptr;
       kp.vc[i] = v_cache[l0 + i];
       kp.kgamma[i] = k_norm ? k_norm[l0 + i] : nullptr;
     }

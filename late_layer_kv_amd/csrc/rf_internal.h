@@ -47,9 +47,11 @@ struct KvParams {
   int32_t M;
   int32_t K;                // d_out (normalised width)
   int32_t w;                // n_kv * head_dim
+  int32_t widx;             // indexer key columns (n_idx * head_dim), after the values
   int32_t head_dim;
   int32_t tiles_m, tiles_n;
-  const uint16_t* wkv;      // [n_layers][2w][K] prepared weights
+  int32_t wrows;            // rows per layer of wkv: 2w + widx rounded up to 256
+  const uint16_t* wkv;      // [n_layers][wrows][K] prepared weights (zero rows past 2w + widx)
   const int32_t* positions; // [n_rows]
   const int32_t* slots;     // [n_rows] or null (slot = row)
   int32_t n_rows, n_slots, max_pos;
@@ -71,20 +73,25 @@ struct KvParams {
   const uint16_t* in[kMaxGroup];
   uint16_t* kc[kMaxGroup];  // [n_slots][w]
   uint16_t* vc[kMaxGroup];
+  uint16_t* ic[kMaxGroup];  // [n_slots][widx] indexer keys (widx > 0)
   const float* vscale[kMaxGroup];  // [n_groups][n_kv] per layer, or null
   const uint16_t* kgamma[kMaxGroup];  // [head_dim] per layer (qk_norm)
   const float* rs[kMaxGroup];  // [M] norm factor of row m of this call, per layer
 };
 
 // Prepared projection weights: out_g[f][k] = bf16(W[f][k] * gamma_g[k]),
-// W = W_k for f < w, W_v (row f - w) otherwise.
+// W = W_k for f < w, W_v (row f - w) for f < 2w, W_idx (row f - 2w) for
+// f < 2w + widx, zero up to rows.
 struct PrepParams {
   int32_t d;       // d_out
   int32_t w;
-  uint16_t* out;   // [n_layers][2w][d]
+  int32_t widx;
+  int32_t rows;    // rows per layer, >= 2w + widx
+  uint16_t* out;   // [n_layers][rows][d]
   const uint16_t* gamma[kMaxGroup];
   const uint16_t* wk[kMaxGroup];
   const uint16_t* wv[kMaxGroup];
+  const uint16_t* wi[kMaxGroup];
 };
 
 // int8 map -> bf16 image: w_g[o][k] = bf16(q_g[o][k] * s_g[o][k / 128]), nearest even.

@@ -468,7 +468,7 @@ __global__ void __launch_bounds__(kThreads) kv_gemm_kernel(const KvParams p) {
   const char* wsrc[8];
   const char* xsrc[8];
   {
-    const char* wbase = reinterpret_cast<const char*>(p.wkv + static_cast<size_t>(c.g) * 2 * p.w * p.K);
+    const char* wbase = reinterpret_cast<const char*>(p.wkv + static_cast<size_t>(c.g) * p.wrows * p.K);
     const char* xbase = reinterpret_cast<const char*>(p.in[c.g]);
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
@@ -536,15 +536,21 @@ __global__ void __launch_bounds__(kThreads) kv_gemm_kernel(const KvParams p) {
 #pragma unroll
     for (int mb = 0; mb < 8; ++mb) slot_of[wm * 128 + mb * 16 + r15] = slot_r[mb];
   }
-  const int fw = n0 + wn * 128;  // first feature of this wave; a whole wave is key or value
-  // (with v_only, a tile may start inside the keys when w is not a multiple of
-  // 256; those key waves are neither rotated nor stored)
-  const bool is_key = fw < p.w && !p.v_only;
+  // First feature of this wave; a whole wave is one kind: attention keys
+  // [0, w), values [w, 2w), indexer keys [2w, 2w + widx) (rotated like keys,
+  // never QK-normed), or padding past them (not stored).  With v_only a tile
+  // may start inside the keys when w is not a multiple of 256; those key
+  // waves are neither rotated nor stored.
+  const int fw = n0 + wn * 128;
+  const bool is_attn_key = fw < p.w && !p.v_only;
+  const bool is_key = is_attn_key || (fw >= 2 * p.w && fw < 2 * p.w + p.widx);
+  const bool is_value = fw >= p.w && fw < 2 * p.w;
+  const bool qk_wave = QK && is_attn_key;
   // Value waves of a rescaled fill: the request's value scale for the wave's
   // first head (and, for heads of 64, the second head, blocks 4-7) is folded
   // into the norm's per-row factor; without a rescale the factor is exactly
   // the norm's scale.
-  const float* const vsw = (VSCALE && !is_key) ? p.vscale[c.g] + (fw - p.w) / HD : nullptr;
+  const float* const vsw = (VSCALE && is_value) ? p.vscale[c.g] + (fw - p.w) / HD : nullptr;
   float rs2[8];
 #pragma unroll
   for (int mb = 0; mb < 8; ++mb) rs2[mb] = rs[mb];
@@ -592,7 +598,7 @@ __global__ void __launch_bounds__(kThreads) kv_gemm_kernel(const KvParams p) {
     for (int mb = 0; mb < 8; ++mb)
 #pragma unroll
       for (int h = 0; h < heads; ++h) kf[mb][h] = rs[mb];
-    if (QK) {
+    if (qk_wave) {
 #pragma unroll
       for (int mb = 0; mb < 8; ++mb) {
 #pragma unroll
@@ -627,7 +633,7 @@ __global__ void __launch_bounds__(kThreads) kv_gemm_kernel(const KvParams p) {
         cs[mb][1] = *reinterpret_cast<const float4*>(trow + 2);
       }
       float g1[4] = {1.0f, 1.0f, 1.0f, 1.0f}, g2[4] = {1.0f, 1.0f, 1.0f, 1.0f};
-      if (QK) {
+      if (qk_wave) {
         // gains of dimensions j and j + hd/2, four consecutive each
         const uint2 a = *reinterpret_cast<const uint2*>(kg + jb + q * 4);
         const uint2 b = *reinterpret_cast<const uint2*>(kg + jb + half + q * 4);
@@ -670,15 +676,18 @@ __global__ void __launch_bounds__(kThreads) kv_gemm_kernel(const KvParams p) {
   __syncthreads();
   const int chunk = threadIdx.x & 31;
   const int f = n0 + chunk * 8;
-  const bool store = !(p.v_only && f < p.w);
-  uint16_t* dst_base = (f < p.w) ? p.kc[c.g] + f : p.vc[c.g] + (f - p.w);
+  const bool store = !(p.v_only && f < p.w) && f < 2 * p.w + p.widx;
+  uint16_t* dst_base = f < p.w       ? p.kc[c.g] + f
+                       : f < 2 * p.w ? p.vc[c.g] + (f - p.w)
+                                     : p.ic[c.g] + (f - 2 * p.w);
+  const int stride = f < 2 * p.w ? p.w : p.widx;
 #pragma unroll 4
   for (int it = 0; it < 32; ++it) {
     const int row = it * 8 + (threadIdx.x >> 5);
     const int slot = slot_of[row];
     if (slot >= 0 && store) {
       const uint4 v = *reinterpret_cast<const uint4*>(smem + stage_off(row, chunk));
-      *reinterpret_cast<uint4*>(dst_base + static_cast<size_t>(slot) * p.w) = v;
+      *reinterpret_cast<uint4*>(dst_base + static_cast<size_t>(slot) * stride) = v;
     }
   }
 }
@@ -688,10 +697,17 @@ __global__ void __launch_bounds__(256) prep_kv_kernel(const PrepParams p) {
   const int g = blockIdx.y;
   const int per_row = p.d >> 3;
   const int64_t idx = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
-  if (idx >= static_cast<int64_t>(2 * p.w) * per_row) return;
+  if (idx >= static_cast<int64_t>(p.rows) * per_row) return;
   const int f = static_cast<int>(idx / per_row);
   const int k8 = static_cast<int>(idx - static_cast<int64_t>(f) * per_row) * 8;
-  const uint16_t* src = (f < p.w) ? p.wk[g] + static_cast<size_t>(f) * p.d : p.wv[g] + static_cast<size_t>(f - p.w) * p.d;
+  uint16_t* dst = p.out + (static_cast<size_t>(g) * p.rows + f) * p.d + k8;
+  if (f >= 2 * p.w + p.widx) {  // padding rows of the last tile
+    *reinterpret_cast<uint4*>(dst) = make_uint4(0, 0, 0, 0);
+    return;
+  }
+  const uint16_t* src = f < p.w       ? p.wk[g] + static_cast<size_t>(f) * p.d
+                        : f < 2 * p.w ? p.wv[g] + static_cast<size_t>(f - p.w) * p.d
+                                      : p.wi[g] + static_cast<size_t>(f - 2 * p.w) * p.d;
   const uint4 wr = *reinterpret_cast<const uint4*>(src + k8);
   const uint4 gr = *reinterpret_cast<const uint4*>(p.gamma[g] + k8);
   const uint32_t wv[4] = {wr.x, wr.y, wr.z, wr.w};
@@ -703,8 +719,7 @@ __global__ void __launch_bounds__(256) prep_kv_kernel(const PrepParams p) {
     const float hi = bf16_to_f32(wv[i] >> 16) * bf16_to_f32(gv[i] >> 16);
     o[i] = pack_bf16x2(lo, hi);
   }
-  *reinterpret_cast<uint4*>(p.out + (static_cast<size_t>(g) * 2 * p.w + f) * p.d + k8) =
-      make_uint4(o[0], o[1], o[2], o[3]);
+  *reinterpret_cast<uint4*>(dst) = make_uint4(o[0], o[1], o[2], o[3]);
 }
 
 // (cos, sin) of pos * theta^(-2j/hd), formed and evaluated in double precision.
@@ -813,7 +828,7 @@ hipError_t launch_kv(const KvParams& p, int n_layers, hipStream_t s) {
 }
 
 hipError_t launch_prep(const PrepParams& p, int n_layers, hipStream_t s) {
-  const int64_t per_layer = static_cast<int64_t>(2 * p.w) * (p.d >> 3);
+  const int64_t per_layer = static_cast<int64_t>(p.rows) * (p.d >> 3);
   const int blocks = static_cast<int>((per_layer + 255) / 256);
   hipLaunchKernelGGL(prep_kv_kernel, dim3(blocks, n_layers), dim3(256), 0, s, p);
   return hipGetLastError();

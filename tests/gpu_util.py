@@ -54,12 +54,18 @@ class DeviceInputs:
         self.positions = i32(w.positions).to(device)
         self.exact = i32(w.exact_rows).to(device)
         self.k_norm = None if w.k_norm is None else [t16(g).to(device) for g in w.k_norm]
+        self.w_idx = None if w.w_idx is None else [t16(a).to(device) for a in w.w_idx]
 
     def caches(self):
         s = self.w.spec
         mk = lambda: [torch.full((s.n_rows, s.kv_width), CANARY, dtype=torch.int16, device=self.device)
                       for _ in range(s.n_late)]
         return mk(), mk()
+
+    def idx_caches(self):
+        s = self.w.spec
+        return [torch.full((s.n_rows, s.idx_heads * s.head_dim), CANARY, dtype=torch.int16, device=self.device)
+                for _ in range(s.n_late)]
 
 
 def plan_for(w, **kw) -> B.Plan:
@@ -79,31 +85,38 @@ def gpu_fill_rows(plan, di: DeviceInputs, exact: torch.Tensor = None):
 
 
 def gpu_fill(plan, di: DeviceInputs, rows: torch.Tensor, n_fill: int, caches=None, layers_per_launch=None,
-             map_a=None, map_b=None, rope=None, slots=None, vscale=None):
+             map_a=None, map_b=None, rope=None, slots=None, vscale=None, idx_caches=None, w_idx=None):
+    """(K caches, V caches), plus the indexer-key caches when the workload has
+    indexer heads."""
     s = di.w.spec
     kc, vc = di.caches() if caches is None else caches
+    ic = None
+    if di.w_idx is not None:
+        ic = di.idx_caches() if idx_caches is None else idx_caches
+    wi = di.w_idx if w_idx is None else w_idx
     g = s.n_late if layers_per_launch is None else layers_per_launch
     ws = torch.empty(max(plan.fill_workspace_bytes(n_fill, g), 256), dtype=torch.uint8, device=di.device)
     if di.q8 and map_a is None:
         B.fill_q8(plan, di.x, rows, n_fill, di.positions, slots, di.map_q, di.map_scale,
                   di.map_b if map_b is None else map_b, di.gamma, di.w_k, di.w_v, rope, kc, vc, ws, vscale=vscale,
-                  k_norm=di.k_norm)
+                  k_norm=di.k_norm, w_idx=wi, idx_cache=ic)
     else:
         B.fill(plan, di.x, rows, n_fill, di.positions, slots, di.map_a if map_a is None else map_a,
                di.map_b if map_b is None else map_b, di.gamma, di.w_k, di.w_v, rope, kc, vc, ws, vscale=vscale,
-               k_norm=di.k_norm)
+               k_norm=di.k_norm, w_idx=wi, idx_cache=ic)
     torch.cuda.synchronize()
-    return kc, vc
+    return (kc, vc) if ic is None else (kc, vc, ic)
 
 
 def gpu_kv_project(plan, di: DeviceInputs, layer_in, rows: torch.Tensor, n: int, caches=None, slots=None):
     s = di.w.spec
     kc, vc = di.caches() if caches is None else caches
+    ic = None if di.w_idx is None else di.idx_caches()
     ws = torch.empty(plan.kv_project_workspace_bytes(s.n_late), dtype=torch.uint8, device=di.device)
     B.kv_project(plan, layer_in, rows, n, di.positions, slots, di.gamma, di.w_k, di.w_v, None, kc, vc, ws,
-                 k_norm=di.k_norm)
+                 k_norm=di.k_norm, w_idx=di.w_idx, idx_cache=ic)
     torch.cuda.synchronize()
-    return kc, vc
+    return (kc, vc) if ic is None else (kc, vc, ic)
 
 
 def kv_errors(got: np.ndarray, ref: np.ndarray, head_dim: int):
@@ -136,14 +149,15 @@ def check_values(kc, vc, ref: dict, rows: np.ndarray, head_dim: int, slots: np.n
     return worst
 
 
-def check_placement(kc, vc, fill_rows: np.ndarray, n_slots: int, slots: np.ndarray = None):
+def check_placement(kc, vc, fill_rows: np.ndarray, n_slots: int, slots: np.ndarray = None, ic=None):
     """Bit-exact placement: written slots are exactly slot(fill rows); every
-    other slot still holds the canary in every byte."""
+    other slot still holds the canary in every byte (K, V and, if given, the
+    indexer keys)."""
     filled = np.zeros(n_slots, dtype=bool)
     filled[fill_rows if slots is None else slots[fill_rows]] = True
     want = torch.from_numpy(filled).to(kc[0].device)
     for l in range(len(kc)):
-        for name, cache in (("K", kc), ("V", vc)):
+        for name, cache in (("K", kc), ("V", vc)) + ((("I", ic),) if ic is not None else ()):
             eq = cache[l] == CANARY
             untouched = eq.all(dim=1)
             anyc = eq.any(dim=1)
@@ -160,3 +174,17 @@ def identity_maps(di: DeviceInputs):
     a = [eye.to(di.device) for _ in range(s.n_late)]
     b = [torch.zeros(s.d_out, dtype=torch.int16, device=di.device) for _ in range(s.n_late)]
     return a, b
+
+
+def check_indexer_values(ic, ref: dict, rows: np.ndarray, head_dim: int, slots: np.ndarray = None):
+    """Compare indexer-key cache rows at slot(rows) with the oracle, per layer."""
+    sl = rows if slots is None else slots[rows]
+    idx = torch.from_numpy(np.asarray(sl, dtype=np.int64)).to(ic[0].device)
+    worst = {"fro": 0.0, "maxel": 0.0, "inf": 0.0}
+    for l, r in ref.items():
+        got = bits_to_f64(ic[l].index_select(0, idx))
+        fro, maxel, inf = kv_errors(got, r, head_dim)
+        worst = {k: max(worst[k], v) for k, v in (("fro", fro), ("maxel", maxel), ("inf", inf))}
+        assert fro <= FRO_TOL, f"layer {l} indexer keys: Frobenius relative error {fro:.3e}"
+        assert maxel <= MAXEL_TOL, f"layer {l} indexer keys: max element error {maxel:.3e}"
+    return worst

@@ -32,7 +32,7 @@ def test_library_exports_every_declared_symbol():
 
 def _shape(**kw):
     base = dict(d_in=256, d_out=256, n_late=4, n_kv=2, head_dim=64, rms_eps=1e-5, rope_theta=1e4,
-                n_rows=512, n_slots=512, max_pos=512)
+                n_rows=512, n_slots=512, max_pos=512, n_idx=0)
     base.update(kw)
     return base
 
@@ -40,6 +40,7 @@ def _shape(**kw):
 @pytest.mark.parametrize("bad,status", [
     (dict(d_in=100), -2), (dict(d_out=320), -2), (dict(n_late=0), -2), (dict(head_dim=96), -2),
     (dict(n_kv=1), -2), (dict(rope_theta=1.0), -2), (dict(max_pos=0), -2), (dict(rms_eps=-1.0), -2),
+    (dict(n_idx=-1), -2), (dict(n_idx=9), -2),
 ])
 def test_plan_rejects_bad_shapes(bad, status):
     with pytest.raises(B.RfError) as e:
@@ -342,3 +343,49 @@ def test_ridge_acc_sums_round_trip():
     for a, b in ((sxx, ref.sxx), (sxy, ref.sxy), (sx, ref.sx), (sy, ref.sy)):
         assert np.allclose(a, b, rtol=1e-12, atol=1e-9)
     assert np.array_equal(sxx, sxx.T)
+
+
+def test_indexer_key_options():
+    """Indexer keys are required exactly when the plan has indexer heads; the
+    prepared weights grow by the indexer rows, padded to a 256-row tile."""
+    L = B.lib()
+    nl = 4
+    fake = C.c_void_p(0x1000)
+    arr = (C.c_void_p * nl)(*([0x1000] * nl))
+    null_arr = (C.c_void_p * nl)(*([0x1000] * (nl - 1) + [0]))
+    ws = 1 << 40
+
+    def opts(wi=None, ic=None):
+        o = B.FillOpts()
+        if wi is not None:
+            o.w_idx = C.cast(wi, C.POINTER(C.c_void_p))
+        if ic is not None:
+            o.idx_cache = C.cast(ic, C.POINTER(C.c_void_p))
+        return o
+
+    def fill(p, o):
+        return L.rf_fill(p.handle, fake, 256, fake, 10, fake, None, arr, arr, arr, arr, arr, None, arr, arr,
+                         None if o is None else C.byref(o), C.c_void_p(0x10000), ws, None)
+
+    def project(p, o):
+        return L.rf_kv_project(p.handle, arr, 256, fake, 10, fake, None, arr, arr, arr, None, arr, arr,
+                               None if o is None else C.byref(o), C.c_void_p(0x10000), ws, None)
+    p0 = B.Plan(**_shape())
+    assert fill(p0, opts(wi=arr, ic=arr)) == -1        # the plan has no indexer heads
+    assert "n_idx" in B.last_error()
+    assert project(p0, opts(ic=arr)) == -1
+    p1 = B.Plan(**_shape(n_idx=1))
+    for call in (fill, project):
+        assert call(p1, None) == -1                    # indexer keys required
+        assert call(p1, opts(wi=arr)) == -1
+        assert call(p1, opts(ic=arr)) == -1
+        assert call(p1, opts(wi=null_arr, ic=arr)) == -1
+        assert call(p1, opts(wi=arr, ic=null_arr)) == -1
+    # prepared rows per layer: 2w + n_idx*hd = 256 + 64, padded to 512
+    up = lambda v: (v + 255) // 256 * 256
+    rope, d = 512 * 32 * 8, 256
+    assert p1.kv_project_workspace_bytes(1) == rope + 256 + 512 * d * 2 + 512 * 4
+    assert p0.kv_project_workspace_bytes(1) == rope + 256 + 256 * d * 2 + 512 * 4
+    assert (p1.fill_workspace_bytes(448, 2) - p0.fill_workspace_bytes(448, 2)) == 2 * 256 * d * 2
+    p0.close()
+    p1.close()

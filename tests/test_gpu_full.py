@@ -40,14 +40,17 @@ def sample_rows(fill: np.ndarray, exact: np.ndarray, positions: np.ndarray, n: i
     return np.array(sorted(pick), dtype=np.int32)
 
 
-FULL_CASES = [(n, "bf16", False) for n in workloads.CONFIG_ORDER] + \
-    [("27b_120k", "q8", False), ("8b_ragged_host", "q8", False), ("27b", "bf16", True)]
+FULL_CASES = [(n, "bf16", False, 0) for n in workloads.CONFIG_ORDER] + \
+    [("27b_120k", "q8", False, 0), ("8b_ragged_host", "q8", False, 0), ("27b", "bf16", True, 0),
+     ("27b_120k", "bf16", False, 1)]
 
 
-@pytest.mark.parametrize("name,fmt,qk", FULL_CASES, ids=[f"{n}-{f}{'-qk' if q else ''}" for n, f, q in FULL_CASES])
-def test_full_size(name, fmt, qk):
-    s = workloads.spec(name, map_format=fmt, qk_norm=qk)
-    print(f"[full] {name} ({fmt} maps{', QK-norm' if qk else ''}): generating inputs", flush=True)
+@pytest.mark.parametrize("name,fmt,qk,idx", FULL_CASES,
+                         ids=[f"{n}-{f}{'-qk' if q else ''}{'-idx' if i else ''}" for n, f, q, i in FULL_CASES])
+def test_full_size(name, fmt, qk, idx):
+    s = workloads.spec(name, map_format=fmt, qk_norm=qk, idx_heads=idx)
+    print(f"[full] {name} ({fmt} maps{', QK-norm' if qk else ''}{', indexer keys' if idx else ''}): "
+          "generating inputs", flush=True)
     w = workloads.make(s)
     di = U.DeviceInputs(w)
     plan = B.Plan.for_spec(s)
@@ -55,11 +58,16 @@ def test_full_size(name, fmt, qk):
     rows, n = U.gpu_fill_rows(plan, di)
     f = rows.cpu().numpy()
     assert np.array_equal(f, oracle.fill_row_set(s.n_rows, w.exact_rows))
-    kc, vc = U.gpu_fill(plan, di, rows, n, layers_per_launch=BENCH_GROUP[name])
+    out = U.gpu_fill(plan, di, rows, n, layers_per_launch=BENCH_GROUP[name])
+    kc, vc = out[:2]
+    ic = out[2] if idx else None
     print(f"[full] {name}: placement over {s.n_late} layers x {s.n_rows} slots", flush=True)
-    U.check_placement(kc, vc, f, s.n_rows)
+    U.check_placement(kc, vc, f, s.n_rows, ic=ic)
     rs = sample_rows(f, w.exact_rows, w.positions)
     print(f"[full] {name}: oracle on {len(rs)} sampled rows x {s.n_late} layers", flush=True)
     ref = oracle.fill_workload(w, rows=rs)
     worst = U.check_values(kc, vc, ref, rs, s.head_dim)
     print(f"[full] {name}: worst {worst}", flush=True)
+    if idx:
+        wi = U.check_indexer_values(ic, oracle.fill_indexer_workload(w, rows=rs), rs, s.head_dim)
+        print(f"[full] {name}: indexer worst {wi}", flush=True)
