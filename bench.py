@@ -165,10 +165,26 @@ def capture_bench(s, rows, steps, warmup):
     ms = e0.elapsed_time(e1) / steps
     flop = 2.0 * rows * s.d_in * (s.d_in / 2 + s.d_out)
     tf = flop / (ms * 1e-3) / 1e12
+    # the solve from the same sums (fp64 blocked Cholesky + two triangular solves)
+    ws = torch.empty(dev.solve_workspace_bytes(), dtype=torch.uint8, device="cuda:0")
+    a = torch.empty((s.d_out, s.d_in), dtype=torch.float32, device="cuda:0")
+    b = torch.empty(s.d_out, dtype=torch.float32, device="cuda:0")
+    dev.solve(0.03, a=a, b=b, workspace=ws)
+    t0 = time.perf_counter()
+    n_solve = max(1, min(steps, 5))
+    for _ in range(n_solve):
+        dev.solve(0.03, a=a, b=b, workspace=ws)   # synchronises
+    solve_ms = (time.perf_counter() - t0) * 1e3 / n_solve
+    solve_flop = s.d_in ** 3 / 3.0 + 2.0 * s.d_in ** 2 * s.d_out
+    stf = solve_flop / (solve_ms * 1e-3) / 1e12
     print(json.dumps({"capture": {"workload": s.name, "rows": rows, "d_in": s.d_in, "d_out": s.d_out,
                                   "ms_per_call": ms, "rows_per_s": rows / (ms * 1e-3),
                                   "roofline": {"bound": "mfma", "achieved": tf, "peak": PEAK_FP64_TFLOPS,
-                                               "unit": "TFLOP/s (fp64)", "frac": tf / PEAK_FP64_TFLOPS}}}),
+                                               "unit": "TFLOP/s (fp64)", "frac": tf / PEAK_FP64_TFLOPS}},
+                      "solve": {"d_in": s.d_in, "d_out": s.d_out, "ms_per_solve": solve_ms,
+                                "flop": solve_flop, "achieved_tflops_fp64": stf,
+                                "frac_of_fp64_peak": stf / PEAK_FP64_TFLOPS,
+                                "note": "wall clock of rf_ridge_dev_solve including its final stream sync"}}),
           flush=True)
 
 

@@ -348,6 +348,22 @@ rf_status rf_ridge_dev_add(rf_ridge_dev* dev, const uint16_t* x, int64_t ld_x, c
 rf_status rf_ridge_dev_merge(rf_ridge_dev* dev, rf_ridge_acc* acc, void* hip_stream);
 void rf_ridge_dev_destroy(rf_ridge_dev* dev);
 
+/* The ridge solve of section 2.2 on the GPU, from the device sums (which it
+ * leaves unchanged, so another lambda needs only another solve).  Same
+ * definition and flags as rf_ridge_solve: centred sums, alpha = lambda *
+ * tr(Xc^T Xc) / d_in, A = Y^T X (X^T X + alpha I)^(-1), b = mu_Y - A mu_X (with
+ * RF_RIDGE_RAW: no centring, alpha = lambda, b = 0), in fp64 with a blocked
+ * Cholesky factorisation and triangular solves; results are bitwise
+ * reproducible.  Outputs are DEVICE fp32, 4-byte aligned: a [d_out][d_in] (the
+ * layout rf_fill's map_a takes, after rounding to bf16), b [d_out].  The
+ * workspace (256-byte aligned, rf_ridge_dev_solve_workspace_bytes) holds the
+ * factor and the right-hand sides in fp64.  The call synchronises hip_stream
+ * before it returns, to report a system that is not positive definite
+ * (RF_E_LINALG; a and b then hold no meaningful values).  Needs n >= 1. */
+size_t rf_ridge_dev_solve_workspace_bytes(const rf_ridge_dev* dev);
+rf_status rf_ridge_dev_solve(const rf_ridge_dev* dev, double lambda, int32_t flags, float* a, float* b,
+                             void* workspace, size_t ws_bytes, void* hip_stream);
+
 /* ---- Kernel timing -------------------------------------------------------
  * With profiling on, every launch and map copy the plan issues is bracketed
  * by a pair of HIP events recorded on the stream it runs on (the caller's

@@ -35,6 +35,7 @@ EXPORTS = [
     "rf_fill_q8", "rf_map_dequantize_q8", "rf_map_quantize_q8",
     "rf_value_scales_workspace_bytes", "rf_value_scales", "rf_value_scales_q8",
     "rf_ridge_dev_create", "rf_ridge_dev_add", "rf_ridge_dev_merge", "rf_ridge_dev_destroy", "rf_ridge_acc_sums",
+    "rf_ridge_dev_solve_workspace_bytes", "rf_ridge_dev_solve",
 ]
 
 KERNEL_KINDS = ["map", "kv", "prep", "rope", "rows", "copy", "dequant", "scale", "norm"]
@@ -106,6 +107,8 @@ def lib():
         "rf_ridge_dev_merge": (i32, [P, P, P]),
         "rf_ridge_dev_destroy": (None, [P]),
         "rf_ridge_acc_sums": (i32, [P, P, P, P, P, P]),
+        "rf_ridge_dev_solve_workspace_bytes": (sz, [P]),
+        "rf_ridge_dev_solve": (i32, [P, dbl, i32, P, P, P, sz, P]),
         "rf_value_scales": (i32, [P, P, i64, PP, i64, P, P, i32, i32, PP, PP, PP, PP, P, P, sz, P]),
         "rf_value_scales_q8": (i32, [P, P, i64, PP, i64, P, P, i32, i32, PP, PP, PP, PP, PP, P, P, sz, P]),
         "rf_map_dequantize_q8": (i32, [P, P, i32, i32, P, P]),
@@ -392,6 +395,23 @@ class RidgeDeviceSums:
 
     def merge(self, acc: "RidgeAccumulator", stream=None) -> None:
         _check("rf_ridge_dev_merge", lib().rf_ridge_dev_merge(self.handle, acc.handle, _stream(stream)))
+
+    def solve_workspace_bytes(self) -> int:
+        return int(lib().rf_ridge_dev_solve_workspace_bytes(self.handle))
+
+    def solve(self, lam: float, raw: bool = False, a=None, b=None, workspace=None, stream=None):
+        """rf_ridge_dev_solve: A [d_out][d_in] and b [d_out] (device fp32) from
+        the device sums; outputs and workspace are allocated when not given."""
+        import torch
+        dev = torch.device("cuda", torch.cuda.current_device())
+        a = torch.empty((self.d_out, self.d_in), dtype=torch.float32, device=dev) if a is None else a
+        b = torch.empty(self.d_out, dtype=torch.float32, device=dev) if b is None else b
+        if workspace is None:
+            workspace = torch.empty(self.solve_workspace_bytes(), dtype=torch.uint8, device=dev)
+        _check("rf_ridge_dev_solve", lib().rf_ridge_dev_solve(
+            self.handle, lam, RF_RIDGE_RAW if raw else 0, _ptr(a), _ptr(b), _ptr(workspace),
+            workspace.numel() * workspace.element_size(), _stream(stream)))
+        return a, b
 
     def close(self):
         if self.handle:

@@ -25,6 +25,7 @@
 #include "../../include/rf.h"
 #include "rf_error.h"
 #include "rf_ridge_internal.h"
+#include "rf_solve.h"
 
 namespace rf {
 namespace {
@@ -301,6 +302,35 @@ rf_status rf_ridge_dev_add(rf_ridge_dev* a, const uint16_t* x, int64_t ld_x, con
     return RF_E_HIP;
   }
   a->n += n;
+  return RF_OK;
+}
+
+size_t rf_ridge_dev_solve_workspace_bytes(const rf_ridge_dev* a) {
+  return a ? rf::ridge_solve_workspace_bytes(a->d_in, a->d_out) : 0;
+}
+
+rf_status rf_ridge_dev_solve(const rf_ridge_dev* a, double lambda, int32_t flags, float* A, float* b, void* ws,
+                             size_t ws_bytes, void* stream) {
+  if (!a || !A || !b) return rf::cfail(RF_E_ARG, "null argument");
+  if (flags & ~RF_RIDGE_RAW) return rf::cfail(RF_E_ARG, "unknown ridge flag");
+  if (a->n < 1) return rf::cfail(RF_E_ARG, "no rows accumulated");
+  if (!(lambda >= 0.0)) return rf::cfail(RF_E_ARG, "lambda must be >= 0");
+  if ((reinterpret_cast<uintptr_t>(A) | reinterpret_cast<uintptr_t>(b)) & 3)
+    return rf::cfail(RF_E_ARG, "a and b must be 4-byte aligned");
+  if (!ws || (reinterpret_cast<uintptr_t>(ws) & 255) || ws_bytes < rf::ridge_solve_workspace_bytes(a->d_in, a->d_out))
+    return rf::cfail(RF_E_WORKSPACE, "workspace too small or not 256-byte aligned");
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  rf::RidgeSolveIn in{a->sxx, a->sxy, a->sx, a->sy, a->n, a->d_in, a->d_out};
+  int* flag = nullptr;
+  hipError_t e = rf::ridge_solve_enqueue(in, lambda, flags & RF_RIDGE_RAW, A, b, ws, &flag, s);
+  int h = 0;
+  if (e == hipSuccess) e = hipMemcpyAsync(&h, flag, sizeof(int), hipMemcpyDeviceToHost, s);
+  if (e == hipSuccess) e = hipStreamSynchronize(s);
+  if (e != hipSuccess) {
+    rf::set_last_error(hipGetErrorString(e));
+    return RF_E_HIP;
+  }
+  if (h) return rf::cfail(RF_E_LINALG, "ridge system is not positive definite");
   return RF_OK;
 }
 

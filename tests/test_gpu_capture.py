@@ -1,10 +1,10 @@
-"""GPU capture of the ridge sums (rf_ridge_dev_*), RidgeFill section 2.2 "Fitting".
+"""GPU capture of the ridge sums and the solve from them (rf_ridge_dev_*),
+RidgeFill section 2.2 "Fitting".
 
-The device sums are merged into the host accumulator and solved there; the
-result is compared with the fp64 oracle on the same bf16 values (relative
-1e-9, the solve's conditioning times fp64 rounding) and with the host
-accumulator fed the same rows (relative 1e-10: only the order of the exact
-products' fp64 additions differs).
+The device sums are merged into the host accumulator and solved there, and
+solved on the GPU (rf_ridge_dev_solve); the results are compared with the
+fp64 oracle on the same bf16 values and with the host accumulator fed the
+same rows (only the order of the exact products' fp64 additions differs).
 """
 import numpy as np
 import pytest
@@ -120,3 +120,95 @@ def test_capture_at_27b_width():
     for got, want in ((sxx, ref.sxx), (sxy, ref.sxy), (sx, ref.sx), (sy, ref.sy)):
         scale = np.max(np.abs(want))
         assert np.max(np.abs(got - want)) <= 1e-12 * scale * np.sqrt(n), float(np.max(np.abs(got - want)) / scale)
+
+
+# ---------------------------------------------------------------- the solve on the GPU
+
+def _fill_sums(d_in, d_out, xb, yb, chunks=None):
+    dev = B.RidgeDeviceSums(d_in, d_out)
+    ref = oracle.RidgeSums(d_in, d_out)
+    r0 = 0
+    for c in (chunks or (xb.shape[0],)):
+        dev.add(U.t16(xb[r0:r0 + c]).cuda(), U.t16(yb[r0:r0 + c]).cuda())
+        ref.add(oracle.bf16_bits_to_f64(xb[r0:r0 + c]), oracle.bf16_bits_to_f64(yb[r0:r0 + c]))
+        r0 += c
+    return dev, ref
+
+
+def _close(got, want, rel):
+    scale = np.max(np.abs(want))
+    err = np.max(np.abs(got - want)) / scale
+    assert err <= rel, f"max error {err:.3e} relative to the largest entry"
+    return err
+
+
+@pytest.mark.parametrize("d_in,d_out", [(256, 384), (512, 256), (1024, 1024)])
+def test_device_solve_matches_oracle(d_in, d_out):
+    """rf_ridge_dev_solve against the fp64 oracle on the same bf16 values
+    (outputs are fp32: 1e-6 of the largest entry), for two lambdas and the raw
+    form; the sums survive the solve, and a repeated solve is bitwise equal."""
+    _say(f"[gpu solve] d_in={d_in} d_out={d_out}")
+    n = 3 * d_in + 17
+    xb, yb = _data(70 + d_in + d_out, n, d_in, d_out)
+    dev, ref = _fill_sums(d_in, d_out, xb, yb, chunks=(n // 3, n - n // 3))
+    xf, yf = oracle.bf16_bits_to_f64(xb), oracle.bf16_bits_to_f64(yb)
+    for lam in (0.03, 1.0):
+        a, b = dev.solve(lam)
+        a_r, b_r = ref.solve(lam)
+        ea = _close(a.cpu().numpy(), a_r, 1e-6)
+        eb = _close(b.cpu().numpy(), b_r, 1e-6)
+        _say(f"[gpu solve] lambda={lam}: A {ea:.2e}, b {eb:.2e}")
+    a_raw, b_raw = dev.solve(0.5, raw=True)
+    a_rr, _ = oracle.ridge_fit_raw(xf, yf, 0.5)
+    _close(a_raw.cpu().numpy(), a_rr, 1e-6)
+    assert not torch.any(b_raw)
+    a1, b1 = dev.solve(0.03)
+    a2, b2 = dev.solve(0.03)
+    assert torch.equal(a1, a2) and torch.equal(b1, b2)
+    # the host solve of the merged sums agrees too
+    merged = B.RidgeAccumulator(d_in, d_out)
+    dev.merge(merged)
+    a_h, b_h = merged.solve(0.03)
+    _close(a1.cpu().numpy(), a_h, 2e-6)
+
+
+def test_device_solve_reports_a_singular_system():
+    """Constant rows: the centred X^T X is zero, so with any lambda the
+    system is singular (alpha scales with its trace) and the call reports it."""
+    d = 128
+    xb = workloads.f32_to_bf16_bits(np.ones((50, d), dtype=np.float32))
+    yb = workloads.f32_to_bf16_bits(np.random.default_rng(5).standard_normal((50, d)).astype(np.float32))
+    dev, _ = _fill_sums(d, d, xb, yb)
+    with pytest.raises(B.RfError) as e:
+        dev.solve(0.1)
+    assert e.value.status == -6
+    assert "positive definite" in B.last_error()
+    # raw with lambda > 0 is regular: X^T X + lambda I
+    a, b = dev.solve(0.1, raw=True)
+    assert torch.isfinite(a).all()
+
+
+def test_device_solve_at_27b_width():
+    """d = 5120 from 4,096 captured rows (fewer rows than width: only the
+    penalty makes the system regular), against the fp64 oracle."""
+    d, n = 5120, 4096
+    _say("[gpu solve 27b width] generating")
+    s = workloads.spec("27b", n_late=1, prompt_lens=(n,), tail=16, seed=63)
+    w = workloads.make(s)
+    xb = w.x
+    yb = workloads.make_layer_truth(s, n, outliers=w.outlier_channels)[0]
+    dev = B.RidgeDeviceSums(d, d)
+    dev.add(U.t16(xb).cuda(), U.t16(yb).cuda())
+    ws = torch.empty(dev.solve_workspace_bytes(), dtype=torch.uint8, device="cuda:0")
+    dev.solve(0.03, workspace=ws)
+    import time
+    t0 = time.perf_counter()
+    a, b = dev.solve(0.03, workspace=ws)
+    ms = (time.perf_counter() - t0) * 1e3
+    _say(f"[gpu solve 27b width] {ms:.1f} ms per solve (including its sync)")
+    ref = oracle.RidgeSums(d, d)
+    ref.add(oracle.bf16_bits_to_f64(xb), oracle.bf16_bits_to_f64(yb))
+    a_r, b_r = ref.solve(0.03)
+    ea = _close(a.cpu().numpy(), a_r, 1e-5)
+    eb = _close(b.cpu().numpy(), b_r, 1e-5)
+    _say(f"[gpu solve 27b width] A {ea:.2e}, b {eb:.2e}")
