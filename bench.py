@@ -215,6 +215,8 @@ def main():
     ap.add_argument("--value-rescale", type=int, default=0, metavar="C",
                     help="include the value rescale measured on the first C tail rows of each prompt")
     ap.add_argument("--qk-norm", action="store_true", help="layers normalise their keys per head before RoPE")
+    ap.add_argument("--separate-measure", action="store_true",
+                    help="with --value-rescale: measure with rf_value_scales, then fill (default: inside the fill)")
     ap.add_argument("--indexer", type=int, default=0, metavar="HEADS",
                     help="layers also write HEADS head_dim-wide indexer key heads (sparse-attention layers)")
     ap.add_argument("--maps", default="bf16", choices=["bf16", "q8"],
@@ -287,7 +289,7 @@ def main():
     plan = B.Plan.for_spec(s)
     g = args.layers_per_launch or GROUP[name]
     ws = torch.empty(plan.fill_workspace_bytes(n_fill, g), dtype=torch.uint8, device=dev)
-    vscale = None
+    vscale = measure = None
     if args.value_rescale:
         c_rows, c_grp = workloads.calibration_row_list(s, args.value_rescale)
         truth = [t16(t, dev) for t in workloads.make_layer_truth(s, len(c_rows), outliers=w.outlier_channels)]
@@ -296,7 +298,9 @@ def main():
         n_groups = len(s.prompt_lens)
         scales = torch.empty((s.n_late, n_groups, s.n_kv), dtype=torch.float32, device=dev)
         ws_scale = torch.empty(plan.value_scales_workspace_bytes(len(c_rows), g), dtype=torch.uint8, device=dev)
-        vscale = (scales, torch.from_numpy(workloads.prompt_of_row(s)).to(dev), n_groups)
+        g_of_row = torch.from_numpy(workloads.prompt_of_row(s)).to(dev)
+        vscale = (scales, g_of_row, n_groups)
+        measure = None if args.separate_measure else (truth, c_rows_d, c_grp_d, g_of_row, n_groups, scales, ws_scale)
     fill_rows = torch.empty(s.n_rows, dtype=torch.int32, device=dev)
     n_fill_dev = torch.empty(1, dtype=torch.int32, device=dev)
     rows_ws = torch.empty(B.fill_rows_workspace_bytes(s.n_rows), dtype=torch.uint8, device=dev)
@@ -304,6 +308,14 @@ def main():
 
     def step():
         B.fill_rows(plan, exact, fill_rows, n_fill_dev, rows_ws)
+        if vscale is not None and measure is not None:
+            if q8:
+                B.fill_q8(plan, x, fill_rows, n_fill, positions, None, map_q, map_s, map_b, gamma, w_k, w_v, None,
+                          kc, vc, ws, k_norm=k_norm, w_idx=w_idx, idx_cache=ic, measure=measure)
+            else:
+                B.fill(plan, x, fill_rows, n_fill, positions, None, map_a, map_b, gamma, w_k, w_v, None, kc, vc, ws,
+                       k_norm=k_norm, w_idx=w_idx, idx_cache=ic, measure=measure)
+            return
         if vscale is not None:
             if q8:
                 B.value_scales(plan, x, truth, c_rows_d, c_grp_d, n_groups, map_q, map_b, gamma, w_v, scales,
@@ -379,6 +391,8 @@ def main():
                    "prompts": list(s.prompt_lens), "maps": "pinned host, streamed" if host_maps else "HBM",
                    "map_format": "int8 + bf16 scale per 128 weights of a row" if q8 else "bf16",
                    "value_rescale_rows": args.value_rescale or None,
+                   "value_measure": (None if not args.value_rescale else
+                                     "rf_value_scales, then rf_fill" if args.separate_measure else "inside rf_fill"),
                    "qk_norm": bool(args.qk_norm),
                    "indexer_key_heads": args.indexer,
                    "layers_per_launch": 1 if host_maps else g},

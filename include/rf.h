@@ -151,6 +151,33 @@ typedef struct rf_vscale {
   int32_t n_groups;             /* >= 1                                                    */
 } rf_vscale;
 
+/* The value-scale measurement (section 2.3, see rf_value_scales below) run
+ * inside the fill: each layer group's scales are measured from the
+ * calibration rows with the maps the fill has already loaded for that group,
+ * written to `scale`, and applied to the group's filled values like an
+ * rf_vscale.  Scales and outputs are bitwise those of rf_value_scales followed
+ * by rf_fill with an rf_vscale; streamed maps (RF_MAPS_HOST) cross PCIe once.
+ *   layer_in     HOST array of n_late device pointers: true input of each
+ *                calibration row, bf16 [n_calib][ld_in], 16-byte aligned
+ *   calib_rows   device int32 [n_calib]: the calibration rows (rows of x)
+ *   calib_group  device int32 [n_calib]: request of each, in [0, n_groups)
+ *   group_of_row device int32 [n_rows]: request of every row (for applying)
+ *   scale        device fp32 [n_late][n_groups][n_kv], 4-byte aligned; written
+ *   workspace    device, >= rf_value_scales_workspace_bytes(plan, n_calib, 1),
+ *                256-byte aligned (separate from the fill's workspace) */
+typedef struct rf_vmeasure {
+  const uint16_t* const* layer_in;
+  int64_t ld_in;
+  const int32_t* calib_rows;
+  const int32_t* calib_group;
+  int32_t n_calib;
+  const int32_t* group_of_row;
+  int32_t n_groups;
+  float* scale;
+  void* workspace;
+  size_t ws_bytes;
+} rf_vmeasure;
+
 /* Options of a fill (HOST struct; pass NULL for none of them).
  *   vscale  value rescale (above), or NULL
  *   k_norm  QK-norm for layers that normalise their keys (RidgeFill section
@@ -167,12 +194,16 @@ typedef struct rf_vscale {
  *           (the indexer key projection), idx_cache bf16
  *           [n_slots][n_idx*head_dim].  Each indexer head is the normalised
  *           input times W_idx, rotated like the attention keys (same theta and
- *           pairing), without QK-norm; it is stored at the row's slot like K. */
+ *           pairing), without QK-norm; it is stored at the row's slot like K.
+ *   measure value-scale measurement inside the fill (rf_vmeasure above), or
+ *           NULL; replaces vscale (give at most one of the two); rf_fill and
+ *           rf_fill_q8 only. */
 typedef struct rf_fill_opts {
   const rf_vscale* vscale;
   const uint16_t* const* k_norm;
   const uint16_t* const* w_idx;
   uint16_t* const* idx_cache;
+  const rf_vmeasure* measure;
 } rf_fill_opts;
 
 /* The fill (steps 1-5 above) for n_fill rows and every late layer.

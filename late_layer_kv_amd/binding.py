@@ -62,10 +62,18 @@ class VScale(C.Structure):
     _fields_ = [("scale", C.c_void_p), ("group_of_row", C.c_void_p), ("n_groups", C.c_int32)]
 
 
+class VMeasure(C.Structure):
+    """rf_vmeasure: the value-scale measurement run inside a fill."""
+    _fields_ = [("layer_in", C.POINTER(C.c_void_p)), ("ld_in", C.c_int64), ("calib_rows", C.c_void_p),
+                ("calib_group", C.c_void_p), ("n_calib", C.c_int32), ("group_of_row", C.c_void_p),
+                ("n_groups", C.c_int32), ("scale", C.c_void_p), ("workspace", C.c_void_p), ("ws_bytes", C.c_size_t)]
+
+
 class FillOpts(C.Structure):
-    """rf_fill_opts: value rescale, QK-norm and indexer keys of a fill."""
+    """rf_fill_opts: value rescale, QK-norm, indexer keys and in-fill measurement of a fill."""
     _fields_ = [("vscale", C.POINTER(VScale)), ("k_norm", C.POINTER(C.c_void_p)),
-                ("w_idx", C.POINTER(C.c_void_p)), ("idx_cache", C.POINTER(C.c_void_p))]
+                ("w_idx", C.POINTER(C.c_void_p)), ("idx_cache", C.POINTER(C.c_void_p)),
+                ("measure", C.POINTER(VMeasure))]
 
 
 _lib = None
@@ -224,9 +232,9 @@ def fill_rows(plan: Plan, exact_rows, fill_rows_out, n_fill_out, workspace, stre
 class _Opts:
     """Keeps an rf_fill_opts and everything it points to alive for one call."""
 
-    def __init__(self, vscale=None, k_norm=None, w_idx=None, idx_cache=None):
+    def __init__(self, vscale=None, k_norm=None, w_idx=None, idx_cache=None, measure=None):
         self.ref = None
-        if vscale is None and k_norm is None and w_idx is None and idx_cache is None:
+        if vscale is None and k_norm is None and w_idx is None and idx_cache is None and measure is None:
             return
         self.opts = FillOpts()
         if vscale is not None:
@@ -242,20 +250,30 @@ class _Opts:
         if idx_cache is not None:
             self.ic = _ptr_array(idx_cache)
             self.opts.idx_cache = C.cast(self.ic, C.POINTER(C.c_void_p))
+        if measure is not None:
+            # (layer_in list, calib_rows, calib_group, group_of_row, n_groups, scale out, workspace)
+            layer_in, calib_rows, calib_group, group_of_row, n_groups, scale, ws = measure
+            self.li = _ptr_array(layer_in)
+            self.vm = VMeasure(C.cast(self.li, C.POINTER(C.c_void_p)), layer_in[0].stride(0), _ptr(calib_rows),
+                               _ptr(calib_group), calib_rows.numel(), _ptr(group_of_row), n_groups, _ptr(scale),
+                               _ptr(ws), ws.numel() * ws.element_size())
+            self.opts.measure = C.pointer(self.vm)
         self.ref = C.byref(self.opts)
 
 
 def fill(plan: Plan, x, fill_rows_t, n_fill: int, positions, slot_of_row, map_a: Sequence, map_b: Sequence,
          gamma: Sequence, w_k: Sequence, w_v: Sequence, rope, k_cache: Sequence, v_cache: Sequence,
          workspace, stream=None, ld_x: Optional[int] = None, vscale=None, k_norm: Sequence = None,
-         w_idx: Sequence = None, idx_cache: Sequence = None) -> None:
+         w_idx: Sequence = None, idx_cache: Sequence = None, measure=None) -> None:
     """rf_fill.  map_a/map_b are device tensors, or pinned host tensors for a
     plan made with maps_on_host.  vscale = (scale [n_late][n_groups][n_kv] fp32,
     group_of_row [n_rows] int32, n_groups) applies a value rescale; k_norm (one
     bf16 [head_dim] gain per late layer) applies QK-norm to the keys; w_idx /
-    idx_cache (per late layer) write the indexer keys of a plan with n_idx > 0."""
+    idx_cache (per late layer) write the indexer keys of a plan with n_idx > 0;
+    measure = (layer_in, calib_rows, calib_group, group_of_row, n_groups, scale,
+    workspace) measures the value scales inside the fill and applies them."""
     ld = x.stride(0) if ld_x is None else ld_x
-    o = _Opts(vscale, k_norm, w_idx, idx_cache)
+    o = _Opts(vscale, k_norm, w_idx, idx_cache, measure)
     _check("rf_fill", lib().rf_fill(
         plan.handle, _ptr(x), ld, _ptr(fill_rows_t), n_fill, _ptr(positions), _ptr(slot_of_row),
         _ptr_array(map_a), _ptr_array(map_b), _ptr_array(gamma), _ptr_array(w_k), _ptr_array(w_v),
@@ -266,11 +284,12 @@ def fill(plan: Plan, x, fill_rows_t, n_fill: int, positions, slot_of_row, map_a:
 def fill_q8(plan: Plan, x, fill_rows_t, n_fill: int, positions, slot_of_row, map_q: Sequence,
             map_scale: Sequence, map_b: Sequence, gamma: Sequence, w_k: Sequence, w_v: Sequence, rope,
             k_cache: Sequence, v_cache: Sequence, workspace, stream=None, ld_x: Optional[int] = None,
-            vscale=None, k_norm: Sequence = None, w_idx: Sequence = None, idx_cache: Sequence = None) -> None:
+            vscale=None, k_norm: Sequence = None, w_idx: Sequence = None, idx_cache: Sequence = None,
+            measure=None) -> None:
     """rf_fill_q8: the fill with int8 maps (codes + bf16 block scales) for a
     plan made with maps_q8; pinned host tensors for a plan with maps_on_host."""
     ld = x.stride(0) if ld_x is None else ld_x
-    o = _Opts(vscale, k_norm, w_idx, idx_cache)
+    o = _Opts(vscale, k_norm, w_idx, idx_cache, measure)
     _check("rf_fill_q8", lib().rf_fill_q8(
         plan.handle, _ptr(x), ld, _ptr(fill_rows_t), n_fill, _ptr(positions), _ptr(slot_of_row),
         _ptr_array(map_q), _ptr_array(map_scale), _ptr_array(map_b), _ptr_array(gamma), _ptr_array(w_k),

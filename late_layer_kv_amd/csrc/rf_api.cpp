@@ -3,6 +3,7 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <memory>
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
@@ -458,17 +459,219 @@ rf_status check_vscale(const rf_plan* p, const rf_vscale* vs) {
   return RF_OK;
 }
 
+// Workspace of the value-scale measurement, in carve order.
+struct ScaleWs {
+  size_t prep, y, dq, v, ratio, pos, ssq, rs, total;
+};
+ScaleWs scale_ws(const rf_plan* p, int n, int g) {
+  const rf_shape& s = p->s;
+  ScaleWs r{};
+  r.prep = prep_bytes(s, g);
+  r.y = y_bytes(s, n, g);
+  r.dq = dq_bytes(s, p->flags, g);
+  r.v = up(static_cast<size_t>(g) * n * kv_width(s) * 2);
+  r.ratio = up(static_cast<size_t>(s.n_late) * n * s.n_kv * 4);
+  r.pos = up(static_cast<size_t>(std::max(n, 1)) * 4);
+  r.ssq = ssq_bytes(s, n, g);
+  r.rs = rs_bytes(n, g);
+  r.total = kFlagBytes + r.prep + r.y + r.dq + 2 * r.v + r.ratio + r.pos + r.ssq + r.rs;
+  return r;
+}
+
+// The value-scale measurement of one layer group, on a workspace carved as
+// ScaleWs (its prep and dq parts unused here): predicted values of the
+// calibration rows from the group's maps, exact values from the true inputs,
+// their per-head norm ratios, and the per-request means for the group's layers.
+class ScaleMeasure {
+ public:
+  ScaleMeasure(rf_plan* p, hipStream_t hs, void* ws, int G, const uint16_t* x, int64_t ld_x,
+               const uint16_t* const* layer_in, int64_t ld_in, const int32_t* calib_rows, const int32_t* calib_group,
+               int n, int n_groups, const uint16_t* prep, int wrows)
+      : p_(p), hs_(hs), s_(p->s), layer_in_(layer_in), ld_in_(ld_in), calib_group_(calib_group), n_(n),
+        n_groups_(n_groups) {
+    const ScaleWs sw = scale_ws(p, n, G);
+    char* c = static_cast<char*>(ws) + kFlagBytes + sw.prep;
+    ybuf_ = reinterpret_cast<uint16_t*>(c);
+    ve_ = reinterpret_cast<uint16_t*>(c += sw.y + sw.dq);
+    vp_ = reinterpret_cast<uint16_t*>(c += sw.v);
+    ratio_ = reinterpret_cast<float*>(c += sw.v);
+    zero_pos_ = reinterpret_cast<int32_t*>(c += sw.ratio);
+    ssq_ = reinterpret_cast<float*>(c += sw.pos);
+    rsb_ = reinterpret_cast<float*>(c += sw.ssq);
+    const int w = kv_width(s_);
+    mp_.x = x;
+    mp_.ld_x = ld_x;
+    mp_.rows = calib_rows;
+    mp_.n_rows = s_.n_rows;
+    mp_.M = n;
+    mp_.K = s_.d_in;
+    mp_.N = s_.d_out;
+    mp_.tiles_m = (n + rf::kTileM - 1) / rf::kTileM;
+    mp_.tiles_n = s_.d_out / rf::kTileN;
+    mp_.y = ybuf_;
+    mp_.ssq = ssq_;
+    // Value features only, row m of the call stored densely at row m (slot =
+    // row, rows numbered 0..n-1; positions are not used by values).
+    kp_.n_in_rows = n;
+    kp_.M = n;
+    kp_.K = s_.d_out;
+    kp_.w = w;
+    kp_.head_dim = s_.head_dim;
+    kp_.tiles_m = mp_.tiles_m;
+    kp_.tiles_n = (2 * w - w / rf::kTileN * rf::kTileN) / rf::kTileN;
+    kp_.wrows = wrows;
+    kp_.wkv = prep;
+    kp_.positions = zero_pos_;
+    kp_.n_rows = n;
+    kp_.n_slots = n;
+    kp_.max_pos = s_.max_pos;
+    kp_.eps = s_.rms_eps;
+    kp_.n_kv = s_.n_kv;
+    kp_.v_only = 1;
+    rp_.n = n;
+    rp_.n_kv = s_.n_kv;
+    rp_.head_dim = s_.head_dim;
+    rmp_.ld_in = ld_in;
+    rmp_.n_in_rows = n;
+    rmp_.M = n;
+    rmp_.K = s_.d_out;
+    rmp_.inv_k = 1.0f / s_.d_out;
+    rmp_.eps = s_.rms_eps;
+    rmp_.rs = rsb_;
+  }
+
+  rf_status begin() {
+    if (n_ == 0) return RF_OK;
+    hipError_t e = rf::launch_zero_i32(zero_pos_, n_, hs_);
+    return e == hipSuccess ? RF_OK : hip_fail(e, "clear launch");
+  }
+
+  // The calibration rows through the maps of layers l0 .. l0+g-1 (device
+  // maps in maps.a / maps.b); then finish().
+  rf_status group(int l0, int g, const rf::MapParams& maps) {
+    hipError_t e;
+    const size_t v_layer = static_cast<size_t>(n_) * kv_width(s_);
+    if (n_ > 0) {
+      for (int i = 0; i < g; ++i) {
+        mp_.a[i] = maps.a[i];
+        mp_.b[i] = maps.b[i];
+        rp_.ve[i] = ve_ + i * v_layer;
+        rp_.vp[i] = vp_ + i * v_layer;
+        rp_.ratio[i] = ratio_ + static_cast<size_t>(l0 + i) * n_ * s_.n_kv;
+      }
+      Timed tm(p_, RF_K_SCALE, hs_);
+      if ((e = rf::launch_map(mp_, g, hs_)) != hipSuccess) return hip_fail(e, "map launch");
+    }
+    return RF_OK;
+  }
+
+  // The rest of the group once the maps may be released: predicted values
+  // from the map's output (norms from its row sums), exact values from the
+  // true inputs (norms from a pass over them), ratios, and the means of the
+  // group's layers into scale [n_late][n_groups][n_kv].
+  rf_status finish(int l0, int g, float* scale) {
+    hipError_t e;
+    const int w = kv_width(s_);
+    const size_t y_layer = static_cast<size_t>(n_) * s_.d_out;
+    const size_t v_layer = static_cast<size_t>(n_) * w;
+    if (n_ > 0) {
+      {
+        Timed tm(p_, RF_K_SCALE, hs_);
+        if ((e = rf::launch_row_scale(ssq_, mp_.tiles_n, n_, g, 1.0f / s_.d_out, s_.rms_eps, rsb_, hs_)) != hipSuccess)
+          return hip_fail(e, "row scale launch");
+      }
+      kp_.ld_in = s_.d_out;
+      for (int i = 0; i < g; ++i) {
+        kp_.in[i] = ybuf_ + i * y_layer;
+        kp_.vc[i] = vp_ + i * v_layer;
+        kp_.rs[i] = rsb_ + static_cast<size_t>(i) * n_;
+      }
+      {
+        Timed tm(p_, RF_K_SCALE, hs_);
+        if ((e = rf::launch_kv(kp_, g, hs_)) != hipSuccess) return hip_fail(e, "kv launch");
+      }
+      kp_.ld_in = ld_in_;
+      for (int i = 0; i < g; ++i) {
+        kp_.in[i] = layer_in_[l0 + i];
+        kp_.vc[i] = ve_ + i * v_layer;
+        rmp_.in[i] = layer_in_[l0 + i];
+      }
+      {
+        // (the same stream: the predicted launch above has read rsb)
+        Timed tm(p_, RF_K_SCALE, hs_);
+        if ((e = rf::launch_row_rms(rmp_, g, hs_)) != hipSuccess) return hip_fail(e, "row rms launch");
+      }
+      {
+        Timed tm(p_, RF_K_SCALE, hs_);
+        if ((e = rf::launch_kv(kp_, g, hs_)) != hipSuccess) return hip_fail(e, "kv launch");
+      }
+      {
+        Timed tm(p_, RF_K_SCALE, hs_);
+        if ((e = rf::launch_head_ratio(rp_, g, hs_)) != hipSuccess) return hip_fail(e, "ratio launch");
+      }
+    }
+    Timed tm(p_, RF_K_SCALE, hs_);
+    const size_t per_layer_ratio = static_cast<size_t>(n_) * s_.n_kv;
+    const size_t per_layer_scale = static_cast<size_t>(n_groups_) * s_.n_kv;
+    if ((e = rf::launch_scale_mean(ratio_ + l0 * per_layer_ratio, calib_group_, n_, s_.n_kv, n_groups_, g,
+                                   scale + l0 * per_layer_scale, hs_)) != hipSuccess)
+      return hip_fail(e, "scale launch");
+    return RF_OK;
+  }
+
+ private:
+  rf_plan* p_;
+  hipStream_t hs_;
+  const rf_shape& s_;
+  const uint16_t* const* layer_in_;
+  int64_t ld_in_;
+  const int32_t* calib_group_;
+  int n_, n_groups_;
+  uint16_t *ybuf_, *ve_, *vp_;
+  float *ratio_, *ssq_, *rsb_;
+  int32_t* zero_pos_;
+  rf::MapParams mp_{};
+  rf::KvParams kp_{};
+  rf::RatioParams rp_{};
+  rf::RmsParams rmp_{};
+};
+
+rf_status check_measure_args(const rf_plan* p, const uint16_t* const* layer_in, int64_t ld_in,
+                             const int32_t* calib_rows, const int32_t* calib_group, int32_t n, int32_t n_groups) {
+  const rf_shape& s = p->s;
+  if (n < 0 || n > s.n_rows) return fail(RF_E_ARG, "n_calib=%d outside [0, n_rows=%d]", n, s.n_rows);
+  if (n_groups < 1) return fail(RF_E_ARG, "n_groups=%d must be >= 1", n_groups);
+  if (ld_in < s.d_out || ld_in % 8)
+    return fail(RF_E_ARG, "ld_in=%lld must be >= d_out and a multiple of 8", (long long)ld_in);
+  if (n > 0 && (!calib_rows || !calib_group)) return fail(RF_E_ARG, "calib_rows or calib_group is null");
+  return check_layer_ptrs(reinterpret_cast<const void* const*>(layer_in), s.n_late, "layer_in");
+}
+
 rf_status fill_impl(rf_plan* p, const char* fn, const uint16_t* x, int64_t ld_x, const int32_t* fill_rows,
                     int32_t n_fill, const int32_t* positions, const int32_t* slot_of_row, const MapSrc& maps,
                     const uint16_t* const* gamma, const uint16_t* const* w_k, const uint16_t* const* w_v,
                     const float* rope, uint16_t* const* k_cache, uint16_t* const* v_cache, const rf_fill_opts* opts,
                     void* ws, size_t ws_bytes, void* stream) {
   const rf_shape& s = p->s;
-  const rf_vscale* vscale = opts ? opts->vscale : nullptr;
+  const rf_vmeasure* meas_in = opts ? opts->measure : nullptr;
+  // with a measurement, its scales are applied like an rf_vscale
+  const rf_vscale measured{meas_in ? meas_in->scale : nullptr, meas_in ? meas_in->group_of_row : nullptr,
+                           meas_in ? meas_in->n_groups : 0};
+  const rf_vscale* vscale = meas_in ? &measured : (opts ? opts->vscale : nullptr);
   const uint16_t* const* k_norm = opts ? opts->k_norm : nullptr;
   const int L = s.n_late;
   rf_status st;
   if ((st = check_maps(p, fn, maps)) != RF_OK) return st;
+  if (meas_in) {
+    if (opts->vscale) return fail(RF_E_ARG, "give opts->vscale or opts->measure, not both");
+    if ((st = check_measure_args(p, meas_in->layer_in, meas_in->ld_in, meas_in->calib_rows, meas_in->calib_group,
+                                 meas_in->n_calib, meas_in->n_groups)) != RF_OK)
+      return st;
+    const size_t m1 = rf_value_scales_workspace_bytes(p, meas_in->n_calib, 1);
+    if (!meas_in->workspace || (reinterpret_cast<uintptr_t>(meas_in->workspace) % kAlign) || meas_in->ws_bytes < m1)
+      return fail(RF_E_WORKSPACE, "measure workspace of %zu bytes given, %zu needed (256-byte aligned)",
+                  meas_in->ws_bytes, m1);
+  }
   if (n_fill < 0 || n_fill > s.n_rows) return fail(RF_E_ARG, "n_fill=%d outside [0, n_rows=%d]", n_fill, s.n_rows);
   if (!x || !aligned16(x)) return fail(RF_E_ARG, "x is null or not 16-byte aligned");
   if (ld_x < s.d_in || ld_x % 8) return fail(RF_E_ARG, "ld_x=%lld must be >= d_in and a multiple of 8", (long long)ld_x);
@@ -488,7 +691,10 @@ rf_status fill_impl(rf_plan* p, const char* fn, const uint16_t* x, int64_t ld_x,
   if (n_fill == 0) return RF_OK;
 
   hipStream_t hs = static_cast<hipStream_t>(stream);
-  const int G = pick_group(p, ws_bytes, [&](int g) { return rf_fill_workspace_bytes(p, n_fill, g); });
+  int G = pick_group(p, ws_bytes, [&](int g) { return rf_fill_workspace_bytes(p, n_fill, g); });
+  if (meas_in)
+    G = std::min(G, pick_group(p, meas_in->ws_bytes,
+                               [&](int g) { return rf_value_scales_workspace_bytes(p, meas_in->n_calib, g); }));
 
   char* w0 = static_cast<char*>(ws);
   float* rope_ws = reinterpret_cast<float*>(w0);
@@ -561,6 +767,13 @@ rf_status fill_impl(rf_plan* p, const char* fn, const uint16_t* x, int64_t ld_x,
   const size_t vs_layer = vscale ? static_cast<size_t>(vscale->n_groups) * s.n_kv : 0;
   MapFeeder feed(p, maps, dq, hs);
   if ((st = feed.begin()) != RF_OK) return st;
+  std::unique_ptr<ScaleMeasure> meas;
+  if (meas_in) {
+    meas.reset(new ScaleMeasure(p, hs, meas_in->workspace, G, x, ld_x, meas_in->layer_in, meas_in->ld_in,
+                                meas_in->calib_rows, meas_in->calib_group, meas_in->n_calib, meas_in->n_groups, prep,
+                                prep_rows(s)));
+    if ((st = meas->begin()) != RF_OK) return st;
+  }
   for (int l0 = 0; l0 < L; l0 += G) {
     const int g = std::min(G, L - l0);
     for (int i = 0; i < g; ++i) {
@@ -585,7 +798,11 @@ rf_status fill_impl(rf_plan* p, const char* fn, const uint16_t* x, int64_t ld_x,
       Timed tm(p, RF_K_MAP, hs);
       if ((e = rf::launch_map(mp, g, hs)) != hipSuccess) return hip_fail(e, "map launch");
     }
+    // the measurement's calibration rows go through the same loaded maps,
+    // and its scales for these layers are in place before the K/V launch
+    if (meas && (st = meas->group(l0, g, mp)) != RF_OK) return st;
     if ((st = feed.consumed(l0)) != RF_OK) return st;
+    if (meas && (st = meas->finish(l0, g, meas_in->scale)) != RF_OK) return st;
     {
       Timed tm(p, RF_K_NORM, hs);
       if ((e = rf::launch_row_scale(ssq, mp.tiles_n, n_fill, g, 1.0f / s.d_out, s.rms_eps, rsb, hs)) != hipSuccess)
@@ -599,25 +816,6 @@ rf_status fill_impl(rf_plan* p, const char* fn, const uint16_t* x, int64_t ld_x,
   return RF_OK;
 }
 
-// Workspace of the value-scale measurement, in carve order.
-struct ScaleWs {
-  size_t prep, y, dq, v, ratio, pos, ssq, rs, total;
-};
-ScaleWs scale_ws(const rf_plan* p, int n, int g) {
-  const rf_shape& s = p->s;
-  ScaleWs r{};
-  r.prep = prep_bytes(s, g);
-  r.y = y_bytes(s, n, g);
-  r.dq = dq_bytes(s, p->flags, g);
-  r.v = up(static_cast<size_t>(g) * n * kv_width(s) * 2);
-  r.ratio = up(static_cast<size_t>(s.n_late) * n * s.n_kv * 4);
-  r.pos = up(static_cast<size_t>(std::max(n, 1)) * 4);
-  r.ssq = ssq_bytes(s, n, g);
-  r.rs = rs_bytes(n, g);
-  r.total = kFlagBytes + r.prep + r.y + r.dq + 2 * r.v + r.ratio + r.pos + r.ssq + r.rs;
-  return r;
-}
-
 rf_status value_scales_impl(rf_plan* p, const char* fn, const uint16_t* x, int64_t ld_x,
                             const uint16_t* const* layer_in, int64_t ld_in, const int32_t* calib_rows,
                             const int32_t* calib_group, int32_t n, int32_t n_groups, const MapSrc& maps,
@@ -627,15 +825,10 @@ rf_status value_scales_impl(rf_plan* p, const char* fn, const uint16_t* x, int64
   const int L = s.n_late;
   rf_status st;
   if ((st = check_maps(p, fn, maps)) != RF_OK) return st;
-  if (n < 0 || n > s.n_rows) return fail(RF_E_ARG, "n_calib=%d outside [0, n_rows=%d]", n, s.n_rows);
-  if (n_groups < 1) return fail(RF_E_ARG, "n_groups=%d must be >= 1", n_groups);
+  if ((st = check_measure_args(p, layer_in, ld_in, calib_rows, calib_group, n, n_groups)) != RF_OK) return st;
   if (!x || !aligned16(x)) return fail(RF_E_ARG, "x is null or not 16-byte aligned");
   if (ld_x < s.d_in || ld_x % 8) return fail(RF_E_ARG, "ld_x=%lld must be >= d_in and a multiple of 8", (long long)ld_x);
-  if (ld_in < s.d_out || ld_in % 8)
-    return fail(RF_E_ARG, "ld_in=%lld must be >= d_out and a multiple of 8", (long long)ld_in);
-  if (n > 0 && (!calib_rows || !calib_group)) return fail(RF_E_ARG, "calib_rows or calib_group is null");
   if (!scale || (reinterpret_cast<uintptr_t>(scale) & 3)) return fail(RF_E_ARG, "scale is null or misaligned");
-  if ((st = check_layer_ptrs(reinterpret_cast<const void* const*>(layer_in), L, "layer_in")) != RF_OK) return st;
   if ((st = check_layer_ptrs(reinterpret_cast<const void* const*>(gamma), L, "gamma")) != RF_OK) return st;
   if ((st = check_layer_ptrs(reinterpret_cast<const void* const*>(w_v), L, "w_v")) != RF_OK) return st;
   const size_t need1 = rf_value_scales_workspace_bytes(p, n, 1);
@@ -647,138 +840,37 @@ rf_status value_scales_impl(rf_plan* p, const char* fn, const uint16_t* x, int64
   const ScaleWs sw = scale_ws(p, n, G);
   char* c = static_cast<char*>(ws) + kFlagBytes;
   uint16_t* prep = reinterpret_cast<uint16_t*>(c);
-  uint16_t* ybuf = reinterpret_cast<uint16_t*>(c += sw.prep);
-  uint16_t* dq = reinterpret_cast<uint16_t*>(c += sw.y);
-  uint16_t* ve = reinterpret_cast<uint16_t*>(c += sw.dq);
-  uint16_t* vp = reinterpret_cast<uint16_t*>(c += sw.v);
-  float* ratio = reinterpret_cast<float*>(c += sw.v);
-  int32_t* zero_pos = reinterpret_cast<int32_t*>(c += sw.ratio);
-  float* ssq = reinterpret_cast<float*>(c += sw.pos);
-  float* rsb = reinterpret_cast<float*>(c += sw.ssq);
-
-  hipError_t e;
+  uint16_t* dq = reinterpret_cast<uint16_t*>(c + sw.prep + sw.y);
   const int w = kv_width(s);
-  if (n > 0) {
-    rf::MapParams mp{};
-    mp.x = x;
-    mp.ld_x = ld_x;
-    mp.rows = calib_rows;
-    mp.n_rows = s.n_rows;
-    mp.M = n;
-    mp.K = s.d_in;
-    mp.N = s.d_out;
-    mp.tiles_m = (n + rf::kTileM - 1) / rf::kTileM;
-    mp.tiles_n = s.d_out / rf::kTileN;
-    mp.y = ybuf;
-    mp.ssq = ssq;
-
-    // Value half only, row m of the call stored densely at row m (slot = row,
-    // rows numbered 0..n-1 for this launch; positions are not used by values).
-    if ((e = rf::launch_zero_i32(zero_pos, n, hs)) != hipSuccess) return hip_fail(e, "clear launch");
-    rf::KvParams kp{};
-    kp.in_rows = nullptr;
-    kp.n_in_rows = n;
-    kp.out_rows = nullptr;
-    kp.M = n;
-    kp.K = s.d_out;
-    kp.w = w;
-    kp.head_dim = s.head_dim;
-    kp.tiles_m = mp.tiles_m;
-    kp.tiles_n = (2 * w - w / rf::kTileN * rf::kTileN) / rf::kTileN;
-    kp.wrows = 2 * w;  // keys and values only (no indexer rows here)
-    kp.wkv = prep;
-    kp.positions = zero_pos;
-    kp.n_rows = n;
-    kp.n_slots = n;
-    kp.max_pos = s.max_pos;
-    kp.eps = s.rms_eps;
-    kp.n_kv = s.n_kv;
-    kp.v_only = 1;
-
-    rf::PrepParams pp{};
-    pp.d = s.d_out;
-    pp.w = w;
-    pp.rows = 2 * w;
-    pp.out = prep;
-
-    rf::RatioParams rp{};
-    rp.n = n;
-    rp.n_kv = s.n_kv;
-    rp.head_dim = s.head_dim;
-
-    const size_t y_layer = static_cast<size_t>(n) * s.d_out;
-    const size_t v_layer = static_cast<size_t>(n) * w;
-    MapFeeder feed(p, maps, dq, hs);
-    if ((st = feed.begin()) != RF_OK) return st;
-    for (int l0 = 0; l0 < L; l0 += G) {
-      const int g = std::min(G, L - l0);
+  ScaleMeasure meas(p, hs, ws, G, x, ld_x, layer_in, ld_in, calib_rows, calib_group, n, n_groups, prep, 2 * w);
+  if ((st = meas.begin()) != RF_OK) return st;
+  rf::PrepParams pp{};
+  pp.d = s.d_out;
+  pp.w = w;
+  pp.rows = 2 * w;  // keys and values only (no indexer rows here)
+  pp.out = prep;
+  MapFeeder feed(p, maps, dq, hs);
+  if (n > 0 && (st = feed.begin()) != RF_OK) return st;
+  hipError_t e;
+  for (int l0 = 0; l0 < L; l0 += G) {
+    const int g = std::min(G, L - l0);
+    if (n > 0) {
       for (int i = 0; i < g; ++i) {
         pp.gamma[i] = gamma[l0 + i];
         pp.wk[i] = w_v[l0 + i];  // the key half of the prepared weights is not used
         pp.wv[i] = w_v[l0 + i];
-        rp.ve[i] = ve + i * v_layer;
-        rp.vp[i] = vp + i * v_layer;
-        rp.ratio[i] = ratio + static_cast<size_t>(l0 + i) * n * s.n_kv;
       }
       {
         Timed tm(p, RF_K_SCALE, hs);
         if ((e = rf::launch_prep(pp, g, hs)) != hipSuccess) return hip_fail(e, "prep launch");
       }
+      rf::MapParams mp{};
       if ((st = feed.load(l0, g, mp)) != RF_OK) return st;
-      {
-        Timed tm(p, RF_K_SCALE, hs);
-        if ((e = rf::launch_map(mp, g, hs)) != hipSuccess) return hip_fail(e, "map launch");
-      }
+      if ((st = meas.group(l0, g, mp)) != RF_OK) return st;
       if ((st = feed.consumed(l0)) != RF_OK) return st;
-      // predicted values from the map's output (norms from its row sums),
-      // exact values from the true inputs (norms from a pass over them)
-      {
-        Timed tm(p, RF_K_SCALE, hs);
-        if ((e = rf::launch_row_scale(ssq, mp.tiles_n, n, g, 1.0f / s.d_out, s.rms_eps, rsb, hs)) != hipSuccess)
-          return hip_fail(e, "row scale launch");
-      }
-      kp.ld_in = s.d_out;
-      for (int i = 0; i < g; ++i) {
-        kp.in[i] = ybuf + i * y_layer;
-        kp.vc[i] = vp + i * v_layer;
-        kp.rs[i] = rsb + static_cast<size_t>(i) * n;
-      }
-      {
-        Timed tm(p, RF_K_SCALE, hs);
-        if ((e = rf::launch_kv(kp, g, hs)) != hipSuccess) return hip_fail(e, "kv launch");
-      }
-      rf::RmsParams rmp{};
-      rmp.ld_in = ld_in;
-      rmp.n_in_rows = n;
-      rmp.M = n;
-      rmp.K = s.d_out;
-      rmp.inv_k = 1.0f / s.d_out;
-      rmp.eps = s.rms_eps;
-      rmp.rs = rsb;
-      kp.ld_in = ld_in;
-      for (int i = 0; i < g; ++i) {
-        kp.in[i] = layer_in[l0 + i];
-        kp.vc[i] = ve + i * v_layer;
-        rmp.in[i] = layer_in[l0 + i];
-      }
-      {
-        // (the same stream: the predicted launch above has read rsb)
-        Timed tm(p, RF_K_SCALE, hs);
-        if ((e = rf::launch_row_rms(rmp, g, hs)) != hipSuccess) return hip_fail(e, "row rms launch");
-      }
-      {
-        Timed tm(p, RF_K_SCALE, hs);
-        if ((e = rf::launch_kv(kp, g, hs)) != hipSuccess) return hip_fail(e, "kv launch");
-      }
-      {
-        Timed tm(p, RF_K_SCALE, hs);
-        if ((e = rf::launch_head_ratio(rp, g, hs)) != hipSuccess) return hip_fail(e, "ratio launch");
-      }
     }
+    if ((st = meas.finish(l0, g, scale)) != RF_OK) return st;
   }
-  Timed tm(p, RF_K_SCALE, hs);
-  if ((e = rf::launch_scale_mean(ratio, calib_group, n, s.n_kv, n_groups, L, scale, hs)) != hipSuccess)
-    return hip_fail(e, "scale launch");
   return RF_OK;
 }
 

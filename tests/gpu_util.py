@@ -85,7 +85,7 @@ def gpu_fill_rows(plan, di: DeviceInputs, exact: torch.Tensor = None):
 
 
 def gpu_fill(plan, di: DeviceInputs, rows: torch.Tensor, n_fill: int, caches=None, layers_per_launch=None,
-             map_a=None, map_b=None, rope=None, slots=None, vscale=None, idx_caches=None, w_idx=None):
+             map_a=None, map_b=None, rope=None, slots=None, vscale=None, idx_caches=None, w_idx=None, measure=None):
     """(K caches, V caches), plus the indexer-key caches when the workload has
     indexer heads."""
     s = di.w.spec
@@ -99,11 +99,11 @@ def gpu_fill(plan, di: DeviceInputs, rows: torch.Tensor, n_fill: int, caches=Non
     if di.q8 and map_a is None:
         B.fill_q8(plan, di.x, rows, n_fill, di.positions, slots, di.map_q, di.map_scale,
                   di.map_b if map_b is None else map_b, di.gamma, di.w_k, di.w_v, rope, kc, vc, ws, vscale=vscale,
-                  k_norm=di.k_norm, w_idx=wi, idx_cache=ic)
+                  k_norm=di.k_norm, w_idx=wi, idx_cache=ic, measure=measure)
     else:
         B.fill(plan, di.x, rows, n_fill, di.positions, slots, di.map_a if map_a is None else map_a,
                di.map_b if map_b is None else map_b, di.gamma, di.w_k, di.w_v, rope, kc, vc, ws, vscale=vscale,
-               k_norm=di.k_norm, w_idx=wi, idx_cache=ic)
+               k_norm=di.k_norm, w_idx=wi, idx_cache=ic, measure=measure)
     torch.cuda.synchronize()
     return (kc, vc) if ic is None else (kc, vc, ic)
 

@@ -389,3 +389,37 @@ def test_indexer_key_options():
     assert (p1.fill_workspace_bytes(448, 2) - p0.fill_workspace_bytes(448, 2)) == 2 * 256 * d * 2
     p0.close()
     p1.close()
+
+
+def test_in_fill_measurement_argument_errors():
+    """rf_fill_opts.measure: checked on the host before any device work."""
+    L = B.lib()
+    p = B.Plan(**_shape())
+    nl = 4
+    fake = C.c_void_p(0x1000)
+    arr = (C.c_void_p * nl)(*([0x1000] * nl))
+    ws = 1 << 40
+    need = p.value_scales_workspace_bytes(16, 1)
+
+    def call(vs=None, **kw):
+        m = dict(layer_in=C.cast(arr, C.POINTER(C.c_void_p)), ld_in=256, calib_rows=0x1000, calib_group=0x1000,
+                 n_calib=16, group_of_row=0x1000, n_groups=2, scale=0x1000, workspace=0x10000, ws_bytes=need)
+        m.update(kw)
+        vm = B.VMeasure(**m)
+        o = B.FillOpts()
+        o.measure = C.pointer(vm)
+        if vs is not None:
+            o.vscale = C.pointer(vs)
+        return L.rf_fill(p.handle, fake, 256, fake, 10, fake, None, arr, arr, arr, arr, arr, None, arr, arr,
+                         C.byref(o), C.c_void_p(0x10000), ws, None)
+    assert call(vs=B.VScale(0x1000, 0x1000, 1)) == -1       # vscale and measure together
+    assert call(n_calib=-1) == -1
+    assert call(n_groups=0) == -1
+    assert call(ld_in=100) == -1
+    assert call(calib_rows=None) == -1
+    assert call(layer_in=None) == -1
+    assert call(scale=None) == -1                            # nowhere to put the scales
+    assert call(group_of_row=None) == -1
+    assert call(ws_bytes=need - 1) == -4
+    assert call(workspace=0x10010) == -4
+    p.close()

@@ -161,3 +161,31 @@ def test_rows_outside_the_groups_are_skipped_and_streamed_equals_resident():
     U.check_placement(k1, v1, kept, s.n_rows)
     for l in range(s.n_late):
         assert torch.equal(k1[l], k2[l]) and torch.equal(v1[l], v2[l]), f"layer {l}"
+
+
+@pytest.mark.parametrize("name,groups", [("tiny_ragged", None), ("8b_mid_two", 1), ("27b_mid_q8", None),
+                                         ("ragged_host", None)])
+def test_measured_fill_equals_two_calls(name, groups):
+    """The measurement run inside the fill (rf_fill_opts.measure, the maps
+    loaded once per layer group) gives bitwise the scales of rf_value_scales
+    and the caches of the fill that applies them, also when the measurement's
+    workspace allows fewer layers per launch than the fill's."""
+    w, rows, grp, truth = _case(name)
+    s = w.spec
+    ng = len(s.prompt_lens)
+    _say(f"[measured fill] {name} groups={groups}")
+    di = U.DeviceInputs(w)
+    plan = U.plan_for(w)
+    td = [U.t16(t).cuda() for t in truth]
+    g_of_row = U.i32(workloads.prompt_of_row(s)).cuda()
+    sc = gpu_scales(plan, di, rows, grp, td, ng)
+    fr, n = U.gpu_fill_rows(plan, di)
+    k1, v1 = U.gpu_fill(plan, di, fr, n, vscale=(sc, g_of_row, ng))
+    sc2 = torch.full_like(sc, -7.0)
+    g = s.n_late if groups is None else groups
+    mws = torch.empty(plan.value_scales_workspace_bytes(len(rows), g), dtype=torch.uint8, device="cuda:0")
+    measure = (td, U.i32(rows).cuda(), U.i32(grp).cuda(), g_of_row, ng, sc2, mws)
+    k2, v2 = U.gpu_fill(plan, di, fr, n, measure=measure)
+    assert torch.equal(sc, sc2)
+    for l in range(s.n_late):
+        assert torch.equal(k1[l], k2[l]) and torch.equal(v1[l], v2[l]), f"layer {l}"
