@@ -4,13 +4,16 @@ The map contraction runs ceil(d_in / 64) stages of 64 columns, with separate
 code for one, two and three stages; the tiles have 256 rows, so fills of 1,
 255, 256 and 257 rows sit on and around a tile edge; d_in and d_out may
 differ (the map is d_out x d_in).  Values against the fp64 oracle to the
-fill's tolerance, placement bit-exact.
+fill's tolerance, placement bit-exact.  The last case turns every option of
+the fill on at once.
 """
 import numpy as np
 import pytest
+import torch
 
 import oracle
 import workloads
+from late_layer_kv_amd import binding as B
 from tests import gpu_util as U
 
 pytestmark = pytest.mark.gpu
@@ -56,3 +59,41 @@ def test_int8_map_depths(d_in):
     """Int8 maps at one and three 128-column scale blocks (2 and 6 stages)."""
     _check(workloads.spec("tiny", d_in=d_in, n_late=2, prompt_lens=(300,), tail=40, map_format="q8",
                           seed=95 + d_in // 128), f"q8 depth {d_in // 64}")
+
+
+def test_every_option_in_one_call():
+    """Streamed int8 maps, QK-norm, one indexer head, the value measurement
+    inside the fill, a slot mapping and a table from rf_rope_table, all in one
+    fill of a ragged four-request batch: scales against the oracle's to 1e-3,
+    K (normalised per head), rescaled V and the indexer keys against the
+    oracle to the fill's tolerance, placement bit-exact at the mapped slots."""
+    s = workloads.spec("8b_ragged_host", n_late=2, prompt_lens=(300, 257, 129, 64), tail=50,
+                       map_format="q8", qk_norm=True, idx_heads=1, seed=70)
+    c = 32
+    print(f"[edges] all options: host={s.maps_on_host} fmt={s.map_format} c={c}", flush=True)
+    w = workloads.make(s)
+    rows_c, grp_c = workloads.calibration_row_list(s, c)
+    truth = workloads.make_layer_truth(s, len(rows_c), outliers=w.outlier_channels)
+    di = U.DeviceInputs(w)
+    plan = U.plan_for(w)
+    fr, n = U.gpu_fill_rows(plan, di)
+    f = fr.cpu().numpy()
+    slots = np.random.default_rng(9).permutation(s.n_rows).astype(np.int32)
+    table = torch.empty((s.max_pos, s.head_dim // 2, 2), dtype=torch.float32, device="cuda:0")
+    B.rope_table(plan, table)
+    ng = len(s.prompt_lens)
+    g_of_row = workloads.prompt_of_row(s)
+    sc = torch.full((s.n_late, ng, s.n_kv), -7.0, dtype=torch.float32, device="cuda:0")
+    mws = torch.empty(plan.value_scales_workspace_bytes(len(rows_c), s.n_late), dtype=torch.uint8, device="cuda:0")
+    measure = ([U.t16(t).cuda() for t in truth], U.i32(rows_c).cuda(), U.i32(grp_c).cuda(),
+               U.i32(g_of_row).cuda(), ng, sc, mws)
+    kc, vc, ic = U.gpu_fill(plan, di, fr, n, slots=U.i32(slots).cuda(), rope=table, measure=measure)
+    U.check_placement(kc, vc, f, s.n_rows, slots=slots, ic=ic)
+    ref_scales = oracle.value_scales(w, truth, rows_c, grp_c, ng)
+    got = sc.cpu().numpy().astype(np.float64)
+    for l in range(s.n_late):
+        err = np.max(np.abs(got[l] - ref_scales[l]) / np.abs(ref_scales[l]))
+        assert err <= 1e-3, f"layer {l}: scale relative error {err:.2e}"
+    U.check_values(kc, vc, oracle.fill_workload_rescaled(w, ref_scales, g_of_row, f), f, s.head_dim, slots=slots)
+    worst = U.check_indexer_values(ic, oracle.fill_indexer_workload(w, rows=f), f, s.head_dim, slots=slots)
+    print(f"[edges] all options: indexer worst {worst}", flush=True)
