@@ -34,7 +34,7 @@ PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA, published
 PEAK_HBM_GBS = 8000.0
 
 # layers per launch used by the benchmark (divides the late-layer count)
-GROUP = {"tiny": 4, "8b": 22, "27b": 6, "27b_120k": 6, "8b_ragged_host": 1}
+GROUP = {"tiny": 4, "8b": 22, "27b": 6, "27b_120k": 6, "8b_ragged_host": 2}
 # rows of the oracle's timed sample (None: every fill row), sized for 10-30 s
 CPU_SAMPLE = {"tiny": None, "8b": 8192, "27b": 4096, "27b_120k": 4096, "8b_ragged_host": 8192}
 ROOT = os.path.dirname(os.path.abspath(__file__))
@@ -395,7 +395,7 @@ def main():
                                      "rf_value_scales, then rf_fill" if args.separate_measure else "inside rf_fill"),
                    "qk_norm": bool(args.qk_norm),
                    "indexer_key_heads": args.indexer,
-                   "layers_per_launch": 1 if host_maps else g},
+                   "layers_per_launch": min(g, B.RF_STREAM_GROUP) if host_maps else g},
         "tflops": step_flops / (ms * 1e-3) / 1e12,
         "frac_of_bf16_peak": step_flops / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS,
         "roofline": {"bound": "mfma", "kernel": "map_gemm", "achieved": map_tflops, "peak": PEAK_BF16_TFLOPS,

@@ -65,15 +65,23 @@ typedef enum rf_status {
 /* rf_plan_create flags */
 enum {
   RF_MAPS_HOST = 1, /* map_a/map_b given to rf_fill are pinned HOST pointers; they are
-                       streamed to the GPU one layer at a time on a side stream,
-                       overlapped with the previous layer's fill (section 4.2:
-                       maps resident or streamed, identical outputs)          */
+                       streamed to the GPU on a side stream, the first layer
+                       alone and then up to RF_STREAM_GROUP layers per launch
+                       group, each group's copy overlapped with the previous
+                       group's fill (section 4.2: maps resident or streamed,
+                       identical outputs)                                     */
   RF_VALIDATE = 2,  /* rf_fill / rf_kv_project check their row indices on the
                        device and synchronise the stream before launching     */
   RF_MAPS_Q8 = 4    /* maps are int8 with bf16 block scales and are passed to
                        rf_fill_q8 instead of rf_fill; d_in % 128 == 0 (see the
                        int8 map section below)                                 */
 };
+
+/* Most late layers one launch group takes when the maps are streamed
+ * (RF_MAPS_HOST): the plan's two device map buffers hold this many layers
+ * each.  Wider groups mean fewer, fuller launches; the first group is one
+ * layer so that only one layer's copy precedes the first launch. */
+#define RF_STREAM_GROUP 2
 
 /* rf_ridge_solve / rf_ridge_fit flags */
 enum {
@@ -98,8 +106,9 @@ typedef struct rf_shape {
 typedef struct rf_plan rf_plan;
 
 /* Create a plan for one shape.  Validates the shape (RF_E_SHAPE / RF_E_ARG).
- * With RF_MAPS_HOST the plan owns two device map buffers (sized for bf16 maps,
- * or for int8 maps with RF_MAPS_Q8), one side stream and four events; these
+ * With RF_MAPS_HOST the plan owns two device map buffers of RF_STREAM_GROUP
+ * layers each (sized for bf16 maps, or for int8 maps with RF_MAPS_Q8; about
+ * 2 x 2 x 52 MB for bf16 maps at d = 5120), one side stream and five events; these
  * are allocated here, on the current device, and released by rf_plan_destroy.
  * Without it the plan allocates nothing on the device. */
 rf_status rf_plan_create(const rf_shape* shape, int32_t flags, rf_plan** out);
@@ -107,7 +116,8 @@ void rf_plan_destroy(rf_plan* plan);
 
 /* Workspace bytes rf_fill (or rf_fill_q8 for an RF_MAPS_Q8 plan) needs for
  * n_fill rows when `layers_per_launch` late layers are processed per launch
- * (1 .. n_late; larger means fewer, wider launches).  The call uses the widest
+ * (1 .. n_late; larger means fewer, wider launches; at most RF_STREAM_GROUP
+ * count for an RF_MAPS_HOST plan, larger values give that figure).  The call uses the widest
  * grouping the given workspace allows, so any size >=
  * rf_fill_workspace_bytes(plan, n_fill, 1) works.  The figure includes the
  * RoPE table built when none is passed, the per-row sums of squares and norm
@@ -117,7 +127,8 @@ size_t rf_fill_workspace_bytes(const rf_plan* plan, int32_t n_fill, int32_t laye
 
 /* Workspace bytes rf_kv_project needs (one prepared [W_k|W_v] copy and one
  * fp32 norm factor per plan row for each layer of a group, plus the RoPE table
- * if none is passed); same grouping rule. */
+ * if none is passed); same grouping rule, except that RF_MAPS_HOST does not
+ * cap the group (no maps are involved). */
 size_t rf_kv_project_workspace_bytes(const rf_plan* plan, int32_t layers_per_launch);
 
 /* Fill `table` (device, fp32 [max_pos][head_dim/2][2] = (cos, sin)) with the

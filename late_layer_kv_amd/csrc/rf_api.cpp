@@ -48,13 +48,15 @@ struct rf_plan {
   hipEvent_t ev_start = nullptr;
   hipEvent_t ev_copied[2] = {nullptr, nullptr};
   hipEvent_t ev_consumed[2] = {nullptr, nullptr};
-  // One streamed layer per buffer: the map (bf16 [d_out][d_in], or int8 codes
-  // [d_out][d_in] then bf16 scales [d_out][d_in/128]) and then b [d_out].
+  // Up to RF_STREAM_GROUP streamed layers per buffer, layer_bytes apart, each
+  // the map (bf16 [d_out][d_in], or int8 codes [d_out][d_in] then bf16 scales
+  // [d_out][d_in/128]) and then b [d_out].
   char* mapbuf[2] = {nullptr, nullptr};
   size_t map_bytes = 0;    // bf16 map, or int8 codes
   size_t scale_off = 0;    // byte offset of the scales (int8 maps)
   size_t scale_bytes = 0;
   size_t bias_off = 0;     // byte offset of b
+  size_t layer_bytes = 0;  // one layer's part of a buffer
   // kernel timing (rf_plan_profile)
   struct Rec {
     int kind;
@@ -157,7 +159,20 @@ rf_status check_shape(const rf_shape* s, int32_t flags) {
   return RF_OK;
 }
 
-int max_group(const rf_plan* p) { return std::min(p->s.n_late, rf::kMaxGroup); }
+// Most layers one launch with maps takes: kMaxGroup, or RF_STREAM_GROUP for
+// streamed maps (the plan's map buffers hold that many layers).
+int max_group(const rf_plan* p) {
+  return std::min(p->s.n_late, (p->flags & RF_MAPS_HOST) ? RF_STREAM_GROUP : rf::kMaxGroup);
+}
+
+// Layers in the launch group that starts at layer l0 when groups of up to G
+// are allowed.  Streamed maps start with a group of one layer, so that only
+// one layer's copy precedes the first launch; later copies overlap the
+// previous group's kernels.
+int group_at(const rf_plan* p, int l0, int G) {
+  if ((p->flags & RF_MAPS_HOST) && l0 == 0) return 1;
+  return std::min(G, p->s.n_late - l0);
+}
 
 rf_status check_layer_ptrs(const void* const* arr, int n, const char* name, bool need16 = true) {
   if (!arr) return fail(RF_E_ARG, "%s array is null", name);
@@ -209,7 +224,8 @@ rf_status rf_plan_create(const rf_shape* shape, int32_t flags, rf_plan** out) {
       p->map_bytes = elems * 2;
       p->bias_off = up(p->map_bytes);
     }
-    const size_t bytes = p->bias_off + static_cast<size_t>(shape->d_out) * 2;
+    p->layer_bytes = up(p->bias_off + static_cast<size_t>(shape->d_out) * 2);
+    const size_t bytes = p->layer_bytes * RF_STREAM_GROUP;
     for (int i = 0; i < 2 && e == hipSuccess; ++i) e = hipMalloc(reinterpret_cast<void**>(&p->mapbuf[i]), bytes);
     if (e == hipSuccess) e = hipStreamCreateWithFlags(&p->side, hipStreamNonBlocking);
     if (e == hipSuccess) e = hipEventCreateWithFlags(&p->ev_start, hipEventDisableTiming);
@@ -267,8 +283,7 @@ rf_status rf_plan_profile_read(rf_plan* p, rf_profile* out) {
 
 size_t rf_fill_workspace_bytes(const rf_plan* p, int32_t n_fill, int32_t g) {
   if (!p || n_fill < 0 || g < 1 || g > p->s.n_late) return 0;
-  g = std::min(g, rf::kMaxGroup);
-  if (p->flags & RF_MAPS_HOST) g = 1;
+  g = std::min(g, max_group(p));
   return rope_bytes(p->s) + kFlagBytes + prep_bytes(p->s, g) + y_bytes(p->s, n_fill, g) + dq_bytes(p->s, p->flags, g) +
          ssq_bytes(p->s, n_fill, g) + rs_bytes(n_fill, g);
 }
@@ -339,10 +354,11 @@ rf_status check_maps(const rf_plan* p, const char* fn, const MapSrc& maps) {
 // Hands the map kernel device bf16 maps, one launch group at a time.  Resident
 // bf16 maps are used as given; resident int8 maps are expanded into the image
 // `dq` first; streamed maps (RF_MAPS_HOST) go through the plan's two device
-// buffers on the side stream, one layer per group: copy l waits until the map
-// kernel of layer l-2 (same buffer) has run, and the kernels of layer l that
-// read the buffer wait for copy l.  The first copies also wait for the work
-// already on the caller's stream, which may still read the buffers.
+// buffers on the side stream, alternately, up to RF_STREAM_GROUP layers per
+// group: the copy of group j waits until the kernels of group j-2 (same
+// buffer) that read the maps have run, and the kernels of group j wait for
+// its copy.  The first copies also wait for the work already on the caller's
+// stream, which may still read the buffers.
 class MapFeeder {
  public:
   MapFeeder(rf_plan* p, const MapSrc& maps, uint16_t* dq, hipStream_t hs)
@@ -382,39 +398,51 @@ class MapFeeder {
       }
       return RF_OK;
     }
-    const int l = l0, buf = l & 1;
+    const int buf = calls_ & 1;
     char* mb = p_->mapbuf[buf];
-    if (l >= 2 && (e = hipStreamWaitEvent(p_->side, p_->ev_consumed[buf], 0)) != hipSuccess)
+    if (calls_ >= 2 && (e = hipStreamWaitEvent(p_->side, p_->ev_consumed[buf], 0)) != hipSuccess)
       return hip_fail(e, "stream wait");
     {
       Timed tm(p_, RF_K_COPY, p_->side);
-      const void* msrc = q8_ ? static_cast<const void*>(maps_.q[l]) : static_cast<const void*>(maps_.a[l]);
-      e = hipMemcpyAsync(mb, msrc, p_->map_bytes, hipMemcpyHostToDevice, p_->side);
-      if (e == hipSuccess && q8_)
-        e = hipMemcpyAsync(mb + p_->scale_off, maps_.scale[l], p_->scale_bytes, hipMemcpyHostToDevice, p_->side);
-      if (e == hipSuccess)
-        e = hipMemcpyAsync(mb + p_->bias_off, maps_.b[l], static_cast<size_t>(p_->s.d_out) * 2, hipMemcpyHostToDevice,
-                           p_->side);
+      e = hipSuccess;
+      for (int i = 0; i < g && e == hipSuccess; ++i) {
+        const int l = l0 + i;
+        char* dst = mb + i * p_->layer_bytes;
+        const void* msrc = q8_ ? static_cast<const void*>(maps_.q[l]) : static_cast<const void*>(maps_.a[l]);
+        e = hipMemcpyAsync(dst, msrc, p_->map_bytes, hipMemcpyHostToDevice, p_->side);
+        if (e == hipSuccess && q8_)
+          e = hipMemcpyAsync(dst + p_->scale_off, maps_.scale[l], p_->scale_bytes, hipMemcpyHostToDevice, p_->side);
+        if (e == hipSuccess)
+          e = hipMemcpyAsync(dst + p_->bias_off, maps_.b[l], static_cast<size_t>(p_->s.d_out) * 2,
+                             hipMemcpyHostToDevice, p_->side);
+      }
       if (e != hipSuccess) return hip_fail(e, "map copy");
     }
     if ((e = hipEventRecord(p_->ev_copied[buf], p_->side)) != hipSuccess) return hip_fail(e, "event record");
     if ((e = hipStreamWaitEvent(hs_, p_->ev_copied[buf], 0)) != hipSuccess) return hip_fail(e, "stream wait");
-    if (q8_) {
-      dp_.q[0] = reinterpret_cast<const int8_t*>(mb);
-      dp_.s[0] = reinterpret_cast<const uint16_t*>(mb + p_->scale_off);
-      dp_.w[0] = dq_;
-      Timed tm(p_, RF_K_DEQUANT, hs_);
-      if ((e = rf::launch_dequant(dp_, 1, hs_)) != hipSuccess) return hip_fail(e, "dequant launch");
+    for (int i = 0; i < g; ++i) {
+      char* src = mb + i * p_->layer_bytes;
+      if (q8_) {
+        dp_.q[i] = reinterpret_cast<const int8_t*>(src);
+        dp_.s[i] = reinterpret_cast<const uint16_t*>(src + p_->scale_off);
+        dp_.w[i] = dq_ + i * elems;
+      }
+      mp.a[i] = q8_ ? dq_ + i * elems : reinterpret_cast<const uint16_t*>(src);
+      mp.b[i] = reinterpret_cast<const uint16_t*>(src + p_->bias_off);
     }
-    mp.a[0] = q8_ ? dq_ : reinterpret_cast<const uint16_t*>(mb);
-    mp.b[0] = reinterpret_cast<const uint16_t*>(mb + p_->bias_off);
+    if (q8_) {
+      Timed tm(p_, RF_K_DEQUANT, hs_);
+      if ((e = rf::launch_dequant(dp_, g, hs_)) != hipSuccess) return hip_fail(e, "dequant launch");
+    }
+    last_buf_ = buf;
+    ++calls_;
     return RF_OK;
   }
 
-  // Call after the map kernel of group l0 is enqueued.
-  rf_status consumed(int l0) {
+  // Call after the last kernel that reads the group just loaded is enqueued.
+  rf_status consumed() {
     if (!host_) return RF_OK;
-    hipError_t e = hipEventRecord(p_->ev_consumed[l0 & 1], hs_);
+    hipError_t e = hipEventRecord(p_->ev_consumed[last_buf_], hs_);
     return e == hipSuccess ? RF_OK : hip_fail(e, "event record");
   }
 
@@ -424,13 +452,13 @@ class MapFeeder {
   uint16_t* dq_;
   hipStream_t hs_;
   bool q8_, host_;
+  int calls_ = 0, last_buf_ = 0;  // streamed groups loaded so far; buffer of the last
   rf::DequantParams dp_{};
 };
 
-// Largest layer group (<= kMaxGroup) whose workspace fits; 1 for streamed maps.
+// Largest layer group (<= max_group) whose workspace fits.
 template <class F>
 int pick_group(const rf_plan* p, size_t ws_bytes, F bytes_for) {
-  if (p->flags & RF_MAPS_HOST) return 1;
   for (int g = max_group(p); g > 1; --g)
     if (bytes_for(g) <= ws_bytes) return g;
   return 1;
@@ -774,8 +802,8 @@ rf_status fill_impl(rf_plan* p, const char* fn, const uint16_t* x, int64_t ld_x,
                                 prep_rows(s)));
     if ((st = meas->begin()) != RF_OK) return st;
   }
-  for (int l0 = 0; l0 < L; l0 += G) {
-    const int g = std::min(G, L - l0);
+  for (int l0 = 0, g = 0; l0 < L; l0 += g) {
+    g = group_at(p, l0, G);
     for (int i = 0; i < g; ++i) {
       pp.gamma[i] = gamma[l0 + i];
       pp.wk[i] = w_k[l0 + i];
@@ -801,7 +829,7 @@ rf_status fill_impl(rf_plan* p, const char* fn, const uint16_t* x, int64_t ld_x,
     // the measurement's calibration rows go through the same loaded maps,
     // and its scales for these layers are in place before the K/V launch
     if (meas && (st = meas->group(l0, g, mp)) != RF_OK) return st;
-    if ((st = feed.consumed(l0)) != RF_OK) return st;
+    if ((st = feed.consumed()) != RF_OK) return st;
     if (meas && (st = meas->finish(l0, g, meas_in->scale)) != RF_OK) return st;
     {
       Timed tm(p, RF_K_NORM, hs);
@@ -852,8 +880,8 @@ rf_status value_scales_impl(rf_plan* p, const char* fn, const uint16_t* x, int64
   MapFeeder feed(p, maps, dq, hs);
   if (n > 0 && (st = feed.begin()) != RF_OK) return st;
   hipError_t e;
-  for (int l0 = 0; l0 < L; l0 += G) {
-    const int g = std::min(G, L - l0);
+  for (int l0 = 0, g = 0; l0 < L; l0 += g) {
+    g = group_at(p, l0, G);
     if (n > 0) {
       for (int i = 0; i < g; ++i) {
         pp.gamma[i] = gamma[l0 + i];
@@ -867,7 +895,7 @@ rf_status value_scales_impl(rf_plan* p, const char* fn, const uint16_t* x, int64
       rf::MapParams mp{};
       if ((st = feed.load(l0, g, mp)) != RF_OK) return st;
       if ((st = meas.group(l0, g, mp)) != RF_OK) return st;
-      if ((st = feed.consumed(l0)) != RF_OK) return st;
+      if ((st = feed.consumed()) != RF_OK) return st;
     }
     if ((st = meas.finish(l0, g, scale)) != RF_OK) return st;
   }
@@ -909,8 +937,7 @@ rf_status rf_fill_q8(rf_plan* p, const uint16_t* x, int64_t ld_x, const int32_t*
 
 size_t rf_value_scales_workspace_bytes(const rf_plan* p, int32_t n_calib, int32_t g) {
   if (!p || n_calib < 0 || g < 1 || g > p->s.n_late) return 0;
-  g = std::min(g, rf::kMaxGroup);
-  if (p->flags & RF_MAPS_HOST) g = 1;
+  g = std::min(g, max_group(p));
   return scale_ws(p, n_calib, g).total;
 }
 
@@ -987,7 +1014,7 @@ rf_status rf_kv_project(rf_plan* p, const uint16_t* const* layer_in, int64_t ld_
 
   hipStream_t hs = static_cast<hipStream_t>(stream);
   int G = 1;
-  for (int g = max_group(p); g > 1; --g)
+  for (int g = std::min(s.n_late, rf::kMaxGroup); g > 1; --g)  // no maps here: any plan groups freely
     if (rf_kv_project_workspace_bytes(p, g) <= ws_bytes) {
       G = g;
       break;
@@ -1046,8 +1073,8 @@ rf_status rf_kv_project(rf_plan* p, const uint16_t* const* layer_in, int64_t ld_
   rp.inv_k = 1.0f / s.d_out;
   rp.eps = s.rms_eps;
   rp.rs = rsb;
-  for (int l0 = 0; l0 < L; l0 += G) {
-    const int g = std::min(G, L - l0);
+  for (int l0 = 0, g = 0; l0 < L; l0 += g) {
+    g = group_at(p, l0, G);
     for (int i = 0; i < g; ++i) {
       pp.gamma[i] = gamma[l0 + i];
       pp.wk[i] = w_k[l0 + i];

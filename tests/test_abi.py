@@ -124,6 +124,12 @@ def test_workspace_sizes():
     p.close()
 
 
+def test_stream_group_constant_matches_header():
+    hdr = open(os.path.join(ROOT, "include", "rf.h")).read()
+    m = re.search(r"#define RF_STREAM_GROUP (\d+)", hdr)
+    assert m and int(m.group(1)) == B.RF_STREAM_GROUP
+
+
 # ---- host ridge (float64 inside the library) against the fp64 oracle
 
 

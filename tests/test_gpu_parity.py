@@ -129,6 +129,32 @@ def test_streamed_maps_equal_resident():
         assert torch.equal(k1[l], k2[l]) and torch.equal(v1[l], v2[l]), f"layer {l}"
 
 
+@pytest.mark.parametrize("fmt", ["bf16", "q8"])
+def test_streamed_groups_equal_resident(fmt):
+    """Five streamed layers go as groups of 1, 2 and 2 (two device buffers
+    of RF_STREAM_GROUP layers, used alternately): the same bytes as resident
+    maps in one launch, bf16 and int8; the workspace of a streamed plan stops
+    growing at RF_STREAM_GROUP layers per launch."""
+    s = workloads.spec("8b_ragged_host", n_late=5, prompt_lens=(300, 257, 129, 64), tail=50, map_format=fmt,
+                       seed=15)
+    _say(f"[streamed groups] {fmt} L={s.n_late}")
+    w = workloads.make(s)
+    res = U.DeviceInputs(w, maps_on_host=False)
+    hst = U.DeviceInputs(w, maps_on_host=True)
+    p_res = U.plan_for(w, maps_on_host=False)
+    p_hst = U.plan_for(w, maps_on_host=True)
+    rows, n = U.gpu_fill_rows(p_res, res)
+    g = B.RF_STREAM_GROUP
+    assert p_hst.fill_workspace_bytes(n, s.n_late) == p_hst.fill_workspace_bytes(n, g)
+    assert p_hst.fill_workspace_bytes(n, g) > p_hst.fill_workspace_bytes(n, 1)
+    k1, v1 = U.gpu_fill(p_res, res, rows, n)
+    k2, v2 = U.gpu_fill(p_hst, hst, rows, n)
+    k3, v3 = U.gpu_fill(p_hst, hst, rows, n, layers_per_launch=1)
+    for l in range(s.n_late):
+        assert torch.equal(k1[l], k2[l]) and torch.equal(v1[l], v2[l]), f"layer {l}"
+        assert torch.equal(k1[l], k3[l]) and torch.equal(v1[l], v3[l]), f"layer {l} (one layer per launch)"
+
+
 def test_layer_grouping_does_not_change_bytes():
     w = _workload("8b_mid")
     _say("[grouping] 8b_mid")

@@ -132,9 +132,12 @@ def test_q8_streamed_equals_resident():
     s = w.spec
     image = s.d_out * s.d_in * 2
     p_bf = U.plan_for(w, maps_on_host=True, maps_q8=False)
-    # a streamed launch holds one layer's bf16 image on top of the bf16 plan's needs
-    assert p_hst.fill_workspace_bytes(100, s.n_late) == p_hst.fill_workspace_bytes(100, 1)
-    assert p_hst.fill_workspace_bytes(100, 1) == p_bf.fill_workspace_bytes(100, 1) + image
+    # a streamed launch holds each of its layers' bf16 images on top of the
+    # bf16 plan's needs, for at most RF_STREAM_GROUP layers
+    g = min(s.n_late, B.RF_STREAM_GROUP)
+    assert p_hst.fill_workspace_bytes(100, s.n_late) == p_hst.fill_workspace_bytes(100, g)
+    for k in range(1, g + 1):
+        assert p_hst.fill_workspace_bytes(100, k) == p_bf.fill_workspace_bytes(100, k) + k * image
     p_bf.close()
     rows, n = U.gpu_fill_rows(p_res, res)
     k1, v1 = U.gpu_fill(p_res, res, rows, n)
