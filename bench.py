@@ -34,7 +34,7 @@ PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA, published
 PEAK_HBM_GBS = 8000.0
 
 # layers per launch used by the benchmark (divides the late-layer count)
-GROUP = {"tiny": 4, "8b": 22, "27b": 6, "27b_120k": 6, "8b_ragged_host": 2}
+GROUP = {"tiny": 4, "8b": 22, "27b": 6, "27b_120k": 6, "8b_ragged_host": 4}
 # rows of the oracle's timed sample (None: every fill row), sized for 10-30 s
 CPU_SAMPLE = {"tiny": None, "8b": 8192, "27b": 4096, "27b_120k": 4096, "8b_ragged_host": 8192}
 ROOT = os.path.dirname(os.path.abspath(__file__))

@@ -81,7 +81,7 @@ enum {
  * (RF_MAPS_HOST): the plan's two device map buffers hold this many layers
  * each.  Wider groups mean fewer, fuller launches; the first group is one
  * layer so that only one layer's copy precedes the first launch. */
-#define RF_STREAM_GROUP 2
+#define RF_STREAM_GROUP 4
 
 /* rf_ridge_solve / rf_ridge_fit flags */
 enum {
@@ -108,7 +108,7 @@ typedef struct rf_plan rf_plan;
 /* Create a plan for one shape.  Validates the shape (RF_E_SHAPE / RF_E_ARG).
  * With RF_MAPS_HOST the plan owns two device map buffers of RF_STREAM_GROUP
  * layers each (sized for bf16 maps, or for int8 maps with RF_MAPS_Q8; about
- * 2 x 2 x 52 MB for bf16 maps at d = 5120), one side stream and five events; these
+ * 2 x 4 x 52 MB for bf16 maps at d = 5120), one side stream and five events; these
  * are allocated here, on the current device, and released by rf_plan_destroy.
  * Without it the plan allocates nothing on the device. */
 rf_status rf_plan_create(const rf_shape* shape, int32_t flags, rf_plan** out);

@@ -21,7 +21,7 @@ RF_MAPS_HOST = 1
 RF_VALIDATE = 2
 RF_MAPS_Q8 = 4
 RF_RIDGE_RAW = 1
-RF_STREAM_GROUP = 2  # most layers per launch with streamed maps (include/rf.h)
+RF_STREAM_GROUP = 4  # most layers per launch with streamed maps (include/rf.h)
 Q8_BLOCK = 128
 
 STATUS = {0: "RF_OK", -1: "RF_E_ARG", -2: "RF_E_SHAPE", -3: "RF_E_ROWS", -4: "RF_E_WORKSPACE",

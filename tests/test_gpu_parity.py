@@ -131,11 +131,13 @@ def test_streamed_maps_equal_resident():
 
 @pytest.mark.parametrize("fmt", ["bf16", "q8"])
 def test_streamed_groups_equal_resident(fmt):
-    """Five streamed layers go as groups of 1, 2 and 2 (two device buffers
-    of RF_STREAM_GROUP layers, used alternately): the same bytes as resident
-    maps in one launch, bf16 and int8; the workspace of a streamed plan stops
-    growing at RF_STREAM_GROUP layers per launch."""
-    s = workloads.spec("8b_ragged_host", n_late=5, prompt_lens=(300, 257, 129, 64), tail=50, map_format=fmt,
+    """Six streamed layers go as groups of 1, RF_STREAM_GROUP and the rest
+    (two device buffers of RF_STREAM_GROUP layers, used alternately, so the
+    third group reuses the first buffer): the same bytes as resident maps in
+    one launch and as one layer per launch, bf16 and int8; the workspace of a
+    streamed plan stops growing at RF_STREAM_GROUP layers per launch."""
+    assert B.RF_STREAM_GROUP < 5  # six layers make at least three groups
+    s = workloads.spec("8b_ragged_host", n_late=6, prompt_lens=(300, 257, 129, 64), tail=50, map_format=fmt,
                        seed=15)
     _say(f"[streamed groups] {fmt} L={s.n_late}")
     w = workloads.make(s)

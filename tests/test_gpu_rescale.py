@@ -29,8 +29,8 @@ CASES = {
     "27b_mid_q8": (workloads.spec("27b", n_late=2, prompt_lens=(900,), tail=300, map_format="q8", seed=43), 256),
     "ragged_host": (workloads.spec("8b_ragged_host", n_late=2, prompt_lens=(300, 257, 129, 64), tail=50,
                                    seed=44), 32),
-    # five streamed layers: launch groups of 1, 2 and 2 layers
-    "ragged_host5": (workloads.spec("8b_ragged_host", n_late=5, prompt_lens=(300, 257, 129, 64), tail=50,
+    # six streamed layers: launch groups of 1, RF_STREAM_GROUP and the rest
+    "ragged_host6": (workloads.spec("8b_ragged_host", n_late=6, prompt_lens=(300, 257, 129, 64), tail=50,
                                     map_format="q8", seed=45), 32),
 }
 
@@ -167,7 +167,7 @@ def test_rows_outside_the_groups_are_skipped_and_streamed_equals_resident():
 
 
 @pytest.mark.parametrize("name,groups", [("tiny_ragged", None), ("8b_mid_two", 1), ("27b_mid_q8", None),
-                                         ("ragged_host", None), ("ragged_host5", None), ("ragged_host5", 1)])
+                                         ("ragged_host", None), ("ragged_host6", None), ("ragged_host6", 1)])
 def test_measured_fill_equals_two_calls(name, groups):
     """The measurement run inside the fill (rf_fill_opts.measure, the maps
     loaded once per layer group) gives bitwise the scales of rf_value_scales
