@@ -242,8 +242,9 @@ def main():
         print(json.dumps(t))
         return
     if args.gpus != 1:
-        print(f"bench.py measures one GPU only (--gpus {args.gpus} asked): the fill runs on a single MI355X "
-              "in this build; see the sharding notes in DESIGN.md", file=sys.stderr)
+        print(f"bench.py measures one GPU only (--gpus {args.gpus} asked): the fill runs on a single MI355X. "
+              "Across GPUs it would shard by late layers or by rows, each GPU running this one-GPU path on "
+              "its share.", file=sys.stderr)
         sys.exit(2)
 
     import torch
