@@ -2,6 +2,8 @@
 import ctypes as C
 import os
 import re
+import subprocess
+import sys
 
 import numpy as np
 import pytest
@@ -429,3 +431,12 @@ def test_in_fill_measurement_argument_errors():
     assert call(ws_bytes=need - 1) == -4
     assert call(workspace=0x10010) == -4
     p.close()
+
+
+def test_bench_refuses_more_than_one_gpu():
+    """bench.py measures one GPU: --gpus 2 exits with status 2 and says why,
+    before touching the GPU."""
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"], capture_output=True,
+                       text=True, timeout=120)
+    assert r.returncode == 2
+    assert "one GPU only" in r.stderr and r.stdout == ""
