@@ -11,6 +11,7 @@ import numpy as np
 import pytest
 import torch
 
+import bench
 import oracle
 import workloads
 from late_layer_kv_amd import binding as B
@@ -18,7 +19,7 @@ from tests import gpu_util as U
 
 pytestmark = [pytest.mark.gpu, pytest.mark.timeout(900)]
 
-BENCH_GROUP = {"tiny": 4, "8b": 22, "27b": 8, "27b_120k": 4, "8b_ragged_host": 1}
+BENCH_GROUP = bench.GROUP  # layers per launch that bench.py times
 
 
 def sample_rows(fill: np.ndarray, exact: np.ndarray, positions: np.ndarray, n: int = 96, seed: int = 0):
