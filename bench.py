@@ -220,7 +220,7 @@ def main():
     ap.add_argument("--indexer", type=int, default=0, metavar="HEADS",
                     help="layers also write HEADS head_dim-wide indexer key heads (sparse-attention layers)")
     ap.add_argument("--maps", default="bf16", choices=["bf16", "q8"],
-                    help="map storage: bf16, or int8 codes with one bf16 scale per 128 weights of each row")
+                    help="map storage: bf16, or int8 codes with one bf16 scale for each 128-weight block of a row")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="after timing, copy MIB mebibytes device-to-device once (PMC calibration)")

@@ -9,10 +9,11 @@
  *   1. predicts the layer's input from the split state:  y = A_l x_S + b_l
  *      (section 2.2, the map equation);
  *   2. applies the layer's own RMSNorm:  h = gamma_l * y / sqrt(mean(y^2) + eps)
- *      (section 2.2, "At inference the predicted input goes through the layer's
- *      own normalization and projections");
+ *      (section 2.2: the prediction is normalised and projected exactly as a
+ *      true input would be);
  *   3. applies its key and value projections:  k = W_k h,  v = W_v h
- *      (sections 2.1-2.2: a late layer computes only what later tokens read);
+ *      (sections 2.1-2.2: for a filled row a late layer produces only the
+ *      cache entries that later tokens attend to);
  *   4. rotates k with RoPE at the row's own position (section 2.2; section 6.6);
  *   5. stores bf16 k and v in that layer's cache slot for the row.  Exact rows
  *      are not touched (section 2.1; Figure 5, first sweep).
@@ -192,8 +193,8 @@ typedef struct rf_vmeasure {
 /* Options of a fill (HOST struct; pass NULL for none of them).
  *   vscale  value rescale (above), or NULL
  *   k_norm  QK-norm for layers that normalise their keys (RidgeFill section
- *           6.6 and section 7: the Qwen layers normalise each query and key
- *           before attention): HOST array of n_late device pointers, each bf16
+ *           6.6 and section 7: in the Qwen layers queries and keys are
+ *           normalised per head ahead of attention): HOST array of n_late device pointers, each bf16
  *           [head_dim], 16-byte aligned; or NULL.  Each key head is divided by
  *           sqrt(mean of its head_dim squares + rms_eps) and multiplied by the
  *           gain per dimension, after the key projection and before RoPE.
@@ -248,7 +249,7 @@ rf_status rf_fill(rf_plan* plan,
 
 /* ---- int8 maps -----------------------------------------------------------
  * Section 2.2 ("Size and cost") and section 4.2: the 27B deployment stores
- * each map as int8 codes with one bf16 scale per 128 weights of each row, half
+ * each map as int8 codes with one bf16 scale for each 128-weight block of a row, half
  * the bytes of a bf16 map.  The weight is w[o][k] = q[o][k] * s[o][k / 128]:
  *    map_q      [d_out][d_in] int8 codes, 16-byte aligned
  *    map_scale  [d_out][d_in / 128] bf16 scales
@@ -328,8 +329,9 @@ rf_status rf_value_scales_q8(rf_plan* plan,
                              float* scale, void* workspace, size_t ws_bytes, void* hip_stream);
 
 /* The exact cache write of each late layer from given true inputs: steps 2-5
- * only (no map).  Section 2.1: exact rows and the tail run the layer from its
- * exact input; with every layer_in[l] = x and A_l = I, b_l = 0, rf_fill gives
+ * only (no map).  Section 2.1: for exact rows and the tail each late layer
+ * starts from the input the full model computes; with every layer_in[l] = x
+ * and A_l = I, b_l = 0, rf_fill gives
  * the same bytes (the identity fill of section 7, POP's fill).
  *   layer_in   HOST array of n_late device pointers, each bf16 [n_rows][ld_in]
  *              (entries may alias), ld_in >= d_out, ld_in % 8 == 0
@@ -351,8 +353,8 @@ rf_status rf_kv_project(rf_plan* plan,
 /* ---- Closed-form ridge map, HOST memory, float64 inside (validation only) ----
  * Section 2.2: with X and Y centred, A = Y^T X (X^T X + alpha I)^(-1) and
  * b = mu_Y - A mu_X, alpha = lambda * tr(Xc^T Xc) / d_in; only A is penalised.
- * "Fitting": running sums of X^T X, X^T Y and the means over documents give
- * the same result as one solve, and a new lambda needs only a new solve.
+ * "Fitting": X^T X, X^T Y and the means, summed over documents, lead to the
+ * same maps as one solve; a different lambda costs one more solve, not a pass.
  * X is [n][d_in] fp32, Y is [n][d_out] fp32 (row-major, HOST).  Products are
  * formed and summed in float64.  A is returned [d_out][d_in] (the layout
  * rf_fill's map_a takes) and b [d_out], both fp32 HOST. */

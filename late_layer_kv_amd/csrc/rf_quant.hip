@@ -2,7 +2,7 @@
 //
 // "RidgeFill: Training-Free Late-Layer Cache Fill for Faster Prefill",
 // section 2.2 ("Size and cost") and section 4.2: a map is stored as int8 codes
-// with one bf16 scale per 128 weights of each row.  The contraction runs on
+// with one bf16 scale for each 128-weight block of a row.  The contraction runs on
 // bf16 matrix instructions, so each launch group's maps are first expanded,
 // w = bf16(q * s) rounded to nearest even.  q * s is exact in fp32 (8-bit code
 // times 8-bit significand), so the only rounding is the final one.

@@ -2,7 +2,7 @@
 //
 // "RidgeFill: Training-Free Late-Layer Cache Fill for Faster Prefill",
 // section 2.2 ("Size and cost") and section 4.2: int8 codes with one bf16
-// scale per 128 weights of each row.  Absmax per block: the scale is the bf16
+// scale for each 128-weight block of a row.  Absmax per block: the scale is the bf16
 // value (nearest even) of the fp32 value nearest max|a| / 127, and each code is
 // a / s rounded to the nearest integer, ties to even, in double precision,
 // clipped to [-127, 127].  An all-zero block gets scale 0 and codes 0.

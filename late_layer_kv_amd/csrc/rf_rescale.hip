@@ -2,8 +2,8 @@
 //
 // "RidgeFill: Training-Free Late-Layer Cache Fill for Faster Prefill",
 // section 2.3 ("Value rescale"): per request, late layer and key-value head,
-// the ratio of the exact value norm to the predicted one, averaged over the
-// request's first c tail rows.  The value vectors come from the K/V kernel
+// the mean over the request's first c tail rows of each row's exact value
+// norm divided by its predicted value norm.  The value vectors come from the K/V kernel
 // (value half only, stored densely by calibration row); these two kernels
 // reduce them.  Work is tiny (c rows per request), so both are plain
 // one-thread-per-output loops with a fixed summation order: the result does not

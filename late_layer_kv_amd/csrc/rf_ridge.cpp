@@ -3,9 +3,9 @@
 // "RidgeFill: Training-Free Late-Layer Cache Fill for Faster Prefill",
 // section 2.2: centre X and Y by their means, A = Y^T X (X^T X + alpha I)^(-1),
 // b = mu_Y - A mu_X, only A penalised, alpha = lambda tr(Xc^T Xc) / d_in.
-// "Fitting": running sums of X^T X, X^T Y and the two means over documents give
-// the same result as one solve on all rows, and a new lambda needs only a new
-// solve.  The solve is a Cholesky factorisation of the symmetric positive
+// "Fitting": X^T X, X^T Y and the two means, summed over documents, lead to the
+// same maps as one solve over all rows; a different lambda costs one more
+// solve, not another pass over the data.  The solve is a Cholesky factorisation of the symmetric positive
 // definite matrix Xc^T Xc + alpha I followed by two triangular solves per
 // output column.
 #include <algorithm>

@@ -14,6 +14,6 @@ def layer_ceiling(n_layers: int, split: int, tail: int, n_rows: int) -> float:
 
 
 def mac_ceiling(skipped_share: float) -> float:
-    """Section 4.4 / Figure 10b: if time were proportional to multiply-accumulates,
-    skipping a share s of them allows 1/(1 - s)."""
+    """Section 4.4 / Figure 10b: when run time scales with the multiply-accumulates
+    done, skipping a share s of them speeds the work up by at most 1/(1 - s)."""
     return 1.0 / (1.0 - skipped_share)

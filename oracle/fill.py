@@ -9,10 +9,12 @@ where they are taken:
 * maps act on row vectors: the paper's column form x_hat = A x_S + b becomes
   x_hat = x_S A^T + b with A stored [d_out][d_in] exactly as the paper sizes
   it (d_out rows, d_in columns, section 2.2 "Size and cost");
-* "the layer's own normalization" is RMSNorm gamma * y / sqrt(mean(y^2) + eps)
-  with a multiplicative gain and eps inside the root;
+* the layer's normalization, which the pages name without writing out, is
+  RMSNorm gamma * y / sqrt(mean(y^2) + eps) with a multiplicative gain and eps
+  inside the root;
 * projections are stored [out][in] and applied as h W^T;
-* "rotary embedding as usual" is the rotate-half form: within every head,
+* the rotary embedding, applied to the keys in the usual way, is the
+  rotate-half form: within every head,
   dimension j < hd/2 is paired with j + hd/2 and the pair is turned by the
   angle pos * theta^(-2j/hd), with no frequency scaling;
 * QK-norm (layers that normalise their keys) is an RMSNorm over each key head
@@ -40,9 +42,10 @@ def bf16_bits_to_f64(bits: np.ndarray) -> np.ndarray:
 def fill_row_set(n_rows: int, exact_rows: Iterable[int]) -> np.ndarray:
     """Rows whose late-layer cache entries come from the fill, ascending.
 
-    Section 2.1 ("Split, tail and prefix"): the tail runs every layer exactly
-    and a prefix row is either exact or filled, so the filled rows are all rows
-    minus the exact set (tail plus chosen rows, section 2.4).
+    Section 2.1 ("Split, tail and prefix"): the tail runs every layer exactly,
+    and prefix rows are split between exact computation and the fill, so the
+    filled rows are all rows minus the exact set (tail plus chosen rows,
+    section 2.4).
     """
     return np.setdiff1d(np.arange(n_rows, dtype=np.int64),
                         np.asarray(list(exact_rows) if not isinstance(exact_rows, np.ndarray)
@@ -58,8 +61,8 @@ def predicted_input(x_s: np.ndarray, a: np.ndarray, b: np.ndarray) -> np.ndarray
 
 
 def rms_norm(y: np.ndarray, gamma: np.ndarray, eps: float) -> np.ndarray:
-    """Section 2.2 ("At inference ..."): the predicted input goes through the
-    layer's own normalization, here RMSNorm over the last axis."""
+    """Section 2.2: the prediction is normalised by the layer's unchanged norm,
+    like a true input; here that norm is RMSNorm over the last axis."""
     return gamma * y / np.sqrt(np.mean(y * y, axis=-1, keepdims=True) + eps)
 
 
@@ -75,8 +78,8 @@ def rope_inv_freq(head_dim: int, theta: float) -> np.ndarray:
 
 
 def rope(k: np.ndarray, positions: np.ndarray, theta: float, head_dim: int) -> np.ndarray:
-    """Section 2.2 (keys "get their rotary embedding as usual") and section 6.6
-    (keys are "rotated at their own positions").
+    """Section 2.2 (predicted keys are rotated the standard way) and section 6.6
+    (each key takes the rotation of its own row's position).
 
     k: [n][n_heads * head_dim]; positions: [n].  Angles in float64.
     """
@@ -93,8 +96,8 @@ def rope(k: np.ndarray, positions: np.ndarray, theta: float, head_dim: int) -> n
 
 
 def qk_norm(k: np.ndarray, k_gamma: np.ndarray, eps: float, head_dim: int) -> np.ndarray:
-    """QK-norm on keys (section 6.6 and section 7: the Qwen models normalise
-    each query and key before attention): every head of every row is scaled to
+    """QK-norm on keys (section 6.6 and section 7: in the Qwen models both
+    queries and keys are normalised per head ahead of attention): every head of every row is scaled to
     unit RMS, RMSNorm over its head_dim values with eps inside the root, then
     multiplied by the per-dimension gain k_gamma [head_dim] shared by the heads.
 
@@ -109,11 +112,11 @@ def qk_norm(k: np.ndarray, k_gamma: np.ndarray, eps: float, head_dim: int) -> np
 def layer_kv(h_in: np.ndarray, gamma: np.ndarray, w_k: np.ndarray, w_v: np.ndarray,
              positions: np.ndarray, theta: float, head_dim: int, eps: float,
              k_gamma: Optional[np.ndarray] = None) -> Tuple[np.ndarray, np.ndarray]:
-    """What a late attention layer writes to its cache from an input row.
+    """The cache entries a late attention layer stores for one input row.
 
-    Section 2.1: from its input a late layer computes only the keys and values
-    that later tokens read; section 2.2: the input goes through the layer's own
-    normalization and projections and the keys get their rotary embedding.
+    Section 2.1: for such a row a late layer produces only the keys and values
+    later tokens attend to; section 2.2: the input is normalised and projected
+    by the layer's unchanged weights, and the keys are rotated.
     With ``k_gamma`` the layer normalises its keys (QK-norm) before the
     rotation, as the Qwen layers do.
     """

@@ -8,9 +8,9 @@ Prefill": with X and Y_l centred by their means mu_S and mu_l,
     A_l = Y_l^T X (X^T X + alpha I)^(-1),   b_l = mu_l - A_l mu_S,
 
 only A is penalised, and ("The penalty") alpha = lambda tr(X^T X) / d_in,
-the trace taken over the centred X.  "Fitting": running sums of X^T X, X^T Y
-and the two means, one document at a time, give the same result as a solve on
-all rows at once, and a new lambda needs only a new solve.
+the trace taken over the centred X.  "Fitting": X^T X, X^T Y and both means,
+accumulated document by document, lead to the same maps as one solve over all
+rows, and changing lambda needs only a new solve.
 
 A is returned [d_out][d_in], the orientation the paper sizes it in.
 """

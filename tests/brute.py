@@ -67,7 +67,7 @@ def filled_row(x_bits, a_bits, b_bits, g_bits, wk_bits, wv_bits, pos, theta, hd,
 
 # ---------------------------------------------------------------- int8 maps
 # Written from the format's description (RidgeFill, section 2.2 "Size and
-# cost": int8 codes, one bf16 scale per 128 weights of each row), with
+# cost": int8 codes, one bf16 scale for each 128-weight block of a row), with
 # Python floats and struct only.
 
 def _f32(v):
@@ -127,8 +127,8 @@ def quantize_q8(a_rows):
 
 # ---------------------------------------------------------------- value rescale
 # Written from the description of the value rescale (RidgeFill, section 2.3):
-# per head, the exact value norm over the predicted one, averaged over the
-# calibration rows of one request.
+# per head, the mean over one request's calibration rows of each row's exact
+# value norm divided by its predicted value norm.
 
 def value_scale(v_exact_rows, v_pred_rows, groups, n_groups, head_dim):
     """Nested lists: scale[g][h] = mean over rows of group g of |ve_h| / |vp_h|."""

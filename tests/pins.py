@@ -281,8 +281,8 @@ def pin_ridge_svd_form(o):
 
 
 def pin_ridge_running_sums(o):
-    """Section 2.2 "Fitting": sums accumulated one document at a time give the same
-    map as one solve on all rows, and a new lambda needs only a new solve."""
+    """Section 2.2 "Fitting": sums accumulated document by document lead to the
+    same map as one solve over all rows; a different lambda needs one more solve."""
     x, y, _, _ = _linear_data(10, 300, 14, 9, noise=0.5)
     acc = o.RidgeSums(14, 9)
     for a0, a1 in ((0, 17), (17, 150), (150, 151), (151, 300)):

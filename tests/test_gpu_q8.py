@@ -1,7 +1,7 @@
 """GPU parity of the int8 map path (rf_fill_q8, rf_map_dequantize_q8).
 
 The format is the 27B deployment's (RidgeFill, section 2.2 "Size and cost",
-section 4.2): int8 codes with one bf16 scale per 128 weights of each row.  The
+section 4.2): int8 codes with one bf16 scale for each 128-weight block of a row.  The
 oracle dequantizes exactly (fp64); the library rounds each q * s once to bf16
 before its bf16 matrix instructions, so values are held to the fill's
 tolerance, the expansion itself bit-exactly, and rf_fill_q8 bitwise to rf_fill

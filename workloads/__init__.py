@@ -22,7 +22,7 @@ value projections):
 * b_l ~ N(0, bias_sigma^2), gamma_l ~ 1 + N(0, gamma_sigma^2);
 * W_k, W_v ~ N(0, 1/d_out), stored [n_kv * head_dim][d_out];
 * int8 maps (``map_format="q8"``, the 27B deployment's format: int8 codes
-  and one bf16 scale per 128 weights of each row) are drawn directly in that
+  and one bf16 scale for each 128-weight block of a row) are drawn directly in that
   format with the same value distribution: a block holding the identity's
   diagonal gets scale ~ (1 + N(0, map_sigma^2)) / 127 and diagonal code 127,
   any other block scale ~ map_sigma * (2.8 + 0.4 |N(0, 1)|) / 127; the other
