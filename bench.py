@@ -217,6 +217,9 @@ def main():
     ap.add_argument("--qk-norm", action="store_true", help="layers normalise their keys per head before RoPE")
     ap.add_argument("--separate-measure", action="store_true",
                     help="with --value-rescale: measure with rf_value_scales, then fill (default: inside the fill)")
+    ap.add_argument("--spans", type=int, default=None, metavar="N",
+                    help="exact 32-row spans scattered in the first prompt's prefix (default: the workload's; "
+                         "e.g. 1113 keeps 30%% of the 27b_120k prefix exact, the density of the pages' 27B runs)")
     ap.add_argument("--indexer", type=int, default=0, metavar="HEADS",
                     help="layers also write HEADS head_dim-wide indexer key heads (sparse-attention layers)")
     ap.add_argument("--maps", default="bf16", choices=["bf16", "q8"],
@@ -259,6 +262,9 @@ def main():
 
     name = args.workload
     s = workloads.spec(name, map_format=args.maps, qk_norm=args.qk_norm, idx_heads=args.indexer)
+    if args.spans is not None:
+        s = workloads.spec(name, map_format=args.maps, qk_norm=args.qk_norm, idx_heads=args.indexer,
+                           n_spans=args.spans)
     q8 = args.maps == "q8"
     dev = "cuda:0"
     log(f"[bench] {name}: drawing inputs")
@@ -395,7 +401,7 @@ def main():
                    "value_measure": (None if not args.value_rescale else
                                      "rf_value_scales, then rf_fill" if args.separate_measure else "inside rf_fill"),
                    "qk_norm": bool(args.qk_norm),
-                   "indexer_key_heads": args.indexer,
+                   "indexer_key_heads": args.indexer, "exact_spans": s.n_spans,
                    "layers_per_launch": min(g, B.RF_STREAM_GROUP) if host_maps else g},
         "tflops": step_flops / (ms * 1e-3) / 1e12,
         "frac_of_bf16_peak": step_flops / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS,

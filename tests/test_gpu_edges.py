@@ -97,3 +97,11 @@ def test_every_option_in_one_call():
     U.check_values(kc, vc, oracle.fill_workload_rescaled(w, ref_scales, g_of_row, f), f, s.head_dim, slots=slots)
     worst = U.check_indexer_values(ic, oracle.fill_indexer_workload(w, rows=f), f, s.head_dim, slots=slots)
     print(f"[edges] all options: indexer worst {worst}", flush=True)
+
+
+def test_dense_scattered_exact_spans():
+    """About 30% of the prefix kept exact as scattered 32-row spans (the
+    density of the pages' 27B runs): the fill gathers the remaining rows
+    across many short runs."""
+    s = workloads.spec("27b_120k", n_late=2, prompt_lens=(1300,), tail=100, n_spans=12, seed=110)
+    _check(s, "30% scattered exact rows")
