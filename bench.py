@@ -407,11 +407,20 @@ def main():
         "frac_of_bf16_peak": step_flops / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS,
         "roofline": {"bound": "mfma", "kernel": "map_gemm", "achieved": map_tflops, "peak": PEAK_BF16_TFLOPS,
                      "unit": "TFLOP/s", "frac": map_tflops / PEAK_BF16_TFLOPS,
-                     "traffic": measured_traffic(name), "algorithmic_bytes_per_launch": map_launch_bytes,
+                     # the counters were taken on the default configuration of the workload
+                     "traffic": (measured_traffic(name) if args.spans is None and g == GROUP[name] else None),
+                     "algorithmic_bytes_per_launch": map_launch_bytes,
                      "flops_per_launch": map_launch_flops, "ms_per_launch": map_avg_ms},
         "kernels": kernels,
         "kv_gemm_tflops": kv_tflops,
     }
+    if host_maps and prof["copy"][1]:
+        per_layer = s.d_out * s.d_in * (1 + 2 / workloads.Q8_BLOCK if q8 else 2) + s.d_out * 2
+        h2d_bytes = s.n_late * per_layer
+        copy_ms = prof["copy"][0] / args.steps
+        out["h2d"] = {"bytes_per_step": h2d_bytes, "copy_ms_per_step": copy_ms,
+                      "gbs": h2d_bytes / (copy_ms * 1e-3) / 1e9,
+                      "note": "maps and biases over PCIe on a side stream, overlapped with the kernels"}
     if q8 and prof["dequant"][1]:
         dq_ms, dq_n = prof["dequant"]
         layers_per_dq = s.n_late * args.steps / dq_n
