@@ -440,3 +440,35 @@ def test_bench_refuses_more_than_one_gpu():
                        text=True, timeout=120)
     assert r.returncode == 2
     assert "one GPU only" in r.stderr and r.stdout == ""
+
+
+def test_traffic_summary_scales_counters_by_the_copy(tmp_path):
+    """bench.py's traffic figure: per-launch FETCH_SIZE and WRITE_SIZE (KiB) of
+    the map kernel, each scaled by bytes / counter of a device copy of known size."""
+    import bench
+
+    def write(path, counter, rows):
+        with open(path, "w") as f:
+            f.write("Kernel_Name,Grid_Size,Counter_Name,Counter_Value\n")
+            for name, grid, v in rows:
+                f.write(f'"{name}",{grid},{counter},{v}\n')   # names hold commas; rocprofv3 quotes them
+
+    calib = 4 << 30
+    fetch, write_ = tmp_path / "fetch.csv", tmp_path / "write.csv"
+    # two map launches, one K/V launch and the calibration copy (which reads half what it moves)
+    write(fetch, "FETCH_SIZE", [("rf::map_gemm_kernel(rf::MapParams)", 256, 1000.0),
+                                ("rf::map_gemm_kernel(rf::MapParams)", 256, 3000.0),
+                                ("void rf::kv_gemm_kernel<128, false, false>(rf::KvParams)", 256, 500.0),
+                                ("__amd_rocclr_copyBuffer", 1 << 20, calib / 1024 / 2)])
+    write(write_, "WRITE_SIZE", [("rf::map_gemm_kernel(rf::MapParams)", 256, 400.0),
+                                 ("rf::map_gemm_kernel(rf::MapParams)", 256, 400.0),
+                                 ("void rf::kv_gemm_kernel<128, false, false>(rf::KvParams)", 256, 100.0),
+                                 ("__amd_rocclr_copyBuffer", 1 << 20, calib / 1024)])
+    t = bench.summarize_pmc(str(fetch), str(write_), "27b_120k", calib)
+    assert t["copy_calibration"]["fetch_factor"] == pytest.approx(2.0)
+    assert t["copy_calibration"]["write_factor"] == pytest.approx(1.0)
+    m = t["kernels"]["map_gemm"]
+    assert m["fetch_kib_per_launch"] == pytest.approx(2000.0) and m["write_kib_per_launch"] == pytest.approx(400.0)
+    assert t["traffic_bytes_per_launch"] == pytest.approx((2000.0 * 2 + 400.0) * 1024)
+    assert t["kernels"]["kv_gemm"]["bytes_per_launch"] == pytest.approx((500.0 * 2 + 100.0) * 1024)
+    assert t["kernel_source_sha256"] == bench.kernel_source_hash()
