@@ -105,3 +105,22 @@ def test_dense_scattered_exact_spans():
     across many short runs."""
     s = workloads.spec("27b_120k", n_late=2, prompt_lens=(1300,), tail=100, n_spans=12, seed=110)
     _check(s, "30% scattered exact rows")
+
+
+def test_widest_launch_group():
+    """33 late layers with a workspace for all of them: one launch of the
+    library's maximum of 32 layers, then one of a single layer."""
+    s = workloads.spec("tiny", n_late=33, prompt_lens=(300,), tail=40, seed=120)
+    print(f"[edges] widest group: L={s.n_late}", flush=True)
+    w = workloads.make(s)
+    di = U.DeviceInputs(w)
+    plan = U.plan_for(w)
+    rows, n = U.gpu_fill_rows(plan, di)
+    assert plan.fill_workspace_bytes(n, 33) == plan.fill_workspace_bytes(n, 32)
+    kc, vc = U.gpu_fill(plan, di, rows, n, layers_per_launch=33)
+    f = rows.cpu().numpy()
+    U.check_placement(kc, vc, f, s.n_rows)
+    U.check_values(kc, vc, oracle.fill_workload(w, rows=f), f, s.head_dim)
+    k1, v1 = U.gpu_fill(plan, di, rows, n, layers_per_launch=1)
+    for l in range(s.n_late):
+        assert torch.equal(kc[l], k1[l]) and torch.equal(vc[l], v1[l]), f"layer {l}"
