@@ -124,3 +124,30 @@ def test_widest_launch_group():
     k1, v1 = U.gpu_fill(plan, di, rows, n, layers_per_launch=1)
     for l in range(s.n_late):
         assert torch.equal(kc[l], k1[l]) and torch.equal(vc[l], v1[l]), f"layer {l}"
+
+
+def test_prompt_that_is_all_exact():
+    """A ragged batch whose second prompt is shorter than the tail: all its
+    rows are exact, none is filled, its slots stay untouched."""
+    _check(workloads.spec("8b_ragged_host", n_late=2, prompt_lens=(300, 40, 129), tail=50, seed=130),
+           "a prompt with no filled rows")
+
+
+def test_cache_larger_than_the_batch():
+    """n_slots = 3 x n_rows, rows scattered to distinct slots anywhere in the
+    cache: only those slots are written, with the oracle's values."""
+    s = workloads.spec("tiny", n_late=2, prompt_lens=(300,), tail=40, seed=140)
+    print(f"[edges] cache of {3 * s.n_rows} slots for {s.n_rows} rows", flush=True)
+    w = workloads.make(s)
+    di = U.DeviceInputs(w)
+    n_slots = 3 * s.n_rows
+    plan = B.Plan(s.d_in, s.d_out, s.n_late, s.n_kv, s.head_dim, s.rms_eps, s.rope_theta, s.n_rows, n_slots,
+                  s.max_pos)
+    rows, n = U.gpu_fill_rows(plan, di)
+    slots = np.random.default_rng(7).choice(n_slots, s.n_rows, replace=False).astype(np.int32)
+    mk = lambda: [torch.full((n_slots, s.kv_width), U.CANARY, dtype=torch.int16, device="cuda:0")
+                  for _ in range(s.n_late)]
+    kc, vc = U.gpu_fill(plan, di, rows, n, caches=(mk(), mk()), slots=U.i32(slots).cuda())
+    f = rows.cpu().numpy()
+    U.check_placement(kc, vc, f, n_slots, slots=slots)
+    U.check_values(kc, vc, oracle.fill_workload(w, rows=f), f, s.head_dim, slots=slots)
