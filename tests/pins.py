@@ -227,6 +227,63 @@ def pin_brute_force_tiny(o):
             assert np.max(np.abs(np.array(vb) - vr)) <= 1e-12 * np.max(np.abs(vr))
 
 
+def _position_in_prompt(prompt_lens, r):
+    """Row r's position inside its own prompt, by walking the prompt lengths."""
+    start = 0
+    for n in prompt_lens:
+        if r < start + n:
+            return r - start
+        start += n
+    raise IndexError(r)
+
+
+def pin_ragged_positions_brute(o):
+    """Sections 2.2 and 6.6: each key is rotated at its own row's position,
+    and in a batch of requests that position restarts at 0 with every
+    request.  A tiny batch of three prompts, rows taken from all three (the
+    first row of a later prompt among them), against the plain-loop row of
+    tests/brute.py for the four workload-level functions: filled K/V, exact
+    K/V from given layer inputs, and the indexer keys of both.  Positions are
+    counted here from the prompt lengths, not read from the workload."""
+    s = workloads.spec("tiny", d_in=128, d_out=128, n_late=2, prompt_lens=(40, 24, 33), tail=8,
+                       idx_heads=1, seed=11)
+    w = workloads.make(s)
+    rows = np.array([3, 41, 55, 64, 80])
+    pos = [_position_in_prompt(s.prompt_lens, int(r)) for r in rows]
+    assert pos == [3, 1, 15, 0, 16]
+    truth = workloads.make_layer_truth(s, s.n_rows, outliers=w.outlier_channels)[0]
+    eye = _bits(np.eye(s.d_out))
+    zero = _bits(np.zeros(s.d_out))
+    fill = o.fill_workload(w, rows=rows)
+    exact = o.exact_kv_workload(w, truth, rows)
+    fidx = o.fill_indexer_workload(w, rows=rows)
+    eidx = o.exact_indexer_workload(w, truth, rows)
+
+    def close(got, want):
+        want = np.array(want)
+        assert np.max(np.abs(got - want)) <= 1e-12 * max(1.0, np.max(np.abs(want)))
+
+    for l in range(s.n_late):
+        args = (w.gamma[l].tolist(), w.w_k[l].tolist(), w.w_v[l].tolist())
+        for i, r in enumerate(rows):
+            p = pos[i]
+            kb, vb = brute.filled_row(w.x[r].tolist(), w.map_a[l].tolist(), w.map_b[l].tolist(), *args,
+                                      p, s.rope_theta, s.head_dim, s.rms_eps)
+            close(fill[l][0][i], kb)
+            close(fill[l][1][i], vb)
+            ke, ve = brute.filled_row(truth[r].tolist(), eye.tolist(), zero.tolist(), *args,
+                                      p, s.rope_theta, s.head_dim, s.rms_eps)
+            close(exact[l][0][i], ke)
+            close(exact[l][1][i], ve)
+            wi = w.w_idx[l].tolist()
+            ki, _ = brute.filled_row(w.x[r].tolist(), w.map_a[l].tolist(), w.map_b[l].tolist(),
+                                     w.gamma[l].tolist(), wi, wi, p, s.rope_theta, s.head_dim, s.rms_eps)
+            close(fidx[l][i], ki)
+            kie, _ = brute.filled_row(truth[r].tolist(), eye.tolist(), zero.tolist(), w.gamma[l].tolist(), wi, wi,
+                                      p, s.rope_theta, s.head_dim, s.rms_eps)
+            close(eidx[l][i], kie)
+
+
 def pin_fill_row_independence(o):
     """Section 2.1: a filled row's input comes straight from its own split state,
     so its K/V do not depend on which other rows are filled with it."""
@@ -689,7 +746,7 @@ def pin_printed_ceilings(o):
 FILL_PINS = [pin_fill_rows_partition, pin_identity_map_is_exact_kv, pin_map_orientation,
              pin_bias_only_map, pin_rmsnorm_closed_forms, pin_one_hot_layer_kv,
              pin_rope_is_complex_rotation, pin_rope_invariants, pin_brute_force_tiny,
-             pin_fill_row_independence, pin_qk_norm_closed_form, pin_qk_norm_invariants,
+             pin_ragged_positions_brute, pin_fill_row_independence, pin_qk_norm_closed_form, pin_qk_norm_invariants,
              pin_qk_layer_brute, pin_indexer_one_hot, pin_indexer_brute, pin_indexer_is_a_plain_key_head]
 RIDGE_PINS = [pin_ridge_recovers_linear_map, pin_ridge_svd_form, pin_ridge_running_sums,
               pin_ridge_penalty_scale, pin_ridge_raw_form]

@@ -4,7 +4,9 @@ Every mutant is the oracle's own source with one plausible mistake edited in
 (a transposed operand, a dropped term, a wrong sign or index, a wrong axis),
 executed as a fresh module.  The real oracle is never modified.
 """
+import itertools
 import os
+import sys
 import types
 
 import pytest
@@ -54,6 +56,15 @@ MUTANTS = {
     "rows_union_not_difference": ("fill.py", [("np.setdiff1d(", "np.union1d(")]),
     "rows_wrong_positions": ("fill.py", [("pos = w.positions[r]\n    out = {}\n    for l in (range(s.n_late) if layers is None else layers):\n        out[l] = fill_layer",
                                           "pos = w.positions[:len(r)]\n    out = {}\n    for l in (range(s.n_late) if layers is None else layers):\n        out[l] = fill_layer")]),
+    # positions: the global row index instead of the row's position in its own prompt
+    "pos_global_row_fill": ("fill.py", [("pos = w.positions[r]\n    out = {}\n    for l in (range(s.n_late) if layers is None else layers):\n        out[l] = fill_layer",
+                                         "pos = r\n    out = {}\n    for l in (range(s.n_late) if layers is None else layers):\n        out[l] = fill_layer")]),
+    "pos_global_row_exact_kv": ("fill.py", [("pos = w.positions[r]\n    out = {}\n    for l in (range(s.n_late) if layers is None else layers):\n        out[l] = layer_kv",
+                                             "pos = r\n    out = {}\n    for l in (range(s.n_late) if layers is None else layers):\n        out[l] = layer_kv")]),
+    "pos_global_row_fill_indexer": ("fill.py", [("pos = w.positions[r]\n    out = {}\n    for l in (range(s.n_late) if layers is None else layers):\n        y = predicted_input",
+                                                 "pos = r\n    out = {}\n    for l in (range(s.n_late) if layers is None else layers):\n        y = predicted_input")]),
+    "pos_global_row_exact_indexer": ("fill.py", [("pos = w.positions[r]\n    return {l: indexer_keys",
+                                                  "pos = r\n    return {l: indexer_keys")]),
     "bf16_decode_shift": ("fill.py", [("astype(np.uint32) << 16", "astype(np.uint32) << 15")]),
     # the ridge fit
     "ridge_not_centred": ("ridge.py", [("xc = x - mu_s", "xc = x")]),
@@ -106,7 +117,20 @@ PINS_FOR = {"fill.py": pins.FILL_PINS, "ridge.py": pins.RIDGE_PINS, "ceiling.py"
             "quant.py": pins.QUANT_PINS, "rescale.py": pins.RESCALE_PINS}
 
 
+_loads = itertools.count()
+
+
 def _load(target, edits):
+    """The oracle's files executed as a fresh package, with one file mutated.
+
+    Each copy is registered under a package name of its own, so the relative
+    imports between the oracle's files (rescale.py takes fill_workload from
+    fill.py; fill.py takes the int8 expansion from quant.py when called)
+    resolve to the copies, mutated one included, never to the real oracle."""
+    pkg_name = f"_oracle_mutant_{next(_loads)}"
+    pkg = types.ModuleType(pkg_name)
+    pkg.__path__ = []
+    sys.modules[pkg_name] = pkg
     ns = types.SimpleNamespace()
     for fn in FILES:
         with open(os.path.join(ORACLE_DIR, fn)) as f:
@@ -115,15 +139,22 @@ def _load(target, edits):
             for old, new in edits:
                 assert src.count(old) >= 1, f"mutation anchor not found in {fn}: {old!r}"
                 src = src.replace(old, new, 1)
-        mod = types.ModuleType("oracle.mutant_" + fn[:-3])
-        mod.__package__ = "oracle"  # relative imports resolve to the unmutated oracle
+        mod = types.ModuleType(f"{pkg_name}.{fn[:-3]}")
+        mod.__package__ = pkg_name
+        sys.modules[mod.__name__] = mod
+        setattr(pkg, fn[:-3], mod)
         exec(compile(src, os.path.join(ORACLE_DIR, fn), "exec"), mod.__dict__)
         for k, v in vars(mod).items():
-            # a name a later file imports from an earlier one keeps the earlier
-            # (possibly mutated) definition
             if not k.startswith("_") and not hasattr(ns, k):
                 setattr(ns, k, v)
     return ns
+
+
+def test_mutant_imports_resolve_to_the_copy():
+    """A mutation in fill.py reaches rescale.py's use of fill_workload."""
+    o = _load("fill.py", [("return x_s @ a.T + b", "return x_s @ a.T + 2 * b")])
+    assert o.fill_workload_rescaled.__globals__["fill_workload"] is o.fill_workload
+    assert o.fill_workload.__module__ != "oracle.fill"
 
 
 def test_unmutated_copy_passes():
