@@ -35,7 +35,12 @@
  * Layouts (per late layer l, all bf16):
  *    x       [n_rows][ld_x]               split state x_S, first d_in columns used
  *    map_a   [d_out][d_in]                A_l, row n = output feature n (the
- *                                         paper's orientation, section 2.2)
+ *                                         paper's orientation, section 2.2,
+ *                                         y = A_l x + b_l).  For the row-vector
+ *                                         form Y = X W_l + b_l, A_l = W_l^T: a
+ *                                         caller holding W_l [d_in][d_out] passes
+ *                                         its transpose.  rf_ridge_fit and
+ *                                         rf_ridge_dev_solve return A_l.
  *    map_b   [d_out]                      b_l
  *    gamma   [d_out]                      RMSNorm gain
  *    w_k,w_v [n_kv*head_dim][d_out]       projection weights, [out][in]

@@ -161,6 +161,131 @@ def _stream(stream) -> Optional[int]:
     return torch.cuda.current_stream().cuda_stream
 
 
+# ---- host-side argument checks ---------------------------------------------
+# The library receives bare pointers, so it cannot see a tensor that is too
+# small, of the wrong type or in the wrong memory; the kernels would then read
+# or write past its end.  Every tensor argument is checked here, before
+# anything is enqueued, against the sizes the plan fixes.  A failed check
+# raises ValueError.
+
+DEVICE_TYPE = "cuda"   # where device arguments must live (torch's name for HIP devices)
+_BF16 = ("int16", "uint16", "bfloat16")
+
+
+def _dtype(t) -> str:
+    return str(t.dtype).replace("torch.", "")
+
+
+def _arg(fn: str, name: str, t, dtypes, numel: int = 0, where: str = "device", optional: bool = False):
+    """t must be a tensor of one of `dtypes` holding at least `numel` elements,
+    with unit stride along its last axis, in device memory (where="device") or
+    pinned host memory (where="pinned")."""
+    if t is None:
+        if optional:
+            return
+        raise ValueError(f"{fn}: {name} is required")
+    if not hasattr(t, "data_ptr") or not hasattr(t, "dtype"):
+        raise ValueError(f"{fn}: {name} must be a tensor, got {type(t).__name__}")
+    if _dtype(t) not in dtypes:
+        raise ValueError(f"{fn}: {name} has dtype {_dtype(t)}, expected one of {', '.join(dtypes)}")
+    if where == "device" and t.device.type != DEVICE_TYPE:
+        raise ValueError(f"{fn}: {name} must be in device memory, not on {t.device}")
+    if where == "pinned" and (t.device.type != "cpu" or not t.is_pinned()):
+        raise ValueError(f"{fn}: {name} must be in pinned host memory (the plan streams its maps)")
+    if t.dim() > 0 and t.stride(-1) != 1:
+        raise ValueError(f"{fn}: {name} must have unit stride along its last axis")
+    if t.numel() < numel:
+        raise ValueError(f"{fn}: {name} holds {t.numel()} elements, at least {numel} needed")
+
+
+def _rows_arg(fn: str, name: str, t, rows: int, cols: int, ld: Optional[int], where: str = "device"):
+    """A row-major bf16 matrix of `rows` rows of which the first `cols`
+    columns are read, rows `ld` elements apart (default: its row stride)."""
+    _arg(fn, name, t, _BF16, 0, where)
+    if t.dim() != 2:
+        raise ValueError(f"{fn}: {name} must be 2-D [rows][columns]")
+    ld = t.stride(0) if ld is None else ld
+    if ld < cols:
+        raise ValueError(f"{fn}: {name} rows are {ld} elements apart, fewer than the {cols} read")
+    need = (rows - 1) * ld + cols if rows > 0 else 0
+    span = (t.shape[0] - 1) * t.stride(0) + t.shape[1] if t.numel() else 0
+    if span < need:
+        raise ValueError(f"{fn}: {name} covers {span} elements, {need} needed for {rows} rows of {cols}")
+
+
+def _layers(fn: str, name: str, ts, n_late: int, dtypes, numel: int, where: str = "device", shape=None):
+    """One tensor per late layer; with `shape`, a 2-D tensor must have exactly
+    that shape and be contiguous (maps: [d_out][d_in], so a transposed map is
+    refused rather than read the wrong way round)."""
+    if ts is None or len(ts) != n_late:
+        raise ValueError(f"{fn}: {name} must hold one tensor per late layer ({n_late})")
+    for i, t in enumerate(ts):
+        _arg(fn, f"{name}[{i}]", t, dtypes, numel, where)
+        if shape is not None and t.dim() == 2 and (tuple(t.shape) != tuple(shape) or not t.is_contiguous()):
+            raise ValueError(f"{fn}: {name}[{i}] is {tuple(t.shape)}"
+                             f"{'' if t.is_contiguous() else ' (not contiguous)'}, expected contiguous "
+                             f"{tuple(shape)} = [d_out][d_in]")
+
+
+def _workspace(fn: str, ws):
+    _arg(fn, "workspace", ws, ("uint8", "int8", "int16", "int32", "float32", "float16", "bfloat16", "float64",
+                                "int64", "uint16", "uint32"), 0)
+
+
+def _check_fill(fn: str, plan: "Plan", x, ld_x, fill_rows_t, n_fill, positions, slot_of_row, maps, map_b, gamma,
+                w_k, w_v, rope, k_cache, v_cache, workspace, vscale, k_norm, w_idx, idx_cache, measure):
+    sh = plan.shape
+    L, d_in, d_out = sh.n_late, sh.d_in, sh.d_out
+    mw = "pinned" if plan.maps_on_host else "device"
+    if not 0 <= n_fill <= sh.n_rows:
+        raise ValueError(f"{fn}: n_fill={n_fill} outside [0, n_rows={sh.n_rows}]")
+    _rows_arg(fn, "x", x, sh.n_rows, d_in, ld_x)
+    _arg(fn, "fill_rows", fill_rows_t, ("int32",), n_fill)
+    _arg(fn, "positions", positions, ("int32",), sh.n_rows)
+    _arg(fn, "slot_of_row", slot_of_row, ("int32",), sh.n_rows, optional=True)
+    if plan.maps_q8:
+        map_q, map_scale = maps
+        _layers(fn, "map_q", map_q, L, ("int8",), d_out * d_in, mw, (d_out, d_in))
+        _layers(fn, "map_scale", map_scale, L, _BF16, d_out * (d_in // Q8_BLOCK), mw, (d_out, d_in // Q8_BLOCK))
+    else:
+        _layers(fn, "map_a", maps, L, _BF16, d_out * d_in, mw, (d_out, d_in))
+    _layers(fn, "map_b", map_b, L, _BF16, d_out, mw)
+    _layers(fn, "gamma", gamma, L, _BF16, d_out)
+    _layers(fn, "w_k", w_k, L, _BF16, plan.kv_width * d_out)
+    _layers(fn, "w_v", w_v, L, _BF16, plan.kv_width * d_out)
+    _arg(fn, "rope", rope, ("float32",), sh.max_pos * sh.head_dim, optional=True)
+    _layers(fn, "k_cache", k_cache, L, _BF16, sh.n_slots * plan.kv_width)
+    _layers(fn, "v_cache", v_cache, L, _BF16, sh.n_slots * plan.kv_width)
+    _workspace(fn, workspace)
+    if k_norm is not None:
+        _layers(fn, "k_norm", k_norm, L, _BF16, sh.head_dim)
+    if w_idx is not None:
+        _layers(fn, "w_idx", w_idx, L, _BF16, plan.idx_width * d_out)
+    if idx_cache is not None:
+        _layers(fn, "idx_cache", idx_cache, L, _BF16, sh.n_slots * plan.idx_width)
+    if vscale is not None:
+        scale, group_of_row, n_groups = vscale
+        _arg(fn, "vscale scale", scale, ("float32",), L * max(n_groups, 1) * sh.n_kv)
+        _arg(fn, "vscale group_of_row", group_of_row, ("int32",), sh.n_rows)
+    if measure is not None:
+        layer_in, calib_rows, calib_group, group_of_row, n_groups, scale, ws = measure
+        _check_measure(fn, plan, layer_in, None, calib_rows, calib_group, n_groups, scale)
+        _arg(fn, "measure group_of_row", group_of_row, ("int32",), sh.n_rows)
+        _workspace(fn, ws)
+
+
+def _check_measure(fn, plan, layer_in, ld_in, calib_rows, calib_group, n_groups, scale):
+    sh = plan.shape
+    _arg(fn, "calib_rows", calib_rows, ("int32",), 0)
+    n = calib_rows.numel()
+    _arg(fn, "calib_group", calib_group, ("int32",), n)
+    if layer_in is None or len(layer_in) != sh.n_late:
+        raise ValueError(f"{fn}: layer_in must hold one tensor per late layer ({sh.n_late})")
+    for i, t in enumerate(layer_in):
+        _rows_arg(fn, f"layer_in[{i}]", t, n, sh.d_out, ld_in)
+    _arg(fn, "scale", scale, ("float32",), sh.n_late * max(n_groups, 1) * sh.n_kv)
+
+
 class Plan:
     """An rf_plan for one shape (see rf_plan_create)."""
 
@@ -171,6 +296,8 @@ class Plan:
                            n_idx)
         self.flags = ((RF_MAPS_HOST if maps_on_host else 0) | (RF_VALIDATE if validate else 0)
                       | (RF_MAPS_Q8 if maps_q8 else 0))
+        self.maps_on_host, self.maps_q8 = bool(maps_on_host), bool(maps_q8)
+        self.kv_width, self.idx_width = n_kv * head_dim, n_idx * head_dim
         h = C.c_void_p()
         _check("rf_plan_create", lib().rf_plan_create(C.byref(self.shape), self.flags, C.byref(h)))
         self.handle = h
@@ -220,11 +347,16 @@ def fill_rows_workspace_bytes(n_rows: int) -> int:
 
 
 def rope_table(plan: Plan, table, stream=None) -> None:
+    _arg("rf_rope_table", "table", table, ("float32",), plan.shape.max_pos * plan.shape.head_dim)
     _check("rf_rope_table", lib().rf_rope_table(plan.handle, _ptr(table), _stream(stream)))
 
 
 def fill_rows(plan: Plan, exact_rows, fill_rows_out, n_fill_out, workspace, stream=None) -> None:
     n_exact = 0 if exact_rows is None else exact_rows.numel()
+    _arg("rf_fill_rows", "exact_rows", exact_rows, ("int32",), 0, optional=True)
+    _arg("rf_fill_rows", "fill_rows_out", fill_rows_out, ("int32",), plan.shape.n_rows)
+    _arg("rf_fill_rows", "n_fill_out", n_fill_out, ("int32",), 1)
+    _workspace("rf_fill_rows", workspace)
     _check("rf_fill_rows", lib().rf_fill_rows(plan.handle, _ptr(exact_rows), n_exact, _ptr(fill_rows_out),
                                               _ptr(n_fill_out), _ptr(workspace), workspace.numel() *
                                               workspace.element_size(), _stream(stream)))
@@ -272,7 +404,14 @@ def fill(plan: Plan, x, fill_rows_t, n_fill: int, positions, slot_of_row, map_a:
     bf16 [head_dim] gain per late layer) applies QK-norm to the keys; w_idx /
     idx_cache (per late layer) write the indexer keys of a plan with n_idx > 0;
     measure = (layer_in, calib_rows, calib_group, group_of_row, n_groups, scale,
-    workspace) measures the value scales inside the fill and applies them."""
+    workspace) measures the value scales inside the fill and applies them.
+
+    map_a[l] is A_l [d_out][d_in], the map in the paper's orientation
+    (y = A_l x + b_l, RidgeFill section 2.2), which is W_l transposed for the
+    row-vector form Y = X W_l + b_l; rf_ridge_fit returns A_l.  A caller
+    holding W_l [d_in][d_out] passes W_l.T made contiguous."""
+    _check_fill("rf_fill", plan, x, ld_x, fill_rows_t, n_fill, positions, slot_of_row, map_a, map_b, gamma, w_k,
+                w_v, rope, k_cache, v_cache, workspace, vscale, k_norm, w_idx, idx_cache, measure)
     ld = x.stride(0) if ld_x is None else ld_x
     o = _Opts(vscale, k_norm, w_idx, idx_cache, measure)
     _check("rf_fill", lib().rf_fill(
@@ -289,6 +428,8 @@ def fill_q8(plan: Plan, x, fill_rows_t, n_fill: int, positions, slot_of_row, map
             measure=None) -> None:
     """rf_fill_q8: the fill with int8 maps (codes + bf16 block scales) for a
     plan made with maps_q8; pinned host tensors for a plan with maps_on_host."""
+    _check_fill("rf_fill_q8", plan, x, ld_x, fill_rows_t, n_fill, positions, slot_of_row, (map_q, map_scale), map_b,
+                gamma, w_k, w_v, rope, k_cache, v_cache, workspace, vscale, k_norm, w_idx, idx_cache, measure)
     ld = x.stride(0) if ld_x is None else ld_x
     o = _Opts(vscale, k_norm, w_idx, idx_cache, measure)
     _check("rf_fill_q8", lib().rf_fill_q8(
@@ -304,6 +445,21 @@ def value_scales(plan: Plan, x, layer_in: Sequence, calib_rows, calib_group, n_g
     """rf_value_scales (bf16 maps) or rf_value_scales_q8 (map_a holds int8 codes
     and map_scale their bf16 block scales): per request, layer and kv head,
     the mean ratio of exact to predicted value norms over the calibration rows."""
+    fn = "rf_value_scales" if map_scale is None else "rf_value_scales_q8"
+    sh = plan.shape
+    mw = "pinned" if plan.maps_on_host else "device"
+    _rows_arg(fn, "x", x, sh.n_rows, sh.d_in, ld_x)
+    _check_measure(fn, plan, layer_in, ld_in, calib_rows, calib_group, n_groups, scale_out)
+    if map_scale is None:
+        _layers(fn, "map_a", map_a, sh.n_late, _BF16, sh.d_out * sh.d_in, mw, (sh.d_out, sh.d_in))
+    else:
+        _layers(fn, "map_q", map_a, sh.n_late, ("int8",), sh.d_out * sh.d_in, mw, (sh.d_out, sh.d_in))
+        _layers(fn, "map_scale", map_scale, sh.n_late, _BF16, sh.d_out * (sh.d_in // Q8_BLOCK), mw,
+                (sh.d_out, sh.d_in // Q8_BLOCK))
+    _layers(fn, "map_b", map_b, sh.n_late, _BF16, sh.d_out, mw)
+    _layers(fn, "gamma", gamma, sh.n_late, _BF16, sh.d_out)
+    _layers(fn, "w_v", w_v, sh.n_late, _BF16, plan.kv_width * sh.d_out)
+    _workspace(fn, workspace)
     ld = x.stride(0) if ld_x is None else ld_x
     ldi = layer_in[0].stride(0) if ld_in is None else ld_in
     n = calib_rows.numel()
@@ -320,7 +476,12 @@ def value_scales(plan: Plan, x, layer_in: Sequence, calib_rows, calib_group, n_g
 
 def map_dequantize_q8(q, scale, w_out, stream=None) -> None:
     """rf_map_dequantize_q8: w_out[o][k] = bf16(q[o][k] * scale[o][k // 128]) on the device."""
+    _arg("rf_map_dequantize_q8", "q", q, ("int8",), 0)
+    if q.dim() != 2 or not q.is_contiguous():
+        raise ValueError("rf_map_dequantize_q8: q must be a contiguous [d_out][d_in] matrix")
     d_out, d_in = q.shape
+    _arg("rf_map_dequantize_q8", "scale", scale, _BF16, d_out * (d_in // Q8_BLOCK))
+    _arg("rf_map_dequantize_q8", "w_out", w_out, _BF16, d_out * d_in)
     _check("rf_map_dequantize_q8", lib().rf_map_dequantize_q8(_ptr(q), _ptr(scale), d_out, d_in, _ptr(w_out),
                                                               _stream(stream)))
 
@@ -340,6 +501,29 @@ def kv_project(plan: Plan, layer_in: Sequence, rows, n: int, positions, slot_of_
                stream=None, ld_in: Optional[int] = None, k_norm: Sequence = None, w_idx: Sequence = None,
                idx_cache: Sequence = None) -> None:
     """rf_kv_project: the exact cache write of every late layer from given inputs."""
+    fn, sh = "rf_kv_project", plan.shape
+    if not 0 <= n <= sh.n_rows:
+        raise ValueError(f"{fn}: n={n} outside [0, n_rows={sh.n_rows}]")
+    if layer_in is None or len(layer_in) != sh.n_late:
+        raise ValueError(f"{fn}: layer_in must hold one tensor per late layer ({sh.n_late})")
+    for i, t in enumerate(layer_in):
+        _rows_arg(fn, f"layer_in[{i}]", t, sh.n_rows, sh.d_out, ld_in)
+    _arg(fn, "rows", rows, ("int32",), n)
+    _arg(fn, "positions", positions, ("int32",), sh.n_rows)
+    _arg(fn, "slot_of_row", slot_of_row, ("int32",), sh.n_rows, optional=True)
+    _layers(fn, "gamma", gamma, sh.n_late, _BF16, sh.d_out)
+    _layers(fn, "w_k", w_k, sh.n_late, _BF16, plan.kv_width * sh.d_out)
+    _layers(fn, "w_v", w_v, sh.n_late, _BF16, plan.kv_width * sh.d_out)
+    _arg(fn, "rope", rope, ("float32",), sh.max_pos * sh.head_dim, optional=True)
+    _layers(fn, "k_cache", k_cache, sh.n_late, _BF16, sh.n_slots * plan.kv_width)
+    _layers(fn, "v_cache", v_cache, sh.n_late, _BF16, sh.n_slots * plan.kv_width)
+    if k_norm is not None:
+        _layers(fn, "k_norm", k_norm, sh.n_late, _BF16, sh.head_dim)
+    if w_idx is not None:
+        _layers(fn, "w_idx", w_idx, sh.n_late, _BF16, plan.idx_width * sh.d_out)
+    if idx_cache is not None:
+        _layers(fn, "idx_cache", idx_cache, sh.n_late, _BF16, sh.n_slots * plan.idx_width)
+    _workspace(fn, workspace)
     ld = layer_in[0].stride(0) if ld_in is None else ld_in
     o = _Opts(None, k_norm, w_idx, idx_cache)
     _check("rf_kv_project", lib().rf_kv_project(
@@ -408,8 +592,10 @@ class RidgeDeviceSums:
 
     def add(self, x, y, stream=None) -> None:
         """x: device bf16 [n][>= d_in], y: device bf16 [n][>= d_out] (row-major)."""
-        if x.shape[0] != y.shape[0]:
-            raise ValueError("x and y must have the same number of rows")
+        if x.dim() != 2 or y.dim() != 2 or x.shape[0] != y.shape[0]:
+            raise ValueError("x and y must be 2-D with the same number of rows")
+        _rows_arg("rf_ridge_dev_add", "x", x, x.shape[0], self.d_in, None)
+        _rows_arg("rf_ridge_dev_add", "y", y, y.shape[0], self.d_out, None)
         _check("rf_ridge_dev_add", lib().rf_ridge_dev_add(self.handle, _ptr(x), x.stride(0), _ptr(y), y.stride(0),
                                                           x.shape[0], _stream(stream)))
 
@@ -428,6 +614,9 @@ class RidgeDeviceSums:
         b = torch.empty(self.d_out, dtype=torch.float32, device=dev) if b is None else b
         if workspace is None:
             workspace = torch.empty(self.solve_workspace_bytes(), dtype=torch.uint8, device=dev)
+        _arg("rf_ridge_dev_solve", "a", a, ("float32",), self.d_out * self.d_in)
+        _arg("rf_ridge_dev_solve", "b", b, ("float32",), self.d_out)
+        _workspace("rf_ridge_dev_solve", workspace)
         _check("rf_ridge_dev_solve", lib().rf_ridge_dev_solve(
             self.handle, lam, RF_RIDGE_RAW if raw else 0, _ptr(a), _ptr(b), _ptr(workspace),
             workspace.numel() * workspace.element_size(), _stream(stream)))

@@ -472,3 +472,145 @@ def test_traffic_summary_scales_counters_by_the_copy(tmp_path):
     assert t["traffic_bytes_per_launch"] == pytest.approx((2000.0 * 2 + 400.0) * 1024)
     assert t["kernels"]["kv_gemm"]["bytes_per_launch"] == pytest.approx((500.0 * 2 + 100.0) * 1024)
     assert t["kernel_source_sha256"] == bench.kernel_source_hash()
+
+
+# ---- the binding's own checks of tensor arguments (sizes, types, memory) -----
+
+class _CpuAsDevice:
+    """Run the binding's checks with CPU tensors standing in for device ones."""
+
+    def __enter__(self):
+        self.old, B.DEVICE_TYPE = B.DEVICE_TYPE, "cpu"
+
+    def __exit__(self, *a):
+        B.DEVICE_TYPE = self.old
+
+
+def _fill_args(d_in=320, d_out=256, n_late=2, n_kv=2, hd=64, n_rows=300, n_fill=200):
+    import torch
+    i16, i32 = torch.int16, torch.int32
+    plan = B.Plan(**_shape(d_in=d_in, d_out=d_out, n_late=n_late, n_kv=n_kv, head_dim=hd, n_rows=n_rows,
+                           n_slots=n_rows, max_pos=n_rows))
+    w = n_kv * hd
+    args = dict(
+        x=torch.zeros((n_rows, d_in), dtype=i16), fill_rows_t=torch.zeros(n_fill, dtype=i32), n_fill=n_fill,
+        positions=torch.zeros(n_rows, dtype=i32), slot_of_row=None,
+        map_a=[torch.zeros((d_out, d_in), dtype=i16) for _ in range(n_late)],
+        map_b=[torch.zeros(d_out, dtype=i16) for _ in range(n_late)],
+        gamma=[torch.zeros(d_out, dtype=i16) for _ in range(n_late)],
+        w_k=[torch.zeros((w, d_out), dtype=i16) for _ in range(n_late)],
+        w_v=[torch.zeros((w, d_out), dtype=i16) for _ in range(n_late)], rope=None,
+        k_cache=[torch.zeros((n_rows, w), dtype=i16) for _ in range(n_late)],
+        v_cache=[torch.zeros((n_rows, w), dtype=i16) for _ in range(n_late)],
+        workspace=torch.zeros(256, dtype=torch.uint8),   # too small: the library refuses it
+        stream=0)
+    return plan, args
+
+
+def _bad_fill_cases():
+    import torch
+    i16, i32 = torch.int16, torch.int32
+    return {
+        "x_too_few_rows": lambda a: a.update(x=a["x"][:299]),
+        "x_float32": lambda a: a.update(x=a["x"].float()),
+        "x_strided_columns": lambda a: a.update(x=torch.zeros((300, 640), dtype=i16)[:, ::2]),
+        "x_narrow_rows": lambda a: a.update(x=torch.zeros((300, 256), dtype=i16)),
+        "fill_rows_short": lambda a: a.update(fill_rows_t=a["fill_rows_t"][:199]),
+        "fill_rows_int64": lambda a: a.update(fill_rows_t=a["fill_rows_t"].long()),
+        "n_fill_above_rows": lambda a: a.update(n_fill=301),
+        "positions_short": lambda a: a.update(positions=a["positions"][:299]),
+        "positions_int16": lambda a: a.update(positions=a["positions"].short()),
+        "slots_short": lambda a: a.update(slot_of_row=torch.zeros(299, dtype=i32)),
+        "map_transposed": lambda a: a.update(map_a=[m.t().contiguous() for m in a["map_a"]]),
+        "map_transposed_view": lambda a: a.update(map_a=[torch.zeros((320, 256), dtype=i16).t()] * 2),
+        "map_short": lambda a: a.update(map_a=[m.flatten()[:-1] for m in a["map_a"]]),
+        "map_one_layer_missing": lambda a: a.update(map_a=a["map_a"][:1]),
+        "bias_short": lambda a: a.update(map_b=[b[:255] for b in a["map_b"]]),
+        "gamma_short": lambda a: a.update(gamma=[g[:255] for g in a["gamma"]]),
+        "w_k_short": lambda a: a.update(w_k=[w[:127] for w in a["w_k"]]),
+        "w_v_float": lambda a: a.update(w_v=[w.float() for w in a["w_v"]]),
+        "rope_short": lambda a: a.update(rope=torch.zeros(300 * 64 - 1, dtype=torch.float32)),
+        "k_cache_short": lambda a: a.update(k_cache=[c[:299] for c in a["k_cache"]]),
+        "v_cache_short": lambda a: a.update(v_cache=[c[:299] for c in a["v_cache"]]),
+        "workspace_not_tensor": lambda a: a.update(workspace=1234),
+    }
+
+
+@pytest.mark.parametrize("case", sorted(_bad_fill_cases()))
+def test_binding_rejects_bad_fill_tensors_before_any_call(case):
+    plan, args = _fill_args()
+    _bad_fill_cases()[case](args)
+    with _CpuAsDevice():
+        with pytest.raises(ValueError):
+            B.fill(plan, **args)
+
+
+def test_binding_passes_good_fill_tensors_to_the_library():
+    plan, args = _fill_args()
+    with _CpuAsDevice():
+        with pytest.raises(B.RfError) as e:   # the binding's checks pass; librf refuses the workspace
+            B.fill(plan, **args)
+    assert e.value.status == -4
+
+
+def test_binding_wants_pinned_host_maps_for_a_streaming_plan():
+    import torch
+    plan, args = _fill_args()
+    plan.maps_on_host = True   # (a streaming plan itself needs a GPU for its map buffers)
+    with _CpuAsDevice():
+        with pytest.raises(ValueError, match="pinned"):
+            B.fill(plan, **args)
+
+
+def test_binding_rejects_device_data_on_the_host():
+    plan, args = _fill_args()
+    with pytest.raises(ValueError, match="device memory"):   # CPU tensors where device ones are needed
+        B.fill(plan, **args)
+
+
+def test_binding_rejects_bad_kv_project_and_fill_rows_tensors():
+    import torch
+    plan, args = _fill_args()
+    with _CpuAsDevice():
+        lay = [torch.zeros((300, 256), dtype=torch.int16)] * 2
+        common = dict(positions=args["positions"], slot_of_row=None, gamma=args["gamma"], w_k=args["w_k"],
+                      w_v=args["w_v"], rope=None, k_cache=args["k_cache"], v_cache=args["v_cache"],
+                      workspace=args["workspace"], stream=0)
+        with pytest.raises(ValueError, match="layer_in"):
+            B.kv_project(plan, [t[:299] for t in lay], torch.zeros(10, dtype=torch.int32), 10, **common)
+        with pytest.raises(ValueError, match="rows"):
+            B.kv_project(plan, lay, torch.zeros(9, dtype=torch.int32), 10, **common)
+        with pytest.raises(B.RfError):
+            B.kv_project(plan, lay, torch.zeros(10, dtype=torch.int32), 10, **common)
+        ws = torch.zeros(4096, dtype=torch.uint8)
+        with pytest.raises(ValueError, match="fill_rows_out"):
+            B.fill_rows(plan, torch.zeros(5, dtype=torch.int32), torch.zeros(299, dtype=torch.int32),
+                        torch.zeros(1, dtype=torch.int32), ws, stream=0)
+        with pytest.raises(ValueError, match="exact_rows"):
+            B.fill_rows(plan, torch.zeros(5, dtype=torch.int64), torch.zeros(300, dtype=torch.int32),
+                        torch.zeros(1, dtype=torch.int32), ws, stream=0)
+
+
+def test_ridge_fit_output_is_the_map_the_fill_takes():
+    """rf_ridge_fit returns A_l [d_out][d_in], the paper's orientation
+    (RidgeFill section 2.2, y = A x + b): rounded to bf16 it passes the fill's
+    map contract as it is, while W_l = A_l^T (the row-vector form Y = X W + b)
+    is refused; on a known map the fit recovers A, not its transpose."""
+    import torch
+    d_in, d_out = 320, 256
+    g = np.random.default_rng(5)
+    a_true = g.standard_normal((d_out, d_in)) / np.sqrt(d_in)
+    x = g.standard_normal((1000, d_in))
+    y = x @ a_true.T
+    a, b = B.ridge_fit(x, y, 1e-9)
+    assert a.shape == (d_out, d_in)
+    assert np.max(np.abs(a - a_true)) < 1e-3
+    plan, args = _fill_args(d_in=d_in, d_out=d_out)
+    bf = lambda m: torch.from_numpy(oracle.f64_to_bf16_bits(m.astype(np.float64)).view(np.int16).copy())
+    args["map_a"] = [bf(a)] * 2
+    with _CpuAsDevice():
+        with pytest.raises(B.RfError):    # reaches the library (too small a workspace)
+            B.fill(plan, **args)
+        args["map_a"] = [bf(a.T)] * 2
+        with pytest.raises(ValueError, match=r"\[d_out\]\[d_in\]"):
+            B.fill(plan, **args)
