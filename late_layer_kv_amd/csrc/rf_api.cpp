@@ -155,6 +155,7 @@ rf_status check_shape(const rf_shape* s, int32_t flags) {
   if (!(s->rope_theta > 1.0)) return fail(RF_E_SHAPE, "rope_theta must be > 1");
   if (s->n_rows < 0 || s->n_slots < 0 || s->max_pos < 1)
     return fail(RF_E_SHAPE, "n_rows, n_slots must be >= 0 and max_pos >= 1");
+  if (s->n_rows > rf::kMaxRows) return fail(RF_E_SHAPE, "n_rows=%d above the limit %d", s->n_rows, rf::kMaxRows);
   if (s->n_idx < 0 || s->n_idx > 8) return fail(RF_E_SHAPE, "n_idx=%d must be in [0, 8]", s->n_idx);
   return RF_OK;
 }
@@ -295,8 +296,8 @@ size_t rf_kv_project_workspace_bytes(const rf_plan* p, int32_t g) {
 }
 
 size_t rf_fill_rows_workspace_bytes(int32_t n_rows) {
-  if (n_rows < 0) return 0;
-  return up(static_cast<size_t>(std::max(n_rows, 1)) * 4);
+  if (n_rows < 0 || n_rows > rf::kMaxRows) return 0;
+  return rf::fill_rows_ws_bytes(n_rows);
 }
 
 rf_status rf_rope_table(const rf_plan* p, float* table, void* stream) {
@@ -316,8 +317,8 @@ rf_status rf_fill_rows(rf_plan* p, const int32_t* exact_rows, int32_t n_exact, i
     return fail(RF_E_WORKSPACE, "workspace needs %zu bytes, 256-byte aligned",
                 rf_fill_rows_workspace_bytes(p->s.n_rows));
   Timed tm(p, RF_K_ROWS, static_cast<hipStream_t>(stream));
-  hipError_t e = rf::launch_fill_rows(exact_rows, n_exact, p->s.n_rows, static_cast<int32_t*>(ws), fill_rows,
-                                      n_fill, static_cast<hipStream_t>(stream));
+  hipError_t e = rf::launch_fill_rows(exact_rows, n_exact, p->s.n_rows, ws, fill_rows, n_fill,
+                                      static_cast<hipStream_t>(stream));
   return e == hipSuccess ? RF_OK : hip_fail(e, "fill-row launch");
 }
 

@@ -139,8 +139,14 @@ struct RmsParams {
 hipError_t launch_row_rms(const RmsParams& p, int n_layers, hipStream_t s);
 hipError_t launch_prep(const PrepParams& p, int n_layers, hipStream_t s);
 hipError_t launch_rope_table(float* table, int max_pos, int head_dim, double theta, hipStream_t s);
-hipError_t launch_fill_rows(const int32_t* exact, int n_exact, int n_rows, int32_t* mask,
-                            int32_t* fill_rows, int32_t* n_fill, hipStream_t s);
+// The fill-row set (rf_rows.hip): fill_rows = ascending rows of [0, n_rows)
+// not in exact, *n_fill their count.  ws holds fill_rows_ws_bytes(n_rows)
+// bytes, 256-byte aligned.
+size_t fill_rows_ws_bytes(int n_rows);
+hipError_t launch_fill_rows(const int32_t* exact, int n_exact, int n_rows, void* ws, int32_t* fill_rows,
+                            int32_t* n_fill, hipStream_t s);
+// Largest batch the library takes (row indices and the padded row mask stay in int).
+constexpr int kMaxRows = 1 << 30;
 // Sets bits in *flag: 1 row out of range, 2 position out of range,
 // 4 slot out of range, 8 rows not strictly ascending.
 hipError_t launch_validate(const int32_t* rows, int n, int n_rows, int ascending,

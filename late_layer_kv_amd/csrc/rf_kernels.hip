@@ -758,38 +758,6 @@ __global__ void __launch_bounds__(256) clear_kernel(int32_t* p, int n) {
   if (i < n) p[i] = 0;
 }
 
-__global__ void __launch_bounds__(256) mark_kernel(const int32_t* exact, int n_exact, int32_t* mask, int n_rows) {
-  const int i = blockIdx.x * 256 + threadIdx.x;
-  if (i >= n_exact) return;
-  const int r = exact[i];
-  if (r >= 0 && r < n_rows) mask[r] = 1;
-}
-
-// One workgroup of 1024 threads: thread t owns a contiguous run of rows,
-// counts the unmarked ones, takes an exclusive scan of the counts and writes
-// its rows in order, so the output ascends.
-__global__ void __launch_bounds__(1024) compact_kernel(const int32_t* mask, int n_rows, int32_t* fill_rows,
-                                                       int32_t* n_fill) {
-  __shared__ int part[1024];
-  const int tid = threadIdx.x;
-  const int per = (n_rows + 1023) / 1024;
-  const int r0 = min(n_rows, tid * per), r1 = min(n_rows, r0 + per);
-  int cnt = 0;
-  for (int r = r0; r < r1; ++r) cnt += (mask[r] == 0);
-  part[tid] = cnt;
-  __syncthreads();
-  for (int off = 1; off < 1024; off <<= 1) {
-    const int v = (tid >= off) ? part[tid - off] : 0;
-    __syncthreads();
-    part[tid] += v;
-    __syncthreads();
-  }
-  int o = part[tid] - cnt;
-  for (int r = r0; r < r1; ++r)
-    if (mask[r] == 0) fill_rows[o++] = r;
-  if (tid == 1023) *n_fill = part[1023];
-}
-
 __global__ void __launch_bounds__(256) validate_kernel(const int32_t* rows, int n, int n_rows, int ascending,
                                                        const int32_t* positions, int max_pos,
                                                        const int32_t* slots, int n_slots, int32_t* flag) {
@@ -858,16 +826,6 @@ hipError_t launch_rope_table(float* table, int max_pos, int head_dim, double the
   const int blocks = static_cast<int>((n + 255) / 256);
   hipLaunchKernelGGL(rope_table_kernel, dim3(blocks), dim3(256), 0, s, reinterpret_cast<float2*>(table),
                      max_pos, head_dim, theta);
-  return hipGetLastError();
-}
-
-hipError_t launch_fill_rows(const int32_t* exact, int n_exact, int n_rows, int32_t* mask, int32_t* fill_rows,
-                            int32_t* n_fill, hipStream_t s) {
-  hipLaunchKernelGGL(clear_kernel, dim3((n_rows + 255) / 256 > 0 ? (n_rows + 255) / 256 : 1), dim3(256), 0, s,
-                     mask, n_rows);
-  if (n_exact > 0)
-    hipLaunchKernelGGL(mark_kernel, dim3((n_exact + 255) / 256), dim3(256), 0, s, exact, n_exact, mask, n_rows);
-  hipLaunchKernelGGL(compact_kernel, dim3(1), dim3(1024), 0, s, mask, n_rows, fill_rows, n_fill);
   return hipGetLastError();
 }
 

@@ -122,7 +122,12 @@ def test_workspace_sizes():
     assert p.fill_workspace_bytes(448, 1) == rope + 256 + prep + y + ssq + rs
     assert p.fill_workspace_bytes(448, 2) == rope + 256 + 2 * (prep + y + ssq + rs)
     assert p.kv_project_workspace_bytes(2) == rope + 256 + 2 * prep + 2 * 512 * 4  # + norm factor per plan row
-    assert B.fill_rows_workspace_bytes(1000) == 4096
+    # row mask padded to whole 4,096-row blocks, then two 256-byte-rounded
+    # arrays of per-block counts and offsets
+    assert B.fill_rows_workspace_bytes(1000) == 4096 + 2 * 256
+    assert B.fill_rows_workspace_bytes(122880) == 122880 + 2 * 256
+    assert B.fill_rows_workspace_bytes(0) == 4096 + 2 * 256
+    assert B.fill_rows_workspace_bytes(-1) == 0
     p.close()
 
 
