@@ -132,21 +132,59 @@ def kv_errors(got: np.ndarray, ref: np.ndarray, head_dim: int):
     return float(fro), maxel, inf
 
 
-def check_values(kc, vc, ref: dict, rows: np.ndarray, head_dim: int, slots: np.ndarray = None):
-    """Compare cache rows at slot(rows) with the oracle, per layer, K and V."""
-    sl = rows if slots is None else slots[rows]
-    idx = torch.from_numpy(np.asarray(sl, dtype=np.int64)).to(kc[0].device)
-    worst = {"fro": 0.0, "maxel": 0.0, "inf": 0.0}
-    for l, (rk, rv) in ref.items():
-        for name, cache, r in (("K", kc, rk), ("V", vc, rv)):
-            got = bits_to_f64(cache[l].index_select(0, idx))
-            fro, maxel, inf = kv_errors(got, r, head_dim)
+# Checked-row counts of the full-size parity runs, printed at the end of the
+# test session (tests/conftest.py), so they show under pytest -q as well.
+RECORDS = []
+
+
+class ValueCheck:
+    """The fill's value tolerance over rows given in chunks: per layer and for
+    K and V separately, the Frobenius relative error over every row checked
+    (squared norms accumulated across chunks), the floored max element error
+    and the inf-norm ratio."""
+
+    def __init__(self, head_dim: int):
+        self.hd = head_dim
+        self.acc = {}   # (layer, name) -> [sum d^2, sum r^2, max floored, max |d|, max |r|]
+        self.rows = 0
+
+    def add(self, caches: dict, ref: dict, rows: np.ndarray, slots: np.ndarray = None):
+        """caches: {"K": list, "V": list, ...}; ref: {layer: {name: array [len(rows)][width]}}."""
+        sl = rows if slots is None else slots[rows]
+        idx = torch.from_numpy(np.asarray(sl, dtype=np.int64)).to(next(iter(caches.values()))[0].device)
+        for l, per in ref.items():
+            for name, r in per.items():
+                got = bits_to_f64(caches[name][l].index_select(0, idx))
+                d = got - r
+                n, width = r.shape
+                rh = r.reshape(n, width // self.hd, self.hd)
+                floor = np.maximum(np.abs(rh), np.sqrt(np.mean(rh * rh, axis=2, keepdims=True)))
+                a = self.acc.setdefault((l, name), [0.0, 0.0, 0.0, 0.0, 0.0])
+                a[0] += float(np.sum(d * d))
+                a[1] += float(np.sum(r * r))
+                a[2] = max(a[2], float(np.max(np.abs(d.reshape(rh.shape)) / floor)))
+                a[3] = max(a[3], float(np.max(np.abs(d))))
+                a[4] = max(a[4], float(np.max(np.abs(r))))
+        self.rows += len(rows)
+        return self
+
+    def finish(self):
+        worst = {"fro": 0.0, "maxel": 0.0, "inf": 0.0}
+        for (l, name), (d2, r2, maxel, md, mr) in sorted(self.acc.items()):
+            fro = float(np.sqrt(d2 / r2))
             worst["fro"] = max(worst["fro"], fro)
             worst["maxel"] = max(worst["maxel"], maxel)
-            worst["inf"] = max(worst["inf"], inf)
+            worst["inf"] = max(worst["inf"], md / mr)
             assert fro <= FRO_TOL, f"layer {l} {name}: Frobenius relative error {fro:.3e}"
             assert maxel <= MAXEL_TOL, f"layer {l} {name}: max element error {maxel:.3e}"
-    return worst
+        return worst
+
+
+def check_values(kc, vc, ref: dict, rows: np.ndarray, head_dim: int, slots: np.ndarray = None):
+    """Compare cache rows at slot(rows) with the oracle, per layer, K and V."""
+    chk = ValueCheck(head_dim)
+    chk.add({"K": kc, "V": vc}, {l: {"K": rk, "V": rv} for l, (rk, rv) in ref.items()}, rows, slots)
+    return chk.finish()
 
 
 def check_placement(kc, vc, fill_rows: np.ndarray, n_slots: int, slots: np.ndarray = None, ic=None):
