@@ -469,13 +469,17 @@ def test_traffic_summary_scales_counters_by_the_copy(tmp_path):
                                  ("rf::map_gemm_kernel(rf::MapParams)", 256, 400.0),
                                  ("void rf::kv_gemm_kernel<128, false, false>(rf::KvParams)", 256, 100.0),
                                  ("__amd_rocclr_copyBuffer", 1 << 20, calib / 1024)])
-    t = bench.summarize_pmc(str(fetch), str(write_), "27b_120k", calib)
+    t = bench.summarize_pmc(str(fetch), str(write_), "27b_120k", calib, steps=2)
     assert t["copy_calibration"]["fetch_factor"] == pytest.approx(2.0)
     assert t["copy_calibration"]["write_factor"] == pytest.approx(1.0)
     m = t["kernels"]["map_gemm"]
     assert m["fetch_kib_per_launch"] == pytest.approx(2000.0) and m["write_kib_per_launch"] == pytest.approx(400.0)
     assert t["traffic_bytes_per_launch"] == pytest.approx((2000.0 * 2 + 400.0) * 1024)
     assert t["kernels"]["kv_gemm"]["bytes_per_launch"] == pytest.approx((500.0 * 2 + 100.0) * 1024)
+    # per step: every kernel's bytes over the two profiled steps, the copy left out
+    per_step = ((1000.0 + 3000.0) * 2 + 800.0 + 500.0 * 2 + 100.0) * 1024 / 2
+    assert t["bytes_per_step"] == pytest.approx(per_step)
+    assert set(t["kernels"]) == {"map_gemm", "kv_gemm"}
     assert t["kernel_source_sha256"] == bench.kernel_source_hash()
 
 
@@ -619,3 +623,4 @@ def test_ridge_fit_output_is_the_map_the_fill_takes():
         args["map_a"] = [bf(a.T)] * 2
         with pytest.raises(ValueError, match=r"\[d_out\]\[d_in\]"):
             B.fill(plan, **args)
+
