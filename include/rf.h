@@ -154,6 +154,20 @@ rf_status rf_fill_rows(rf_plan* plan, const int32_t* exact_rows, int32_t n_exact
                        int32_t* fill_rows, int32_t* n_fill,
                        void* workspace, size_t ws_bytes, void* hip_stream);
 
+/* rf_fill_rows for callers that cannot allocate device memory (code under
+ * HIP graph capture, tight serving loops, harnesses that forbid allocation):
+ * the same fill-row set, same arguments without the workspace.  Its scratch
+ * (row mask, block counts and offsets) is a device array owned by the library,
+ * sized for RF_NOALLOC_MAX_ROWS rows (about 1 MiB) and held on each GPU the
+ * library runs on until the process ends; the call allocates nothing.  Plans
+ * with n_rows > RF_NOALLOC_MAX_ROWS get RF_E_SHAPE, before anything is
+ * enqueued.  All calls on one GPU share that array: calls ordered on one
+ * stream are fine (each call clears what it uses with a kernel, no memset),
+ * calls that overlap on one GPU race. */
+#define RF_NOALLOC_MAX_ROWS (1 << 20)
+rf_status rf_fill_rows_noalloc(rf_plan* plan, const int32_t* exact_rows, int32_t n_exact,
+                               int32_t* fill_rows, int32_t* n_fill, void* hip_stream);
+
 /* Value rescale applied by the fill (section 2.3, "Value rescale"; see
  * rf_value_scales below).  With a non-NULL rf_vscale, value head h of filled
  * row r in late layer l is multiplied by

@@ -22,6 +22,7 @@ RF_VALIDATE = 2
 RF_MAPS_Q8 = 4
 RF_RIDGE_RAW = 1
 RF_STREAM_GROUP = 4  # most layers per launch with streamed maps (include/rf.h)
+RF_NOALLOC_MAX_ROWS = 1 << 20  # rows rf_fill_rows_noalloc takes (include/rf.h)
 Q8_BLOCK = 128
 
 STATUS = {0: "RF_OK", -1: "RF_E_ARG", -2: "RF_E_SHAPE", -3: "RF_E_ROWS", -4: "RF_E_WORKSPACE",
@@ -36,7 +37,7 @@ EXPORTS = [
     "rf_fill_q8", "rf_map_dequantize_q8", "rf_map_quantize_q8",
     "rf_value_scales_workspace_bytes", "rf_value_scales", "rf_value_scales_q8",
     "rf_ridge_dev_create", "rf_ridge_dev_add", "rf_ridge_dev_merge", "rf_ridge_dev_destroy", "rf_ridge_acc_sums",
-    "rf_ridge_dev_solve_workspace_bytes", "rf_ridge_dev_solve",
+    "rf_ridge_dev_solve_workspace_bytes", "rf_ridge_dev_solve", "rf_fill_rows_noalloc",
 ]
 
 KERNEL_KINDS = ["map", "kv", "prep", "rope", "rows", "copy", "dequant", "scale", "norm"]
@@ -99,6 +100,7 @@ def lib():
         "rf_rope_table": (i32, [P, P, P]),
         "rf_fill_rows_workspace_bytes": (sz, [i32]),
         "rf_fill_rows": (i32, [P, P, i32, P, P, P, sz, P]),
+        "rf_fill_rows_noalloc": (i32, [P, P, i32, P, P, P]),
         "rf_fill": (i32, [P, P, i64, P, i32, P, P, PP, PP, PP, PP, PP, P, PP, PP, P, P, sz, P]),
         "rf_kv_project": (i32, [P, PP, i64, P, i32, P, P, PP, PP, PP, P, PP, PP, P, P, sz, P]),
         "rf_ridge_acc_create": (i32, [i32, i32, C.POINTER(P)]),
@@ -360,6 +362,18 @@ def fill_rows(plan: Plan, exact_rows, fill_rows_out, n_fill_out, workspace, stre
     _check("rf_fill_rows", lib().rf_fill_rows(plan.handle, _ptr(exact_rows), n_exact, _ptr(fill_rows_out),
                                               _ptr(n_fill_out), _ptr(workspace), workspace.numel() *
                                               workspace.element_size(), _stream(stream)))
+
+
+def fill_rows_noalloc(plan: Plan, exact_rows, fill_rows_out, n_fill_out, stream=None) -> None:
+    """rf_fill_rows_noalloc: rf_fill_rows with the library's own scratch array
+    (no workspace; plans of at most RF_NOALLOC_MAX_ROWS rows)."""
+    n_exact = 0 if exact_rows is None else exact_rows.numel()
+    _arg("rf_fill_rows_noalloc", "exact_rows", exact_rows, ("int32",), 0, optional=True)
+    _arg("rf_fill_rows_noalloc", "fill_rows_out", fill_rows_out, ("int32",), plan.shape.n_rows)
+    _arg("rf_fill_rows_noalloc", "n_fill_out", n_fill_out, ("int32",), 1)
+    _check("rf_fill_rows_noalloc", lib().rf_fill_rows_noalloc(plan.handle, _ptr(exact_rows), n_exact,
+                                                              _ptr(fill_rows_out), _ptr(n_fill_out),
+                                                              _stream(stream)))
 
 
 class _Opts:

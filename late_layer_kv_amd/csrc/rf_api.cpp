@@ -322,6 +322,21 @@ rf_status rf_fill_rows(rf_plan* p, const int32_t* exact_rows, int32_t n_exact, i
   return e == hipSuccess ? RF_OK : hip_fail(e, "fill-row launch");
 }
 
+rf_status rf_fill_rows_noalloc(rf_plan* p, const int32_t* exact_rows, int32_t n_exact, int32_t* fill_rows,
+                               int32_t* n_fill, void* stream) {
+  static_assert(RF_NOALLOC_MAX_ROWS == rf::kNoAllocMaxRows, "header and library agree on the limit");
+  if (!p) return fail(RF_E_ARG, "plan is null");
+  if (n_exact < 0 || (n_exact > 0 && !exact_rows)) return fail(RF_E_ARG, "bad exact rows");
+  if (!fill_rows || !n_fill) return fail(RF_E_ARG, "null output");
+  if (p->s.n_rows > RF_NOALLOC_MAX_ROWS)
+    return fail(RF_E_SHAPE, "rf_fill_rows_noalloc takes at most %d rows (plan has %d); use rf_fill_rows",
+                RF_NOALLOC_MAX_ROWS, p->s.n_rows);
+  Timed tm(p, RF_K_ROWS, static_cast<hipStream_t>(stream));
+  hipError_t e = rf::launch_fill_rows_noalloc(exact_rows, n_exact, p->s.n_rows, fill_rows, n_fill,
+                                              static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? RF_OK : hip_fail(e, "fill-row launch (library scratch)");
+}
+
 }  // extern "C"
 
 namespace {

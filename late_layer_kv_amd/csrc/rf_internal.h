@@ -147,6 +147,11 @@ hipError_t launch_fill_rows(const int32_t* exact, int n_exact, int n_rows, void*
                             int32_t* n_fill, hipStream_t s);
 // Largest batch the library takes (row indices and the padded row mask stay in int).
 constexpr int kMaxRows = 1 << 30;
+// The same with the library's own scratch array (no workspace): at most
+// kNoAllocMaxRows rows (RF_NOALLOC_MAX_ROWS in rf.h).
+constexpr int kNoAllocMaxRows = 1 << 20;
+hipError_t launch_fill_rows_noalloc(const int32_t* exact, int n_exact, int n_rows, int32_t* fill_rows,
+                                    int32_t* n_fill, hipStream_t s);
 // Sets bits in *flag: 1 row out of range, 2 position out of range,
 // 4 slot out of range, 8 rows not strictly ascending.
 hipError_t launch_validate(const int32_t* rows, int n, int n_rows, int ascending,

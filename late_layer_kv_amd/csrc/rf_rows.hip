@@ -19,6 +19,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <mutex>
+
 #include "rf_internal.h"
 
 namespace rf {
@@ -29,7 +31,14 @@ constexpr int kRowsPerThread = 16;
 constexpr int kRowsPerBlock = kRowThreads * kRowsPerThread;  // 4,096 rows per workgroup
 constexpr int kScanThreads = 1024;
 
-size_t round_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
+constexpr size_t round_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
+
+// Workspace of the fill-row set for n_rows rows: the mask padded to whole
+// blocks, then the per-block counts and offsets.
+constexpr size_t ws_bytes_for(int n_rows) {
+  return round_up(round_up(static_cast<size_t>(n_rows > 0 ? n_rows : 1), kRowsPerBlock), 256) +
+         2 * round_up(round_up(static_cast<size_t>(n_rows > 0 ? n_rows : 1), kRowsPerBlock) / kRowsPerBlock * 4, 256);
+}
 
 // Exclusive prefix sum of v over the workgroup (kWaves waves of 64); `total`
 // receives the workgroup's sum.  wave_sums holds kWaves ints of LDS.
@@ -123,11 +132,7 @@ __global__ void __launch_bounds__(kRowThreads) rows_write_kernel(const uint8_t* 
 
 }  // namespace
 
-size_t fill_rows_ws_bytes(int n_rows) {
-  const size_t pad = round_up(static_cast<size_t>(n_rows > 0 ? n_rows : 1), kRowsPerBlock);
-  const size_t blocks = pad / kRowsPerBlock;
-  return round_up(pad, 256) + 2 * round_up(blocks * 4, 256);
-}
+size_t fill_rows_ws_bytes(int n_rows) { return ws_bytes_for(n_rows); }
 
 // Workspace carve: mask [pad] bytes, cnt [blocks] int32, off [blocks] int32.
 hipError_t launch_fill_rows(const int32_t* exact, int n_exact, int n_rows, void* ws, int32_t* fill_rows,
@@ -147,6 +152,49 @@ hipError_t launch_fill_rows(const int32_t* exact, int n_exact, int n_rows, void*
   hipLaunchKernelGGL(rows_scan_kernel, dim3(1), dim3(kScanThreads), 0, s, cnt, blocks, off, n_fill);
   hipLaunchKernelGGL(rows_write_kernel, dim3(blocks), dim3(kRowThreads), 0, s, mask, off, fill_rows);
   return hipGetLastError();
+}
+
+}  // namespace rf
+
+// ---- The fill-row set without allocation ----------------------------------
+// For callers that cannot allocate device memory, the scratch of the
+// fill-row set (mask, block counts, block offsets) can live in this
+// library-owned array instead of a workspace: room for kNoAllocMaxRows rows,
+// about 1 MiB, held on every GPU the library runs on until the process ends.
+// Host code never passes `scratch` itself to a kernel (on the host the name
+// only stands in for the device symbol); it uses the device address that
+// hipGetSymbolAddress returns, looked up once per device with that device
+// current and kept per device.  All calls on one GPU share the array: the
+// clear kernel resets the mask on every call, and calls that overlap on one
+// GPU (unordered streams) race.
+static __device__ __align__(256) uint8_t scratch[rf::ws_bytes_for(rf::kNoAllocMaxRows)];
+
+namespace rf {
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_dev[kMaxDevices] = {};
+}  // namespace
+
+hipError_t launch_fill_rows_noalloc(const int32_t* exact, int n_exact, int n_rows, int32_t* fill_rows,
+                                    int32_t* n_fill, hipStream_t s) {
+  if (n_rows > kNoAllocMaxRows) return hipErrorInvalidValue;  // the caller reports the limit first
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  void* ws = nullptr;
+  {
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_dev[dev]) {
+      void* p = nullptr;
+      e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+      if (e != hipSuccess) return e;
+      g_scratch_dev[dev] = p;
+    }
+    ws = g_scratch_dev[dev];
+  }
+  return launch_fill_rows(exact, n_exact, n_rows, ws, fill_rows, n_fill, s);
 }
 
 }  // namespace rf

@@ -624,3 +624,19 @@ def test_ridge_fit_output_is_the_map_the_fill_takes():
         with pytest.raises(ValueError, match=r"\[d_out\]\[d_in\]"):
             B.fill(plan, **args)
 
+
+def test_fill_rows_noalloc_limit_and_header_constant():
+    """rf_fill_rows_noalloc refuses a plan over RF_NOALLOC_MAX_ROWS rows on the
+    host, before anything is enqueued (no GPU needed to see it)."""
+    hdr = open(os.path.join(ROOT, "include", "rf.h")).read()
+    m = re.search(r"#define RF_NOALLOC_MAX_ROWS \(1 << (\d+)\)", hdr)
+    assert m and (1 << int(m.group(1))) == B.RF_NOALLOC_MAX_ROWS
+    L = B.lib()
+    n = B.RF_NOALLOC_MAX_ROWS + 1
+    p = B.Plan(**_shape(n_rows=n, n_slots=n, max_pos=n))
+    st = L.rf_fill_rows_noalloc(p.handle, None, 0, C.c_void_p(0x10000), C.c_void_p(0x20000), None)
+    assert st == -2 and "at most" in B.last_error()
+    assert L.rf_fill_rows_noalloc(None, None, 0, C.c_void_p(0x10000), C.c_void_p(0x20000), None) == -1
+    q = B.Plan(**_shape())
+    assert L.rf_fill_rows_noalloc(q.handle, None, -1, C.c_void_p(0x10000), C.c_void_p(0x20000), None) == -1
+    assert L.rf_fill_rows_noalloc(q.handle, None, 0, None, C.c_void_p(0x20000), None) == -1
