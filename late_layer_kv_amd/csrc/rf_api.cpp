@@ -118,6 +118,17 @@ int kv_width(const rf_shape& s) { return s.n_kv * s.head_dim; }
 int idx_width(const rf_shape& s) { return s.n_idx * s.head_dim; }
 // prepared-weight rows per layer: keys, values, indexer keys, zero rows up to a whole tile
 int prep_rows(const rf_shape& s) { return (2 * kv_width(s) + idx_width(s) + rf::kTileN - 1) / rf::kTileN * rf::kTileN; }
+// Indexer key columns ending half way into a 256-feature tile (a 128-wide
+// remainder) go to tall tiles of the K/V launch (512 rows x 128 features)
+// instead of a tile that is half zero padding, when every layer input spans
+// less than 4 GiB (those tiles' loads use 32-bit offsets).  Returns the first feature of the
+// remainder, or -1 to let the K/V kernel cover every column.
+int tall_f0(const rf_shape& s, int64_t in_rows, int64_t ld_in) {
+  const int cols = 2 * s.n_kv * s.head_dim + s.n_idx * s.head_dim;
+  if (s.n_idx == 0 || cols % rf::kTileN != 128) return -1;
+  if (in_rows * ld_in * 2 >= (int64_t(1) << 32)) return -1;
+  return cols - 128;
+}
 size_t rope_bytes(const rf_shape& s) { return up(static_cast<size_t>(s.max_pos) * (s.head_dim / 2) * 8); }
 size_t prep_bytes(const rf_shape& s, int g) {
   return up(static_cast<size_t>(g) * prep_rows(s) * s.d_out * 2);
@@ -784,7 +795,8 @@ rf_status fill_impl(rf_plan* p, const char* fn, const uint16_t* x, int64_t ld_x,
   kp.w = w;
   kp.head_dim = s.head_dim;
   kp.tiles_m = mp.tiles_m;
-  kp.tiles_n = prep_rows(s) / rf::kTileN;
+  kp.tall_f0 = tall_f0(s, n_fill, s.d_out);
+  kp.tiles_n = (kp.tall_f0 >= 0 ? kp.tall_f0 : prep_rows(s)) / rf::kTileN;
   kp.wrows = prep_rows(s);
   kp.widx = idx_width(s);
   kp.wkv = prep;
@@ -1060,7 +1072,8 @@ rf_status rf_kv_project(rf_plan* p, const uint16_t* const* layer_in, int64_t ld_
   kp.w = w;
   kp.head_dim = s.head_dim;
   kp.tiles_m = (n + rf::kTileM - 1) / rf::kTileM;
-  kp.tiles_n = prep_rows(s) / rf::kTileN;
+  kp.tall_f0 = tall_f0(s, s.n_rows, ld_in);
+  kp.tiles_n = (kp.tall_f0 >= 0 ? kp.tall_f0 : prep_rows(s)) / rf::kTileN;
   kp.wrows = prep_rows(s);
   kp.widx = idx_width(s);
   kp.wkv = prep;

@@ -50,6 +50,11 @@ struct KvParams {
   int32_t widx;             // indexer key columns (n_idx * head_dim), after the values
   int32_t head_dim;
   int32_t tiles_m, tiles_n;
+  int32_t group_m;          // row tiles per group of the tile order (set by launch_kv)
+  // Indexer remainder: >= 0, the first of 128 features (prepared-weight rows)
+  // that tall tiles of 512 rows compute (tiles_n then stops short of them);
+  // -1: none.  Value-only launches ignore it.
+  int32_t tall_f0;
   int32_t wrows;            // rows per layer of wkv: 2w + widx rounded up to 256
   const uint16_t* wkv;      // [n_layers][wrows][K] prepared weights (zero rows past 2w + widx)
   const int32_t* positions; // [n_rows]

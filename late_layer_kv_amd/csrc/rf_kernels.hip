@@ -101,6 +101,16 @@ __device__ __forceinline__ float sq4(float s, uint32_t lo, uint32_t hi) {
   return __builtin_amdgcn_fdot2_f32_bf16(b, b, s, false);
 }
 
+// RoPE of one (j, j + hd/2) pair of already-scaled values.  The fused form is
+// spelled out: left to contract x1 c - x2 s itself, the compiler may keep
+// either product rounded, and its choice differed between call sites.  Every
+// rotation (key heads, indexer heads in either tile shape) calls this, so a
+// key head and an indexer head with the same weights round identically.
+__device__ __forceinline__ void rotate(float x1, float x2, float co, float si, float& y1, float& y2) {
+  y1 = __builtin_fmaf(x1, co, -(x2 * si));
+  y2 = __builtin_fmaf(x2, co, x1 * si);
+}
+
 // Workgroups are dealt round-robin to the 8 XCDs.  Two renumberings, so that
 // the 32 workgroups an XCD runs at once are consecutive logical tiles (which
 // the tile order below makes share operand strips in that XCD's L2):
@@ -141,6 +151,25 @@ __device__ __forceinline__ TileCoord tile_coord(int t, int tiles_m, int tiles_n)
   const int grp = u / per_group;
   const int first_m = grp * GM;
   const int gsz = min(tiles_m - first_m, GM);
+  const int v = u - grp * per_group;
+  c.tm = first_m + v % gsz;
+  c.tn = v / gsz;
+  return c;
+}
+
+// The same order with the group height chosen at launch (the K/V contraction:
+// 4 row tiles when the launch has 8 or fewer feature tiles per layer that
+// divide 32, so that an XCD's 32 co-running tiles are whole groups; 2 when
+// an indexer head makes it 9, measured 2.5% faster for that launch).
+__device__ __forceinline__ TileCoord tile_coord_rt(int t, int tiles_m, int tiles_n, int gm) {
+  const int per_layer = tiles_m * tiles_n;
+  TileCoord c;
+  c.g = t / per_layer;
+  const int u = t - c.g * per_layer;
+  const int per_group = gm * tiles_n;
+  const int grp = u / per_group;
+  const int first_m = grp * gm;
+  const int gsz = min(tiles_m - first_m, gm);
   const int v = u - grp * per_group;
   c.tm = first_m + v % gsz;
   c.tn = v / gsz;
@@ -212,6 +241,14 @@ __device__ __forceinline__ void mfma16(f32x4& acc, const bf16x8& a, const bf16x8
   asm volatile("v_mfma_f32_16x16x32_bf16 %0, %1, %2, %0" : "+a"(acc) : "v"(a), "v"(b));
 }
 
+// The first MFMA into an accumulator: the addend is the inline constant 0,
+// so the accumulators are never written by vector instructions before the
+// MFMA chain (no zeroing, and no wait states between such writes and the
+// first MFMA that reads them).
+__device__ __forceinline__ void mfma16_first(f32x4& acc, const bf16x8& a, const bf16x8& b) {
+  asm volatile("v_mfma_f32_16x16x32_bf16 %0, %1, %2, 0" : "=a"(acc) : "v"(a), "v"(b));
+}
+
 // One accumulator value read out of its AGPR where it is used.  The compiler
 // otherwise copies all 256 accumulators into VGPRs at the end of the main
 // loop, which leaves the epilogue no registers for its loads.
@@ -228,14 +265,19 @@ __device__ __forceinline__ float agpr(float a) {
 // step reach the texture path at about a third of the rate they do bunched
 // after every second MFMA, and the waves' instruction streams stall less
 // behind a full load queue (both contractions ran 1-2% faster).
-template <bool READ, bool LOAD>
+// With FIRST (the first step of a tile), every MFMA starts its accumulator
+// from 0 (each of the 64 blocks is met exactly once per step).
+template <bool READ, bool LOAD, bool FIRST = false>
 __device__ __forceinline__ void mma_step(const Frags& f, f32x4 (&acc)[8][8], Frags& nf, const char* ws,
                                            const char* xs, int aoff, int boff, const char* const (&src)[8],
                                            size_t kbyte, char* dst) {
 #pragma unroll
   for (int i = 0; i < 64; ++i) {
     const int nb = i >> 3, mb = i & 7;
-    mfma16(acc[nb][mb], f.a[nb], f.b[mb]);
+    if (FIRST)
+      mfma16_first(acc[nb][mb], f.a[nb], f.b[mb]);
+    else
+      mfma16(acc[nb][mb], f.a[nb], f.b[mb]);
     if (READ && i < 8) nf.a[i] = *reinterpret_cast<const bf16x8*>(ws + aoff + i * 16 * kRowBytes);
     if (READ && i >= 8 && i < 16) nf.b[i - 8] = *reinterpret_cast<const bf16x8*>(xs + boff + (i - 8) * 16 * kRowBytes);
     if (LOAD && i >= 16 && (i - 16) % 6 == 0 && i <= 58) {
@@ -256,14 +298,14 @@ __device__ __forceinline__ void mma_step(const Frags& f, f32x4 (&acc)[8][8], Fra
 //          needs u <= 2t+3 landed; u = 2t+4 may still fly).
 // Step 0 reads step 1's fragments from the current slots; after the barrier,
 // step 1 reads the next stage's step-0 fragments.
-template <bool PEND, bool ISSUE, int WAIT>
+template <bool PEND, bool ISSUE, int WAIT, bool FIRST = false>
 __device__ __forceinline__ void stage(Frags& fa, Frags& fb, f32x4 (&acc)[8][8], int& sw, int t,
                                         char* smem, char* mydst, const char* const (&wsrc)[8],
                                         const char* const (&xsrc)[8], const int (&aoff)[2], const int (&boff)[2]) {
   const char* ws = smem + sw * kSlotBytes;
   const char* xs = smem + ring(sw + 1) * kSlotBytes;
-  mma_step<true, PEND>(fa, acc, fb, ws, xs, aoff[1], boff[1], wsrc, static_cast<size_t>(t + 2) * kRowBytes,
-                         mydst + ring(sw + 4) * kSlotBytes);
+  mma_step<true, PEND, FIRST>(fa, acc, fb, ws, xs, aoff[1], boff[1], wsrc, static_cast<size_t>(t + 2) * kRowBytes,
+                                mydst + ring(sw + 4) * kSlotBytes);
   wait_slots(WAIT);
   barrier();
   const int nsw = ring(sw + 2);
@@ -289,15 +331,6 @@ __device__ __forceinline__ void mainloop(const char* const (&wsrc)[8], const cha
     aoff[st] = slot_pos(wn * 128 + r15, 4 * st + q);
     boff[st] = slot_pos(wm * 128 + r15, 4 * st + q);
   }
-#pragma unroll
-  for (int i = 0; i < 8; ++i)
-#pragma unroll
-    for (int j = 0; j < 8; ++j) acc[i][j] = f32x4{};
-  // accumulator writes land before the first MFMA reads them
-  __builtin_amdgcn_sched_barrier(0);
-  asm volatile("s_nop 4" ::: "memory");
-  __builtin_amdgcn_sched_barrier(0);
-
   const int total = 2 * nk;
 #pragma unroll
   for (int u = 0; u < 4; ++u)
@@ -308,15 +341,26 @@ __device__ __forceinline__ void mainloop(const char* const (&wsrc)[8], const cha
   Frags fa, fb;
   int sw = 0;
   read_frags(fa, smem, smem + kSlotBytes, aoff[0], boff[0]);
+  // The first step of the tile (in whichever stage comes first: nk >= 3, 2
+  // or 1) starts the accumulators from 0.
   int t = 0;
-  for (; t + 3 <= nk; ++t) stage<true, true, 1>(fa, fb, acc, sw, t, smem, mydst, wsrc, xsrc, aoff, boff);
+  if (nk >= 3) {
+    stage<true, true, 1, true>(fa, fb, acc, sw, t, smem, mydst, wsrc, xsrc, aoff, boff);
+    for (t = 1; t + 3 <= nk; ++t) stage<true, true, 1>(fa, fb, acc, sw, t, smem, mydst, wsrc, xsrc, aoff, boff);
+  }
   if (t + 2 == nk) {
-    stage<false, false, 0>(fa, fb, acc, sw, t, smem, mydst, wsrc, xsrc, aoff, boff);
+    if (t == 0)
+      stage<false, false, 0, true>(fa, fb, acc, sw, t, smem, mydst, wsrc, xsrc, aoff, boff);
+    else
+      stage<false, false, 0>(fa, fb, acc, sw, t, smem, mydst, wsrc, xsrc, aoff, boff);
     ++t;
   }
   const char* ws = smem + sw * kSlotBytes;
   const char* xs = smem + ring(sw + 1) * kSlotBytes;
-  mma_step<true, false>(fa, acc, fb, ws, xs, aoff[1], boff[1], wsrc, 0, mydst);
+  if (nk == 1)
+    mma_step<true, false, true>(fa, acc, fb, ws, xs, aoff[1], boff[1], wsrc, 0, mydst);
+  else
+    mma_step<true, false>(fa, acc, fb, ws, xs, aoff[1], boff[1], wsrc, 0, mydst);
   mma_step<false, false>(fb, acc, fa, ws, xs, 0, 0, wsrc, 0, mydst);
   // The compiler does not see the MFMAs in the assembly statements: give the
   // last ones the wait states an MFMA result needs before other instructions
@@ -471,6 +515,253 @@ __global__ void __launch_bounds__(256) row_rms_kernel(const RmsParams p) {
   if (lane == 0) p.rs[static_cast<size_t>(g) * p.M + m] = rsqrtf(total * p.inv_k + p.eps);
 }
 
+// ---- Indexer-key remainder: a "tall" tile of 128 features x 512 rows --------
+// When the indexer key columns end half way into a 256-feature tile (one
+// 128-wide head, or an odd count of them), that tile would be half zero
+// padding.  A tall tile of kv_gemm_kernel's launch computes those 128
+// features alone, for the 512 rows of two row tiles: each of the 4 waves owns
+// 128 features x 128 rows (the same 8x8 blocks of v_mfma_f32_16x16x32_bf16 and lane layout as the
+// main loop), all waves share the weight fragments.  LDS holds two buffers of
+// one 64-column stage each: 128 weight rows (16 KB) then 512 data rows
+// (64 KB), rows of 128 bytes with the main loop's chunk swizzle.  Stage t+2's
+// loads go into stage t's buffer once every wave is past the barrier that
+// ends the reads of it, so one stage of loads is always in flight.
+constexpr int kTallRows = 512;
+constexpr int kTallA = 128 * kRowBytes;               // 16 KB of weight rows
+constexpr int kTallBuf = kTallA + kTallRows * kRowBytes;  // 80 KB per stage buffer
+constexpr int kTallLoads = 20;                        // per wave per stage: 4 weight + 16 data
+constexpr int kTallStageRow = 128 * 2;                // 256 B per staged output row
+constexpr int kTallSlotOffset = kTallRows * kTallStageRow;  // 128 KB, then 512 int32 slot ids
+static_assert(2 * kTallBuf <= kLdsBytes && kTallSlotOffset + kTallRows * 4 <= 2 * kTallBuf, "tall tile LDS");
+
+__device__ __forceinline__ void tall_wait(int slots) {
+  if (slots == 0)
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  else
+    asm volatile("s_waitcnt vmcnt(20)" ::: "memory");
+}
+static_assert(kTallLoads == 20, "tall_wait immediates assume 20 loads per stage");
+
+// Where the 20 loads of a stage read: a uniform base per operand (the layer's
+// prepared weights, its input rows) plus a 32-bit byte offset per lane and
+// load, so the loads take one VGPR of address each (the host uses this kernel
+// only when every layer input spans less than 4 GiB).
+struct TallSrc {
+  const char* wbase;
+  const char* xbase;
+  uint32_t off[kTallLoads];
+};
+
+// The 20 loads of one stage for this wave into buffer `buf`: j < 4 weight rows
+// 32 w + 8 j + i / 8, j >= 4 data rows 128 w + 8 (j - 4) + i / 8 (lane i lands
+// at position i % 8 of its row).
+__device__ __forceinline__ void tall_load(int j, const TallSrc& src, size_t kbyte, char* buf, int wave) {
+  char* dst = j < 4 ? buf + (32 * wave + 8 * j) * kRowBytes
+                    : buf + kTallA + (128 * wave + 8 * (j - 4)) * kRowBytes;
+  const char* base = (j < 4 ? src.wbase : src.xbase) + kbyte;
+  __builtin_amdgcn_global_load_lds((gbl_ptr_t*)(base + src.off[j]), (lds_ptr_t*)dst, 16, 0, 0);
+}
+
+// One 32-column step on fragments f from buffer `cur`; READ: the 16 fragment
+// reads of the next step (from `nbuf` at offsets aoff / boff) follow MFMAs
+// 0..15; LOAD: the 20 loads of a stage (into `lbuf`) follow MFMAs 4, 7, ..., 61.
+template <bool READ, bool LOAD, bool FIRST>
+__device__ __forceinline__ void tall_step(const Frags& f, f32x4 (&acc)[8][8], Frags& nf, const char* nbuf, int aoff,
+                                          int boff, const TallSrc& src, size_t kbyte, char* lbuf, int wave) {
+#pragma unroll
+  for (int i = 0; i < 64; ++i) {
+    const int nb = i >> 3, mb = i & 7;
+    if (FIRST)
+      mfma16_first(acc[nb][mb], f.a[nb], f.b[mb]);
+    else
+      mfma16(acc[nb][mb], f.a[nb], f.b[mb]);
+    if (READ && i < 8) nf.a[i] = *reinterpret_cast<const bf16x8*>(nbuf + aoff + i * 16 * kRowBytes);
+    if (READ && i >= 8 && i < 16)
+      nf.b[i - 8] = *reinterpret_cast<const bf16x8*>(nbuf + kTallA + boff + (i - 8) * 16 * kRowBytes);
+    if (LOAD && i >= 4 && (i - 4) % 3 == 0 && i <= 61) tall_load((i - 4) / 3, src, kbyte, lbuf, wave);
+  }
+}
+
+// Stage t from buffer t % 2: step 0 reads step 1's fragments from the same
+// buffer; the wave's loads of stage t+1 have landed (vmcnt) and the barrier
+// publishes them and ends every read of buffer t % 2; step 1 reads stage
+// t+1's first fragments and loads stage t+2 into buffer t % 2.
+template <bool NEXT, bool LOAD, bool FIRST>
+__device__ __forceinline__ void tall_stage(Frags& fa, Frags& fb, f32x4 (&acc)[8][8], int t, char* smem,
+                                           const TallSrc& src, const int (&aoff)[2], const int (&boff)[2], int wave) {
+  char* cur = smem + (t & 1) * kTallBuf;
+  char* nxt = smem + ((t + 1) & 1) * kTallBuf;
+  tall_step<true, false, FIRST>(fa, acc, fb, cur, aoff[1], boff[1], src, 0, cur, wave);
+  if (NEXT) {
+    tall_wait(0);
+    barrier();
+  }
+  tall_step<NEXT, LOAD, false>(fb, acc, fa, nxt, aoff[0], boff[0], src, static_cast<size_t>(t + 2) * kRowBytes, cur,
+                               wave);
+}
+
+// One tall tile: layer g, rows m0 .. m0 + 511 of the call, features
+// [tall_f0, tall_f0 + 128) of the prepared weights; smem is the workgroup's LDS.
+template <int HD>
+__device__ __forceinline__ void tall_tile(const KvParams& p, int g, int m0, char* smem) {
+  int* const slot_of = reinterpret_cast<int*>(smem + kTallSlotOffset);
+  const int f0 = p.tall_f0;  // first prepared-weight row (feature) of the tile
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int r15 = lane & 15, q = lane >> 4;
+
+  TallSrc src;
+  src.wbase = reinterpret_cast<const char*>(p.wkv + static_cast<size_t>(g) * p.wrows * p.K);
+  src.xbase = reinterpret_cast<const char*>(p.in[g]);
+#pragma unroll
+  for (int j = 0; j < kTallLoads; ++j) {
+    const int chunk = load_chunk(lane, j);
+    if (j < 4) {
+      const int lr = 32 * wave + 8 * j + (lane >> 3);
+      src.off[j] = static_cast<uint32_t>((static_cast<size_t>(f0 + lr) * p.K + chunk * 8) * 2);
+    } else {
+      const int lr = 128 * wave + 8 * (j - 4) + (lane >> 3);
+      const int m = min(m0 + lr, p.M - 1);
+      int row = p.in_rows ? p.in_rows[m] : m;
+      row = (row >= 0 && row < p.n_in_rows) ? row : 0;
+      src.off[j] = static_cast<uint32_t>((static_cast<size_t>(row) * p.ld_in + chunk * 8) * 2);
+    }
+  }
+
+  // fragment offsets: weight rows 16 nb + r15 (shared), data rows 128 w + 16 mb + r15
+  int aoff[2], boff[2];
+#pragma unroll
+  for (int st = 0; st < 2; ++st) {
+    aoff[st] = slot_pos(r15, 4 * st + q);
+    boff[st] = slot_pos(wave * 128 + r15, 4 * st + q);
+  }
+  f32x4 acc[8][8];
+  const int nk = p.K / kBK;
+#pragma unroll
+  for (int j = 0; j < kTallLoads; ++j) tall_load(j, src, 0, smem, wave);
+  if (nk > 1) {
+#pragma unroll
+    for (int j = 0; j < kTallLoads; ++j) tall_load(j, src, kRowBytes, smem + kTallBuf, wave);
+    tall_wait(1);
+  } else {
+    tall_wait(0);
+  }
+  barrier();
+  Frags fa, fb;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) fa.a[i] = *reinterpret_cast<const bf16x8*>(smem + aoff[0] + i * 16 * kRowBytes);
+#pragma unroll
+  for (int i = 0; i < 8; ++i) fa.b[i] = *reinterpret_cast<const bf16x8*>(smem + kTallA + boff[0] + i * 16 * kRowBytes);
+  // stage 0 starts the accumulators from 0; stages t <= nk-3 load stage t+2
+  if (nk >= 3) {
+    tall_stage<true, true, true>(fa, fb, acc, 0, smem, src, aoff, boff, wave);
+    for (int t = 1; t + 3 <= nk; ++t) tall_stage<true, true, false>(fa, fb, acc, t, smem, src, aoff, boff, wave);
+    tall_stage<true, false, false>(fa, fb, acc, nk - 2, smem, src, aoff, boff, wave);
+    tall_stage<false, false, false>(fa, fb, acc, nk - 1, smem, src, aoff, boff, wave);
+  } else if (nk == 2) {
+    tall_stage<true, false, true>(fa, fb, acc, 0, smem, src, aoff, boff, wave);
+    tall_stage<false, false, false>(fa, fb, acc, 1, smem, src, aoff, boff, wave);
+  } else {
+    tall_stage<false, false, true>(fa, fb, acc, 0, smem, src, aoff, boff, wave);
+  }
+  // the accumulators are read only after the wait states an MFMA result needs
+  __builtin_amdgcn_sched_barrier(0);
+  asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory");
+  __builtin_amdgcn_sched_barrier(0);
+
+  // row bookkeeping as in kv_gemm_kernel: bad rows get slot -1 and are not stored
+  int orow[8], pos[8], slot_r[8];
+  float rs[8];
+#pragma unroll
+  for (int mb = 0; mb < 8; ++mb) {
+    const int m = min(m0 + wave * 128 + mb * 16 + r15, p.M - 1);
+    orow[mb] = p.out_rows ? p.out_rows[m] : m;
+    rs[mb] = p.rs[g][m];
+  }
+#pragma unroll
+  for (int mb = 0; mb < 8; ++mb) {
+    const int r = orow[mb];
+    const bool ok = (m0 + wave * 128 + mb * 16 + r15 < p.M) & (r >= 0) & (r < p.n_rows);
+    orow[mb] = ok ? r : 0;
+    slot_r[mb] = ok ? 0 : -1;
+  }
+#pragma unroll
+  for (int mb = 0; mb < 8; ++mb) pos[mb] = p.positions[orow[mb]];
+  if (p.slots) {
+#pragma unroll
+    for (int mb = 0; mb < 8; ++mb) slot_r[mb] = slot_r[mb] < 0 ? -1 : p.slots[orow[mb]];
+  } else {
+#pragma unroll
+    for (int mb = 0; mb < 8; ++mb) slot_r[mb] = slot_r[mb] < 0 ? -1 : orow[mb];
+  }
+#pragma unroll
+  for (int mb = 0; mb < 8; ++mb) {
+    const bool good = (slot_r[mb] >= 0) & (pos[mb] >= 0) & (pos[mb] < p.max_pos) & (slot_r[mb] < p.n_slots);
+    slot_r[mb] = good ? slot_r[mb] : -1;
+    pos[mb] = good ? pos[mb] : 0;
+  }
+  __builtin_amdgcn_sched_barrier(0);
+  __syncthreads();  // every wave is done with the operand buffers
+  if (q == 0) {
+#pragma unroll
+    for (int mb = 0; mb < 8; ++mb) slot_of[wave * 128 + mb * 16 + r15] = slot_r[mb];
+  }
+  // RoPE over the 128 features (one head of 128 or two of 64), scaled by the
+  // row's norm factor, rounded, staged: row r of 256 bytes, 16-byte chunk c
+  // at position c ^ (r & 15).
+  constexpr int half = HD / 2;
+  constexpr int pstep = half / 16;
+  const float2* tab = reinterpret_cast<const float2*>(p.rope);
+  auto stage4 = [&](int nb, int mb, float v0, float v1, float v2, float v3) {
+    const int row = wave * 128 + mb * 16 + r15;
+    const int chunk = nb * 2 + (q >> 1);
+    uint2 o;
+    o.x = pack_bf16x2(v0, v1);
+    o.y = pack_bf16x2(v2, v3);
+    *reinterpret_cast<uint2*>(smem + row * kTallStageRow + ((chunk ^ (row & 15)) << 4) + (q & 1) * 8) = o;
+  };
+#pragma unroll
+  for (int nb = 0; nb < 8; ++nb) {
+    const int jb = (nb * 16) & (HD - 1);
+    if (jb >= half) continue;
+    const int nb2 = nb + pstep;
+    float4 cs[8][2];
+#pragma unroll
+    for (int mb = 0; mb < 8; ++mb) {
+      const float2* trow = tab + static_cast<size_t>(pos[mb]) * half + jb + q * 4;
+      cs[mb][0] = *reinterpret_cast<const float4*>(trow);
+      cs[mb][1] = *reinterpret_cast<const float4*>(trow + 2);
+    }
+#pragma unroll
+    for (int mb = 0; mb < 8; ++mb) {
+      const float c4[8] = {cs[mb][0].x, cs[mb][0].y, cs[mb][0].z, cs[mb][0].w,
+                           cs[mb][1].x, cs[mb][1].y, cs[mb][1].z, cs[mb][1].w};
+      float y1[4], y2[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float x1 = agpr(acc[nb][mb][i]) * rs[mb];
+        const float x2 = agpr(acc[nb2][mb][i]) * rs[mb];
+        rotate(x1, x2, c4[2 * i], c4[2 * i + 1], y1[i], y2[i]);
+      }
+      stage4(nb, mb, y1[0], y1[1], y1[2], y1[3]);
+      stage4(nb2, mb, y2[0], y2[1], y2[2], y2[3]);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  __syncthreads();
+  const int chunk = threadIdx.x & 15;
+  uint16_t* dst_base = p.ic[g] + (f0 - 2 * p.w) + chunk * 8;
+#pragma unroll 4
+  for (int it = 0; it < kTallRows / 16; ++it) {
+    const int row = it * 16 + (threadIdx.x >> 4);
+    const int slot = slot_of[row];
+    if (slot >= 0) {
+      const uint4 v = *reinterpret_cast<const uint4*>(smem + row * kTallStageRow + ((chunk ^ (row & 15)) << 4));
+      *reinterpret_cast<uint4*>(dst_base + static_cast<size_t>(slot) * p.widx) = v;
+    }
+  }
+}
+
 // VSCALE: the value rescale is applied; QK: keys are RMS-normalised per head
 // with a per-dimension gain before RoPE.  Each option is its own
 // instantiation, so the plain fill's epilogue keeps its register budget.
@@ -479,7 +770,30 @@ __global__ void __launch_bounds__(kThreads) kv_gemm_kernel(const KvParams p) {
   __shared__ __attribute__((aligned(1024))) char smem[kLdsBytes];
   int* const slot_of = reinterpret_cast<int*>(smem + kSlotOffset);
   const int t = xcd_remap_contiguous(blockIdx.x, gridDim.x);
-  const TileCoord c = tile_coord<4>(t, p.tiles_m, p.tiles_n);
+  TileCoord c;
+  if (p.tall_f0 >= 0) {
+    // Each group of (up to) two row tiles is one tall tile of the indexer
+    // remainder, then its tiles_n regular tiles; the tall tile's rows are the
+    // ones the group's regular tiles read at the same time, so its loads of
+    // them mostly hit L2.
+    const int full = p.tiles_m / 2;
+    const int per_group = 2 * p.tiles_n + 1;
+    const int per_layer = p.tiles_m * p.tiles_n + (p.tiles_m + 1) / 2;
+    const int g = t / per_layer;
+    const int u = t - g * per_layer;
+    const int grp = u < full * per_group ? u / per_group : full;
+    const int v = u - grp * per_group;
+    const int gsz = min(p.tiles_m - 2 * grp, 2);
+    if (v == 0) {
+      tall_tile<HD>(p, g, grp * 2 * kTileM, smem);
+      return;
+    }
+    c.g = g;
+    c.tm = 2 * grp + (v - 1) % gsz;
+    c.tn = (v - 1) / gsz;
+  } else {
+    c = tile_coord_rt(t, p.tiles_m, p.tiles_n, p.group_m);
+  }
   const int m0 = c.tm * kTileM, n0 = c.tn * kTileN + (p.v_only ? p.w / kTileN * kTileN : 0);
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
@@ -670,9 +984,7 @@ __global__ void __launch_bounds__(kThreads) kv_gemm_kernel(const KvParams p) {
         for (int i = 0; i < 4; ++i) {
           const float x1 = agpr(acc[nb][mb][i]) * kf[mb][h] * g1[i];
           const float x2 = agpr(acc[nb2][mb][i]) * kf[mb][h] * g2[i];
-          const float co = c4[2 * i], si = c4[2 * i + 1];
-          y1[i] = x1 * co - x2 * si;
-          y2[i] = x2 * co + x1 * si;
+          rotate(x1, x2, c4[2 * i], c4[2 * i + 1], y1[i], y2[i]);
         }
         stage4(nb, mb, y1[0], y1[1], y1[2], y1[3]);
         stage4(nb2, mb, y2[0], y2[1], y2[2], y2[3]);
@@ -798,8 +1110,13 @@ hipError_t launch_row_rms(const RmsParams& p, int n_layers, hipStream_t s) {
   return hipGetLastError();
 }
 
-hipError_t launch_kv(const KvParams& p, int n_layers, hipStream_t s) {
-  const int grid = n_layers * p.tiles_m * p.tiles_n;
+hipError_t launch_kv(const KvParams& p_in, int n_layers, hipStream_t s) {
+  KvParams p = p_in;
+  p.group_m = (p.tiles_n * 4 <= 32 && 32 % p.tiles_n == 0) ? 4 : 2;
+  // tall tiles only for indexer columns past the keys and values (a value-
+  // initialised KvParams has tall_f0 = 0, which means none)
+  if (p.v_only || p.widx == 0 || p.tall_f0 < 2 * p.w) p.tall_f0 = -1;
+  const int grid = n_layers * (p.tiles_m * p.tiles_n + (p.tall_f0 >= 0 ? (p.tiles_m + 1) / 2 : 0));
   const int variant = (p.head_dim == 128 ? 4 : 0) | (p.group_of_row ? 2 : 0) | (p.qk_norm ? 1 : 0);
   switch (variant) {
     case 0: hipLaunchKernelGGL((kv_gemm_kernel<64, false, false>), dim3(grid), dim3(kThreads), 0, s, p); break;

@@ -29,6 +29,12 @@ CASES = {
                                         map_format="q8", qk_norm=True, idx_heads=1, seed=63),
     "ragged_host_idx": workloads.spec("8b_ragged_host", n_late=2, prompt_lens=(300, 257, 129, 64), tail=50,
                                       idx_heads=2, seed=64),
+    # the indexer columns end half way into a 256-feature tile: those 128
+    # features go to the 512-row tall kernel (heads of 64: two heads; heads of
+    # 128: a whole indexer tile plus the remainder, three tall tiles, the last
+    # one ragged)
+    "tiny_idx2_tall": workloads.spec("tiny", idx_heads=2, seed=65),
+    "8b_mid_idx3_tall": workloads.spec("8b", n_late=2, prompt_lens=(1500,), tail=60, idx_heads=3, seed=66),
 }
 
 _cache = {}
@@ -60,7 +66,7 @@ def test_indexer_fill_matches_oracle(name):
     _say(f"[idx fill] {name} indexer worst {worst}")
 
 
-@pytest.mark.parametrize("name", ["tiny_idx", "8b_mid_idx", "27b_mid_q8_qk_idx"])
+@pytest.mark.parametrize("name", ["tiny_idx", "8b_mid_idx", "27b_mid_q8_qk_idx", "8b_mid_idx3_tall"])
 def test_indexer_heads_leave_kv_unchanged(name):
     """The extra columns change nothing else: K and V are bitwise those of the
     same fill on a plan without indexer heads."""
@@ -80,7 +86,7 @@ def test_indexer_heads_leave_kv_unchanged(name):
         assert torch.equal(k1[l], k2[l]) and torch.equal(v1[l], v2[l]), f"layer {l}"
 
 
-@pytest.mark.parametrize("name", ["tiny_idx", "8b_mid_idx"])
+@pytest.mark.parametrize("name", ["tiny_idx", "8b_mid_idx", "tiny_idx2_tall", "8b_mid_idx3_tall"])
 def test_indexer_head_with_key_weights_equals_key_head(name):
     """An indexer head given the first key head's weights (layers without
     QK-norm) stores exactly that key head."""
@@ -100,7 +106,7 @@ def test_indexer_head_with_key_weights_equals_key_head(name):
             assert torch.equal(ic[l].index_select(0, f)[:, h * hd:(h + 1) * hd], k0), f"layer {l} head {h}"
 
 
-@pytest.mark.parametrize("name", ["tiny_idx3", "8b_mid_idx"])
+@pytest.mark.parametrize("name", ["tiny_idx3", "8b_mid_idx", "tiny_idx2_tall", "8b_mid_idx3_tall"])
 def test_indexer_identity_fill_equals_exact_projection(name):
     """Identity maps give the exact-row path's bytes, indexer keys included,
     and those match the oracle's exact indexer keys."""
@@ -120,10 +126,11 @@ def test_indexer_identity_fill_equals_exact_projection(name):
     U.check_indexer_values(i2, oracle.exact_indexer_workload(w, w.x, f), f, s.head_dim)
 
 
-def test_indexer_grouping_and_streaming_are_bitwise_neutral():
+@pytest.mark.parametrize("name", ["ragged_host_idx", "8b_mid_idx3_tall"])
+def test_indexer_grouping_and_streaming_are_bitwise_neutral(name):
     """One layer per launch, all layers per launch and streamed maps give the
     same indexer bytes."""
-    w = _workload("ragged_host_idx")
+    w = _workload(name)
     s = w.spec
     _say("[idx grouping]")
     dev = U.DeviceInputs(w, maps_on_host=False)
