@@ -107,6 +107,8 @@ def summarize_pmc(fetch_csv: str, write_csv: str, name: str, calib_bytes: int, s
     process ran `steps` steps)."""
     import csv
 
+    lib_kernels = set()
+
     def per_kernel(path, counter):
         sums, n, copy = {}, {}, []
         for r in csv.DictReader(open(path)):
@@ -117,6 +119,8 @@ def summarize_pmc(fetch_csv: str, write_csv: str, name: str, calib_bytes: int, s
                 copy.append((int(r["Grid_Size"]), v))
                 continue
             kk = _short_kernel(k)
+            if "rf::" in k:
+                lib_kernels.add(kk)
             sums[kk] = sums.get(kk, 0.0) + v
             n[kk] = n.get(kk, 0) + 1
         return sums, n, (max(copy)[1] if copy else None)
@@ -138,7 +142,11 @@ def summarize_pmc(fetch_csv: str, write_csv: str, name: str, calib_bytes: int, s
            "copy_calibration": {"bytes": calib_bytes, "fetch_kib": fc, "write_kib": wc,
                                 "fetch_factor": kf, "write_factor": kw},
            "kernels": kernels,
-           "bytes_per_step": sum(v["bytes_per_step"] for v in kernels.values()),
+           # the library's kernels launched every step (not the RoPE table a plan
+           # builds once, nor the profiled process's own torch kernels)
+           "bytes_per_step": sum(v["bytes_per_step"] for k, v in kernels.items()
+                                 if k in lib_kernels and v["dispatches"] >= steps),
+           "counted_per_step": sorted(k for k, v in kernels.items() if k in lib_kernels and v["dispatches"] >= steps),
            "source": {"FETCH_SIZE": cmd.format(c="FETCH_SIZE", d="fetch"),
                       "WRITE_SIZE": cmd.format(c="WRITE_SIZE", d="write"),
                       "summary": (f"python bench.py --workload {name} --pmc-summary "
@@ -461,8 +469,8 @@ def run_workload(name, args, headline: bool) -> dict:
         res["hbm"] = {"bytes_per_step": hbm, "gbs": hbm / (ms * 1e-3) / 1e9, "peak": PEAK_HBM_GBS,
                       "frac": hbm / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS,
                       "source": os.path.relpath(traffic_path(name), ROOT),
-                      "note": "FETCH_SIZE + WRITE_SIZE of every kernel of a step, copy-calibrated, "
-                              "over the step time measured here"}
+                      "note": "copy-calibrated FETCH_SIZE + WRITE_SIZE of the library's kernels of one step "
+                              "(what the L2 moves to and from the MALL or HBM), over the step time measured here"}
     if q8 and prof["dequant"][1]:
         dq_ms, dq_n = prof["dequant"]
         layers_per_dq = s.n_late * args.steps / dq_n

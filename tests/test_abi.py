@@ -461,13 +461,19 @@ def test_traffic_summary_scales_counters_by_the_copy(tmp_path):
     calib = 4 << 30
     fetch, write_ = tmp_path / "fetch.csv", tmp_path / "write.csv"
     # two map launches, one K/V launch and the calibration copy (which reads half what it moves)
+    kv = "void rf::kv_gemm_kernel<128, false, false>(rf::KvParams)"
+    torch_fill = "void at::native::vectorized_elementwise_kernel<4, at::native::FillFunctor<short>>(int, ...)"
     write(fetch, "FETCH_SIZE", [("rf::map_gemm_kernel(rf::MapParams)", 256, 1000.0),
                                 ("rf::map_gemm_kernel(rf::MapParams)", 256, 3000.0),
-                                ("void rf::kv_gemm_kernel<128, false, false>(rf::KvParams)", 256, 500.0),
+                                (kv, 256, 500.0), (kv, 256, 500.0),
+                                ("rf::rope_table_kernel(float2*, int, int, double)", 64, 90.0),
+                                (torch_fill, 4096, 77.0),
                                 ("__amd_rocclr_copyBuffer", 1 << 20, calib / 1024 / 2)])
     write(write_, "WRITE_SIZE", [("rf::map_gemm_kernel(rf::MapParams)", 256, 400.0),
                                  ("rf::map_gemm_kernel(rf::MapParams)", 256, 400.0),
-                                 ("void rf::kv_gemm_kernel<128, false, false>(rf::KvParams)", 256, 100.0),
+                                 (kv, 256, 100.0), (kv, 256, 100.0),
+                                 ("rf::rope_table_kernel(float2*, int, int, double)", 64, 900.0),
+                                 (torch_fill, 4096, 7777.0),
                                  ("__amd_rocclr_copyBuffer", 1 << 20, calib / 1024)])
     t = bench.summarize_pmc(str(fetch), str(write_), "27b_120k", calib, steps=2)
     assert t["copy_calibration"]["fetch_factor"] == pytest.approx(2.0)
@@ -476,10 +482,12 @@ def test_traffic_summary_scales_counters_by_the_copy(tmp_path):
     assert m["fetch_kib_per_launch"] == pytest.approx(2000.0) and m["write_kib_per_launch"] == pytest.approx(400.0)
     assert t["traffic_bytes_per_launch"] == pytest.approx((2000.0 * 2 + 400.0) * 1024)
     assert t["kernels"]["kv_gemm"]["bytes_per_launch"] == pytest.approx((500.0 * 2 + 100.0) * 1024)
-    # per step: every kernel's bytes over the two profiled steps, the copy left out
-    per_step = ((1000.0 + 3000.0) * 2 + 800.0 + 500.0 * 2 + 100.0) * 1024 / 2
+    # per step: the library kernels launched every step, over the two profiled
+    # steps; the copy, the once-per-plan RoPE table and torch's kernels left out
+    per_step = ((1000.0 + 3000.0) * 2 + 800.0 + (500.0 * 2 + 100.0) * 2) * 1024 / 2
     assert t["bytes_per_step"] == pytest.approx(per_step)
-    assert set(t["kernels"]) == {"map_gemm", "kv_gemm"}
+    assert set(t["kernels"]) == {"map_gemm", "kv_gemm", "rope_table", "vectorized_elementwise"}
+    assert t["counted_per_step"] == ["kv_gemm", "map_gemm"]
     assert t["kernel_source_sha256"] == bench.kernel_source_hash()
 
 
