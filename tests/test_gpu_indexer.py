@@ -142,3 +142,54 @@ def test_indexer_grouping_and_streaming_are_bitwise_neutral(name):
     _, _, i3 = U.gpu_fill(U.plan_for(w, maps_on_host=True), host, rows, n)
     for l in range(s.n_late):
         assert torch.equal(i1[l], i2[l]) and torch.equal(i1[l], i3[l]), f"layer {l}"
+
+
+def _tall_case(n_rows, tail, seed):
+    # d = 512 keeps the oracle cheap; 8 kv heads of 128 and one indexer head
+    # make 2176 columns: 8 regular feature tiles and a 128-wide remainder,
+    # which takes the tall tiles of 512 rows
+    return workloads.spec("8b", d_in=512, d_out=512, n_late=2, prompt_lens=(n_rows,), tail=tail, idx_heads=1,
+                          seed=seed)
+
+
+@pytest.mark.parametrize("n_fill", [1, 511, 512, 513])
+def test_tall_tiles_around_their_512_row_edge(n_fill):
+    """One row, and fills that end one row before, on and after a tall tile."""
+    s = _tall_case(n_fill + 64, 64, 70 + n_fill % 97)
+    w = workloads.make(s)
+    _say(f"[tall edge] {n_fill} rows")
+    di = U.DeviceInputs(w)
+    plan = U.plan_for(w)
+    rows, n = U.gpu_fill_rows(plan, di)
+    assert n == n_fill
+    kc, vc, ic = U.gpu_fill(plan, di, rows, n)
+    f = rows.cpu().numpy()
+    U.check_placement(kc, vc, f, s.n_rows, ic=ic)
+    U.check_values(kc, vc, oracle.fill_workload(w, rows=f), f, s.head_dim)
+    U.check_indexer_values(ic, oracle.fill_indexer_workload(w, rows=f), f, s.head_dim)
+
+
+def test_tall_tiles_with_a_slot_map_and_skipped_rows():
+    """Tall tiles store at slot(row) under a scattered slot map into a cache
+    of twice as many slots, and skip rows whose slot is out of range, like
+    the regular tiles do."""
+    s = _tall_case(1500, 60, 77)
+    w = workloads.make(s)
+    _say("[tall slots]")
+    di = U.DeviceInputs(w)
+    n_slots = 2 * s.n_rows
+    plan = B.Plan(s.d_in, s.d_out, s.n_late, s.n_kv, s.head_dim, s.rms_eps, s.rope_theta, s.n_rows, n_slots,
+                  s.max_pos, n_idx=s.idx_heads)
+    rows, n = U.gpu_fill_rows(plan, di)
+    f = rows.cpu().numpy()
+    slots = np.random.default_rng(7).permutation(n_slots)[: s.n_rows].astype(np.int32)
+    bad = f[::37]
+    slots[bad] = n_slots + 5          # out of range: these rows are not stored
+    mk = lambda width: [torch.full((n_slots, width), U.CANARY, dtype=torch.int16, device="cuda:0")
+                        for _ in range(s.n_late)]
+    kc, vc, ic = U.gpu_fill(plan, di, rows, n, caches=(mk(s.kv_width), mk(s.kv_width)),
+                            idx_caches=mk(s.idx_heads * s.head_dim), slots=U.i32(slots).cuda())
+    kept = np.setdiff1d(f, bad)
+    U.check_placement(kc, vc, kept, n_slots, slots=slots, ic=ic)
+    U.check_values(kc, vc, oracle.fill_workload(w, rows=kept), kept, s.head_dim, slots=slots)
+    U.check_indexer_values(ic, oracle.fill_indexer_workload(w, rows=kept), kept, s.head_dim, slots=slots)
