@@ -163,7 +163,8 @@ rf_status rf_fill_rows(rf_plan* plan, const int32_t* exact_rows, int32_t n_exact
  * with n_rows > RF_NOALLOC_MAX_ROWS get RF_E_SHAPE, before anything is
  * enqueued.  All calls on one GPU share that array: calls ordered on one
  * stream are fine (each call clears what it uses with a kernel, no memset),
- * calls that overlap on one GPU race. */
+ * calls that overlap on one GPU race.  The call is not timed by
+ * rf_plan_profile (timing would create events). */
 #define RF_NOALLOC_MAX_ROWS (1 << 20)
 rf_status rf_fill_rows_noalloc(rf_plan* plan, const int32_t* exact_rows, int32_t n_exact,
                                int32_t* fill_rows, int32_t* n_fill, void* hip_stream);

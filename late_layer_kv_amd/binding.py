@@ -194,7 +194,7 @@ def _arg(fn: str, name: str, t, dtypes, numel: int = 0, where: str = "device", o
         raise ValueError(f"{fn}: {name} must be in device memory, not on {t.device}")
     if where == "pinned" and (t.device.type != "cpu" or not t.is_pinned()):
         raise ValueError(f"{fn}: {name} must be in pinned host memory (the plan streams its maps)")
-    if t.dim() > 0 and t.stride(-1) != 1:
+    if t.dim() > 0 and t.numel() > 0 and t.stride(-1) != 1:   # an empty tensor has no layout to check
         raise ValueError(f"{fn}: {name} must have unit stride along its last axis")
     if t.numel() < numel:
         raise ValueError(f"{fn}: {name} holds {t.numel()} elements, at least {numel} needed")

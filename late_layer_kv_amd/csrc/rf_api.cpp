@@ -342,7 +342,8 @@ rf_status rf_fill_rows_noalloc(rf_plan* p, const int32_t* exact_rows, int32_t n_
   if (p->s.n_rows > RF_NOALLOC_MAX_ROWS)
     return fail(RF_E_SHAPE, "rf_fill_rows_noalloc takes at most %d rows (plan has %d); use rf_fill_rows",
                 RF_NOALLOC_MAX_ROWS, p->s.n_rows);
-  Timed tm(p, RF_K_ROWS, static_cast<hipStream_t>(stream));
+  // (no Timed bracket: with profiling on it may create events, and this entry
+  // point allocates nothing in any mode)
   hipError_t e = rf::launch_fill_rows_noalloc(exact_rows, n_exact, p->s.n_rows, fill_rows, n_fill,
                                               static_cast<hipStream_t>(stream));
   return e == hipSuccess ? RF_OK : hip_fail(e, "fill-row launch (library scratch)");

@@ -648,3 +648,16 @@ def test_fill_rows_noalloc_limit_and_header_constant():
     q = B.Plan(**_shape())
     assert L.rf_fill_rows_noalloc(q.handle, None, -1, C.c_void_p(0x10000), C.c_void_p(0x20000), None) == -1
     assert L.rf_fill_rows_noalloc(q.handle, None, 0, None, C.c_void_p(0x20000), None) == -1
+
+
+def test_binding_takes_an_empty_exact_row_set():
+    """No exact rows at all (a zero tail): an empty tensor passes the
+    binding's checks whatever its stride, and reaches the library."""
+    import torch
+    plan, args = _fill_args()
+    empty = torch.from_numpy(np.zeros(0, dtype=np.int32))
+    with _CpuAsDevice():
+        with pytest.raises(B.RfError) as e:   # the binding passes it on; librf refuses the workspace
+            B.fill_rows(plan, empty, torch.zeros(300, dtype=torch.int32), torch.zeros(1, dtype=torch.int32),
+                        torch.zeros(16, dtype=torch.uint8), stream=0)
+    assert e.value.status == -4

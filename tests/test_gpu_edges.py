@@ -151,3 +151,11 @@ def test_cache_larger_than_the_batch():
     f = rows.cpu().numpy()
     U.check_placement(kc, vc, f, n_slots, slots=slots)
     U.check_values(kc, vc, oracle.fill_workload(w, rows=f), f, s.head_dim, slots=slots)
+
+
+def test_no_exact_rows():
+    """An empty exact set (no tail, no spans): every row of a ragged batch is
+    filled, each at its own prompt's positions (RidgeFill section 2.1 with a
+    zero tail; rf_fill_rows given no exact rows)."""
+    _check(workloads.spec("8b_ragged_host", n_late=2, prompt_lens=(300, 257, 129), tail=0, seed=150),
+           "no exact rows")
