@@ -229,7 +229,11 @@ typedef struct rf_vmeasure {
  *           pairing), without QK-norm; it is stored at the row's slot like K.
  *   measure value-scale measurement inside the fill (rf_vmeasure above), or
  *           NULL; replaces vscale (give at most one of the two); rf_fill and
- *           rf_fill_q8 only. */
+ *           rf_fill_q8 only.  The measurement runs on a stream of the plan's
+ *           own, beside the fill's launches (each layer group's K/V launch
+ *           waits for its scales, and the call's work ends on hip_stream as
+ *           usual); the first fill that measures creates that stream and two
+ *           events, kept until rf_plan_destroy. */
 typedef struct rf_fill_opts {
   const rf_vscale* vscale;
   const uint16_t* const* k_norm;

@@ -43,6 +43,18 @@ void rf::set_last_error(const char* msg) { g_err = msg; }
 struct rf_plan {
   rf_shape s{};
   int32_t flags = 0;
+  // The value-scale measurement inside a fill runs on its own stream, beside
+  // the fill's launches: to_meas orders it after the fill's stream, from_meas
+  // the other way.  Created by the first fill that measures.
+  hipStream_t meas = nullptr;
+  hipEvent_t to_meas = nullptr, from_meas = nullptr;
+  hipError_t make_meas_stream() {
+    if (meas) return hipSuccess;
+    hipError_t e = hipEventCreateWithFlags(&to_meas, hipEventDisableTiming);
+    if (e == hipSuccess) e = hipEventCreateWithFlags(&from_meas, hipEventDisableTiming);
+    if (e == hipSuccess) e = hipStreamCreateWithFlags(&meas, hipStreamNonBlocking);
+    return e;
+  }
   // RF_MAPS_HOST only
   hipStream_t side = nullptr;
   hipEvent_t ev_start = nullptr;
@@ -255,6 +267,10 @@ rf_status rf_plan_create(const rf_shape* shape, int32_t flags, rf_plan** out) {
 
 void rf_plan_destroy(rf_plan* p) {
   if (!p) return;
+  if (p->meas) (void)hipStreamSynchronize(p->meas);
+  if (p->to_meas) (void)hipEventDestroy(p->to_meas);
+  if (p->from_meas) (void)hipEventDestroy(p->from_meas);
+  if (p->meas) (void)hipStreamDestroy(p->meas);
   if (p->side) (void)hipStreamSynchronize(p->side);
   for (int i = 0; i < 2; ++i) {
     if (p->mapbuf[i]) (void)hipFree(p->mapbuf[i]);
@@ -824,9 +840,32 @@ rf_status fill_impl(rf_plan* p, const char* fn, const uint16_t* x, int64_t ld_x,
   const size_t vs_layer = vscale ? static_cast<size_t>(vscale->n_groups) * s.n_kv : 0;
   MapFeeder feed(p, maps, dq, hs);
   if ((st = feed.begin()) != RF_OK) return st;
+  // The in-fill measurement runs on the plan's measurement stream, beside
+  // the fill's own launches: each group's measurement starts once the
+  // group's prepared weights and maps are in place on the fill's stream, and
+  // the group's K/V launch waits for its scales.  Its kernels and inputs are
+  // those of rf_value_scales, so the scales are the same bytes; only the
+  // small launches now overlap the group's map contraction instead of
+  // queueing behind it.  Every exit joins the two streams again.
   std::unique_ptr<ScaleMeasure> meas;
+  struct Join {
+    rf_plan* p = nullptr;
+    hipStream_t hs = nullptr;
+    ~Join() {
+      if (p && hipEventRecord(p->from_meas, p->meas) == hipSuccess) (void)hipStreamWaitEvent(hs, p->from_meas, 0);
+    }
+  } join;
+  auto to_meas = [&]() -> rf_status {
+    hipError_t er = hipEventRecord(p->to_meas, hs);
+    if (er == hipSuccess) er = hipStreamWaitEvent(p->meas, p->to_meas, 0);
+    return er == hipSuccess ? RF_OK : hip_fail(er, "measurement stream wait");
+  };
   if (meas_in) {
-    meas.reset(new ScaleMeasure(p, hs, meas_in->workspace, G, x, ld_x, meas_in->layer_in, meas_in->ld_in,
+    if ((e = p->make_meas_stream()) != hipSuccess) return hip_fail(e, "measurement stream");
+    if ((st = to_meas()) != RF_OK) return st;
+    join.p = p;
+    join.hs = hs;
+    meas.reset(new ScaleMeasure(p, p->meas, meas_in->workspace, G, x, ld_x, meas_in->layer_in, meas_in->ld_in,
                                 meas_in->calib_rows, meas_in->calib_group, meas_in->n_calib, meas_in->n_groups, prep,
                                 prep_rows(s)));
     if ((st = meas->begin()) != RF_OK) return st;
@@ -851,20 +890,27 @@ rf_status fill_impl(rf_plan* p, const char* fn, const uint16_t* x, int64_t ld_x,
       if ((e = rf::launch_prep(pp, g, hs)) != hipSuccess) return hip_fail(e, "prep launch");
     }
     if ((st = feed.load(l0, g, mp)) != RF_OK) return st;
+    // the measurement's calibration rows go through the same loaded maps
+    // (and prepared weights), on the measurement stream
+    if (meas && (st = to_meas()) != RF_OK) return st;
     {
       Timed tm(p, RF_K_MAP, hs);
       if ((e = rf::launch_map(mp, g, hs)) != hipSuccess) return hip_fail(e, "map launch");
     }
-    // the measurement's calibration rows go through the same loaded maps,
-    // and its scales for these layers are in place before the K/V launch
-    if (meas && (st = meas->group(l0, g, mp)) != RF_OK) return st;
-    if ((st = feed.consumed()) != RF_OK) return st;
-    if (meas && (st = meas->finish(l0, g, meas_in->scale)) != RF_OK) return st;
+    if (meas) {
+      if ((st = meas->group(l0, g, mp)) != RF_OK) return st;
+      if ((st = meas->finish(l0, g, meas_in->scale)) != RF_OK) return st;
+      if ((e = hipEventRecord(p->from_meas, p->meas)) != hipSuccess) return hip_fail(e, "event record");
+    }
     {
       Timed tm(p, RF_K_NORM, hs);
       if ((e = rf::launch_row_scale(ssq, mp.tiles_n, n_fill, g, 1.0f / s.d_out, s.rms_eps, rsb, hs)) != hipSuccess)
         return hip_fail(e, "row scale launch");
     }
+    // the group's scales are in place before its K/V launch, and the
+    // measurement has read the group's maps before their buffer is released
+    if (meas && (e = hipStreamWaitEvent(hs, p->from_meas, 0)) != hipSuccess) return hip_fail(e, "stream wait");
+    if ((st = feed.consumed()) != RF_OK) return st;
     {
       Timed tm(p, RF_K_KV, hs);
       if ((e = rf::launch_kv(kp, g, hs)) != hipSuccess) return hip_fail(e, "kv launch");
