@@ -447,6 +447,26 @@ def test_bench_refuses_more_than_one_gpu():
     assert "one GPU only" in r.stderr and r.stdout == ""
 
 
+def test_binding_fails_loudly_without_the_library():
+    """With librf.so absent the binding raises on first use; nothing falls
+    back to another implementation (run in a child so the loaded library of
+    this session is untouched)."""
+    code = (
+        "import sys\n"
+        "from late_layer_kv_amd import binding as B\n"
+        "B.LIB_PATH = B.LIB_PATH + '.absent'\n"
+        "try:\n"
+        "    B.Plan(256, 256, 1, 1, 128, 1e-6, 1e4, 256, 256, 256)\n"
+        "except RuntimeError as e:\n"
+        "    print('raised:', e)\n"
+        "    sys.exit(0)\n"
+        "sys.exit(1)\n"
+    )
+    r = subprocess.run([sys.executable, "-c", code], capture_output=True, text=True, timeout=120, cwd=ROOT)
+    assert r.returncode == 0, r.stdout + r.stderr
+    assert "is not built" in r.stdout
+
+
 def test_traffic_summary_scales_counters_by_the_copy(tmp_path):
     """bench.py's traffic figure: per-launch FETCH_SIZE and WRITE_SIZE (KiB) of
     the map kernel, each scaled by bytes / counter of a device copy of known size."""
