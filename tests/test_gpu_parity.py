@@ -114,6 +114,45 @@ def test_identity_fill_equals_exact_projection(name):
     U.check_values(kc2, vc2, ref, f, s.head_dim)
 
 
+def _spread_rows(x: torch.Tensor) -> torch.Tensor:
+    """x's rows copied into a strided view whose rows lie so far apart that
+    the view spans more than 4 GiB (row starts stay 16-byte aligned)."""
+    n, d = x.shape
+    ld = ((1 << 32) // (2 * n) + 64) // 8 * 8
+    assert n * ld * 2 >= (1 << 32)
+    flat = torch.zeros((n - 1) * ld + d, dtype=x.dtype, device=x.device)
+    v = torch.as_strided(flat, (n, d), (ld, 1))
+    v.copy_(x)
+    return v
+
+
+def test_operands_spanning_4gib():
+    """An operand whose rows span 4 GiB or more is read through 64-bit
+    pointers (the usual path reads through a buffer resource with 32-bit
+    offsets): the fill with such a split-layer state, and rf_kv_project with
+    such layer inputs, write the same bytes as with the compact layout."""
+    w = _workload("tiny")
+    s = w.spec
+    _say("[wide] tiny, rows spread over more than 4 GiB")
+    di = U.DeviceInputs(w, maps_on_host=False)
+    plan = U.plan_for(w, maps_on_host=False)
+    rows, n = U.gpu_fill_rows(plan, di)
+    kc1, vc1 = U.gpu_fill(plan, di, rows, n)
+    kp1, vp1 = U.gpu_kv_project(plan, di, [di.x] * s.n_late, rows, n)
+    compact = di.x
+    di.x = _spread_rows(compact)
+    assert di.x.stride(0) * s.n_rows * 2 >= (1 << 32)
+    kc2, vc2 = U.gpu_fill(plan, di, rows, n)
+    kp2, vp2 = U.gpu_kv_project(plan, di, [di.x] * s.n_late, rows, n)
+    di.x = None
+    torch.cuda.empty_cache()
+    for l in range(s.n_late):
+        assert torch.equal(kc1[l], kc2[l]) and torch.equal(vc1[l], vc2[l]), f"fill, layer {l}"
+        assert torch.equal(kp1[l], kp2[l]) and torch.equal(vp1[l], vp2[l]), f"rf_kv_project, layer {l}"
+    f = rows.cpu().numpy()
+    U.check_values(kc1, vc1, oracle.fill_workload(w, rows=f), f, s.head_dim)
+
+
 def test_streamed_maps_equal_resident():
     """Maps streamed from pinned host memory give the same bytes as resident maps."""
     w = _workload("ragged_mid")
