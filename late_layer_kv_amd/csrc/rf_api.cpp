@@ -132,13 +132,15 @@ int idx_width(const rf_shape& s) { return s.n_idx * s.head_dim; }
 int prep_rows(const rf_shape& s) { return (2 * kv_width(s) + idx_width(s) + rf::kTileN - 1) / rf::kTileN * rf::kTileN; }
 // Indexer key columns ending half way into a 256-feature tile (a 128-wide
 // remainder) go to tall tiles of the K/V launch (512 rows x 128 features)
-// instead of a tile that is half zero padding, when every layer input spans
-// less than 4 GiB (those tiles' loads use 32-bit offsets).  Returns the first feature of the
-// remainder, or -1 to let the K/V kernel cover every column.
+// instead of a tile that is half zero padding, when every layer input and the
+// layer's prepared weights span less than 4 GiB (those tiles' loads use 32-bit
+// offsets).  Returns the first feature of the remainder, or -1 to let the K/V
+// kernel cover every column.
 int tall_f0(const rf_shape& s, int64_t in_rows, int64_t ld_in) {
   const int cols = 2 * s.n_kv * s.head_dim + s.n_idx * s.head_dim;
   if (s.n_idx == 0 || cols % rf::kTileN != 128) return -1;
-  if (in_rows * ld_in * 2 >= (int64_t(1) << 32)) return -1;
+  const int64_t limit = int64_t(1) << 32;
+  if (in_rows * ld_in * 2 >= limit || int64_t(prep_rows(s)) * s.d_out * 2 >= limit) return -1;
   return cols - 128;
 }
 size_t rope_bytes(const rf_shape& s) { return up(static_cast<size_t>(s.max_pos) * (s.head_dim / 2) * 8); }

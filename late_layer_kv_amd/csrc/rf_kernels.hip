@@ -576,13 +576,12 @@ __device__ __forceinline__ void tall_wait(int slots) {
 }
 static_assert(kTallLoads == 20, "tall_wait immediates assume 20 loads per stage");
 
-// Where the 20 loads of a stage read: a uniform base per operand (the layer's
-// prepared weights, its input rows) plus a 32-bit byte offset per lane and
-// load, so the loads take one VGPR of address each (the host uses this kernel
-// only when every layer input spans less than 4 GiB).
+// Where the 20 loads of a stage read: a raw buffer resource per operand (the
+// layer's prepared weights, its input rows) plus a 32-bit byte offset per
+// lane and load, so the loads take one VGPR of address each (the host uses
+// tall tiles only when every layer input spans less than 4 GiB).
 struct TallSrc {
-  const char* wbase;
-  const char* xbase;
+  __amdgpu_buffer_rsrc_t w, x;
   uint32_t off[kTallLoads];
 };
 
@@ -592,8 +591,8 @@ struct TallSrc {
 __device__ __forceinline__ void tall_load(int j, const TallSrc& src, size_t kbyte, char* buf, int wave) {
   char* dst = j < 4 ? buf + (32 * wave + 8 * j) * kRowBytes
                     : buf + kTallA + (128 * wave + 8 * (j - 4)) * kRowBytes;
-  const char* base = (j < 4 ? src.wbase : src.xbase) + kbyte;
-  __builtin_amdgcn_global_load_lds((gbl_ptr_t*)(base + src.off[j]), (lds_ptr_t*)dst, 16, 0, 0);
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(j < 4 ? src.w : src.x, (lds_ptr_t*)dst, 16, src.off[j],
+                                           static_cast<int>(kbyte), 0, 0);
 }
 
 // One 32-column step on fragments f from buffer `cur`; READ: the 16 fragment
@@ -645,8 +644,12 @@ __device__ __forceinline__ void tall_tile(const KvParams& p, int g, int m0, char
   const int r15 = lane & 15, q = lane >> 4;
 
   TallSrc src;
-  src.wbase = reinterpret_cast<const char*>(p.wkv + static_cast<size_t>(g) * p.wrows * p.K);
-  src.xbase = reinterpret_cast<const char*>(p.in[g]);
+  src.w = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(p.wkv + static_cast<size_t>(g) * p.wrows * p.K),
+                                            static_cast<short>(0), static_cast<int>(static_cast<uint32_t>(
+                                                static_cast<size_t>(p.wrows) * p.K * 2)), 0x00020000);
+  src.x = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(p.in[g]), static_cast<short>(0),
+                                            static_cast<int>(static_cast<uint32_t>(
+                                                static_cast<size_t>(p.n_in_rows) * p.ld_in * 2)), 0x00020000);
 #pragma unroll
   for (int j = 0; j < kTallLoads; ++j) {
     const int chunk = load_chunk(lane, j);
