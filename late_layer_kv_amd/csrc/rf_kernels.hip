@@ -557,9 +557,11 @@ __global__ void __launch_bounds__(256) row_rms_kernel(const RmsParams p) {
 // 128 features x 128 rows (the same 8x8 blocks of v_mfma_f32_16x16x32_bf16 and lane layout as the
 // main loop), all waves share the weight fragments.  LDS holds two buffers of
 // one 64-column stage each: 128 weight rows (16 KB) then 512 data rows
-// (64 KB), rows of 128 bytes with the main loop's chunk swizzle.  Stage t+2's
-// loads go into stage t's buffer once every wave is past the barrier that
-// ends the reads of it, so one stage of loads is always in flight.
+// (64 KB), rows of 128 bytes with the main loop's chunk swizzle.  Each wave
+// loads and reads only its own 128 data rows, so it loads stage t+2's rows
+// into stage t's buffer as soon as its own reads of them have returned, half
+// way through stage t's first step; the weight rows, which every wave reads,
+// follow in the second step, after the barrier that ends all reads of stage t.
 constexpr int kTallRows = 512;
 constexpr int kTallA = 128 * kRowBytes;               // 16 KB of weight rows
 constexpr int kTallBuf = kTallA + kTallRows * kRowBytes;  // 80 KB per stage buffer
@@ -568,9 +570,11 @@ constexpr int kTallStageRow = 128 * 2;                // 256 B per staged output
 constexpr int kTallSlotOffset = kTallRows * kTallStageRow;  // 128 KB, then 512 int32 slot ids
 static_assert(2 * kTallBuf <= kLdsBytes && kTallSlotOffset + kTallRows * 4 <= 2 * kTallBuf, "tall tile LDS");
 
-__device__ __forceinline__ void tall_wait(int slots) {
-  if (slots == 0)
+__device__ __forceinline__ void tall_wait(int loads) {
+  if (loads == 0)
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  else if (loads == 16)
+    asm volatile("s_waitcnt vmcnt(16)" ::: "memory");
   else
     asm volatile("s_waitcnt vmcnt(20)" ::: "memory");
 }
@@ -598,7 +602,12 @@ __device__ __forceinline__ void tall_load(int j, const TallSrc& src, size_t kbyt
 // One 32-column step on fragments f from buffer `cur`; READ: the 16 fragment
 // reads of the next step (from `nbuf` at offsets aoff / boff) follow MFMAs
 // 0..15; LOAD: the 20 loads of a stage (into `lbuf`) follow MFMAs 4, 7, ..., 61.
-template <bool READ, bool LOAD, bool FIRST>
+// LOADX (step 0): once this wave's own fragment reads have returned (after
+// MFMA 23), the 16 loads of its quarter of the data rows follow MFMAs 24, 26,
+// ..., 54 (no other wave reads or writes that quarter, so no barrier is
+// needed); LOADA (step 1, after the barrier): the 4 weight-row loads follow
+// MFMAs 16, 28, 40, 52.
+template <bool READ, bool LOADX, bool LOADA, bool FIRST>
 __device__ __forceinline__ void tall_step(const Frags& f, f32x4 (&acc)[8][8], Frags& nf, const char* nbuf, int aoff,
                                           int boff, const TallSrc& src, size_t kbyte, char* lbuf, int wave) {
 #pragma unroll
@@ -611,7 +620,9 @@ __device__ __forceinline__ void tall_step(const Frags& f, f32x4 (&acc)[8][8], Fr
     if (READ && i < 8) nf.a[i] = *reinterpret_cast<const bf16x8*>(nbuf + aoff + i * 16 * kRowBytes);
     if (READ && i >= 8 && i < 16)
       nf.b[i - 8] = *reinterpret_cast<const bf16x8*>(nbuf + kTallA + boff + (i - 8) * 16 * kRowBytes);
-    if (LOAD && i >= 4 && (i - 4) % 3 == 0 && i <= 61) tall_load((i - 4) / 3, src, kbyte, lbuf, wave);
+    if (LOADX && i == 23) asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    if (LOADX && i >= 24 && (i - 24) % 2 == 0 && i <= 54) tall_load(4 + (i - 24) / 2, src, kbyte, lbuf, wave);
+    if (LOADA && i >= 16 && (i - 16) % 12 == 0 && i <= 52) tall_load((i - 16) / 12, src, kbyte, lbuf, wave);
   }
 }
 
@@ -624,13 +635,13 @@ __device__ __forceinline__ void tall_stage(Frags& fa, Frags& fb, f32x4 (&acc)[8]
                                            const TallSrc& src, const int (&aoff)[2], const int (&boff)[2], int wave) {
   char* cur = smem + (t & 1) * kTallBuf;
   char* nxt = smem + ((t + 1) & 1) * kTallBuf;
-  tall_step<true, false, FIRST>(fa, acc, fb, cur, aoff[1], boff[1], src, 0, cur, wave);
+  const size_t kb = static_cast<size_t>(t + 2) * kRowBytes;
+  tall_step<true, LOAD, false, FIRST>(fa, acc, fb, cur, aoff[1], boff[1], src, kb, cur, wave);
   if (NEXT) {
-    tall_wait(0);
+    tall_wait(LOAD ? 16 : 0);  // stage t+1 landed; this stage's data-row loads may fly
     barrier();
   }
-  tall_step<NEXT, LOAD, false>(fb, acc, fa, nxt, aoff[0], boff[0], src, static_cast<size_t>(t + 2) * kRowBytes, cur,
-                               wave);
+  tall_step<NEXT, false, LOAD, false>(fb, acc, fa, nxt, aoff[0], boff[0], src, kb, cur, wave);
 }
 
 // One tall tile: layer g, rows m0 .. m0 + 511 of the call, features
@@ -679,7 +690,7 @@ __device__ __forceinline__ void tall_tile(const KvParams& p, int g, int m0, char
   if (nk > 1) {
 #pragma unroll
     for (int j = 0; j < kTallLoads; ++j) tall_load(j, src, kRowBytes, smem + kTallBuf, wave);
-    tall_wait(1);
+    tall_wait(20);
   } else {
     tall_wait(0);
   }
