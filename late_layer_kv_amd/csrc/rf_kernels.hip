@@ -25,8 +25,8 @@
 // these kernels the switch gained 7-10%.  The MFMAs are inline assembly (see
 // mfma16) so their accumulators stay in place.
 //
-// Operand tiles stream global -> LDS with global_load_lds_dwordx4 (no VGPR
-// staging) in stages of 64 contraction columns, so every operand row of a
+// Operand tiles stream global -> LDS with buffer_load_dwordx4 ... lds (no VGPR
+// staging; see OpSrc) in stages of 64 contraction columns, so every operand row of a
 // stage is one full 128-byte line (one L2 request per row per stage; 32-column
 // stages fetched half lines and cost the texture path about 14% of the map
 // contraction's speed).  The 160 KB of LDS is a ring of five 32 KB slots, each
