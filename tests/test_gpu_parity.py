@@ -126,31 +126,43 @@ def _spread_rows(x: torch.Tensor) -> torch.Tensor:
     return v
 
 
-def test_operands_spanning_4gib():
+WIDE_CASES = {
+    "tiny": workloads.spec("tiny"),
+    # one 128-wide indexer head over one kv head of 128: 384 K/V/indexer
+    # columns, so compact inputs take tall tiles and the spread ones the
+    # padded tile
+    "tiny_idx": workloads.spec("tiny", n_kv=1, head_dim=128, idx_heads=1, seed=7),
+}
+
+
+@pytest.mark.parametrize("name", list(WIDE_CASES))
+def test_operands_spanning_4gib(name):
     """An operand whose rows span 4 GiB or more is read through 64-bit
     pointers (the usual path reads through a buffer resource with 32-bit
-    offsets): the fill with such a split-layer state, and rf_kv_project with
-    such layer inputs, write the same bytes as with the compact layout."""
-    w = _workload("tiny")
+    offsets, and tall indexer tiles are not used): the fill with such a
+    split-layer state, and rf_kv_project with such layer inputs, write the
+    same bytes as with the compact layout."""
+    w = workloads.make(WIDE_CASES[name])
     s = w.spec
-    _say("[wide] tiny, rows spread over more than 4 GiB")
+    _say(f"[wide] {name}, rows spread over more than 4 GiB")
     di = U.DeviceInputs(w, maps_on_host=False)
     plan = U.plan_for(w, maps_on_host=False)
     rows, n = U.gpu_fill_rows(plan, di)
-    kc1, vc1 = U.gpu_fill(plan, di, rows, n)
-    kp1, vp1 = U.gpu_kv_project(plan, di, [di.x] * s.n_late, rows, n)
+    fill1 = U.gpu_fill(plan, di, rows, n)
+    proj1 = U.gpu_kv_project(plan, di, [di.x] * s.n_late, rows, n)
     compact = di.x
     di.x = _spread_rows(compact)
     assert di.x.stride(0) * s.n_rows * 2 >= (1 << 32)
-    kc2, vc2 = U.gpu_fill(plan, di, rows, n)
-    kp2, vp2 = U.gpu_kv_project(plan, di, [di.x] * s.n_late, rows, n)
+    fill2 = U.gpu_fill(plan, di, rows, n)
+    proj2 = U.gpu_kv_project(plan, di, [di.x] * s.n_late, rows, n)
     di.x = None
     torch.cuda.empty_cache()
-    for l in range(s.n_late):
-        assert torch.equal(kc1[l], kc2[l]) and torch.equal(vc1[l], vc2[l]), f"fill, layer {l}"
-        assert torch.equal(kp1[l], kp2[l]) and torch.equal(vp1[l], vp2[l]), f"rf_kv_project, layer {l}"
+    for what, a, b in (("fill", fill1, fill2), ("rf_kv_project", proj1, proj2)):
+        for cache, ca, cb in zip("KVI", a, b):
+            for l in range(s.n_late):
+                assert torch.equal(ca[l], cb[l]), f"{what}, {cache} cache, layer {l}"
     f = rows.cpu().numpy()
-    U.check_values(kc1, vc1, oracle.fill_workload(w, rows=f), f, s.head_dim)
+    U.check_values(fill1[0], fill1[1], oracle.fill_workload(w, rows=f), f, s.head_dim)
 
 
 def test_streamed_maps_equal_resident():
