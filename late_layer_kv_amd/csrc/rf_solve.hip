@@ -11,13 +11,15 @@
 //
 // C is factored C = L L^T by a right-looking blocked Cholesky with 64 x 64
 // blocks, then L Z = R and L^T W = Z are solved block row by block row.  Per
-// block step: the diagonal block is factored by one workgroup in LDS, the
-// blocks below it are solved against it (one workgroup per block), and the
-// trailing matrix takes a rank-64 update; the two triangular solves take the
-// same shape, with the right-hand side's 64-column blocks in parallel.  The
-// updates are 64 x 64 x 64 products on v_mfma_f64_16x16x4_f64 (lane l supplies
-// A[l % 16][l / 16] and B[l / 16][l % 16] and holds D[4 v + l / 16][l % 16]).
-// Every sum runs in a fixed order: the result is bitwise reproducible.
+// block step: one workgroup factors the diagonal block in LDS and forms the
+// inverse of its factor, Linv_k = L_kk^-1; the blocks below it become
+// C_ik Linv_k^T and the trailing matrix takes a rank-64 update.  The two
+// triangular solves take the same shape: Z_k = Linv_k R_k (or Linv_k^T Z_k),
+// then a rank-64 update of the block rows still to come, with the right-hand
+// side's 64-column blocks in parallel.  Every product is a 64 x 64 x 64
+// product on v_mfma_f64_16x16x4_f64 (lane l supplies A[l % 16][l / 16] and
+// B[l / 16][l % 16] and holds D[4 v + l / 16][l % 16]).  Every sum runs in a
+// fixed order: the result is bitwise reproducible.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -31,6 +33,7 @@ namespace {
 typedef double d4 __attribute__((ext_vector_type(4)));
 
 constexpr int kB = 64;        // block size
+constexpr int kSuper = 4;     // block rows per pass of the triangular solves' updates
 constexpr int kLd = kB + 1;   // LDS row length in doubles (odd: rows fall in different banks)
 
 struct SolveArgs {
@@ -88,148 +91,123 @@ __global__ void __launch_bounds__(256) ridge_diag_kernel(const SolveArgs a) {
   for (int i = threadIdx.x; i < a.d_in; i += 256) a.c[static_cast<size_t>(i) * a.d_in + i] += alpha;
 }
 
-// Cholesky of diagonal block k in place (its lower triangle).
-__global__ void __launch_bounds__(256) potrf_kernel(double* c, int d, int k, int* flag) {
-  __shared__ double s[kB * kLd];
+// Cholesky of diagonal block k in place (its lower triangle) and the inverse
+// of its factor, Linv_k = L_kk^-1, in one right-looking sweep over the
+// columns.  Thread t owns column l = t / 4 and rows i = t % 4 + 4 r (r < 16)
+// of both the block (sv) and of Y, which starts as the identity.  At column
+// j the pivot's owner publishes sqrt(C_jj); the owners of column j scale it
+// by the pivot's reciprocal (column j of L), the owners of row j scale row j
+// of Y (row j of Linv: Y_j = e_j - sum_{p<j} L_jp Linv_p by then), and every
+// thread updates its entries below row j: C_il -= L_ij L_lj and
+// Y_il -= L_ij Linv_jl.  Two barriers per column; the rows of the block
+// travel through LDS only as column j of L and row j of Linv.
+__global__ void __launch_bounds__(256) potrf_inv_kernel(double* c, int d, int k, int* flag, double* linv) {
+  __shared__ double colj[kB];  // column j of L
+  __shared__ double rowj[kB];  // row j of Linv
+  __shared__ double dg[kB];    // the pivots
   double* blk = c + (static_cast<size_t>(k) * kB) * d + k * kB;
-  for (int e = threadIdx.x; e < kB * kB; e += 256) {
-    const int r = e / kB, q = e % kB;
-    s[r * kLd + q] = blk[static_cast<size_t>(r) * d + q];
+  const int t = threadIdx.x;
+  const int l = t >> 2, rg = t & 3;
+  double sv[16], yv[16];
+#pragma unroll
+  for (int r = 0; r < 16; ++r) {
+    const int i = rg + 4 * r;
+    sv[r] = i >= l ? blk[static_cast<size_t>(i) * d + l] : 0.0;
+    yv[r] = i == l ? 1.0 : 0.0;
   }
-  __syncthreads();
   for (int j = 0; j < kB; ++j) {
-    // column j: its pivot (thread 0), then the entries below it
-    if (threadIdx.x == 0) {
-      double v = s[j * kLd + j];
-      for (int p = 0; p < j; ++p) v -= s[j * kLd + p] * s[j * kLd + p];
+    const int rj = j >> 2;
+    if (l == j && rg == (j & 3)) {
+      double v = 0.0;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) v = r == rj ? sv[r] : v;
       if (!(v > 0.0)) {
         *flag = 1;
         v = 1.0;  // keep going with finite values; the call reports the failure
       }
-      s[j * kLd + j] = sqrt(v);
+      dg[j] = sqrt(v);
     }
     __syncthreads();
-    const int i = j + 1 + static_cast<int>(threadIdx.x);
-    if (i < kB) {
-      double v = s[i * kLd + j];
-      for (int p = 0; p < j; ++p) v -= s[i * kLd + p] * s[j * kLd + p];
-      s[i * kLd + j] = v / s[j * kLd + j];
+    const double rp = 1.0 / dg[j];
+    if (l == j) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int i = rg + 4 * r;
+        if (i > j) {
+          sv[r] *= rp;
+          colj[i] = sv[r];
+        }
+      }
+    }
+    if (rg == (j & 3)) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r)
+        if (r == rj) {
+          yv[r] *= rp;
+          rowj[l] = yv[r];
+        }
     }
     __syncthreads();
-  }
-  for (int e = threadIdx.x; e < kB * kB; e += 256) {
-    const int r = e / kB, q = e % kB;
-    if (q <= r) blk[static_cast<size_t>(r) * d + q] = s[r * kLd + q];
-  }
-}
-
-// Block (k + 1 + blockIdx.x, k) := B L_kk^-T: row r of B solves x L_kk^T = b
-// by forward substitution (one thread per row).
-__global__ void __launch_bounds__(64) trsm_panel_kernel(double* c, int d, int k) {
-  __shared__ double l[kB * kLd];
-  __shared__ double b[kB * kLd];
-  const int i = k + 1 + blockIdx.x;
-  const double* lk = c + (static_cast<size_t>(k) * kB) * d + k * kB;
-  double* bk = c + (static_cast<size_t>(i) * kB) * d + k * kB;
-  for (int e = threadIdx.x; e < kB * kB; e += 64) {
-    const int r = e / kB, q = e % kB;
-    l[r * kLd + q] = q <= r ? lk[static_cast<size_t>(r) * d + q] : 0.0;
-    b[r * kLd + q] = bk[static_cast<size_t>(r) * d + q];
-  }
-  __syncthreads();
-  const int r = threadIdx.x;
-  for (int q = 0; q < kB; ++q) {
-    double v = b[r * kLd + q];
-    for (int p = 0; p < q; ++p) v -= b[r * kLd + p] * l[q * kLd + p];
-    b[r * kLd + q] = v / l[q * kLd + q];
-  }
-  __syncthreads();
-  for (int e = threadIdx.x; e < kB * kB; e += 64) {
-    const int rr = e / kB, q = e % kB;
-    bk[static_cast<size_t>(rr) * d + q] = b[rr * kLd + q];
-  }
-}
-
-// Block row k of the right-hand side: forward (FWD: L_kk z = r) or backward
-// (L_kk^T w = z) substitution, one thread per column.
-template <bool FWD>
-__global__ void __launch_bounds__(256) trsv_rows_kernel(const double* c, int d, double* rhs, int d_out, int k) {
-  __shared__ double l[kB * kLd];
-  const double* lk = c + (static_cast<size_t>(k) * kB) * d + k * kB;
-  for (int e = threadIdx.x; e < kB * kB; e += 256) {
-    const int r = e / kB, q = e % kB;
-    l[r * kLd + q] = q <= r ? lk[static_cast<size_t>(r) * d + q] : 0.0;
-  }
-  __syncthreads();
-  const int col = blockIdx.x * 256 + threadIdx.x;
-  if (col >= d_out) return;
-  double* x = rhs + (static_cast<size_t>(k) * kB) * d_out + col;
-  double v[kB];
+    const double cl = l > j ? colj[l] : 0.0;
+    const double yj = rowj[l];
 #pragma unroll
-  for (int r = 0; r < kB; ++r) v[r] = x[static_cast<size_t>(r) * d_out];
-  if (FWD) {
-#pragma unroll
-    for (int r = 0; r < kB; ++r) {
-      double t = v[r];
-#pragma unroll
-      for (int p = 0; p < r; ++p) t -= l[r * kLd + p] * v[p];
-      v[r] = t / l[r * kLd + r];
-    }
-  } else {
-#pragma unroll
-    for (int r = kB - 1; r >= 0; --r) {
-      double t = v[r];
-#pragma unroll
-      for (int p = r + 1; p < kB; ++p) t -= l[p * kLd + r] * v[p];
-      v[r] = t / l[r * kLd + r];
+    for (int r = 0; r < 16; ++r) {
+      const int i = rg + 4 * r;
+      if (i > j) {
+        const double ci = colj[i];
+        if (l > j && l <= i) sv[r] -= ci * cl;
+        yv[r] -= ci * yj;
+      }
     }
   }
+  double* out = linv + static_cast<size_t>(k) * kB * kB;
 #pragma unroll
-  for (int r = 0; r < kB; ++r) x[static_cast<size_t>(r) * d_out] = v[r];
+  for (int r = 0; r < 16; ++r) {
+    const int i = rg + 4 * r;
+    if (i > l) blk[static_cast<size_t>(i) * d + l] = sv[r];
+    else if (i == l) blk[static_cast<size_t>(i) * d + l] = dg[l];
+    out[i * kB + l] = yv[r];
+  }
 }
 
-// D -= P Q on 64 x 64 blocks with fp64 MFMA; P and Q are staged in LDS as
-// P[row][p] and Q[p][col] (each mode fills them from its own layout).
-//   MODE 0 (Cholesky update, step k): C[i][j] -= C[i][k] C[j][k]^T, k < j <= i
-//   MODE 1 (forward, step k):         R[i][cb] -= C[i][k] R[k][cb],  i > k
-//   MODE 2 (backward, step k):        R[i][cb] -= C[k][i]^T R[k][cb], i < k
+// D -= sum_kk P_kk Q_kk (modes 0-2) or D = P Q (modes 3-5) on 64 x 64 blocks
+// with fp64 MFMA.  Each P and Q is staged in LDS as P[row][p] and Q[p][col]
+// (each mode fills them from its own layout) before D, which may be one of
+// them, is written; the nk pieces of modes 1 and 2 accumulate in registers in
+// increasing kk, so D is read and written once for all of them.
+//   MODE 0 (Cholesky update, step k): C[i][j] -= C[i][k] C[j][k]^T,        k < j <= i
+//   MODE 1 (forward, steps k..k+nk-1): R[i][cb] -= sum C[i][kk] R[kk][cb],  rows i = i0 + y
+//   MODE 2 (backward, steps k..k+nk-1): R[i][cb] -= sum C[kk][i]^T R[kk][cb], rows i = i0 + y
+//   MODE 3 (panel, step k):           C[i][k] = C[i][k] Linv_k^T,          i > k
+//   MODE 4 (forward, step k):         R[k][cb] = Linv_k R[k][cb]
+//   MODE 5 (backward, step k):        R[k][cb] = Linv_k^T R[k][cb]
 template <int MODE>
-__global__ void __launch_bounds__(256) update_kernel(double* c, int d, double* rhs, int d_out, int k) {
+__global__ void __launch_bounds__(256) update_kernel(double* c, int d, double* rhs, int d_out, int k, int nk, int i0,
+                                                     const double* linv) {
+  constexpr bool kReplace = MODE >= 3;
   __shared__ double ps[kB * kLd];
   __shared__ double qs[kB * kLd];
-  int i, j;
+  const int cb = blockIdx.x;  // modes 1, 2, 4, 5: column block of the right-hand side
+  int i = 0;
   double* dst;
   int ldd;
-  const double *p_src, *q_src;
-  int ldp, ldq;
   if (MODE == 0) {
     i = k + 1 + blockIdx.y;
-    j = k + 1 + blockIdx.x;
-    if (j > i) return;  // (whole workgroup)
-    dst = c + (static_cast<size_t>(i) * kB) * d + j * kB;
+    if (k + 1 + static_cast<int>(blockIdx.x) > i) return;  // (whole workgroup)
+    dst = c + (static_cast<size_t>(i) * kB) * d + (k + 1 + blockIdx.x) * kB;
     ldd = d;
-    p_src = c + (static_cast<size_t>(i) * kB) * d + k * kB;
-    q_src = c + (static_cast<size_t>(j) * kB) * d + k * kB;  // used transposed
-    ldp = ldq = d;
-  } else {
-    i = MODE == 1 ? k + 1 + blockIdx.y : blockIdx.y;
-    j = blockIdx.x;  // column block of the right-hand side
-    dst = rhs + (static_cast<size_t>(i) * kB) * d_out + j * kB;
+  } else if (MODE == 3) {
+    i = k + 1 + blockIdx.x;
+    dst = c + (static_cast<size_t>(i) * kB) * d + k * kB;
+    ldd = d;
+  } else if (MODE >= 4) {
+    dst = rhs + (static_cast<size_t>(k) * kB) * d_out + cb * kB;
     ldd = d_out;
-    p_src = MODE == 1 ? c + (static_cast<size_t>(i) * kB) * d + k * kB   // L_ik
-                      : c + (static_cast<size_t>(k) * kB) * d + i * kB;  // L_ki, used transposed
-    ldp = d;
-    q_src = rhs + (static_cast<size_t>(k) * kB) * d_out + j * kB;
-    ldq = d_out;
+  } else {
+    i = i0 + blockIdx.y;
+    dst = rhs + (static_cast<size_t>(i) * kB) * d_out + cb * kB;
+    ldd = d_out;
   }
-  for (int e = threadIdx.x; e < kB * kB; e += 256) {
-    const int r = e / kB, q = e % kB;
-    const double pv = p_src[static_cast<size_t>(r) * ldp + q];
-    const double qv = q_src[static_cast<size_t>(r) * ldq + q];
-    if (MODE == 2) ps[q * kLd + r] = pv; else ps[r * kLd + q] = pv;
-    if (MODE == 0) qs[q * kLd + r] = qv; else qs[r * kLd + q] = qv;
-  }
-  __syncthreads();
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int wr = (wave >> 1) * 32, wc = (wave & 1) * 32;
   const int l16 = lane & 15, lk = lane >> 4;
@@ -238,17 +216,55 @@ __global__ void __launch_bounds__(256) update_kernel(double* c, int d, double* r
   for (int a = 0; a < 2; ++a)
 #pragma unroll
     for (int b = 0; b < 2; ++b) acc[a][b] = d4{0.0, 0.0, 0.0, 0.0};
+  const int pieces = (MODE == 1 || MODE == 2) ? nk : 1;
+  for (int kk = 0; kk < pieces; ++kk) {
+    const int kc = k + kk;
+    const double* li = linv + static_cast<size_t>(kc) * kB * kB;
+    const double *p_src, *q_src;
+    int ldp, ldq;
+    if (MODE == 0) {
+      p_src = c + (static_cast<size_t>(i) * kB) * d + kc * kB;
+      q_src = c + (static_cast<size_t>(k + 1 + blockIdx.x) * kB) * d + kc * kB;  // used transposed
+      ldp = ldq = d;
+    } else if (MODE == 3) {
+      p_src = dst;
+      ldp = d;
+      q_src = li;  // used transposed
+      ldq = kB;
+    } else if (MODE >= 4) {
+      p_src = li;  // MODE 5: used transposed
+      ldp = kB;
+      q_src = dst;
+      ldq = d_out;
+    } else {
+      p_src = MODE == 1 ? c + (static_cast<size_t>(i) * kB) * d + kc * kB   // L_i,kc
+                        : c + (static_cast<size_t>(kc) * kB) * d + i * kB;  // L_kc,i, used transposed
+      ldp = d;
+      q_src = rhs + (static_cast<size_t>(kc) * kB) * d_out + cb * kB;
+      ldq = d_out;
+    }
+    if (kk) __syncthreads();  // every wave is done with the previous piece
+    for (int e = threadIdx.x; e < kB * kB; e += 256) {
+      const int r = e / kB, q = e % kB;
+      const double pv = p_src[static_cast<size_t>(r) * ldp + q];
+      const double qv = q_src[static_cast<size_t>(r) * ldq + q];
+      if (MODE == 2 || MODE == 5) ps[q * kLd + r] = pv; else ps[r * kLd + q] = pv;
+      if (MODE == 0 || MODE == 3) qs[q * kLd + r] = qv; else qs[r * kLd + q] = qv;
+    }
+    __syncthreads();
 #pragma unroll 4
-  for (int p = 0; p < kB; p += 4) {
-    double av[2], bv[2];
+    for (int p = 0; p < kB; p += 4) {
+      double av[2], bv[2];
 #pragma unroll
-    for (int a = 0; a < 2; ++a) av[a] = ps[(wr + 16 * a + l16) * kLd + p + lk];
+      for (int a = 0; a < 2; ++a) av[a] = ps[(wr + 16 * a + l16) * kLd + p + lk];
 #pragma unroll
-    for (int b = 0; b < 2; ++b) bv[b] = qs[(p + lk) * kLd + wc + 16 * b + l16];
+      for (int b = 0; b < 2; ++b) bv[b] = qs[(p + lk) * kLd + wc + 16 * b + l16];
 #pragma unroll
-    for (int a = 0; a < 2; ++a)
+      for (int a = 0; a < 2; ++a)
 #pragma unroll
-      for (int b = 0; b < 2; ++b) acc[a][b] = __builtin_amdgcn_mfma_f64_16x16x4f64(av[a], bv[b], acc[a][b], 0, 0, 0);
+        for (int b = 0; b < 2; ++b)
+          acc[a][b] = __builtin_amdgcn_mfma_f64_16x16x4f64(av[a], bv[b], acc[a][b], 0, 0, 0);
+    }
   }
 #pragma unroll
   for (int a = 0; a < 2; ++a)
@@ -257,7 +273,10 @@ __global__ void __launch_bounds__(256) update_kernel(double* c, int d, double* r
 #pragma unroll
       for (int v = 0; v < 4; ++v) {
         const int row = wr + 16 * a + 4 * v + lk, col = wc + 16 * b + l16;
-        dst[static_cast<size_t>(row) * ldd + col] -= acc[a][b][v];
+        if (kReplace)
+          dst[static_cast<size_t>(row) * ldd + col] = acc[a][b][v];
+        else
+          dst[static_cast<size_t>(row) * ldd + col] -= acc[a][b][v];
       }
 }
 
@@ -272,13 +291,26 @@ __global__ void __launch_bounds__(256) transpose_out_kernel(const double* w, int
   for (int r = ty; r < 32; r += 8) a[static_cast<size_t>(j0 + r) * d_in + i0 + tx] = t[tx][r];
 }
 
-__global__ void __launch_bounds__(256) offset_kernel(const double* w, const double* mx, const double* my, int d_in,
-                                                     int d_out, float* b) {
+// b[j] = my[j] - sum_i W[i][j] mx[i] (b = 0 when raw, since then my = mx = 0),
+// in two fixed-order levels: partial sums over 128-row chunks of i, then the
+// chunks in increasing order.
+constexpr int kOffRows = 128;
+__global__ void __launch_bounds__(256) offset_part_kernel(const double* w, const double* mx, int d_out, double* part) {
   const int j = blockIdx.x * 256 + threadIdx.x;
   if (j >= d_out) return;
-  double v = my[j];
-  for (int i = 0; i < d_in; ++i) v -= w[static_cast<size_t>(i) * d_out + j] * mx[i];
-  b[j] = static_cast<float>(v);
+  const int i0 = blockIdx.y * kOffRows;
+  double v = 0.0;
+  for (int i = i0; i < i0 + kOffRows; ++i) v += w[static_cast<size_t>(i) * d_out + j] * mx[i];
+  part[static_cast<size_t>(blockIdx.y) * d_out + j] = v;
+}
+
+__global__ void __launch_bounds__(256) offset_kernel(const double* part, const double* my, int n_part, int d_out,
+                                                     float* b) {
+  const int j = blockIdx.x * 256 + threadIdx.x;
+  if (j >= d_out) return;
+  double v = 0.0;
+  for (int c = 0; c < n_part; ++c) v += part[static_cast<size_t>(c) * d_out + j];
+  b[j] = static_cast<float>(my[j] - v);
 }
 
 }  // namespace
@@ -287,7 +319,8 @@ size_t ridge_solve_workspace_bytes(int d_in, int d_out) {
   const size_t up = 256;
   auto r = [&](size_t v) { return (v + up - 1) / up * up; };
   return r(sizeof(double) * static_cast<size_t>(d_in) * d_in) + r(sizeof(double) * static_cast<size_t>(d_in) * d_out) +
-         r(sizeof(double) * d_in) + r(sizeof(double) * d_out) + up;
+         r(sizeof(double) * d_in) + r(sizeof(double) * d_out) + r(sizeof(double) * static_cast<size_t>(d_in) * kB) +
+         r(sizeof(double) * static_cast<size_t>(d_in / kOffRows) * d_out) + up;
 }
 
 hipError_t ridge_solve_enqueue(const RidgeSolveIn& in, double lambda, bool raw, float* a_out, float* b_out, void* ws,
@@ -314,6 +347,10 @@ hipError_t ridge_solve_enqueue(const RidgeSolveIn& in, double lambda, bool raw, 
   p += r(sizeof(double) * di);
   a.my = reinterpret_cast<double*>(p);
   p += r(sizeof(double) * dout);
+  double* linv = reinterpret_cast<double*>(p);  // [d_in / 64][64][64]
+  p += r(sizeof(double) * static_cast<size_t>(di) * kB);
+  double* part = reinterpret_cast<double*>(p);  // [d_in / 128][d_out]
+  p += r(sizeof(double) * static_cast<size_t>(di / kOffRows) * dout);
   a.flag = reinterpret_cast<int*>(p);
   *flag_out = a.flag;
 
@@ -322,23 +359,43 @@ hipError_t ridge_solve_enqueue(const RidgeSolveIn& in, double lambda, bool raw, 
   hipLaunchKernelGGL(ridge_diag_kernel, dim3(1), dim3(256), 0, s, a);
   const int T = di / kB, TC = dout / kB;
   for (int k = 0; k < T; ++k) {
-    hipLaunchKernelGGL(potrf_kernel, dim3(1), dim3(256), 0, s, a.c, di, k, a.flag);
+    hipLaunchKernelGGL(potrf_inv_kernel, dim3(1), dim3(256), 0, s, a.c, di, k, a.flag, linv);
     if (k + 1 < T) {
-      hipLaunchKernelGGL(trsm_panel_kernel, dim3(T - k - 1), dim3(64), 0, s, a.c, di, k);
-      hipLaunchKernelGGL((update_kernel<0>), dim3(T - k - 1, T - k - 1), dim3(256), 0, s, a.c, di, a.r, dout, k);
+      hipLaunchKernelGGL((update_kernel<3>), dim3(T - k - 1), dim3(256), 0, s, a.c, di, a.r, dout, k, 1, 0, linv);
+      hipLaunchKernelGGL((update_kernel<0>), dim3(T - k - 1, T - k - 1), dim3(256), 0, s, a.c, di, a.r, dout, k, 1, 0,
+                         linv);
     }
   }
-  for (int k = 0; k < T; ++k) {
-    hipLaunchKernelGGL((trsv_rows_kernel<true>), dim3((dout + 255) / 256), dim3(256), 0, s, a.c, di, a.r, dout, k);
-    if (k + 1 < T)
-      hipLaunchKernelGGL((update_kernel<1>), dim3(TC, T - k - 1), dim3(256), 0, s, a.c, di, a.r, dout, k);
+  // L Z = R, kSuper block rows at a time: within the group, Z_k = Linv_k R_k
+  // and a rank-64 update of the group's later rows; then one update of every
+  // row below the group with all of its pieces.
+  for (int k0 = 0; k0 < T; k0 += kSuper) {
+    const int k1 = std::min(k0 + kSuper, T);
+    for (int k = k0; k < k1; ++k) {
+      hipLaunchKernelGGL((update_kernel<4>), dim3(TC), dim3(256), 0, s, a.c, di, a.r, dout, k, 1, 0, linv);
+      if (k + 1 < k1)
+        hipLaunchKernelGGL((update_kernel<1>), dim3(TC, k1 - k - 1), dim3(256), 0, s, a.c, di, a.r, dout, k, 1, k + 1,
+                           linv);
+    }
+    if (k1 < T)
+      hipLaunchKernelGGL((update_kernel<1>), dim3(TC, T - k1), dim3(256), 0, s, a.c, di, a.r, dout, k0, k1 - k0, k1,
+                         linv);
   }
-  for (int k = T - 1; k >= 0; --k) {
-    hipLaunchKernelGGL((trsv_rows_kernel<false>), dim3((dout + 255) / 256), dim3(256), 0, s, a.c, di, a.r, dout, k);
-    if (k > 0) hipLaunchKernelGGL((update_kernel<2>), dim3(TC, k), dim3(256), 0, s, a.c, di, a.r, dout, k);
+  // L^T W = Z the same way, from the last block row up.
+  for (int k1 = T; k1 > 0; k1 -= kSuper) {
+    const int k0 = std::max(k1 - kSuper, 0);
+    for (int k = k1 - 1; k >= k0; --k) {
+      hipLaunchKernelGGL((update_kernel<5>), dim3(TC), dim3(256), 0, s, a.c, di, a.r, dout, k, 1, 0, linv);
+      if (k > k0)
+        hipLaunchKernelGGL((update_kernel<2>), dim3(TC, k - k0), dim3(256), 0, s, a.c, di, a.r, dout, k, 1, k0, linv);
+    }
+    if (k0 > 0)
+      hipLaunchKernelGGL((update_kernel<2>), dim3(TC, k0), dim3(256), 0, s, a.c, di, a.r, dout, k0, k1 - k0, 0, linv);
   }
   hipLaunchKernelGGL(transpose_out_kernel, dim3(dout / 32, di / 32), dim3(256), 0, s, a.r, di, dout, a_out);
-  hipLaunchKernelGGL(offset_kernel, dim3((dout + 255) / 256), dim3(256), 0, s, a.r, a.mx, a.my, di, dout, b_out);
+  hipLaunchKernelGGL(offset_part_kernel, dim3((dout + 255) / 256, di / kOffRows), dim3(256), 0, s, a.r, a.mx, dout,
+                     part);
+  hipLaunchKernelGGL(offset_kernel, dim3((dout + 255) / 256), dim3(256), 0, s, part, a.my, di / kOffRows, dout, b_out);
   return hipGetLastError();
 }
 
