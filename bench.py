@@ -27,7 +27,6 @@ from __future__ import annotations
 
 import argparse
 import gc
-import glob
 import json
 import os
 import re
@@ -70,13 +69,18 @@ def flops_per_row_layer(s):
     return 2 * s.d_in * s.d_out, 2 * s.d_out * (2 * s.kv_width + s.idx_heads * s.head_dim)
 
 
+# The sources a fill's kernels and launches come from (the fit's capture and
+# solve are not on the fill path and do not change its traffic).
+FILL_SOURCES = ("rf_kernels.hip", "rf_rows.hip", "rf_quant.hip", "rf_rescale.hip", "rf_internal.h", "rf_api.cpp")
+
+
 def kernel_source_hash() -> str:
-    """SHA-256 over the device sources (every .hip file of the library)."""
+    """SHA-256 over the sources of the fill's kernels and of their launches."""
     import hashlib
     h = hashlib.sha256()
-    for path in sorted(glob.glob(os.path.join(CSRC, "*.hip"))):
-        h.update(os.path.basename(path).encode())
-        with open(path, "rb") as f:
+    for name in FILL_SOURCES:
+        h.update(name.encode())
+        with open(os.path.join(CSRC, name), "rb") as f:
             h.update(f.read())
     return h.hexdigest()
 
