@@ -13,7 +13,9 @@ against the fp64 oracle:
 The deployed 27B configuration of the pages (int8 maps and the value rescale
 on the first 512 tail rows, RidgeFill sections 2.3 and 4.2) runs at the 120K
 size with the measurement inside the fill.  Each case prints how many rows it
-checked; the session's summary lists them (tests/conftest.py).
+checked; the session's summary lists them (tests/conftest.py).  The 120K
+fill is also checked bitwise against itself: rerun, one layer per launch,
+and filled in two interleaved halves.
 """
 import numpy as np
 import pytest
@@ -163,3 +165,34 @@ def test_full_size_deployed_27b_q8_value_rescale():
     rs = sample_rows(f, w.exact_rows, w.positions, n_min=4096, seed=1)
     worst = _check_layers(f"{name} deployed", w, {"K": kc, "V": vc}, rs, False, rescale=(ref_scales, g_of_row))
     _record(f"{name} q8 + value rescale c={c} (measured in the fill)", len(rs), len(f), s.n_late, worst)
+
+
+def test_full_size_bitwise_rerun_grouping_and_row_split():
+    """The 27B-shaped 120K fill in the benchmark's configuration, bitwise: a
+    second identical call, one layer per launch instead of six, and the fill
+    rows split in two halves that interleave 64-row runs (so every 256-row
+    tile holds other rows than before) all give the same caches."""
+    name = "27b_120k"
+    s = workloads.spec(name)
+    _say(f"[full] {name}: bitwise rerun, grouping and row split")
+    w = workloads.make(s)
+    di = U.DeviceInputs(w)
+    plan = B.Plan.for_spec(s)
+    rows, n = U.gpu_fill_rows(plan, di)
+    g = BENCH_GROUP[name]
+    ref = U.gpu_fill(plan, di, rows, n, layers_per_launch=g)
+
+    def same(out, what):
+        for l in range(s.n_late):
+            assert torch.equal(ref[0][l], out[0][l]) and torch.equal(ref[1][l], out[1][l]), f"{what}: layer {l}"
+        _say(f"[full] {name}: {what} bitwise equal")
+
+    same(U.gpu_fill(plan, di, rows, n, layers_per_launch=g), "second call")
+    same(U.gpu_fill(plan, di, rows, n, layers_per_launch=1), "one layer per launch")
+    f = rows.cpu().numpy()
+    run = (np.arange(len(f)) // 64) % 2 == 0
+    a = torch.from_numpy(f[run].copy()).cuda()
+    b = torch.from_numpy(f[~run].copy()).cuda()
+    caches = di.caches()
+    U.gpu_fill(plan, di, a, a.numel(), caches=caches, layers_per_launch=g)
+    same(U.gpu_fill(plan, di, b, b.numel(), caches=caches, layers_per_launch=g), "two interleaved halves")
