@@ -10,7 +10,9 @@ against the fp64 oracle:
     every 16-row block and both row halves of the tile are met across tiles),
     the first and last fill rows, the rows on both sides of every exact span
     and prompt boundary, the largest positions, and seeded random rows.
-The deployed 27B configuration of the pages (int8 maps and the value rescale
+The 120K workload also runs with 30% of its prefix exact in 1,113 spans and
+an indexer head (a ragged last tile).  The deployed 27B configuration of the
+pages (int8 maps and the value rescale
 on the first 512 tail rows, RidgeFill sections 2.3 and 4.2) runs at the 120K
 size with the measurement inside the fill.  Each case prints how many rows it
 checked; the session's summary lists them (tests/conftest.py).  The 120K
@@ -62,17 +64,22 @@ def sample_rows(fill: np.ndarray, exact: np.ndarray, positions: np.ndarray, n_mi
     return np.array(sorted(pick), dtype=np.int32)
 
 
-# (workload, map format, QK-norm, indexer heads, rows checked: "all" or a minimum)
+# (workload, map format, QK-norm, indexer heads, rows checked: "all" or a
+# minimum, exact spans: None for the workload's own)
 FULL_CASES = [
-    ("tiny", "bf16", False, 0, "all"),
-    ("8b", "bf16", False, 0, "all"),
-    ("27b", "bf16", False, 0, 4096),
-    ("27b_120k", "bf16", False, 0, 4096),
-    ("8b_ragged_host", "bf16", False, 0, "all"),
-    ("27b_120k", "q8", False, 0, 4096),
-    ("8b_ragged_host", "q8", False, 0, "all"),
-    ("27b", "bf16", True, 0, 4096),
-    ("27b_120k", "bf16", False, 1, 4096),
+    ("tiny", "bf16", False, 0, "all", None),
+    ("8b", "bf16", False, 0, "all", None),
+    ("27b", "bf16", False, 0, 4096, None),
+    ("27b_120k", "bf16", False, 0, 4096, None),
+    ("8b_ragged_host", "bf16", False, 0, "all", None),
+    ("27b_120k", "q8", False, 0, 4096, None),
+    ("8b_ragged_host", "q8", False, 0, "all", None),
+    ("27b", "bf16", True, 0, 4096, None),
+    ("27b_120k", "bf16", False, 1, 4096, None),
+    # 30% of the prefix kept exact in 1,113 scattered spans, as the pages'
+    # 27B runs keep 28-31%: 83,168 fill rows, so the last 256-row tile holds
+    # 224 rows and the last tall indexer tile covers one row tile
+    ("27b_120k", "bf16", False, 1, 4096, 1113),
 ]
 
 
@@ -102,12 +109,14 @@ def _record(label, checked, n_fill, n_late, worst):
     _say(f"[full] {line}")
 
 
-@pytest.mark.parametrize("name,fmt,qk,idx,checked", FULL_CASES,
-                         ids=[f"{n}-{f}{'-qk' if q else ''}{'-idx' if i else ''}" for n, f, q, i, _ in FULL_CASES])
-def test_full_size(name, fmt, qk, idx, checked):
-    s = workloads.spec(name, map_format=fmt, qk_norm=qk, idx_heads=idx)
-    _say(f"[full] {name} ({fmt} maps{', QK-norm' if qk else ''}{', indexer keys' if idx else ''}): "
-         "generating inputs")
+@pytest.mark.parametrize("name,fmt,qk,idx,checked,spans", FULL_CASES,
+                         ids=[f"{n}-{f}{'-qk' if q else ''}{'-idx' if i else ''}{f'-spans{sp}' if sp else ''}"
+                              for n, f, q, i, _, sp in FULL_CASES])
+def test_full_size(name, fmt, qk, idx, checked, spans):
+    over = {} if spans is None else {"n_spans": spans}
+    s = workloads.spec(name, map_format=fmt, qk_norm=qk, idx_heads=idx, **over)
+    _say(f"[full] {name} ({fmt} maps{', QK-norm' if qk else ''}{', indexer keys' if idx else ''}"
+         f"{f', {spans} exact spans' if spans else ''}): generating inputs")
     w = workloads.make(s)
     di = U.DeviceInputs(w)
     plan = B.Plan.for_spec(s)
@@ -126,7 +135,8 @@ def test_full_size(name, fmt, qk, idx, checked):
     if idx:
         caches["I"] = ic
     worst = _check_layers(name, w, caches, rs, bool(idx))
-    _record(f"{name} {fmt}{' qk-norm' if qk else ''}{' indexer' if idx else ''}", len(rs), len(f), s.n_late, worst)
+    _record(f"{name} {fmt}{' qk-norm' if qk else ''}{' indexer' if idx else ''}{f' {spans} spans' if spans else ''}",
+            len(rs), len(f), s.n_late, worst)
 
 
 def test_full_size_deployed_27b_q8_value_rescale():
