@@ -31,5 +31,5 @@ from .rescale import (  # noqa: F401
     calibration_rows, fill_workload_rescaled, head_norms, rescale_values, scales_from_values, value_scales,
 )
 from .quant import (  # noqa: F401
-    dequantize_q8, dequantize_q8_bf16, f64_to_bf16_bits, quantize_q8,
+    dequantize_q8, dequantize_q8_bf16, f64_to_bf16_bits, map_bytes, quantize_q8,
 )

@@ -25,6 +25,17 @@ import numpy as np
 BLOCK = 128
 
 
+def map_bytes(d_in: int, d_out: int, fmt: str) -> int:
+    """Stored bytes of one map (section 2.2, "Size and cost": d_out rows of
+    d_in weights): two per weight in bf16; for int8, one code per weight plus
+    one two-byte bf16 scale for each block of BLOCK weights of a row."""
+    if fmt == "bf16":
+        return 2 * d_in * d_out
+    if fmt == "q8":
+        return d_in * d_out + 2 * d_out * (d_in // BLOCK)
+    raise ValueError(f"unknown map format {fmt!r}")
+
+
 def _decode_bf16(bits: np.ndarray) -> np.ndarray:
     """Exact value of bf16 bit patterns (uint16) as float64."""
     b = np.asarray(bits, dtype=np.uint16).astype(np.uint32) << 16

@@ -743,6 +743,20 @@ def pin_printed_ceilings(o):
         assert abs(v - c["printed"]) <= 0.005 + 1e-12, (c, v)
 
 
+def pin_printed_map_sizes(o):
+    """The map sizes the pages print (tests/golden/map_sizes.json), at the
+    precision printed.  The 0.60 GiB of Flash-Next's maps pins the int8
+    format's scale overhead to between 1.55% and 3.3% of the codes: a
+    two-byte scale per 128 weights (1.56%) fits, one scale per row or none
+    does not, and neither does bf16 storage."""
+    with open(os.path.join(GOLDEN, "map_sizes.json")) as f:
+        gold = json.load(f)
+    for c in gold["cases"]:
+        total = c["layers"] * o.map_bytes(c["d_in"], c["d_out"], c["format"])
+        v = round(total / c["unit_bytes"], c["digits"])
+        assert abs(v - c["printed"]) < 1e-9, (c, total / c["unit_bytes"])
+
+
 FILL_PINS = [pin_fill_rows_partition, pin_identity_map_is_exact_kv, pin_map_orientation,
              pin_bias_only_map, pin_rmsnorm_closed_forms, pin_one_hot_layer_kv,
              pin_rope_is_complex_rotation, pin_rope_invariants, pin_brute_force_tiny,
@@ -753,7 +767,7 @@ RIDGE_PINS = [pin_ridge_recovers_linear_map, pin_ridge_svd_form, pin_ridge_runni
 CEILING_PINS = [pin_printed_ceilings]
 QUANT_PINS = [pin_q8_dequant_closed_form, pin_q8_dequant_brute, pin_q8_grid_fixpoint,
               pin_q8_quantize_bounds, pin_q8_quantize_ties, pin_q8_quantize_brute,
-              pin_bf16_rounding_library]
+              pin_bf16_rounding_library, pin_printed_map_sizes]
 RESCALE_PINS = [pin_rescale_closed_form, pin_rescale_identity_and_invariances, pin_rescale_brute,
                 pin_calibration_rows, pin_rescaled_fill]
 ALL_PINS = FILL_PINS + RIDGE_PINS + CEILING_PINS + QUANT_PINS + RESCALE_PINS

@@ -96,6 +96,10 @@ MUTANTS = {
     "q8_scale_truncated": ("quant.py", [("((u + 0x7FFF + ((u >> 16) & 1)) >> 16)", "(u >> 16)")]),
     "q8_max_over_rows": ("quant.py", [("m = np.abs(blocks).max(axis=2)", "m = np.abs(blocks).max(axis=2).max(axis=0, keepdims=True) + 0 * blocks[:, :, 0]")]),
     "bf16_round_truncates": ("quant.py", [("return ((u + 0x7FFF + lsb) >> 16)", "return ((u) >> 16)")]),
+    "q8_size_one_scale_per_row": ("quant.py", [("return d_in * d_out + 2 * d_out * (d_in // BLOCK)",
+                                                "return d_in * d_out + 2 * d_out")]),
+    "q8_size_as_bf16": ("quant.py", [("return d_in * d_out + 2 * d_out * (d_in // BLOCK)",
+                                      "return 2 * d_in * d_out + 2 * d_out * (d_in // BLOCK)")]),
     "bf16_round_ties_up": ("quant.py", [("return ((u + 0x7FFF + lsb) >> 16)", "return ((u + 0x8000) >> 16)")]),
     # the value rescale
     "rescale_ratio_of_means": ("rescale.py", [("np.mean(ne[ok, h] / npr[ok, h])", "np.mean(ne[ok, h]) / np.mean(npr[ok, h])")]),
