@@ -114,12 +114,12 @@ def test_identity_fill_equals_exact_projection(name):
     U.check_values(kc2, vc2, ref, f, s.head_dim)
 
 
-def _spread_rows(x: torch.Tensor) -> torch.Tensor:
+def _spread_rows(x: torch.Tensor, span: int) -> torch.Tensor:
     """x's rows copied into a strided view whose rows lie so far apart that
-    the view spans more than 4 GiB (row starts stay 16-byte aligned)."""
+    n_rows * row stride covers about `span` bytes (row starts stay 16-byte
+    aligned)."""
     n, d = x.shape
-    ld = ((1 << 32) // (2 * n) + 64) // 8 * 8
-    assert n * ld * 2 >= (1 << 32)
+    ld = (span // (2 * n) + 64) // 8 * 8
     flat = torch.zeros((n - 1) * ld + d, dtype=x.dtype, device=x.device)
     v = torch.as_strided(flat, (n, d), (ld, 1))
     v.copy_(x)
@@ -135,24 +135,26 @@ WIDE_CASES = {
 }
 
 
-@pytest.mark.parametrize("name", list(WIDE_CASES))
-def test_operands_spanning_4gib(name):
+@pytest.mark.parametrize("name,gib", [(n, g) for n in WIDE_CASES for g in (3, 4)])
+def test_operands_spanning_4gib(name, gib):
     """An operand whose rows span 4 GiB or more is read through 64-bit
     pointers (the usual path reads through a buffer resource with 32-bit
-    offsets, and tall indexer tiles are not used): the fill with such a
-    split-layer state, and rf_kv_project with such layer inputs, write the
-    same bytes as with the compact layout."""
+    offsets, and tall indexer tiles are not used); one spanning 3 GiB stays
+    on the usual path with a buffer size above 2^31 bytes.  Either way the
+    fill with such a split-layer state, and rf_kv_project with such layer
+    inputs, write the same bytes as with the compact layout."""
     w = workloads.make(WIDE_CASES[name])
     s = w.spec
-    _say(f"[wide] {name}, rows spread over more than 4 GiB")
+    _say(f"[wide] {name}, rows spread over about {gib} GiB")
     di = U.DeviceInputs(w, maps_on_host=False)
     plan = U.plan_for(w, maps_on_host=False)
     rows, n = U.gpu_fill_rows(plan, di)
     fill1 = U.gpu_fill(plan, di, rows, n)
     proj1 = U.gpu_kv_project(plan, di, [di.x] * s.n_late, rows, n)
     compact = di.x
-    di.x = _spread_rows(compact)
-    assert di.x.stride(0) * s.n_rows * 2 >= (1 << 32)
+    di.x = _spread_rows(compact, gib << 30)
+    span = di.x.stride(0) * s.n_rows * 2
+    assert (span >= (1 << 32)) if gib >= 4 else ((1 << 31) < span < (1 << 32)), span
     fill2 = U.gpu_fill(plan, di, rows, n)
     proj2 = U.gpu_kv_project(plan, di, [di.x] * s.n_late, rows, n)
     di.x = None
