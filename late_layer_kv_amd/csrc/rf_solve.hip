@@ -220,7 +220,11 @@ __global__ void __launch_bounds__(256) update_kernel(double* c, int d, double* r
 #pragma unroll
     for (int b = 0; b < 2; ++b) acc[a][b] = d4{0.0, 0.0, 0.0, 0.0};
   const int pieces = (MODE == 1 || MODE == 2) ? nk : 1;
-  for (int kk = 0; kk < pieces; ++kk) {
+  // Piece kk's 64 x 64 blocks of P and Q go through registers: the loads of
+  // piece kk + 1 are issued before the products of piece kk, so their latency
+  // hides behind them; the order of the products is unchanged.
+  double pv[kB * kB / 256], qv[kB * kB / 256];
+  auto fetch = [&](int kk) {
     const int kc = k + kk;
     const double* li = linv + static_cast<size_t>(kc) * kB * kB;
     const double *p_src, *q_src;
@@ -246,15 +250,28 @@ __global__ void __launch_bounds__(256) update_kernel(double* c, int d, double* r
       q_src = rhs + (static_cast<size_t>(kc) * kB) * d_out + cb * kB;
       ldq = d_out;
     }
-    if (kk) __syncthreads();  // every wave is done with the previous piece
-    for (int e = threadIdx.x; e < kB * kB; e += 256) {
+#pragma unroll
+    for (int n = 0; n < kB * kB / 256; ++n) {
+      const int e = static_cast<int>(threadIdx.x) + 256 * n;
       const int r = e / kB, q = e % kB;
-      const double pv = p_src[static_cast<size_t>(r) * ldp + q];
-      const double qv = q_src[static_cast<size_t>(r) * ldq + q];
-      if (MODE == 2 || MODE == 5) ps[q * kLd + r] = pv; else ps[r * kLd + q] = pv;
-      if (MODE == 0 || MODE == 3) qs[q * kLd + r] = qv; else qs[r * kLd + q] = qv;
+      pv[n] = p_src[static_cast<size_t>(r) * ldp + q];
+      qv[n] = q_src[static_cast<size_t>(r) * ldq + q];
     }
-    __syncthreads();
+  };
+  auto put = [&]() {
+#pragma unroll
+    for (int n = 0; n < kB * kB / 256; ++n) {
+      const int e = static_cast<int>(threadIdx.x) + 256 * n;
+      const int r = e / kB, q = e % kB;
+      if (MODE == 2 || MODE == 5) ps[q * kLd + r] = pv[n]; else ps[r * kLd + q] = pv[n];
+      if (MODE == 0 || MODE == 3) qs[q * kLd + r] = qv[n]; else qs[r * kLd + q] = qv[n];
+    }
+  };
+  fetch(0);
+  put();
+  __syncthreads();
+  for (int kk = 0; kk < pieces; ++kk) {
+    if (kk + 1 < pieces) fetch(kk + 1);
 #pragma unroll 4
     for (int p = 0; p < kB; p += 4) {
       double av[2], bv[2];
@@ -268,7 +285,16 @@ __global__ void __launch_bounds__(256) update_kernel(double* c, int d, double* r
         for (int b = 0; b < 2; ++b)
           acc[a][b] = __builtin_amdgcn_mfma_f64_16x16x4f64(av[a], bv[b], acc[a][b], 0, 0, 0);
     }
+    if (kk + 1 < pieces) {
+      __syncthreads();  // every wave is done with piece kk
+      put();
+      __syncthreads();
+    }
   }
+  // D's old values are all read before any store, so the 16 reads are in
+  // flight together (a read-modify-write per element would wait out each one:
+  // the compiler cannot tell that the stores do not alias the later reads).
+  double old[2][2][4];
 #pragma unroll
   for (int a = 0; a < 2; ++a)
 #pragma unroll
@@ -276,10 +302,16 @@ __global__ void __launch_bounds__(256) update_kernel(double* c, int d, double* r
 #pragma unroll
       for (int v = 0; v < 4; ++v) {
         const int row = wr + 16 * a + 4 * v + lk, col = wc + 16 * b + l16;
-        if (kReplace)
-          dst[static_cast<size_t>(row) * ldd + col] = acc[a][b][v];
-        else
-          dst[static_cast<size_t>(row) * ldd + col] -= acc[a][b][v];
+        old[a][b][v] = kReplace ? 0.0 : dst[static_cast<size_t>(row) * ldd + col];
+      }
+#pragma unroll
+  for (int a = 0; a < 2; ++a)
+#pragma unroll
+    for (int b = 0; b < 2; ++b)
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        const int row = wr + 16 * a + 4 * v + lk, col = wc + 16 * b + l16;
+        dst[static_cast<size_t>(row) * ldd + col] = kReplace ? acc[a][b][v] : old[a][b][v] - acc[a][b][v];
       }
 }
 
