@@ -97,17 +97,20 @@ __global__ void __launch_bounds__(256) ridge_diag_kernel(const SolveArgs a) {
 // Cholesky of diagonal block k in place (its lower triangle) and the inverse
 // of its factor, Linv_k = L_kk^-1, in one right-looking sweep over the
 // columns.  Thread t owns column l = t / 4 and rows i = t % 4 + 4 r (r < 16)
-// of both the block (sv) and of Y, which starts as the identity.  At column
-// j the pivot's owner publishes sqrt(C_jj); the owners of column j scale it
-// by the pivot's reciprocal (column j of L), the owners of row j scale row j
-// of Y (row j of Linv: Y_j = e_j - sum_{p<j} L_jp Linv_p by then), and every
-// thread updates its entries below row j: C_il -= L_ij L_lj and
-// Y_il -= L_ij Linv_jl.  Two barriers per column; the rows of the block
-// travel through LDS only as column j of L and row j of Linv.
+// of both the block (sv) and of Y, which starts as the identity; the four
+// owners of a column are one lane quad.  At column j the quad of column j
+// shares the pivot C_jj (a quad shuffle), scales the column by the pivot's
+// reciprocal (column j of L) and publishes it; after the one barrier of the
+// step every quad takes Y_jl, the entry of row j in its own column, from its
+// own lane (j & 3) and scales it (row j of Linv: Y_j = e_j - sum_{p<j} L_jp
+// Linv_p by then), and every thread updates its entries below row j:
+// C_il -= L_ij L_lj and Y_il -= L_ij Linv_jl.  Column j of L travels through
+// LDS in a double buffer, so the next column's quad may publish while others
+// still read this one.
 __global__ void __launch_bounds__(256) potrf_inv_kernel(double* c, int d, int k, int* flag, double* linv) {
-  __shared__ double colj[kB];  // column j of L
-  __shared__ double rowj[kB];  // row j of Linv
-  __shared__ double dg[kB];    // the pivots
+  __shared__ double colj[2][kB];  // column j of L, by step parity
+  __shared__ double rinv[2];      // 1 / L_jj, by step parity
+  __shared__ double dg[kB];       // the pivots
   double* blk = c + (static_cast<size_t>(k) * kB) * d + k * kB;
   const int t = threadIdx.x;
   const int l = t >> 2, rg = t & 3;
@@ -118,51 +121,50 @@ __global__ void __launch_bounds__(256) potrf_inv_kernel(double* c, int d, int k,
     sv[r] = i >= l ? blk[static_cast<size_t>(i) * d + l] : 0.0;
     yv[r] = i == l ? 1.0 : 0.0;
   }
-  for (int j = 0; j < kB; ++j) {
-    const int rj = j >> 2;
-    if (l == j && rg == (j & 3)) {
-      double v = 0.0;
+  // j = 4 rj + src: the register index rj of row j is a constant of the
+  // unrolled outer loop, and rows above it (r < rj) are skipped statically
 #pragma unroll
-      for (int r = 0; r < 16; ++r) v = r == rj ? sv[r] : v;
-      if (!(v > 0.0)) {
-        *flag = 1;
-        v = 1.0;  // keep going with finite values; the call reports the failure
+  for (int rj = 0; rj < 16; ++rj) {
+#pragma unroll 1
+    for (int src = 0; src < 4; ++src) {
+      const int j = 4 * rj + src, pb = src & 1;
+      if (l == j) {
+        double v = __shfl(sv[rj], src, 4);  // C_jj, from the quad's lane that holds row j
+        if (!(v > 0.0)) {
+          if (rg == 0) *flag = 1;
+          v = 1.0;  // keep going with finite values; the call reports the failure
+        }
+        const double dj = sqrt(v);
+        const double rp = 1.0 / dj;
+        if (rg == 0) {
+          dg[j] = dj;
+          rinv[pb] = rp;
+        }
+#pragma unroll
+        for (int r = rj; r < 16; ++r) {
+          if (r > rj || rg > src) {  // i = rg + 4 r > j
+            sv[r] *= rp;
+            colj[pb][rg + 4 * r] = sv[r];
+          }
+        }
       }
-      dg[j] = sqrt(v);
-    }
-    __syncthreads();
-    const double rp = 1.0 / dg[j];
-    if (l == j) {
+      __syncthreads();
+      const double rp = rinv[pb];
+      const double yj = __shfl(yv[rj], src, 4) * rp;  // Linv_jl for this thread's column l
+      if (rg == src) yv[rj] = yj;
+      const double cl = l > j ? colj[pb][l] : 0.0;
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
+      for (int r = rj; r < 16; ++r) {
         const int i = rg + 4 * r;
-        if (i > j) {
-          sv[r] *= rp;
-          colj[i] = sv[r];
+        if (r > rj || rg > src) {  // i > j
+          const double ci = colj[pb][i];
+          if (l > j && l <= i) sv[r] -= ci * cl;
+          yv[r] -= ci * yj;
         }
-      }
-    }
-    if (rg == (j & 3)) {
-#pragma unroll
-      for (int r = 0; r < 16; ++r)
-        if (r == rj) {
-          yv[r] *= rp;
-          rowj[l] = yv[r];
-        }
-    }
-    __syncthreads();
-    const double cl = l > j ? colj[l] : 0.0;
-    const double yj = rowj[l];
-#pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const int i = rg + 4 * r;
-      if (i > j) {
-        const double ci = colj[i];
-        if (l > j && l <= i) sv[r] -= ci * cl;
-        yv[r] -= ci * yj;
       }
     }
   }
+  __syncthreads();  // dg complete
   double* out = linv + static_cast<size_t>(k) * kB * kB;
 #pragma unroll
   for (int r = 0; r < 16; ++r) {
