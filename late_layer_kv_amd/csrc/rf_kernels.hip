@@ -317,7 +317,11 @@ __device__ __forceinline__ float agpr(float a) {
 // after every second MFMA, and the waves' instruction streams stall less
 // behind a full load queue (both contractions ran 1-2% faster).
 // With FIRST (the first step of a tile), every MFMA starts its accumulator
-// from 0 (each of the 64 blocks is met exactly once per step).
+// from 0 (each of the 64 blocks is met exactly once per step).  A fragment
+// register is refilled at least 8 MFMA issues after the last MFMA that read
+// it: A fragment n is last read by MFMA 8n+7 and refilled after MFMA n of the
+// next step, B fragment m last read by MFMA 63-m (the last row of blocks runs
+// right to left) and refilled after MFMA 8+m.
 template <bool READ, bool LOAD, bool FIRST = false, class Src>
 __device__ __forceinline__ void mma_step(const Frags& f, f32x4 (&acc)[8][8], Frags& nf, const char* ws,
                                            const char* xs, int aoff, int boff, const Src& src,
