@@ -30,6 +30,10 @@
  *    thread-local message for the last non-OK status.
  *  - rf_fill, rf_kv_project and rf_fill_rows allocate no device memory: all
  *    scratch comes from the caller's workspace.
+ *  - With maps in device memory and no in-fill value measurement, rf_fill and
+ *    rf_fill_q8 issue only kernel launches on hip_stream (no memory sets,
+ *    events or synchronisation) and keep no state between calls, so they may
+ *    be captured in a HIP graph and replayed.
  *  - Calls that share a plan must be issued from one host thread at a time.
  *
  * Layouts (per late layer l, all bf16):
