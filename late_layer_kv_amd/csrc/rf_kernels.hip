@@ -272,8 +272,7 @@ struct Frags {
 // blocks in serpentine order, so consecutive MFMAs always share an operand
 // fragment (the A fragment along a row, the B fragment at each turn).  Taking
 // the rows left to right every time instead ran both contractions 0.4-0.5%
-// slower (bitwise the same results; the part is power-limited and operand
-// reuse moves fewer register bytes).
+// slower (bitwise the same results; interleaved runs on one box).
 __device__ __forceinline__ constexpr int mfma_col(int i) { return ((i >> 3) & 1) ? 7 - (i & 7) : (i & 7); }
 
 __device__ __forceinline__ void read_frags(Frags& f, const char* ws, const char* xs, int aoff, int boff) {
