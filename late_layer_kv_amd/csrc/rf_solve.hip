@@ -107,7 +107,7 @@ __global__ void __launch_bounds__(256) ridge_diag_kernel(const SolveArgs a) {
 // C_il -= L_ij L_lj and Y_il -= L_ij Linv_jl.  Column j of L travels through
 // LDS in a double buffer, so the next column's quad may publish while others
 // still read this one.
-__global__ void __launch_bounds__(256) potrf_inv_kernel(double* c, int d, int k, int* flag, double* linv) {
+__device__ __forceinline__ void potrf_inv_block(double* c, int d, int k, int* flag, double* linv) {
   __shared__ double colj[2][kB];  // column j of L, by step parity
   __shared__ double rinv[2];      // 1 / L_jj, by step parity
   __shared__ double dg[kB];       // the pivots
@@ -175,6 +175,10 @@ __global__ void __launch_bounds__(256) potrf_inv_kernel(double* c, int d, int k,
   }
 }
 
+__global__ void __launch_bounds__(256) potrf_inv_kernel(double* c, int d, int k, int* flag, double* linv) {
+  potrf_inv_block(c, d, k, flag, linv);
+}
+
 // D -= sum_kk P_kk Q_kk (modes 0-2) or D = P Q (modes 3-5) on 64 x 64 blocks
 // with fp64 MFMA.  Each P and Q is staged in LDS as P[row][p] and Q[p][col]
 // (each mode fills them from its own layout) before D, which may be one of
@@ -186,9 +190,11 @@ __global__ void __launch_bounds__(256) potrf_inv_kernel(double* c, int d, int k,
 //   MODE 3 (panel, step k):           C[i][k] = C[i][k] Linv_k^T,          i > k
 //   MODE 4 (forward, step k):         R[k][cb] = Linv_k R[k][cb]
 //   MODE 5 (backward, step k):        R[k][cb] = Linv_k^T R[k][cb]
+//   MODE 0 also factors the next diagonal block: the workgroup of block
+//   (k+1, k+1) runs potrf_inv_block on it right after its own update.
 template <int MODE>
 __global__ void __launch_bounds__(256) update_kernel(double* c, int d, double* rhs, int d_out, int k, int nk, int i0,
-                                                     const double* linv) {
+                                                     double* linv, int* flag) {
   constexpr bool kReplace = MODE >= 3;
   __shared__ double ps[kB * kLd];
   __shared__ double qs[kB * kLd];
@@ -315,6 +321,14 @@ __global__ void __launch_bounds__(256) update_kernel(double* c, int d, double* r
         const int row = wr + 16 * a + 4 * v + lk, col = wc + 16 * b + l16;
         dst[static_cast<size_t>(row) * ldd + col] = kReplace ? acc[a][b][v] : old[a][b][v] - acc[a][b][v];
       }
+  // The next step's diagonal block depends on this step only through its own
+  // update, so its workgroup factors it at once (its stores are visible to the
+  // whole workgroup after the barrier) and the next panel product needs no
+  // separate factor launch in between.
+  if (MODE == 0 && blockIdx.x == 0 && blockIdx.y == 0) {
+    __syncthreads();
+    potrf_inv_block(c, d, k + 1, flag, linv);
+  }
 }
 
 // A[j][i] = float(W[i][j]) through a 32 x 32 LDS tile; b[j] = my[j] - sum_i W[i][j] mx[i]
@@ -395,13 +409,13 @@ hipError_t ridge_solve_enqueue(const RidgeSolveIn& in, double lambda, bool raw, 
   hipLaunchKernelGGL(form_kernel, dim3((di + dout + 255) / 256, di), dim3(256), 0, s, a);
   hipLaunchKernelGGL(ridge_diag_kernel, dim3(1), dim3(256), 0, s, a);
   const int T = di / kB, TC = dout / kB;
-  for (int k = 0; k < T; ++k) {
-    hipLaunchKernelGGL(potrf_inv_kernel, dim3(1), dim3(256), 0, s, a.c, di, k, a.flag, linv);
-    if (k + 1 < T) {
-      hipLaunchKernelGGL((update_kernel<3>), dim3(T - k - 1), dim3(256), 0, s, a.c, di, a.r, dout, k, 1, 0, linv);
-      hipLaunchKernelGGL((update_kernel<0>), dim3(T - k - 1, T - k - 1), dim3(256), 0, s, a.c, di, a.r, dout, k, 1, 0,
-                         linv);
-    }
+  // block 0 is factored alone; the trailing update of step k factors block k+1
+  hipLaunchKernelGGL(potrf_inv_kernel, dim3(1), dim3(256), 0, s, a.c, di, 0, a.flag, linv);
+  for (int k = 0; k + 1 < T; ++k) {
+    hipLaunchKernelGGL((update_kernel<3>), dim3(T - k - 1), dim3(256), 0, s, a.c, di, a.r, dout, k, 1, 0, linv,
+                       a.flag);
+    hipLaunchKernelGGL((update_kernel<0>), dim3(T - k - 1, T - k - 1), dim3(256), 0, s, a.c, di, a.r, dout, k, 1, 0,
+                       linv, a.flag);
   }
   // L Z = R, kSuper block rows at a time: within the group, Z_k = Linv_k R_k
   // and a rank-64 update of the group's later rows; then one update of every
@@ -409,25 +423,27 @@ hipError_t ridge_solve_enqueue(const RidgeSolveIn& in, double lambda, bool raw, 
   for (int k0 = 0; k0 < T; k0 += kSuper) {
     const int k1 = std::min(k0 + kSuper, T);
     for (int k = k0; k < k1; ++k) {
-      hipLaunchKernelGGL((update_kernel<4>), dim3(TC), dim3(256), 0, s, a.c, di, a.r, dout, k, 1, 0, linv);
+      hipLaunchKernelGGL((update_kernel<4>), dim3(TC), dim3(256), 0, s, a.c, di, a.r, dout, k, 1, 0, linv, a.flag);
       if (k + 1 < k1)
         hipLaunchKernelGGL((update_kernel<1>), dim3(TC, k1 - k - 1), dim3(256), 0, s, a.c, di, a.r, dout, k, 1, k + 1,
-                           linv);
+                           linv, a.flag);
     }
     if (k1 < T)
       hipLaunchKernelGGL((update_kernel<1>), dim3(TC, T - k1), dim3(256), 0, s, a.c, di, a.r, dout, k0, k1 - k0, k1,
-                         linv);
+                         linv, a.flag);
   }
   // L^T W = Z the same way, from the last block row up.
   for (int k1 = T; k1 > 0; k1 -= kSuper) {
     const int k0 = std::max(k1 - kSuper, 0);
     for (int k = k1 - 1; k >= k0; --k) {
-      hipLaunchKernelGGL((update_kernel<5>), dim3(TC), dim3(256), 0, s, a.c, di, a.r, dout, k, 1, 0, linv);
+      hipLaunchKernelGGL((update_kernel<5>), dim3(TC), dim3(256), 0, s, a.c, di, a.r, dout, k, 1, 0, linv, a.flag);
       if (k > k0)
-        hipLaunchKernelGGL((update_kernel<2>), dim3(TC, k - k0), dim3(256), 0, s, a.c, di, a.r, dout, k, 1, k0, linv);
+        hipLaunchKernelGGL((update_kernel<2>), dim3(TC, k - k0), dim3(256), 0, s, a.c, di, a.r, dout, k, 1, k0, linv,
+                           a.flag);
     }
     if (k0 > 0)
-      hipLaunchKernelGGL((update_kernel<2>), dim3(TC, k0), dim3(256), 0, s, a.c, di, a.r, dout, k0, k1 - k0, 0, linv);
+      hipLaunchKernelGGL((update_kernel<2>), dim3(TC, k0), dim3(256), 0, s, a.c, di, a.r, dout, k0, k1 - k0, 0, linv,
+                         a.flag);
   }
   hipLaunchKernelGGL(transpose_out_kernel, dim3(dout / 32, di / 32), dim3(256), 0, s, a.r, di, dout, a_out);
   hipLaunchKernelGGL(offset_part_kernel, dim3((dout + 255) / 256, di / kOffRows), dim3(256), 0, s, a.r, a.mx, dout,
