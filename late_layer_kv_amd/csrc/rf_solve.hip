@@ -190,32 +190,30 @@ __global__ void __launch_bounds__(256) potrf_inv_kernel(double* c, int d, int k,
 //   MODE 3 (panel, step k):           C[i][k] = C[i][k] Linv_k^T,          i > k
 //   MODE 4 (forward, step k):         R[k][cb] = Linv_k R[k][cb]
 //   MODE 5 (backward, step k):        R[k][cb] = Linv_k^T R[k][cb]
-//   MODE 0 also factors the next diagonal block: the workgroup of block
-//   (k+1, k+1) runs potrf_inv_block on it right after its own update.
+// (bx, by) is the block's place in the launch grid; false: an empty block of
+// MODE 0 (above the diagonal), nothing done.
 template <int MODE>
-__global__ void __launch_bounds__(256) update_kernel(double* c, int d, double* rhs, int d_out, int k, int nk, int i0,
-                                                     double* linv, int* flag) {
+__device__ __forceinline__ bool block_update(double* c, int d, double* rhs, int d_out, int k, int nk, int i0,
+                                             const double* linv, int bx, int by, double* ps, double* qs) {
   constexpr bool kReplace = MODE >= 3;
-  __shared__ double ps[kB * kLd];
-  __shared__ double qs[kB * kLd];
-  const int cb = blockIdx.x;  // modes 1, 2, 4, 5: column block of the right-hand side
+  const int cb = bx;  // modes 1, 2, 4, 5: column block of the right-hand side
   int i = 0;
   double* dst;
   int ldd;
   if (MODE == 0) {
-    i = k + 1 + blockIdx.y;
-    if (k + 1 + static_cast<int>(blockIdx.x) > i) return;  // (whole workgroup)
-    dst = c + (static_cast<size_t>(i) * kB) * d + (k + 1 + blockIdx.x) * kB;
+    i = k + 1 + by;
+    if (k + 1 + bx > i) return false;  // (whole workgroup)
+    dst = c + (static_cast<size_t>(i) * kB) * d + (k + 1 + bx) * kB;
     ldd = d;
   } else if (MODE == 3) {
-    i = k + 1 + blockIdx.x;
+    i = k + 1 + bx;
     dst = c + (static_cast<size_t>(i) * kB) * d + k * kB;
     ldd = d;
   } else if (MODE >= 4) {
     dst = rhs + (static_cast<size_t>(k) * kB) * d_out + cb * kB;
     ldd = d_out;
   } else {
-    i = i0 + blockIdx.y;
+    i = i0 + by;
     dst = rhs + (static_cast<size_t>(i) * kB) * d_out + cb * kB;
     ldd = d_out;
   }
@@ -239,7 +237,7 @@ __global__ void __launch_bounds__(256) update_kernel(double* c, int d, double* r
     int ldp, ldq;
     if (MODE == 0) {
       p_src = c + (static_cast<size_t>(i) * kB) * d + kc * kB;
-      q_src = c + (static_cast<size_t>(k + 1 + blockIdx.x) * kB) * d + kc * kB;  // used transposed
+      q_src = c + (static_cast<size_t>(k + 1 + bx) * kB) * d + kc * kB;  // used transposed
       ldp = ldq = d;
     } else if (MODE == 3) {
       p_src = dst;
@@ -321,13 +319,36 @@ __global__ void __launch_bounds__(256) update_kernel(double* c, int d, double* r
         const int row = wr + 16 * a + 4 * v + lk, col = wc + 16 * b + l16;
         dst[static_cast<size_t>(row) * ldd + col] = kReplace ? acc[a][b][v] : old[a][b][v] - acc[a][b][v];
       }
-  // The next step's diagonal block depends on this step only through its own
-  // update, so its workgroup factors it at once (its stores are visible to the
-  // whole workgroup after the barrier) and the next panel product needs no
-  // separate factor launch in between.
-  if (MODE == 0 && blockIdx.x == 0 && blockIdx.y == 0) {
+  return true;
+}
+
+// One launch of block_update<MODE> over its grid.  Some workgroups then take
+// the next step of the chain at once, because it depends on the launch only
+// through the block they have just written (their stores are visible to the
+// whole workgroup after the barrier), so no launch sits between the steps:
+//   MODE 0: the workgroup of block (k+1, k+1) factors it (potrf_inv_block);
+//   MODE 1 with fuse (rows k+1 .. of a group): the workgroups of row k+1 form
+//           Z_{k+1} = Linv_{k+1} R_{k+1} for their column block (MODE 4);
+//   MODE 2 with fuse (rows i0 .. k-1 of a group): the workgroups of row k-1
+//           form Linv_{k-1}^T Z_{k-1} for their column block (MODE 5).
+template <int MODE>
+__global__ void __launch_bounds__(256) update_kernel(double* c, int d, double* rhs, int d_out, int k, int nk, int i0,
+                                                     double* linv, int* flag, int fuse) {
+  __shared__ double ps[kB * kLd];
+  __shared__ double qs[kB * kLd];
+  const int bx = blockIdx.x, by = blockIdx.y;
+  if (!block_update<MODE>(c, d, rhs, d_out, k, nk, i0, linv, bx, by, ps, qs)) return;
+  if (MODE == 0 && bx == 0 && by == 0) {
     __syncthreads();
     potrf_inv_block(c, d, k + 1, flag, linv);
+  }
+  if (MODE == 1 && fuse && by == 0) {
+    __syncthreads();
+    block_update<4>(c, d, rhs, d_out, k + 1, 1, 0, linv, bx, 0, ps, qs);
+  }
+  if (MODE == 2 && fuse && by == static_cast<int>(gridDim.y) - 1) {
+    __syncthreads();
+    block_update<5>(c, d, rhs, d_out, k - 1, 1, 0, linv, bx, 0, ps, qs);
   }
 }
 
@@ -413,37 +434,34 @@ hipError_t ridge_solve_enqueue(const RidgeSolveIn& in, double lambda, bool raw, 
   hipLaunchKernelGGL(potrf_inv_kernel, dim3(1), dim3(256), 0, s, a.c, di, 0, a.flag, linv);
   for (int k = 0; k + 1 < T; ++k) {
     hipLaunchKernelGGL((update_kernel<3>), dim3(T - k - 1), dim3(256), 0, s, a.c, di, a.r, dout, k, 1, 0, linv,
-                       a.flag);
+                       a.flag, 0);
     hipLaunchKernelGGL((update_kernel<0>), dim3(T - k - 1, T - k - 1), dim3(256), 0, s, a.c, di, a.r, dout, k, 1, 0,
-                       linv, a.flag);
+                       linv, a.flag, 0);
   }
   // L Z = R, kSuper block rows at a time: within the group, Z_k = Linv_k R_k
   // and a rank-64 update of the group's later rows; then one update of every
   // row below the group with all of its pieces.
   for (int k0 = 0; k0 < T; k0 += kSuper) {
     const int k1 = std::min(k0 + kSuper, T);
-    for (int k = k0; k < k1; ++k) {
-      hipLaunchKernelGGL((update_kernel<4>), dim3(TC), dim3(256), 0, s, a.c, di, a.r, dout, k, 1, 0, linv, a.flag);
-      if (k + 1 < k1)
-        hipLaunchKernelGGL((update_kernel<1>), dim3(TC, k1 - k - 1), dim3(256), 0, s, a.c, di, a.r, dout, k, 1, k + 1,
-                           linv, a.flag);
-    }
+    hipLaunchKernelGGL((update_kernel<4>), dim3(TC), dim3(256), 0, s, a.c, di, a.r, dout, k0, 1, 0, linv, a.flag, 0);
+    for (int k = k0; k + 1 < k1; ++k)  // also Z_{k+1} = Linv_{k+1} R_{k+1}
+      hipLaunchKernelGGL((update_kernel<1>), dim3(TC, k1 - k - 1), dim3(256), 0, s, a.c, di, a.r, dout, k, 1, k + 1,
+                         linv, a.flag, 1);
     if (k1 < T)
       hipLaunchKernelGGL((update_kernel<1>), dim3(TC, T - k1), dim3(256), 0, s, a.c, di, a.r, dout, k0, k1 - k0, k1,
-                         linv, a.flag);
+                         linv, a.flag, 0);
   }
   // L^T W = Z the same way, from the last block row up.
   for (int k1 = T; k1 > 0; k1 -= kSuper) {
     const int k0 = std::max(k1 - kSuper, 0);
-    for (int k = k1 - 1; k >= k0; --k) {
-      hipLaunchKernelGGL((update_kernel<5>), dim3(TC), dim3(256), 0, s, a.c, di, a.r, dout, k, 1, 0, linv, a.flag);
-      if (k > k0)
-        hipLaunchKernelGGL((update_kernel<2>), dim3(TC, k - k0), dim3(256), 0, s, a.c, di, a.r, dout, k, 1, k0, linv,
-                           a.flag);
-    }
+    hipLaunchKernelGGL((update_kernel<5>), dim3(TC), dim3(256), 0, s, a.c, di, a.r, dout, k1 - 1, 1, 0, linv, a.flag,
+                       0);
+    for (int k = k1 - 1; k > k0; --k)  // also row k-1's Linv_{k-1}^T product
+      hipLaunchKernelGGL((update_kernel<2>), dim3(TC, k - k0), dim3(256), 0, s, a.c, di, a.r, dout, k, 1, k0, linv,
+                         a.flag, 1);
     if (k0 > 0)
       hipLaunchKernelGGL((update_kernel<2>), dim3(TC, k0), dim3(256), 0, s, a.c, di, a.r, dout, k0, k1 - k0, 0, linv,
-                         a.flag);
+                         a.flag, 0);
   }
   hipLaunchKernelGGL(transpose_out_kernel, dim3(dout / 32, di / 32), dim3(256), 0, s, a.r, di, dout, a_out);
   hipLaunchKernelGGL(offset_part_kernel, dim3((dout + 255) / 256, di / kOffRows), dim3(256), 0, s, a.r, a.mx, dout,
