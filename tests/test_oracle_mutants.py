@@ -115,6 +115,26 @@ MUTANTS = {
     "rescale_heads_interleaved": ("rescale.py", [("np.repeat(scale[np.asarray(group_of_rows)], head_dim, axis=1)",
                                                   "np.tile(scale[np.asarray(group_of_rows)], (1, head_dim))")]),
     "rescale_zero_rows_counted": ("rescale.py", [("ok = sel & (npr[:, h] > 0)", "ok = sel")]),
+    # more rotary, norm and ridge slips
+    "rope_cos_sin_swapped": ("fill.py", [("c = np.cos(ang)[:, None, :]\n    s = np.sin(ang)[:, None, :]",
+                                          "c = np.sin(ang)[:, None, :]\n    s = np.cos(ang)[:, None, :]")]),
+    "rope_theta_exponent_positive": ("fill.py", [("np.power(np.float64(theta), -2.0 * j / head_dim)",
+                                                  "np.power(np.float64(theta), 2.0 * j / head_dim)")]),
+    "rope_theta_fixed_1e4": ("fill.py", [("np.power(np.float64(theta), -2.0 * j / head_dim)",
+                                          "np.power(np.float64(10000.0), -2.0 * j / head_dim)")]),
+    "norm_eps_dropped": ("fill.py", [("np.mean(y * y, axis=-1, keepdims=True) + eps)",
+                                      "np.mean(y * y, axis=-1, keepdims=True))")]),
+    "qk_eps_dropped": ("fill.py", [("np.sqrt(ms + eps)", "np.sqrt(ms)")]),
+    "ridge_alpha_over_d_out": ("ridge.py", [("alpha = lam * np.trace(gram) / x.shape[1]",
+                                             "alpha = lam * np.trace(gram) / y.shape[1]")]),
+    "ridge_alpha_not_scaled": ("ridge.py", [("alpha = lam * np.trace(gram) / x.shape[1]", "alpha = lam")]),
+    "ridge_sums_alpha_over_d_out": ("ridge.py", [("alpha = lam * np.trace(cxx) / cxx.shape[0]",
+                                                  "alpha = lam * np.trace(cxx) / cxy.shape[1]")]),
+    "ridge_sums_cross_not_centred": ("ridge.py", [("cxy = self.sxy - self.n * np.outer(mu_s, mu_l)", "cxy = self.sxy")]),
+    "ridge_offset_mean_only": ("ridge.py", [("b = mu_l - a @ mu_s\n    return a, b", "b = mu_l\n    return a, b")]),
+    # Not planted: leaving Y uncentred in ridge_fit while X is centred.  The
+    # columns of Xc sum to zero, so Xc^T Y = Xc^T Yc and that copy computes the
+    # same map (an equivalent mutant, not a mistake).
 }
 
 PINS_FOR = {"fill.py": pins.FILL_PINS, "ridge.py": pins.RIDGE_PINS, "ceiling.py": pins.CEILING_PINS,
