@@ -5,9 +5,8 @@
 // the mean over the request's first c tail rows of each row's exact value
 // norm divided by its predicted value norm.  The value vectors come from the K/V kernel
 // (value half only, stored densely by calibration row); these two kernels
-// reduce them.  Work is tiny (c rows per request), so both are plain
-// one-thread-per-output loops with a fixed summation order: the result does not
-// depend on the launch shape.
+// reduce them, each in a fixed summation order, so the result does not depend
+// on the launch shape.
 #include <hip/hip_runtime.h>
 
 #include "rf_internal.h"
@@ -44,25 +43,34 @@ __global__ void __launch_bounds__(256) head_ratio_kernel(const RatioParams p) {
   p.ratio[g][idx] = sp > 0.0f ? sqrtf(se) / sqrtf(sp) : -1.0f;
 }
 
-// One thread per (layer, group, head): mean of the group's ratios in row order.
+// One wave per (layer, group, head): the mean of the group's ratios.  Lane t
+// adds rows t, t + 64, t + 128, ... in order; the 64 lane sums and counts then
+// combine in a fixed butterfly (a row loop per output took 150 us at 512
+// calibration rows).
 __global__ void __launch_bounds__(256) scale_mean_kernel(const float* ratio, const int32_t* group, int n, int n_kv,
                                                          int n_groups, int n_late, float* scale) {
-  const int idx = blockIdx.x * 256 + threadIdx.x;
-  if (idx >= n_late * n_groups * n_kv) return;
+  const int idx = blockIdx.x * 4 + static_cast<int>(threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  if (idx >= n_late * n_groups * n_kv) return;  // (whole wave)
   const int h = idx % n_kv;
   const int grp = (idx / n_kv) % n_groups;
   const int l = idx / (n_kv * n_groups);
   const float* r = ratio + static_cast<size_t>(l) * n * n_kv + h;
   float sum = 0.0f;
   int cnt = 0;
-  for (int m = 0; m < n; ++m) {
+  for (int m = lane; m < n; m += 64) {
     const float v = r[static_cast<size_t>(m) * n_kv];
     if (group[m] == grp && v >= 0.0f) {
       sum += v;
       ++cnt;
     }
   }
-  scale[idx] = cnt ? sum / static_cast<float>(cnt) : 1.0f;
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) {
+    sum += __shfl_xor(sum, o);
+    cnt += __shfl_xor(cnt, o);
+  }
+  if (lane == 0) scale[idx] = cnt ? sum / static_cast<float>(cnt) : 1.0f;
 }
 
 __global__ void __launch_bounds__(256) zero_i32_kernel(int32_t* p, int n) {
@@ -85,8 +93,8 @@ hipError_t launch_head_ratio(const RatioParams& p, int n_layers, hipStream_t s) 
 
 hipError_t launch_scale_mean(const float* ratio, const int32_t* group, int n, int n_kv, int n_groups, int n_late,
                              float* scale, hipStream_t s) {
-  const int total = n_late * n_groups * n_kv;
-  hipLaunchKernelGGL(scale_mean_kernel, dim3((total + 255) / 256), dim3(256), 0, s, ratio, group, n, n_kv, n_groups,
+  const int total = n_late * n_groups * n_kv;  // one wave each, four per workgroup
+  hipLaunchKernelGGL(scale_mean_kernel, dim3((total + 3) / 4), dim3(256), 0, s, ratio, group, n, n_kv, n_groups,
                      n_late, scale);
   return hipGetLastError();
 }
